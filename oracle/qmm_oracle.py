@@ -1,0 +1,254 @@
+"""Plain CPU oracle for block-quantized MUL_MAT on GGUF Q4_0 / Q8_0 weights.
+
+TEST INFRASTRUCTURE. Only the tests, the package entry point's smoke check and
+the benchmark's CPU-baseline leg may import this module. The library never
+calls it, links it or shares code with it: it is the independent definition
+the HIP kernels are checked against. It is deliberately plain and slow.
+
+Sources (the pages are cited by title and section):
+  [Bind]  "llama.cpp 源码分析：GGUF 权重与计算图的绑定" (yeyulingfeng.com),
+          section 2.3 "量化类型与数据布局" (the block_q4_0 struct and the
+          remark that blocks are dequantised inside MUL_MAT), section 3.2
+          "load_tensors()" (weight shapes {ne0 = k, ne1 = rows}).
+  [Arch]  "llama.cpp 源码完全拆解(一)：整体架构与模块全景" (pinghaoyang.com.cn),
+          section "权重装载：GGUF、mmap 与 4 bit 块": the uniform block
+          quantisation equation q(w) = clip(round(w/s) + z, qmin, qmax) with
+          reconstruction w_hat = s (q - z), the error-variance equation, the
+          legacy-family paragraph (32 weights per block, one shared scale) and
+          the quality table (Q8_0 row: 46.87 % smaller than F16).
+  [Graph] "llama.cpp 源码完全拆解(二)：ggml 计算图与内存分配器", section
+          "ggml_tensor：一个图节点的全部字段" (nb[0] = block bytes,
+          nb[1] = nb[0] * ne[0] / block_size + padding, ne[0] contiguous).
+  [Load]  "llama.cpp 源码完全拆解(三)：GGUF 装载、mmap 与张量放置", section
+          "第六步：能力校验" (the MUL_MAT probe takes F32 activations of shape
+          [ne0, 512]) and section "校验：--check-tensors 与并行验证" (rows with
+          NaN/Inf scales are rejected when a model is loaded).
+
+Readings taken where the pages are silent (also listed in the design notes):
+  * Q4_0 nibble order: low nibble of code byte j is element j, high nibble is
+    element j + 16.
+  * Q4_0 zero point z = 8 with 4-bit codes 0..15, so w = d * (q - 8); Q8_0 has
+    z = 0 and signed int8 codes, so w = d * q.
+  * Q8_0 block = fp16 d followed by 32 int8 codes (34 bytes); 34/32 bytes per
+    weight is exactly the table's 46.87 % reduction versus 16-bit weights.
+  * The scale d is stored little-endian as IEEE-754 binary16.
+  * Activations X are [n_tokens][k] with k contiguous; Y is [n_tokens][n_rows]
+    with rows contiguous, fully overwritten.
+  * Dequantisation is to fp32 (the product d * (q - z) is exact in fp32 for
+    every finite binary16 d and every code); the dot products are
+    accumulated in fp64 here.
+
+Parity pins live in tests/test_oracle_pins.py. No function here is unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Type ids follow ggml's enumeration (the pages name the types, not the ids).
+TYPE_Q4_0 = 2
+TYPE_Q8_0 = 8
+
+QK = 32  # weights per block for both legacy types ([Arch] legacy-family paragraph)
+
+BLOCK_BYTES = {
+    TYPE_Q4_0: 2 + QK // 2,  # ggml_half d + uint8_t qs[16]  ([Bind] section 2.3)
+    TYPE_Q8_0: 2 + QK,       # ggml_half d + int8 qs[32]     (reading, see header)
+}
+
+ZERO_POINT = {TYPE_Q4_0: 8, TYPE_Q8_0: 0}
+CODE_RANGE = {TYPE_Q4_0: (0, 15), TYPE_Q8_0: (-128, 127)}
+
+
+# --------------------------------------------------------------------------
+# IEEE-754 binary16 -> real number, written out from the format's definition.
+# --------------------------------------------------------------------------
+def half_bits_to_double(bits) -> np.ndarray:
+    """Value of each binary16 bit pattern, as float64 (always exact).
+
+    sign s = bit 15, exponent e = bits 14..10, fraction m = bits 9..0:
+      e == 0        -> (-1)^s * m * 2^-24            (zero and subnormals)
+      1 <= e <= 30  -> (-1)^s * (1024 + m) * 2^(e-25) (normal numbers)
+      e == 31       -> (-1)^s * inf if m == 0, else NaN
+    """
+    b = np.asarray(bits, dtype=np.uint32) & 0xFFFF
+    s = (b >> 15) & 1
+    e = ((b >> 10) & 0x1F).astype(np.int64)
+    m = (b & 0x3FF).astype(np.float64)
+    sign = np.where(s == 1, -1.0, 1.0)
+    sub = m * np.ldexp(1.0, -24)
+    nrm = np.ldexp(1024.0 + m, np.clip(e - 25, -24, 5))
+    special = np.where(m == 0.0, np.inf, np.nan)
+    mag = np.where(e == 0, sub, np.where(e == 31, special, nrm))
+    return sign * mag
+
+
+def row_bytes(qtype: int, k: int) -> int:
+    """Dense row stride nb[1] without padding: (k / 32) blocks of nb[0] bytes
+    ([Graph] ggml_tensor stride comment; [Bind] section 2.3 on ggml_nbytes)."""
+    if qtype not in BLOCK_BYTES:
+        raise ValueError(f"unsupported type {qtype}")
+    if k <= 0 or k % QK:
+        raise ValueError("k must be a positive multiple of 32")
+    return (k // QK) * BLOCK_BYTES[qtype]
+
+
+def _check_layout(W: np.ndarray, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
+    W = np.asarray(W, dtype=np.uint8)
+    dense = row_bytes(qtype, k)
+    if nb1 < dense:
+        raise ValueError("row stride smaller than the row's blocks")
+    if W.ndim != 2 or W.shape[0] != n_rows or W.shape[1] != nb1:
+        raise ValueError(f"W must be uint8 [{n_rows}][{nb1}], got {W.shape}")
+    return W
+
+
+# --------------------------------------------------------------------------
+# Block decoder ([Bind] section 2.3 struct; [Arch] reconstruction equation).
+# --------------------------------------------------------------------------
+def block_scales_and_codes(W, qtype: int, n_rows: int, k: int, nb1: int):
+    """Split every block of every row into (d as float64, integer codes q).
+
+    Returns d with shape [n_rows, k/32] and q with shape [n_rows, k] (int64),
+    where q[r, 32*b + i] is the code of element i of block b. Padding bytes
+    beyond the row's blocks are never looked at.
+    """
+    W = _check_layout(W, qtype, n_rows, k, nb1)
+    nblk = k // QK
+    bpb = BLOCK_BYTES[qtype]
+    blocks = W[:, : nblk * bpb].reshape(n_rows, nblk, bpb)
+    d_bits = blocks[:, :, 0].astype(np.uint32) | (blocks[:, :, 1].astype(np.uint32) << 8)
+    d = half_bits_to_double(d_bits)
+    payload = blocks[:, :, 2:]
+    if qtype == TYPE_Q4_0:
+        low = (payload & 0x0F).astype(np.int64)   # element j      <- low nibble of byte j
+        high = (payload >> 4).astype(np.int64)    # element j + 16 <- high nibble of byte j
+        q = np.concatenate([low, high], axis=2)   # [n_rows, nblk, 32]
+    else:
+        q = payload.view(np.int8).astype(np.int64)
+    return d, q.reshape(n_rows, k)
+
+
+def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
+    """Weights as fp32 [n_rows][k]: w = fp32(d) * fp32(q - z).
+
+    z = 8 for Q4_0 and 0 for Q8_0. The multiply is a single IEEE fp32
+    multiply; for finite d it is exact, so this is the bit-exact target.
+    """
+    d, q = block_scales_and_codes(W, qtype, n_rows, k, nb1)
+    c = (q - ZERO_POINT[qtype]).astype(np.float32)
+    d32 = np.repeat(d.astype(np.float32), QK, axis=1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return d32 * c
+
+
+def _activations_f64(X, k: int) -> np.ndarray:
+    X = np.asarray(X)
+    if X.dtype not in (np.float32, np.float16):
+        raise ValueError("activations must be float32 or float16")
+    if X.ndim != 2 or X.shape[1] != k:
+        raise ValueError(f"X must be [n_tokens][{k}]")
+    return X.astype(np.float64)  # widening is exact
+
+
+def matmul(W, qtype: int, n_rows: int, k: int, nb1: int, X):
+    """MUL_MAT of quantised W [n_rows][k] with activations X [n_tokens][k].
+
+    Returns (y, s), both float64 [n_tokens][n_rows]:
+      y[t][r] = sum_i w[r][i] * x[t][i]
+      s[t][r] = sum_i |w[r][i] * x[t][i]|   (scale of the rounding tolerance)
+    with w the fp32 dequantised weights, everything widened to fp64, and the
+    sums taken by a library fp64 matrix product.
+    """
+    Wd = dequantize(W, qtype, n_rows, k, nb1).astype(np.float64)
+    X64 = _activations_f64(X, k)
+    with np.errstate(invalid="ignore", over="ignore"):
+        y = X64 @ Wd.T
+        s = np.abs(X64) @ np.abs(Wd).T
+    return y, s
+
+
+def matmul_sampled(W, qtype: int, n_rows: int, k: int, nb1: int, X, tokens, rows):
+    """y and s for the listed (token, row) pairs only, each as a plain fp64
+    dot product of one dequantised row with one activation row."""
+    X64 = _activations_f64(X, k)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    W = _check_layout(W, qtype, n_rows, k, nb1)
+    uniq, inv = np.unique(rows, return_inverse=True)
+    Wd = dequantize(W[uniq], qtype, len(uniq), k, nb1).astype(np.float64)
+    y = np.empty(len(rows))
+    s = np.empty(len(rows))
+    with np.errstate(invalid="ignore", over="ignore"):
+        for n, (t, j) in enumerate(zip(tokens, inv)):
+            p = Wd[j] * X64[t]
+            y[n] = np.sum(p)
+            s[n] = np.sum(np.abs(p))
+    return y, s
+
+
+def within_tolerance(y, y_ref, s, rel: float = 1e-3, abs_: float = 1e-5) -> np.ndarray:
+    """Element-wise acceptance: |y - y_ref| <= rel * s + abs_, and a result
+    is non-finite exactly where the oracle's is."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    fin_ref = np.isfinite(y_ref) & np.isfinite(s)
+    fin = np.isfinite(y)
+    ok = fin == fin_ref
+    with np.errstate(invalid="ignore"):
+        close = np.abs(y - y_ref) <= rel * s + abs_
+    return ok & (close | ~fin_ref)
+
+
+# --------------------------------------------------------------------------
+# Test quantiser ([Arch] uniform block quantisation equation). Used only to
+# build round-trip inputs; the configured workloads draw codes directly.
+# --------------------------------------------------------------------------
+def _round_half_away(v: np.ndarray) -> np.ndarray:
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+def quantize_codes(w, d, qtype: int) -> np.ndarray:
+    """q = clip(round(w / d) + z, qmin, qmax) per element, for a given block
+    scale d (broadcast over the block). d == 0 gives q = z."""
+    w = np.asarray(w, dtype=np.float64)
+    d = np.asarray(d, dtype=np.float64)
+    lo, hi = CODE_RANGE[qtype]
+    z = ZERO_POINT[qtype]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(d != 0.0, _round_half_away(w / np.where(d != 0.0, d, 1.0)), 0.0)
+    return np.clip(r + z, lo, hi).astype(np.int64)
+
+
+def quantize(w, qtype: int) -> np.ndarray:
+    """Quantise fp32 weights [n_rows][k] into dense rows of blocks (uint8
+    [n_rows][row_bytes]). Scale choice: d = fp16(amax / 7) for Q4_0 and
+    fp16(amax / 127) for Q8_0, so |w / d| stays inside the code range."""
+    w = np.asarray(w, dtype=np.float32)
+    n_rows, k = w.shape
+    nblk = k // QK
+    wb = w.reshape(n_rows, nblk, QK).astype(np.float64)
+    amax = np.max(np.abs(wb), axis=2)
+    div = 7.0 if qtype == TYPE_Q4_0 else 127.0
+    d16 = (amax / div).astype(np.float16)
+    d = d16.astype(np.float64)
+    q = quantize_codes(wb, d[:, :, None], qtype)
+    return pack_blocks(d16.view(np.uint16), q, qtype)
+
+
+def pack_blocks(d_bits, q, qtype: int) -> np.ndarray:
+    """Lay out blocks: d as little-endian binary16, then the codes (Q4_0: code
+    of element j in the low nibble and of element j + 16 in the high nibble of
+    byte j; Q8_0: 32 int8 codes). q has shape [n_rows, nblk, 32]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    q = np.asarray(q, dtype=np.int64)
+    n_rows, nblk = d_bits.shape
+    bpb = BLOCK_BYTES[qtype]
+    out = np.zeros((n_rows, nblk, bpb), dtype=np.uint8)
+    out[:, :, 0] = d_bits & 0xFF
+    out[:, :, 1] = d_bits >> 8
+    if qtype == TYPE_Q4_0:
+        out[:, :, 2:] = (q[:, :, :16] | (q[:, :, 16:] << 4)).astype(np.uint8)
+    else:
+        out[:, :, 2:] = q.astype(np.int8).view(np.uint8)
+    return out.reshape(n_rows, nblk * bpb)
