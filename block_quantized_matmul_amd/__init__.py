@@ -1,1 +1,155 @@
-"""Block-quantized MUL_MAT (GGUF Q4_0 / Q8_0) for the AMD MI355X (gfx950)."""
+"""Block-quantized MUL_MAT (GGUF Q4_0 / Q8_0) for the AMD MI355X (gfx950).
+
+A thin ctypes binding over libqmm.so, whose C ABI is declared in
+include/qmm.h. The functions here carry the C names and only marshal
+arguments: torch tensors supply device pointers and the current HIP stream;
+every step of the computation runs in the library's HIP kernels. There is no
+CPU fallback: a missing library or a tensor that is not on a GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+QMM_TYPE_Q4_0 = 2
+QMM_TYPE_Q8_0 = 8
+QMM_X_F32 = 0
+QMM_X_F16 = 1
+QMM_PATH_AUTO = 0
+QMM_PATH_GEMV = 1
+QMM_PATH_GEMM = 2
+QMM_GEMV_MAX_TOKENS = 8
+
+QMM_OK = 0
+QMM_ERR_NULL = -1
+QMM_ERR_TYPE = -2
+QMM_ERR_SHAPE = -3
+QMM_ERR_STRIDE = -4
+QMM_ERR_ALIGN = -5
+QMM_ERR_HIP = -6
+QMM_ERR_PATH = -7
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
+
+_lib = None
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {qmm_status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqmm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run python -m block_quantized_matmul_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.qmm_matmul.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
+        L.qmm_matmul_x16.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
+        L.qmm_matmul_path.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, vp]
+        L.qmm_dequantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize"):
+            getattr(L, f).restype = i32
+        L.qmm_row_bytes.argtypes = [i32, i64]
+        L.qmm_row_bytes.restype = i64
+        L.qmm_supports.argtypes = [i32, i64, i64]
+        L.qmm_supports.restype = i32
+        L.qmm_status_string.argtypes = [i32]
+        L.qmm_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def qmm_status_string(status: int) -> str:
+    return lib().qmm_status_string(int(status)).decode()
+
+
+def qmm_row_bytes(ggml_type: int, k: int) -> int:
+    return int(lib().qmm_row_bytes(int(ggml_type), int(k)))
+
+
+def qmm_supports(ggml_type: int, k: int, row_stride_bytes: int) -> bool:
+    return bool(lib().qmm_supports(int(ggml_type), int(k), int(row_stride_bytes)))
+
+
+def _gpu_ptr(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _weights_geometry(W, n_rows, row_stride_bytes):
+    import torch
+    if W.dtype != torch.uint8:
+        raise TypeError("W must be a uint8 tensor of raw blocks")
+    if n_rows is None or row_stride_bytes is None:
+        if W.dim() != 2 or not W.is_contiguous():
+            raise ValueError("pass n_rows and row_stride_bytes for a W that is not a contiguous [rows][nb1] tensor")
+        n_rows, row_stride_bytes = W.shape
+    return int(n_rows), int(row_stride_bytes)
+
+
+def qmm_matmul_path(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_tokens=None, Y=None,
+                    path=QMM_PATH_AUTO, stream=None):
+    """Y[n_tokens][n_rows] = MUL_MAT(W, X) with the kernel chosen by `path`.
+    X is a GPU fp32 or fp16 tensor [n_tokens][k]; Y is allocated if None."""
+    import torch
+    n_rows, nb1 = _weights_geometry(W, n_rows, row_stride_bytes)
+    if X.dtype == torch.float32:
+        x_type = QMM_X_F32
+    elif X.dtype == torch.float16:
+        x_type = QMM_X_F16
+    else:
+        raise TypeError("X must be float32 or float16")
+    if n_tokens is None:
+        if X.dim() != 2 or not X.is_contiguous():
+            raise ValueError("X must be a contiguous [n_tokens][k] tensor")
+        n_tokens = X.shape[0]
+    if Y is None:
+        Y = torch.empty((int(n_tokens), n_rows), dtype=torch.float32, device=X.device)
+    st = lib().qmm_matmul_path(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(X, "X"), x_type,
+                               int(n_tokens), _gpu_ptr(Y, "Y"), int(path), _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_matmul_path")
+    return Y
+
+
+def qmm_matmul(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_tokens=None, Y=None, stream=None):
+    """MUL_MAT with fp32 activations (C: qmm_matmul)."""
+    import torch
+    if X.dtype != torch.float32:
+        raise TypeError("qmm_matmul takes float32 activations; use qmm_matmul_x16 for float16")
+    return qmm_matmul_path(W, ggml_type, k, X, n_rows, row_stride_bytes, n_tokens, Y, QMM_PATH_AUTO, stream)
+
+
+def qmm_matmul_x16(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_tokens=None, Y=None, stream=None):
+    """MUL_MAT with fp16 activations (C: qmm_matmul_x16)."""
+    import torch
+    if X.dtype != torch.float16:
+        raise TypeError("qmm_matmul_x16 takes float16 activations")
+    return qmm_matmul_path(W, ggml_type, k, X, n_rows, row_stride_bytes, n_tokens, Y, QMM_PATH_AUTO, stream)
+
+
+def qmm_dequantize(W, ggml_type, k, n_rows=None, row_stride_bytes=None, out=None, stream=None):
+    """The block decoder alone: fp32 [n_rows][k] (C: qmm_dequantize)."""
+    import torch
+    n_rows, nb1 = _weights_geometry(W, n_rows, row_stride_bytes)
+    if out is None:
+        out = torch.empty((n_rows, int(k)), dtype=torch.float32, device=W.device)
+    st = lib().qmm_dequantize(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(out, "out"),
+                              _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_dequantize")
+    return out

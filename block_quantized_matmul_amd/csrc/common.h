@@ -1,0 +1,98 @@
+// Device-side helpers shared by the kernels: vector types, binary16 handling
+// and in-register unpacking of GGUF block codes into exact fp16 integers.
+//
+// Block layout ([Bind] = "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section
+// 2.3): Q4_0 = binary16 d + 16 bytes of nibbles (element j in the low nibble
+// of byte j, element j + 16 in the high nibble); Q8_0 = binary16 d + 32 int8.
+// Reconstruction ([Arch] = "llama.cpp 源码完全拆解(一)：整体架构与模块全景",
+// section "权重装载：GGUF、mmap 与 4 bit 块"): w = d * (q - z), z = 8 for Q4_0
+// and 0 for Q8_0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Multi-dword global loads need only dword alignment on CDNA, so these types
+// let the compiler emit dwordx2/x3/x4 loads from 4-byte-aligned addresses.
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int QT> struct Block;
+template <> struct Block<QMM_TYPE_Q4_0> { static constexpr int bytes = 18; };
+template <> struct Block<QMM_TYPE_Q8_0> { static constexpr int bytes = 34; };
+
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
+__device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+__device__ __forceinline__ u32x2_t ld_u32x2(const uint8_t *p) {
+  u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(p);
+  return u32x2_t{v.x, v.y};
+}
+
+// Exact binary16 -> fp32 widening of a scale (hardware conversion; every
+// binary16 value, subnormals included, is representable in fp32).
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+__device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Bytes [2, 6) of the 8-byte window (lo, hi): a dword that starts 2 bytes
+// into `lo`.
+__device__ __forceinline__ uint32_t shift16(uint32_t lo, uint32_t hi) { return __builtin_amdgcn_alignbit(hi, lo, 16); }
+
+// v_perm_b32 selectors: destination bytes take source bytes 4..7 (the first
+// operand) or 0x64 from the magic second operand. Half (lo) = 0x64bb where
+// bb is the selected byte, i.e. the fp16 value 1024 + bb.
+constexpr uint32_t kMagic64 = 0x64646464u;
+constexpr uint32_t kSelB01 = 0x00050004u;  // halves (1024 + byte0, 1024 + byte1)
+constexpr uint32_t kSelB23 = 0x00070006u;  // halves (1024 + byte2, 1024 + byte3)
+
+__device__ __forceinline__ half2_t bytes01_plus_1024(uint32_t v) { return as_half2(__builtin_amdgcn_perm(v, kMagic64, kSelB01)); }
+__device__ __forceinline__ half2_t bytes23_plus_1024(uint32_t v) { return as_half2(__builtin_amdgcn_perm(v, kMagic64, kSelB23)); }
+
+// Four Q4_0 code bytes qs[j..j+3] -> eight exact fp16 values (q - 8):
+//   out[0] = (e_j, e_j+1), out[1] = (e_j+2, e_j+3)          (low nibbles)
+//   out[2] = (e_j+16, e_j+17), out[3] = (e_j+18, e_j+19)    (high nibbles)
+// Low nibble n: 1024 + n - 1032 = n - 8. High nibble m (kept in place, so the
+// byte is 16 m): (1024 + 16 m) / 16 - 72 = m - 8. Both steps are exact.
+__device__ __forceinline__ void q4_unpack(uint32_t qs, half2_t out[4]) {
+  const half2_t m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const half2_t s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t lo = qs & 0x0F0F0F0Fu;
+  const uint32_t hi = qs & 0xF0F0F0F0u;
+  out[0] = bytes01_plus_1024(lo) + m1032;
+  out[1] = bytes23_plus_1024(lo) + m1032;
+  out[2] = bytes01_plus_1024(hi) * s16 + m72;
+  out[3] = bytes23_plus_1024(hi) * s16 + m72;
+}
+
+// Four Q8_0 int8 codes -> four exact fp16 values: (c ^ 0x80) = c + 128 as an
+// unsigned byte u; 1024 + u - 1152 = c.
+__device__ __forceinline__ void q8_unpack(uint32_t qs, half2_t out[2]) {
+  const half2_t m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t u = qs ^ 0x80808080u;
+  out[0] = bytes01_plus_1024(u) + m1152;
+  out[1] = bytes23_plus_1024(u) + m1152;
+}
+
+__device__ __forceinline__ half8_t make_half8(half2_t a, half2_t b, half2_t c, half2_t d) {
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// fp32 -> fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ half2_t cvt_half2(float a, float b) { return __builtin_convertvector(float2_t{a, b}, half2_t); }
+
+}  // namespace qmm

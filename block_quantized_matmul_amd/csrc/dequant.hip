@@ -1,0 +1,64 @@
+// Block decoder: out[r][i] = fp32(d) * fp32(q - z), bit-exact.
+//
+// [Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3 (block
+// layout); [Arch] "llama.cpp 源码完全拆解(一)：整体架构与模块全景", section
+// "权重装载：GGUF、mmap 与 4 bit 块" (w_hat = s (q - z)).
+//
+// One thread writes eight consecutive outputs (one quarter of a block), so a
+// wavefront stores 2 KiB of contiguous fp32 with 16-byte stores. HBM-bound:
+// 18 (or 34) bytes read and 128 bytes written per block.
+#include "common.h"
+#include "launch.h"
+
+namespace qmm {
+
+template <int QT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ W, int64_t n_quarters, int nblk,
+                                                      int64_t nb1, float *__restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n_quarters; t += stride) {
+    const int part = static_cast<int>(t & 3);  // elements [8 part, 8 part + 8)
+    const int64_t blk = t >> 2;
+    const int64_t row = blk / nblk;
+    const int b = static_cast<int>(blk - row * nblk);
+    const uint8_t *p = W + row * nb1 + static_cast<int64_t>(b) * Block<QT>::bytes;
+    const float d = half_bits_to_float(ld_u16(p));
+    float v[8];
+    if constexpr (QT == QMM_TYPE_Q4_0) {
+      // part 0/1: low nibbles of qs[0..7] / qs[8..15]; part 2/3: high nibbles.
+      const uint8_t *q = p + 2 + 8 * (part & 1);
+      const int shift = (part & 2) ? 4 : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t two = ld_u16(q + 2 * j);
+        v[2 * j] = d * static_cast<float>(static_cast<int>((two >> shift) & 0xF) - 8);
+        v[2 * j + 1] = d * static_cast<float>(static_cast<int>((two >> (8 + shift)) & 0xF) - 8);
+      }
+    } else {
+      const uint8_t *q = p + 2 + 8 * part;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t two = ld_u16(q + 2 * j);
+        v[2 * j] = d * static_cast<float>(static_cast<int8_t>(two & 0xFF));
+        v[2 * j + 1] = d * static_cast<float>(static_cast<int8_t>(two >> 8));
+      }
+    }
+    float4_t *o = reinterpret_cast<float4_t *>(out + blk * 32 + 8 * part);
+    o[0] = float4_t{v[0], v[1], v[2], v[3]};
+    o[1] = float4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,
+                          hipStream_t stream) {
+  const int nblk = static_cast<int>(k / 32);
+  const int64_t quarters = n_rows * nblk * 4;
+  const int64_t want = (quarters + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+  const uint8_t *w = static_cast<const uint8_t *>(W);
+  if (qtype == QMM_TYPE_Q4_0)
+    return launch(dequant_kernel<QMM_TYPE_Q4_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, out);
+  return launch(dequant_kernel<QMM_TYPE_Q8_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, out);
+}
+
+}  // namespace qmm

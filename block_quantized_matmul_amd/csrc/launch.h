@@ -1,0 +1,38 @@
+// Internal launch interface between the C ABI (qmm_api.hip) and the kernel
+// translation units. Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace qmm {
+
+// hipLaunchKernel returns its status directly, so a launch error is reported
+// without touching (or clearing) any earlier sticky error of the caller.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  Args &&...args) {
+  std::tuple<KArgs...> values(std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto &...v) {
+        void *argv[] = {static_cast<void *>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, shmem, stream);
+      },
+      values);
+}
+
+hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,
+                          hipStream_t stream);
+
+// Decode kernel, 1 <= n_tokens <= QMM_GEMV_MAX_TOKENS.
+hipError_t launch_gemv(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
+                       int64_t n_tokens, float *Y, hipStream_t stream);
+
+// Matrix-core kernel, any n_tokens >= 1.
+hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
+                       int64_t n_tokens, float *Y, hipStream_t stream);
+
+}  // namespace qmm

@@ -1,0 +1,136 @@
+// C ABI entry points: argument validation, kernel choice and launch.
+//
+// The op is ggml's MUL_MAT of a block-quantized weight with activations
+// ([Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3). Row
+// strides follow the nb[1] = nb[0] * (ne[0] / block) + padding rule of
+// [Graph] "llama.cpp 源码完全拆解(二)：ggml 计算图与内存分配器", section
+// "ggml_tensor：一个图节点的全部字段". One-token and many-token calls use
+// different kernels, as the batch-of-512 capability probe of [Load]
+// "llama.cpp 源码完全拆解(三)：GGUF 装载、mmap 与张量放置", section "第六步"
+// explains backends do; the switch point is QMM_GEMV_MAX_TOKENS.
+//
+// Every check runs on the host before any HIP call, so invalid arguments are
+// reported without a GPU and nothing is enqueued. Setting QMM_TRACE=1 in the
+// environment prints each dispatch decision to stderr.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+int block_bytes(int type) {
+  switch (type) {
+    case QMM_TYPE_Q4_0: return 18;
+    case QMM_TYPE_Q8_0: return 34;
+    default: return 0;
+  }
+}
+
+bool trace_on() {
+  static const bool on = [] {
+    const char *e = getenv("QMM_TRACE");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// Checks shared by every entry point that takes a weight matrix.
+int check_weights(const void *W, int type, int64_t n_rows, int64_t k, int64_t nb1) {
+  if (W == nullptr) return QMM_ERR_NULL;
+  const int bb = block_bytes(type);
+  if (bb == 0) return QMM_ERR_TYPE;
+  if (k <= 0 || k % 32 != 0 || k > kMaxDim || n_rows < 0 || n_rows > kMaxDim) return QMM_ERR_SHAPE;
+  if (nb1 % 2 != 0 || nb1 < (k / 32) * bb) return QMM_ERR_STRIDE;
+  if (!aligned(W, 2)) return QMM_ERR_ALIGN;
+  return QMM_OK;
+}
+
+const char *type_name(int t) { return t == QMM_TYPE_Q4_0 ? "q4_0" : "q8_0"; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t qmm_row_bytes(int ggml_type, int64_t k) {
+  const int bb = block_bytes(ggml_type);
+  if (bb == 0) return QMM_ERR_TYPE;
+  if (k <= 0 || k % 32 != 0 || k > kMaxDim) return QMM_ERR_SHAPE;
+  return (k / 32) * bb;
+}
+
+int qmm_supports(int ggml_type, int64_t k, int64_t row_stride_bytes) {
+  const int bb = block_bytes(ggml_type);
+  if (bb == 0 || k <= 0 || k % 32 != 0 || k > kMaxDim) return 0;
+  return (row_stride_bytes % 2 == 0 && row_stride_bytes >= (k / 32) * bb) ? 1 : 0;
+}
+
+const char *qmm_status_string(int status) {
+  switch (status) {
+    case QMM_OK: return "QMM_OK";
+    case QMM_ERR_NULL: return "QMM_ERR_NULL: a required pointer is NULL";
+    case QMM_ERR_TYPE: return "QMM_ERR_TYPE: unsupported weight or activation type";
+    case QMM_ERR_SHAPE: return "QMM_ERR_SHAPE: k must be a positive multiple of 32; sizes must be in [0, 2^31)";
+    case QMM_ERR_STRIDE: return "QMM_ERR_STRIDE: row stride must be even and cover the row's blocks";
+    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte, X 16-byte, Y 4-byte, out 16-byte alignment";
+    case QMM_ERR_HIP: return "QMM_ERR_HIP: the HIP runtime rejected the kernel launch";
+    case QMM_ERR_PATH: return "QMM_ERR_PATH: unknown path, or GEMV forced with more than 8 tokens";
+    default: return "unknown qmm status";
+  }
+}
+
+int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, const void *X,
+                    int x_type, int64_t n_tokens, float *Y, int path, void *stream) {
+  if (X == nullptr || Y == nullptr) return QMM_ERR_NULL;
+  int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
+  if (st != QMM_OK) return st;
+  if (x_type != QMM_X_F32 && x_type != QMM_X_F16) return QMM_ERR_TYPE;
+  if (n_tokens < 0 || n_tokens > kMaxDim) return QMM_ERR_SHAPE;
+  if (path != QMM_PATH_AUTO && path != QMM_PATH_GEMV && path != QMM_PATH_GEMM) return QMM_ERR_PATH;
+  if (path == QMM_PATH_GEMV && n_tokens > QMM_GEMV_MAX_TOKENS) return QMM_ERR_PATH;
+  if (!aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+  if (n_rows == 0 || n_tokens == 0) return QMM_OK;
+
+  const bool gemv = path == QMM_PATH_GEMV || (path == QMM_PATH_AUTO && n_tokens <= QMM_GEMV_MAX_TOKENS);
+  const bool x_f16 = x_type == QMM_X_F16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (trace_on())
+    fprintf(stderr, "qmm: %s %s rows=%lld k=%lld nb1=%lld tokens=%lld x=%s align4=%d\n", gemv ? "gemv" : "gemm",
+            type_name(ggml_type), (long long)n_rows, (long long)k, (long long)row_stride_bytes, (long long)n_tokens,
+            x_f16 ? "f16" : "f32", (int)(aligned(W, 4) && row_stride_bytes % 4 == 0));
+  hipError_t e = gemv ? qmm::launch_gemv(W, ggml_type, n_rows, k, row_stride_bytes, X, x_f16, n_tokens, Y, s)
+                      : qmm::launch_gemm(W, ggml_type, n_rows, k, row_stride_bytes, X, x_f16, n_tokens, Y, s);
+  return status_of(e);
+}
+
+int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, const float *X,
+               int64_t n_tokens, float *Y, void *stream) {
+  return qmm_matmul_path(W, ggml_type, n_rows, k, row_stride_bytes, X, QMM_X_F32, n_tokens, Y, QMM_PATH_AUTO, stream);
+}
+
+int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                   const uint16_t *X, int64_t n_tokens, float *Y, void *stream) {
+  return qmm_matmul_path(W, ggml_type, n_rows, k, row_stride_bytes, X, QMM_X_F16, n_tokens, Y, QMM_PATH_AUTO, stream);
+}
+
+int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, float *out,
+                   void *stream) {
+  if (out == nullptr) return QMM_ERR_NULL;
+  int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
+  if (st != QMM_OK) return st;
+  if (!aligned(out, 16)) return QMM_ERR_ALIGN;
+  if (n_rows == 0) return QMM_OK;
+  if (trace_on())
+    fprintf(stderr, "qmm: dequant %s rows=%lld k=%lld nb1=%lld\n", type_name(ggml_type), (long long)n_rows,
+            (long long)k, (long long)row_stride_bytes);
+  return status_of(qmm::launch_dequant(W, ggml_type, n_rows, k, row_stride_bytes, out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -141,7 +141,8 @@ def config_cases() -> dict[int, list[Case]]:
             c2.append(Case(f"{TYPE_NAMES[qt]} {nm} {rows}x{k} n1", 2, qt, rows, k,
                            dense_row_bytes(qt, k), 1, tensor=3 * t + j))
     c[2] = c2
-    c[3] = [Case(f"q4_0 output 32000x4096 nb1=2560 n{n}", 3, q4, N_VOCAB, N_EMBD, 2560, n, tensor=n)
+    # one output-projection matrix, four activation batch sizes
+    c[3] = [Case(f"q4_0 output 32000x4096 nb1=2560 n{n}", 3, q4, N_VOCAB, N_EMBD, 2560, n)
             for n in (1, 2, 4, 8)]
     c[4] = [Case(f"q4_0 {nm} {rows}x{k} prefill n512 x16", 4, q4, rows, k, dense_row_bytes(q4, k), 512,
                  np.float16, tensor=j)

@@ -1,0 +1,163 @@
+/*
+ * qmm.h - C ABI of the block-quantized MUL_MAT library for AMD MI355X (gfx950).
+ *
+ * The library computes ggml's MUL_MAT of a GGUF block-quantized weight matrix
+ * with fp32 (or fp16) activations, dequantising the blocks inside the
+ * kernels. Sources, cited by page title and section:
+ *
+ *   [Bind]  "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3
+ *           "量化类型与数据布局": struct block_q4_0 { ggml_half d;
+ *           uint8_t qs[16]; } holds 32 weights; ggml_nbytes depends on the
+ *           type; blocks are read and dequantised inside MUL_MAT, then
+ *           multiplied. Section 3.2: weights are created as {ne0 = k,
+ *           ne1 = rows} (e.g. ffn_up {n_embd, n_ff}).
+ *   [Arch]  "llama.cpp 源码完全拆解(一)：整体架构与模块全景", section
+ *           "权重装载：GGUF、mmap 与 4 bit 块": block reconstruction
+ *           w_hat = s (q - z); legacy types (Q4_0 ... Q8_0) use 32 weights per
+ *           block with one shared scale; the quantised matmul kernels decode
+ *           scale and integer weights per block and multiply-add them with the
+ *           activations in registers, with no separate fp16 restore step.
+ *   [Graph] "llama.cpp 源码完全拆解(二)：ggml 计算图与内存分配器", section
+ *           "ggml_tensor：一个图节点的全部字段": nb[0] is the block size in
+ *           bytes, nb[1] = nb[0] * (ne[0] / block_size) + padding, ne[0] is
+ *           the contiguous dimension.
+ *   [Load]  "llama.cpp 源码完全拆解(三)：GGUF 装载、mmap 与张量放置", section
+ *           "第六步：能力校验": MUL_MAT takes F32 activations of shape
+ *           [ne0, n_tokens] and backends use different kernels for one token
+ *           and for many; section "校验": rows with NaN/Inf scales are
+ *           rejected when a model is loaded.
+ *
+ * Data layout (all entry points):
+ *   W  weights, n_rows rows; row r starts at W + r * row_stride_bytes and holds
+ *      k / 32 consecutive blocks. Q4_0 block = 18 bytes: little-endian binary16
+ *      d, then 16 bytes qs; element j (0..15) is the low nibble of qs[j],
+ *      element j + 16 the high nibble; weight = d * (q - 8). Q8_0 block = 34
+ *      bytes: binary16 d, then 32 int8 codes; weight = d * q. Bytes between
+ *      the last block of a row and the next row (padding) are never read.
+ *   X  activations [n_tokens][k], k contiguous (fp32, or fp16 for *_x16).
+ *   Y  output [n_tokens][n_rows] fp32, n_rows contiguous; fully overwritten.
+ *
+ * Ownership and asynchrony: every pointer is device memory owned by the
+ * caller; the library keeps no reference after a call returns, allocates
+ * nothing and holds no mutable global state, so calls on different streams
+ * may run concurrently. Work is enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream) and the call returns without waiting. A fault inside a
+ * kernel surfaces at the caller's next synchronisation. Y must not overlap W
+ * or X.
+ *
+ * Errors: arguments are validated before anything is launched; a failing
+ * check returns its negative status code and enqueues nothing. A launch that
+ * HIP rejects returns QMM_ERR_HIP. qmm_status_string() names every code.
+ *
+ * Numerics: dequantised weights are exact (fp32 d * (q - z) is exact for every
+ * finite binary16 d). The matmul accumulates in fp32. Decode-sized calls
+ * (n_tokens <= QMM_GEMV_MAX_TOKENS) round activations to fp16 and multiply
+ * them by the exact integer codes, applying d in fp32 once per block; larger
+ * calls round both the dequantised weights and the activations to fp16 for
+ * the matrix cores. Every element satisfies
+ *   |y - y_exact| <= 1e-3 * sum_i |w_i x_i| + 1e-5
+ * for activations of magnitude at most 65504 (fp16 range) and, on the
+ * matrix-core path, |d * (q - z)| <= 65504. Scales d must be finite (the
+ * loader rejects NaN/Inf scales); a non-finite d or x yields a non-finite
+ * result in every output it touches.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight types; the values follow ggml's type enumeration. */
+#define QMM_TYPE_Q4_0 2
+#define QMM_TYPE_Q8_0 8
+
+/* Activation element types for qmm_matmul_path. */
+#define QMM_X_F32 0
+#define QMM_X_F16 1
+
+/* Kernel choice for qmm_matmul_path. */
+#define QMM_PATH_AUTO 0 /* decode kernel if n_tokens <= QMM_GEMV_MAX_TOKENS, else matrix-core kernel */
+#define QMM_PATH_GEMV 1 /* decode kernel; n_tokens must be <= QMM_GEMV_MAX_TOKENS */
+#define QMM_PATH_GEMM 2 /* matrix-core (MFMA) kernel; any n_tokens */
+
+#define QMM_GEMV_MAX_TOKENS 8
+
+/* Status codes. */
+#define QMM_OK 0
+#define QMM_ERR_NULL (-1)   /* a required pointer is NULL */
+#define QMM_ERR_TYPE (-2)   /* unknown ggml_type or activation type */
+#define QMM_ERR_SHAPE (-3)  /* k not a positive multiple of 32, negative or too large sizes */
+#define QMM_ERR_STRIDE (-4) /* row_stride_bytes odd or smaller than the row's blocks */
+#define QMM_ERR_ALIGN (-5)  /* pointer alignment requirement not met */
+#define QMM_ERR_HIP (-6)    /* HIP reported an error for the launch */
+#define QMM_ERR_PATH (-7)   /* unknown path, or GEMV forced with too many tokens */
+
+/*
+ * qmm_matmul - Y = MUL_MAT(W, X) with fp32 activations ([Bind] section 2.3,
+ * [Load] section 第六步, [Arch] section 权重装载).
+ *   W                device pointer, 2-byte aligned, n_rows rows of
+ *                    row_stride_bytes bytes (see layout above)
+ *   ggml_type        QMM_TYPE_Q4_0 or QMM_TYPE_Q8_0
+ *   n_rows           ne1 of W (>= 0)
+ *   k                ne0 of W and of X; positive multiple of 32
+ *   row_stride_bytes nb1 of W; even and >= qmm_row_bytes(ggml_type, k)
+ *   X                device pointer, fp32 [n_tokens][k], 16-byte aligned
+ *   n_tokens         ne1 of X (>= 0)
+ *   Y                device pointer, fp32 [n_tokens][n_rows], 4-byte aligned
+ *   stream           hipStream_t or NULL
+ * n_rows == 0 or n_tokens == 0 returns QMM_OK and launches nothing. Sizes must
+ * satisfy n_rows, n_tokens, k < 2^31. Returns QMM_OK or a negative code.
+ */
+int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+               const float *X, int64_t n_tokens, float *Y, void *stream);
+
+/*
+ * qmm_matmul_x16 - as qmm_matmul, but X holds fp16 (IEEE binary16 bit
+ * patterns) activations [n_tokens][k], 16-byte aligned.
+ */
+int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                   const uint16_t *X, int64_t n_tokens, float *Y, void *stream);
+
+/*
+ * qmm_matmul_path - as qmm_matmul with the activation type (x_type =
+ * QMM_X_F32 or QMM_X_F16) and the kernel (path = QMM_PATH_*) chosen by the
+ * caller. QMM_PATH_GEMV with n_tokens > QMM_GEMV_MAX_TOKENS returns
+ * QMM_ERR_PATH. Meant for tests that compare the two kernels.
+ */
+int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                    const void *X, int x_type, int64_t n_tokens, float *Y, int path, void *stream);
+
+/*
+ * qmm_dequantize - the block decoder alone ([Bind] section 2.3 layout,
+ * [Arch] reconstruction equation): out[r][i] = fp32(d) * fp32(q - z) for
+ * element i of row r. out is fp32 [n_rows][k], 16-byte aligned, caller-owned.
+ * The result is bit-exact (NaN scales give NaN). n_rows == 0 is a no-op.
+ */
+int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                   float *out, void *stream);
+
+/*
+ * qmm_row_bytes - the dense row stride (k / 32) * block bytes, i.e. nb[1]
+ * without padding ([Graph] ggml_tensor stride comment). Negative status code
+ * for an unknown type or a k that is not a positive multiple of 32.
+ */
+int64_t qmm_row_bytes(int ggml_type, int64_t k);
+
+/*
+ * qmm_supports - 1 if (ggml_type, k, row_stride_bytes) is a weight layout the
+ * library accepts, else 0 (the role a backend's supports_op query plays for
+ * MUL_MAT in [Load] section 第六步). Pointer alignment is checked per call.
+ */
+int qmm_supports(int ggml_type, int64_t k, int64_t row_stride_bytes);
+
+/* qmm_status_string - a static, human-readable name for a status code. */
+const char *qmm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The shared library must load, export every function include/qmm.h declares,
+and reject each class of invalid argument with its status code before any
+HIP call. Pointers passed here are fake (never dereferenced): validation
+happens on the host first, and zero-sized calls return before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_quantized_matmul_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+Q4, Q8 = qmm.QMM_TYPE_Q4_0, qmm.QMM_TYPE_Q8_0
+
+P = ctypes.c_void_p(0x10000)   # fake, 16-byte-aligned device addresses
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qmm.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s+\*?\s*(qmm_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize",
+                            "qmm_row_bytes", "qmm_supports", "qmm_status_string"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert hasattr(qmm, name), f"python binding lacks {name}"
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name, val in re.findall(r"#define (QMM_[A-Z_0-9]+) \(?(-?\d+)\)?", text):
+        assert getattr(qmm, name) == int(val), name
+
+
+def test_row_bytes_and_supports(L):
+    assert L.qmm_row_bytes(Q4, 4096) == 2304
+    assert L.qmm_row_bytes(Q8, 4096) == 4352
+    assert L.qmm_row_bytes(Q4, 11008) == 6192
+    assert L.qmm_row_bytes(Q8, 32) == 34
+    assert L.qmm_row_bytes(3, 4096) == qmm.QMM_ERR_TYPE
+    for bad_k in (0, -32, 48, 1 << 31):
+        assert L.qmm_row_bytes(Q4, bad_k) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_supports(Q4, 4096, 2304) == 1
+    assert L.qmm_supports(Q4, 4096, 2560) == 1
+    assert L.qmm_supports(Q4, 96, 54) == 1
+    assert L.qmm_supports(Q4, 4096, 2303) == 0
+    assert L.qmm_supports(Q4, 4096, 2302) == 0
+    assert L.qmm_supports(Q8, 48, 100) == 0
+    assert L.qmm_supports(7, 4096, 4096) == 0
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        s = qmm.qmm_status_string(code)
+        assert s.startswith("QMM_OK" if code == 0 else "QMM_ERR_")
+    assert qmm.qmm_status_string(-99) == "unknown qmm status"
+
+
+def _mm(L, W=P, t=Q4, rows=16, k=64, nb1=36, X=P2, xt=qmm.QMM_X_F32, n=1, Y=P3, path=0):
+    return L.qmm_matmul_path(W, t, rows, k, nb1, X, xt, n, Y, path, NULL)
+
+
+def test_validation_codes(L):
+    E = qmm
+    assert _mm(L, W=NULL) == E.QMM_ERR_NULL
+    assert _mm(L, X=NULL) == E.QMM_ERR_NULL
+    assert _mm(L, Y=NULL) == E.QMM_ERR_NULL
+    assert _mm(L, t=0) == E.QMM_ERR_TYPE
+    assert _mm(L, t=3) == E.QMM_ERR_TYPE
+    assert _mm(L, xt=2) == E.QMM_ERR_TYPE
+    assert _mm(L, k=0) == E.QMM_ERR_SHAPE
+    assert _mm(L, k=40) == E.QMM_ERR_SHAPE
+    assert _mm(L, k=-64) == E.QMM_ERR_SHAPE
+    assert _mm(L, rows=-1) == E.QMM_ERR_SHAPE
+    assert _mm(L, rows=1 << 31) == E.QMM_ERR_SHAPE
+    assert _mm(L, n=-1) == E.QMM_ERR_SHAPE
+    assert _mm(L, nb1=35) == E.QMM_ERR_STRIDE
+    assert _mm(L, nb1=34) == E.QMM_ERR_STRIDE
+    assert _mm(L, t=Q8, nb1=36) == E.QMM_ERR_STRIDE
+    assert _mm(L, W=ctypes.c_void_p(0x10001)) == E.QMM_ERR_ALIGN
+    assert _mm(L, X=ctypes.c_void_p(0x20004)) == E.QMM_ERR_ALIGN
+    assert _mm(L, Y=ctypes.c_void_p(0x30002)) == E.QMM_ERR_ALIGN
+    assert _mm(L, path=3) == E.QMM_ERR_PATH
+    assert _mm(L, path=qmm.QMM_PATH_GEMV, n=9) == E.QMM_ERR_PATH
+
+
+def test_zero_sized_calls_launch_nothing(L):
+    # 2-byte-aligned W and a padded odd stride are valid; nothing is launched.
+    assert _mm(L, rows=0) == qmm.QMM_OK
+    assert _mm(L, n=0) == qmm.QMM_OK
+    assert _mm(L, W=ctypes.c_void_p(0x10002), nb1=38, n=0) == qmm.QMM_OK
+    assert _mm(L, path=qmm.QMM_PATH_GEMM, n=0) == qmm.QMM_OK
+    assert L.qmm_matmul(P, Q8, 0, 64, 68, P2, 4, P3, NULL) == qmm.QMM_OK
+    assert L.qmm_matmul_x16(P, Q8, 5, 64, 68, P2, 0, P3, NULL) == qmm.QMM_OK
+    assert L.qmm_dequantize(P, Q4, 0, 64, 36, P2, NULL) == qmm.QMM_OK
+
+
+def test_dequantize_validation(L):
+    assert L.qmm_dequantize(NULL, Q4, 4, 64, 36, P2, NULL) == qmm.QMM_ERR_NULL
+    assert L.qmm_dequantize(P, Q4, 4, 64, 36, NULL, NULL) == qmm.QMM_ERR_NULL
+    assert L.qmm_dequantize(P, 9, 4, 64, 36, P2, NULL) == qmm.QMM_ERR_TYPE
+    assert L.qmm_dequantize(P, Q4, 4, 63, 36, P2, NULL) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_dequantize(P, Q4, 4, 64, 30, P2, NULL) == qmm.QMM_ERR_STRIDE
+    assert L.qmm_dequantize(P, Q4, 4, 64, 36, ctypes.c_void_p(0x20008), NULL) == qmm.QMM_ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    W = torch.zeros((4, 36), dtype=torch.uint8)
+    X = torch.zeros((1, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        qmm.qmm_matmul(W, Q4, 64, X, Y=torch.empty((1, 4)))
+    with pytest.raises(TypeError):
+        qmm.qmm_dequantize(W, Q4, 64, out=torch.empty((4, 64)))

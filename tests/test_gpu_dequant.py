@@ -1,0 +1,68 @@
+"""Block decoder parity: qmm_dequantize must equal the oracle bit for bit
+(NaN scales: NaN positions must match)."""
+import numpy as np
+import pytest
+
+import oracle.qmm_oracle as O
+from block_quantized_matmul_amd import synth
+from gpu_util import assert_bitwise, run_dequant, say
+
+pytestmark = pytest.mark.gpu
+Q4, Q8 = O.TYPE_Q4_0, O.TYPE_Q8_0
+
+
+def _check(Wnp, qtype, k, offset=0, what=""):
+    rows, nb1 = Wnp.shape
+    say(f"dequant {what} type={qtype} rows={rows} k={k} nb1={nb1} offset={offset}")
+    got = run_dequant(Wnp, qtype, k, offset)
+    want = O.dequantize(Wnp, qtype, rows, k, nb1)
+    assert_bitwise(got, want, what)
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_every_scale_pattern(qtype):
+    # 65536 blocks, block i has scale bits i; codes seeded random bytes.
+    rng = np.random.Generator(np.random.PCG64(100 + qtype))
+    rows, k = 2048, 1024
+    d = np.arange(65536, dtype=np.uint16).reshape(rows, 32)
+    payload = 16 if qtype == Q4 else 32
+    codes = rng.integers(0, 256, size=(rows, 32, payload), dtype=np.uint8)
+    W = synth.assemble_rows(d, codes, synth.dense_row_bytes(qtype, k))
+    _check(W, qtype, k, what="all scales")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_every_code_byte(qtype):
+    payload = 16 if qtype == Q4 else 32
+    nblk = 256 // payload * 8
+    rows, k = 4, nblk * 32
+    d = np.array([0x3C00, 0xB800, 0x0001, 0x7BFF], np.uint16)[:, None].repeat(nblk, 1)
+    codes = (np.arange(nblk * payload) % 256).astype(np.uint8).reshape(1, nblk, payload).repeat(rows, 0)
+    W = synth.assemble_rows(d, codes, synth.dense_row_bytes(qtype, k))
+    _check(W, qtype, k, what="all code bytes")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_config_weights(cfg):
+    seen = set()
+    for case in synth.config_cases()[cfg]:
+        key = (case.qtype, case.rows, case.k, case.nb1)
+        if key in seen:
+            continue
+        seen.add(key)
+        _check(case.weights(), case.qtype, case.k, what=case.name)
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("k,extra,offset", [(32, 0, 0), (96, 0, 0), (96, 2, 2), (160, 6, 0), (512, 30, 2),
+                                            (4096, 256, 0)])
+def test_strides_alignment_and_ragged(qtype, k, extra, offset):
+    rng = np.random.Generator(np.random.PCG64(7 * k + extra + qtype))
+    rows = 37
+    nb1 = synth.dense_row_bytes(qtype, k) + extra
+    W = synth.make_weights(qtype, rows, k, nb1, rng, d_lo=-2.0, d_hi=2.0)
+    _check(W, qtype, k, offset, what=f"k={k} pad={extra}")
+    if extra:  # padding must not matter
+        W2 = W.copy()
+        W2[:, nb1 - extra:] ^= 0xFF
+        _check(W2, qtype, k, offset, what=f"k={k} pad={extra} refilled")

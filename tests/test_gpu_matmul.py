@@ -1,0 +1,201 @@
+"""MUL_MAT parity on the GPU: the decode kernel (GEMV) and the matrix-core
+kernel (GEMM) against the oracle, element by element, within
+|y - y_ref| <= 1e-3 * sum|w x| + 1e-5, plus closed-form invariants that hold
+bitwise, and the configured workloads at their full sizes."""
+import numpy as np
+import pytest
+
+import block_quantized_matmul_amd as qmm
+import oracle.qmm_oracle as O
+from block_quantized_matmul_amd import synth
+from gpu_util import assert_bitwise, assert_close_to_oracle, run_matmul, say
+
+pytestmark = pytest.mark.gpu
+Q4, Q8 = O.TYPE_Q4_0, O.TYPE_Q8_0
+GEMV, GEMM, AUTO = qmm.QMM_PATH_GEMV, qmm.QMM_PATH_GEMM, qmm.QMM_PATH_AUTO
+
+
+def _inputs(qtype, rows, k, n, extra=0, seed=0, xdt=np.float32, d_lo=0.001, d_hi=0.05):
+    rng = np.random.Generator(np.random.PCG64([seed, qtype, rows, k, n, extra]))
+    nb1 = synth.dense_row_bytes(qtype, k) + extra
+    W = synth.make_weights(qtype, rows, k, nb1, rng, d_lo, d_hi)
+    X = synth.make_activations(n, k, rng, xdt)
+    return W, X
+
+
+def _parity(W, qtype, k, X, path, offset=0, what=""):
+    say(f"matmul {what} type={qtype} rows={W.shape[0]} k={k} nb1={W.shape[1]} n={X.shape[0]} "
+        f"x={X.dtype} path={path} offset={offset}")
+    Y = run_matmul(W, qtype, k, X, path, offset)
+    return assert_close_to_oracle(Y, W, qtype, k, X, what)
+
+
+# ------------------------------------------------------------ small shapes, every kernel variant
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("xdt", [np.float32, np.float16])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8])
+def test_gemv_ragged(qtype, xdt, n):
+    for rows, k, extra, offset in ((1, 32, 0, 0), (37, 96, 0, 0), (37, 96, 2, 2), (300, 512, 4, 0),
+                                   (17, 4096, 256, 0), (33, 11008, 0, 2)):
+        W, X = _inputs(qtype, rows, k, n, extra, xdt=xdt)
+        _parity(W, qtype, k, X, GEMV, offset, f"gemv rows={rows} k={k}")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("xdt", [np.float32, np.float16])
+@pytest.mark.parametrize("n", [1, 9, 16, 37, 128, 200])
+def test_gemm_ragged(qtype, xdt, n):
+    for rows, k, extra, offset in ((1, 32, 0, 0), (37, 96, 2, 2), (130, 160, 0, 0), (300, 512, 4, 0),
+                                   (129, 4096, 256, 2)):
+        W, X = _inputs(qtype, rows, k, n, extra, xdt=xdt)
+        _parity(W, qtype, k, X, GEMM, offset, f"gemm rows={rows} k={k}")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_dispatch_and_cross_check(qtype):
+    """AUTO picks GEMV up to 8 tokens; for n = 1..16 both kernels agree with
+    the oracle (and therefore with each other) on the same inputs."""
+    for n in range(1, 17):
+        W, X = _inputs(qtype, 200, 1024, n, seed=n)
+        ya = run_matmul(W, qtype, 1024, X, AUTO)
+        yg = run_matmul(W, qtype, 1024, X, GEMM)
+        expect = run_matmul(W, qtype, 1024, X, GEMV) if n <= 8 else yg
+        assert_bitwise(ya, expect, f"auto n={n}")
+        assert_close_to_oracle(yg, W, qtype, 1024, X, f"gemm n={n}")
+        assert_close_to_oracle(ya, W, qtype, 1024, X, f"auto n={n}")
+
+
+# ------------------------------------------------------------ closed-form invariants
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("path,n", [(GEMV, 1), (GEMV, 8), (GEMM, 24)])
+def test_one_hot_activation(qtype, path, n):
+    """x = e_j: every other product is an exact zero, so y equals the
+    dequantised weight (decode kernel) or its fp16 rounding (matrix cores)."""
+    rows, k = 70, 512
+    W, _ = _inputs(qtype, rows, k, 1, 6, d_lo=-1.5, d_hi=1.5)
+    cols = np.array([0, 1, 15, 16, 31, 32, 250, k - 1] * 3)[:n]
+    X = np.zeros((n, k), np.float32)
+    X[np.arange(n), cols] = 1.0
+    say(f"one-hot type={qtype} path={path} n={n}")
+    Y = run_matmul(W, qtype, k, X, path)
+    w = O.dequantize(W, qtype, rows, k, W.shape[1])[:, cols].T
+    if path == GEMM:
+        w = w.astype(np.float16).astype(np.float32)
+    # a zero weight may be -0.0 (negative d times code 0); sums give +0.0
+    assert_bitwise(Y + np.float32(0.0), w + np.float32(0.0), "one-hot")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("path,n", [(GEMV, 3), (GEMM, 40)])
+def test_zero_codes_scaling_permutation_padding_determinism(qtype, path, n):
+    rows, k = 150, 1024
+    W, X = _inputs(qtype, rows, k, n, 10)
+    # keep |x| away from the fp16 subnormal range so fp16(4 x) == 4 fp16(x)
+    X = np.where(np.abs(X) < 1e-3, np.float32(1e-3), X).astype(np.float32)
+    say(f"invariants type={qtype} path={path} n={n}")
+    y = run_matmul(W, qtype, k, X, path)
+    # determinism
+    assert_bitwise(run_matmul(W, qtype, k, X, path), y, "rerun")
+    # y(2^e x) = 2^e y(x)
+    assert_bitwise(run_matmul(W, qtype, k, X * np.float32(4.0), path), 4.0 * y, "scale x by 4")
+    # permuting rows permutes outputs
+    perm = np.random.default_rng(5).permutation(rows)
+    assert_bitwise(run_matmul(W[perm], qtype, k, X, path), y[:, perm], "row permutation")
+    # padding bytes are never read; a dense copy gives the same result
+    W2 = W.copy()
+    W2[:, -10:] ^= 0xA5
+    assert_bitwise(run_matmul(W2, qtype, k, X, path), y, "padding refill")
+    dense = synth.dense_row_bytes(qtype, k)
+    assert_bitwise(run_matmul(np.ascontiguousarray(W[:, :dense]), qtype, k, X, path), y, "dense copy")
+    # zero codes (q = z) give exactly zero
+    Wz = W.copy().reshape(rows, -1)
+    bpb = O.BLOCK_BYTES[qtype]
+    blk = Wz[:, :dense].reshape(rows, -1, bpb)
+    blk[:, :, 2:] = 0x88 if qtype == Q4 else 0
+    Wz[:, :dense] = blk.reshape(rows, dense)
+    yz = run_matmul(Wz, qtype, k, X, path)
+    assert np.all(yz == 0.0)
+
+
+@pytest.mark.parametrize("path,n", [(GEMV, 2), (GEMM, 20)])
+def test_nonfinite_scale_propagates(path, n):
+    rows, k = 20, 256
+    W, X = _inputs(Q4, rows, k, n)
+    W[3, 0:2] = [0x00, 0x7E]        # NaN scale, block 0 of row 3
+    W[7, 18 * 2:18 * 2 + 2] = [0x00, 0x7C]  # +inf scale, block 2 of row 7
+    say(f"non-finite scales path={path}")
+    Y = run_matmul(W, Q4, k, X, path)
+    assert np.all(np.isnan(Y[:, 3]))
+    assert not np.any(np.isfinite(Y[:, 7]))
+    others = np.delete(np.arange(rows), [3, 7])
+    assert np.all(np.isfinite(Y[:, others]))
+    assert_close_to_oracle(Y[:, others], W[others], Q4, k, X, "finite rows")
+
+
+# ------------------------------------------------------------ configured workloads, full size
+def _run_case(case, path=AUTO):
+    W, X = case.weights(), case.activations()
+    return _parity(W, case.qtype, case.k, X, path, 0, case.name)
+
+
+def test_config1_single_gemv():
+    for case in synth.config_cases()[1]:
+        _run_case(case)
+
+
+def test_config2_decode_projections():
+    for case in synth.config_cases()[2]:
+        _run_case(case)
+
+
+def test_config3_output_projection_padded():
+    cases = synth.config_cases()[3]
+    W = cases[0].weights()
+    for case in cases:
+        X = case.activations()
+        say(f"{case.name}")
+        Y = run_matmul(W, case.qtype, case.k, X)
+        rng = np.random.default_rng(case.n_tokens)
+        rows = rng.integers(0, case.rows, 2048)
+        toks = rng.integers(0, case.n_tokens, 2048)
+        y_ref, s = O.matmul_sampled(W, case.qtype, case.rows, case.k, case.nb1, X, toks, rows)
+        assert O.within_tolerance(Y[toks, rows], y_ref, s).all(), case.name
+    # padding must be ignored: refill it and compare bitwise at n = 8
+    W2 = W.copy()
+    W2[:, 2304:] = 255 - W2[:, 2304:]
+    X = cases[-1].activations()
+    assert_bitwise(run_matmul(W2, Q4, 4096, X), run_matmul(W, Q4, 4096, X), "padding refill")
+
+
+def test_config4_prefill_gemm():
+    for case in synth.config_cases()[4]:
+        W, X = case.weights(), case.activations()
+        say(case.name)
+        Y16 = run_matmul(W, case.qtype, case.k, X)        # fp16 activations (qmm_matmul_x16)
+        Y32 = run_matmul(W, case.qtype, case.k, X.astype(np.float32))  # the same values as fp32
+        assert_bitwise(Y32, Y16, "fp32 copy of fp16 activations")
+        rng = np.random.default_rng(case.rows)
+        rows = rng.integers(0, case.rows, 4096)
+        toks = rng.integers(0, case.n_tokens, 4096)
+        y_ref, s = O.matmul_sampled(W, case.qtype, case.rows, case.k, case.nb1, X, toks, rows)
+        assert O.within_tolerance(Y16[toks, rows], y_ref, s).all(), case.name
+    c = synth.config_cases()[4][0]
+    _run_case(c)  # the 4096 x 4096 case element by element
+
+
+@pytest.mark.parametrize("n_tokens", [1, 2048])
+def test_config5_stack_layers_sampled(n_tokens):
+    """Full-size layer tensors of the 32-layer stack (layers 0 and 31), in the
+    launch configuration the benchmark times, checked on sampled outputs."""
+    for case in synth.stack_cases(n_tokens):
+        if case.layer not in (0, 31):
+            continue
+        W, X = case.weights(), case.activations()
+        say(case.name)
+        Y = run_matmul(W, case.qtype, case.k, X)
+        rng = np.random.default_rng(case.layer * 10 + case.tensor)
+        m = 4096
+        rows = rng.integers(0, case.rows, m)
+        toks = rng.integers(0, case.n_tokens, m)
+        y_ref, s = O.matmul_sampled(W, case.qtype, case.rows, case.k, case.nb1, X, toks, rows)
+        assert O.within_tolerance(Y[toks, rows], y_ref, s).all(), case.name
