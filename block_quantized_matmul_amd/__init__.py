@@ -34,6 +34,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 _lib = None
 
 
+class qmm_matmul_desc(ctypes.Structure):
+    """Mirror of the C struct qmm_matmul_desc (include/qmm.h)."""
+    _fields_ = [("W", ctypes.c_void_p), ("ggml_type", ctypes.c_int), ("n_rows", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("row_stride_bytes", ctypes.c_int64), ("X", ctypes.c_void_p),
+                ("x_type", ctypes.c_int), ("n_tokens", ctypes.c_int64), ("Y", ctypes.c_void_p)]
+
+
 class QmmError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -53,7 +60,8 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_x16.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
         L.qmm_matmul_path.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, vp]
         L.qmm_dequantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
-        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize"):
+        L.qmm_matmul_batch.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp]
+        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch"):
             getattr(L, f).restype = i32
         L.qmm_row_bytes.argtypes = [i32, i64]
         L.qmm_row_bytes.restype = i64
@@ -153,3 +161,25 @@ def qmm_dequantize(W, ggml_type, k, n_rows=None, row_stride_bytes=None, out=None
     if st != QMM_OK:
         raise QmmError(st, "qmm_dequantize")
     return out
+
+
+def qmm_matmul_batch(items, stream=None):
+    """Independent MUL_MATs in one call (C: qmm_matmul_batch).
+
+    items: sequence of (W, ggml_type, k, X, Y) with W a contiguous uint8
+    [rows][nb1] GPU tensor, X a contiguous fp32/fp16 [n_tokens][k] GPU tensor
+    and Y a preallocated fp32 [n_tokens][rows] GPU tensor. Returns the Ys.
+    """
+    import torch
+    arr = (qmm_matmul_desc * max(1, len(items)))()
+    for i, (W, t, k, X, Y) in enumerate(items):
+        rows, nb1 = _weights_geometry(W, None, None)
+        if X.dtype not in (torch.float32, torch.float16):
+            raise TypeError("X must be float32 or float16")
+        arr[i] = qmm_matmul_desc(_gpu_ptr(W, "W").value, int(t), rows, int(k), nb1, _gpu_ptr(X, "X").value,
+                                 QMM_X_F16 if X.dtype == torch.float16 else QMM_X_F32, int(X.shape[0]),
+                                 _gpu_ptr(Y, "Y").value)
+    st = lib().qmm_matmul_batch(arr, len(items), _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_matmul_batch")
+    return [it[4] for it in items]

@@ -1,4 +1,6 @@
-// Decode MUL_MAT (1 <= n_tokens <= 8): y[t][r] = sum_b d_rb * sum_i (q - z) x[t][32 b + i].
+// Decode MUL_MAT (1 <= n_tokens <= 8), general layouts: any even row stride and
+// 2-byte-aligned W. (16-byte-aligned layouts take the streaming kernel in
+// gemv_stream.hip.) y[t][r] = sum_b d_rb * sum_i (q - z) x[t][32 b + i].
 //
 // What is computed: [Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section
 // 2.3 (blocks are dequantised inside MUL_MAT, then multiplied) and [Arch]
@@ -7,35 +9,41 @@
 // per block and multiply-add them with activations in registers).
 //
 // Design (MI355X, gfx950). The kernel is bound by HBM: every weight byte is
-// read exactly once, with dword-aligned vector loads that together cover each
-// row contiguously. One workgroup owns 16 rows; its 8 wavefronts split the
+// read exactly once. One workgroup owns 16 rows; its 8 wavefronts split the
 // row's blocks into contiguous ranges and meet in LDS at the end, in a fixed
 // order (no atomics, so results are bitwise reproducible).
 //
+// Latency hiding: each wavefront keeps kRing units of weights in flight on the
+// vector-memory counter. The activations are staged once per workgroup into
+// LDS as fp16, already in MFMA operand order, so reading them never waits on
+// (and never drains) the weight stream. Activations that do not fit the LDS
+// budget are staged in chunks of k.
+//
 // The dot products run on the matrix cores: one v_mfma_f32_16x16x32_f16 per
 // block covers 16 rows x 32 weights x 16 token slots. The B operand holds the
-// integer codes (q - z), which are exact in fp16; the A operand holds the
-// activations rounded to fp16; each lane then applies its row's block scale d
-// in fp32 (acc += d * partial), so the weights enter the sum exactly. Lane l
-// of the B operand serves row l % 16 and the 8 elements of block-slice
-// l / 16; the A operand uses the same element order, so each MFMA is exactly
-// that block's partial dot product. D holds token 4 (l / 16) + e, row l % 16
-// in element e of lane l.
+// integer codes (q - z), exact in fp16; the A operand holds the activations
+// rounded to fp16; each lane then applies its row's block scale d in fp32
+// (acc += d * partial), so the weights enter the sum exactly. Lane l of the B
+// operand serves row l % 16 and 8 elements of block-slice l / 16; the A
+// operand uses the same element order, so each MFMA is exactly that block's
+// partial dot product. D holds token 4 (l / 16) + e, row l % 16 in element e
+// of lane l.
 //
-// Memory access for the common case (row starts 4-byte aligned): a unit is a
-// pair of blocks (36 bytes Q4_0, 68 bytes Q8_0). The four lanes of a row load
-// overlapping dword windows that together cover the pair once; the two
-// scales are forwarded from the lanes that loaded them with ds_bpermute. Rows
-// whose start is only 2-byte aligned (odd block count with dense rows, or a
-// 2-byte-aligned W) take 16-bit loads, one block per unit.
+// Weight access (row start 4-byte aligned): a unit is a pair of blocks (36
+// bytes Q4_0, 68 bytes Q8_0). The four lanes of a row load overlapping dword
+// windows that together cover the pair once; the two scales are forwarded
+// from the lanes that loaded them with ds_bpermute. Rows whose start is only
+// 2-byte aligned take 16-bit loads, one block per unit.
 #include "common.h"
+#include "gemv_common.h"
 #include "launch.h"
 
 namespace qmm {
 
 constexpr int kGemvWaves = 8;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kPrefetch = 2;  // units in flight ahead of the one being computed
+constexpr int kRing = 8;                  // weight units in flight per wavefront
+constexpr int kXLdsBudget = 64 * 1024;    // bytes of LDS for staged activations
 
 template <int QT, bool ALIGN4> struct GemvRaw;
 // Q4_0 pair: dwords g, g + 1 (even block, codes start 2 bytes in) and 5 + g (odd block).
@@ -74,131 +82,106 @@ __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int 
   return r;
 }
 
-// A-operand (activations) for block `blk`, in the element order of the
-// B-operand built by gemv_codes(). Token rows beyond n_tokens were clamped to
-// a valid row by the caller; their D entries are never stored.
-template <int QT, bool XF16>
-__device__ __forceinline__ half8_t gemv_x(const void *xrow, int blk, int g) {
-  if constexpr (QT == QMM_TYPE_Q4_0) {
-    const int o = 32 * blk + 4 * g;  // elements o..o+3 and o+16..o+19
-    if constexpr (XF16) {
-      const half4_t a = *reinterpret_cast<const half4_t *>(static_cast<const _Float16 *>(xrow) + o);
-      const half4_t b = *reinterpret_cast<const half4_t *>(static_cast<const _Float16 *>(xrow) + o + 16);
-      return half8_t{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    } else {
-      const float4_t a = *reinterpret_cast<const float4_t *>(static_cast<const float *>(xrow) + o);
-      const float4_t b = *reinterpret_cast<const float4_t *>(static_cast<const float *>(xrow) + o + 16);
-      return make_half8(cvt_half2(a.x, a.y), cvt_half2(a.z, a.w), cvt_half2(b.x, b.y), cvt_half2(b.z, b.w));
-    }
-  } else {
-    const int o = 32 * blk + 8 * g;  // elements o..o+7
-    if constexpr (XF16) {
-      return *reinterpret_cast<const half8_t *>(static_cast<const _Float16 *>(xrow) + o);
-    } else {
-      const float4_t a = *reinterpret_cast<const float4_t *>(static_cast<const float *>(xrow) + o);
-      const float4_t b = *reinterpret_cast<const float4_t *>(static_cast<const float *>(xrow) + o + 4);
-      return make_half8(cvt_half2(a.x, a.y), cvt_half2(a.z, a.w), cvt_half2(b.x, b.y), cvt_half2(b.z, b.w));
-    }
-  }
-}
-
-// B-operand: this lane's 8 exact codes (q - z) of one block.
-template <int QT> __device__ __forceinline__ half8_t gemv_codes(uint32_t q0, uint32_t q1);
-template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q4_0>(uint32_t q0, uint32_t) {
-  half2_t h[4];
-  q4_unpack(q0, h);
-  return make_half8(h[0], h[1], h[2], h[3]);
-}
-template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q8_0>(uint32_t q0, uint32_t q1) {
-  half2_t lo[2], hi[2];
-  q8_unpack(q0, lo);
-  q8_unpack(q1, hi);
-  return make_half8(lo[0], lo[1], hi[0], hi[1]);
-}
-
-template <int NT>
-__device__ __forceinline__ void gemv_block(float acc[4], half8_t xop, half8_t wop, uint32_t d_bits) {
-  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
-  const float4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, zero, 0, 0, 0);
-  const float d = half_bits_to_float(d_bits);
-  constexpr int E = NT < 4 ? NT : 4;
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(d, part[e], acc[e]);
-}
-
-template <int QT, int NT, bool XF16, bool ALIGN4>
-__device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4> &r, const void *xrow, int u, int g,
-                                          int r16) {
+// One unit: blocks 2u, 2u + 1 (pairs) or block u (single), global indices;
+// xs is the staged chunk starting at block b_lo.
+template <int QT, int NT, bool ALIGN4>
+__device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4> &r, const half8_t *xs, int u,
+                                          int b_lo, int g, int r16, int xslot) {
   if constexpr (ALIGN4) {
+    const half8_t xe = xs[(4 * (2 * u - b_lo) + g) * NT + xslot];
+    const half8_t xo = xs[(4 * (2 * u + 1 - b_lo) + g) * NT + xslot];
     if constexpr (QT == QMM_TYPE_Q4_0) {
       // Even block: scale = low half of dword 0 (lane g = 0's a.x); odd block:
       // scale = high half of dword 4 (lane g = 3's a.y).
       const uint32_t de = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * r16, static_cast<int>(r.a.x)));
       const uint32_t dd = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * (r16 + 48), static_cast<int>(r.a.y)));
-      gemv_block<NT>(acc, gemv_x<QT, XF16>(xrow, 2 * u, g), gemv_codes<QT>(shift16(r.a.x, r.a.y), 0), de & 0xFFFFu);
-      gemv_block<NT>(acc, gemv_x<QT, XF16>(xrow, 2 * u + 1, g), gemv_codes<QT>(r.b, 0), dd >> 16);
+      gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(r.a.x, r.a.y), 0), de & 0xFFFFu);
+      gemv_block<NT>(acc, xo, gemv_codes<QT>(r.b, 0), dd >> 16);
     } else {
       // Even block: scale = low half of dword 0 (lane g = 0's a0); odd block
       // starts at byte 34: scale = high half of dword 8 (lane g = 3's a2).
       const uint32_t de = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * r16, static_cast<int>(r.a0)));
       const uint32_t dd = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * (r16 + 48), static_cast<int>(r.a2)));
-      gemv_block<NT>(acc, gemv_x<QT, XF16>(xrow, 2 * u, g),
-                     gemv_codes<QT>(shift16(r.a0, r.a1), shift16(r.a1, r.a2)), de & 0xFFFFu);
-      gemv_block<NT>(acc, gemv_x<QT, XF16>(xrow, 2 * u + 1, g), gemv_codes<QT>(r.b.x, r.b.y), dd >> 16);
+      gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(r.a0, r.a1), shift16(r.a1, r.a2)), de & 0xFFFFu);
+      gemv_block<NT>(acc, xo, gemv_codes<QT>(r.b.x, r.b.y), dd >> 16);
     }
   } else {
+    const half8_t x = xs[(4 * (u - b_lo) + g) * NT + xslot];
     if constexpr (QT == QMM_TYPE_Q4_0)
-      gemv_block<NT>(acc, gemv_x<QT, XF16>(xrow, u, g), gemv_codes<QT>(r.q, 0), r.d);
+      gemv_block<NT>(acc, x, gemv_codes<QT>(r.q, 0), r.d);
     else
-      gemv_block<NT>(acc, gemv_x<QT, XF16>(xrow, u, g), gemv_codes<QT>(r.q0, r.q1), r.d);
+      gemv_block<NT>(acc, x, gemv_codes<QT>(r.q0, r.q1), r.d);
   }
 }
 
+// Dynamic LDS: the staged activations of one chunk, chunk_blocks * 64 * NT bytes.
 template <int QT, int NT, bool XF16, bool ALIGN4>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
                                                             int64_t nb1, const void *__restrict__ X, int n_tokens,
-                                                            int k, float *__restrict__ Y) {
+                                                            int k, float *__restrict__ Y, int chunk_blocks) {
+  extern __shared__ __attribute__((aligned(16))) half8_t xs[];
+  __shared__ float red[kGemvWaves][NT > 4 ? 32 : 16][4];
+
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int row0 = blockIdx.x * 16;
-  // Rows past the end and token slots past n_tokens read valid memory (the
-  // last row / token) and their results are dropped at the store.
+  // Rows past the end read the last row (valid memory); their results are
+  // dropped at the store. Token slots past n_tokens read the last staged
+  // token; their D entries are never stored.
   const int row = min(row0 + r16, n_rows - 1);
   const uint8_t *rp = W + static_cast<int64_t>(row) * nb1;
-  const int tok = min(r16, n_tokens - 1);
-  const void *xrow = XF16 ? static_cast<const void *>(static_cast<const _Float16 *>(X) + static_cast<int64_t>(tok) * k)
-                          : static_cast<const void *>(static_cast<const float *>(X) + static_cast<int64_t>(tok) * k);
-
-  const int n_units = ALIGN4 ? (nblk >> 1) : nblk;
-  const int u0 = static_cast<int>((static_cast<int64_t>(wave) * n_units) / kGemvWaves);
-  const int u1 = static_cast<int>((static_cast<int64_t>(wave + 1) * n_units) / kGemvWaves);
+  const int xslot = min(r16, n_tokens - 1);
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (u0 < u1) {
-    // Software pipeline: kPrefetch units of weights are in flight while one
-    // is computed. Prefetch indices are clamped to the wave's last unit so
-    // every load is unconditional and in bounds.
-    GemvRaw<QT, ALIGN4> ring[kPrefetch];
+  for (int b_lo = 0; b_lo < nblk; b_lo += chunk_blocks) {
+    const int b_hi = min(nblk, b_lo + chunk_blocks);
+    const int nu = ALIGN4 ? ((b_hi - b_lo) >> 1) : (b_hi - b_lo);
+    const int ubase = ALIGN4 ? (b_lo >> 1) : b_lo;
+    // Waves take contiguous ranges of 8-block groups when the chunk has
+    // whole groups (as the streaming kernel does, so both kernels sum in
+    // the same order and agree bitwise), else of units.
+    const int upg = ALIGN4 ? 4 : 8;  // units per 8-block group
+    const int span = ((b_hi - b_lo) & 7) == 0 ? upg : 1;
+    const int ng = nu / span;
+    const int u0 = ubase + span * static_cast<int>((static_cast<int64_t>(wave) * ng) / kGemvWaves);
+    const int u1 = ubase + span * static_cast<int>((static_cast<int64_t>(wave + 1) * ng) / kGemvWaves);
+    const bool has_units = u0 < u1;
+
+    // Weight loads go out first, so the activation staging below overlaps
+    // their latency. Ring indices are clamped to the wave's last unit so all
+    // loads are in bounds.
+    GemvRaw<QT, ALIGN4> ring[kRing];
+    if (has_units) {
 #pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) ring[i] = gemv_load<QT, ALIGN4>(rp, min(u0 + i, u1 - 1), g);
-    for (int u = u0; u < u1; ++u) {
-      const GemvRaw<QT, ALIGN4> cur = ring[0];
-#pragma unroll
-      for (int i = 0; i + 1 < kPrefetch; ++i) ring[i] = ring[i + 1];
-      ring[kPrefetch - 1] = gemv_load<QT, ALIGN4>(rp, min(u + kPrefetch, u1 - 1), g);
-      gemv_unit<QT, NT, XF16, ALIGN4>(acc, cur, xrow, u, g, r16);
+      for (int i = 0; i < kRing; ++i) ring[i] = gemv_load<QT, ALIGN4>(rp, min(u0 + i, u1 - 1), g);
     }
-  }
-  if (ALIGN4 && (nblk & 1) && wave == kGemvWaves - 1) {
-    // Odd block count: the last block starts 4-byte aligned; 16-bit loads.
-    const GemvRaw<QT, false> t = gemv_load<QT, false>(rp, nblk - 1, g);
-    gemv_unit<QT, NT, XF16, false>(acc, t, xrow, nblk - 1, g, r16);
+    if (b_lo > 0) __syncthreads();  // previous chunk's activations no longer read
+    gemv_stage_x<QT, NT, XF16, kGemvThreads>(xs, X, n_tokens, k, b_lo, b_hi);
+    __syncthreads();
+
+    if (has_units) {
+      for (int base = u0; base < u1; base += kRing) {
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) {
+          const int u = base + i;
+          if (u < u1) {
+            gemv_unit<QT, NT, ALIGN4>(acc, ring[i], xs, u, b_lo, g, r16, xslot);
+            ring[i] = gemv_load<QT, ALIGN4>(rp, min(u + kRing, u1 - 1), g);
+          }
+        }
+      }
+    }
+    if (ALIGN4 && ((b_hi - b_lo) & 1) && wave == kGemvWaves - 1) {
+      // Odd block count in this chunk (only the last one): the final block
+      // starts 4-byte aligned; 16-bit loads.
+      const GemvRaw<QT, false> t = gemv_load<QT, false>(rp, b_hi - 1, g);
+      gemv_unit<QT, NT, false>(acc, t, xs, b_hi - 1, b_lo, g, r16, xslot);
+    }
   }
 
   constexpr int kRedLanes = NT > 4 ? 32 : 16;
-  __shared__ float red[kGemvWaves][kRedLanes][4];
   if (lane < kRedLanes) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][lane][e] = acc[e];
@@ -216,36 +199,73 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__res
   }
 }
 
+struct GemvLaunch {
+  dim3 grid;
+  size_t lds;
+  hipStream_t s;
+  const uint8_t *w;
+  int n_rows, nblk;
+  int64_t nb1;
+  const void *X;
+  int n_tokens, k;
+  float *Y;
+  int chunk_blocks;
+};
+
+// Allow the kernel more than the default dynamic LDS (once per instantiation).
+template <typename K> static hipError_t allow_lds(K kernel) {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsBudget);
+  return e;
+}
+
 template <int QT, int NT, bool XF16>
-static hipError_t gemv_dispatch_align(bool align4, dim3 grid, hipStream_t s, const uint8_t *w, int n_rows, int nblk,
-                                      int64_t nb1, const void *X, int n_tokens, int k, float *Y) {
+static hipError_t gemv_go(bool align4, const GemvLaunch &a) {
+  hipError_t e = allow_lds(align4 ? gemv_kernel<QT, NT, XF16, true> : gemv_kernel<QT, NT, XF16, false>);
+  if (e != hipSuccess) return e;
   if (align4)
-    return launch(gemv_kernel<QT, NT, XF16, true>, grid, dim3(kGemvThreads), 0, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y);
-  return launch(gemv_kernel<QT, NT, XF16, false>, grid, dim3(kGemvThreads), 0, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y);
+    return launch(gemv_kernel<QT, NT, XF16, true>, a.grid, dim3(kGemvThreads), a.lds, a.s, a.w, a.n_rows, a.nblk,
+                  a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks);
+  return launch(gemv_kernel<QT, NT, XF16, false>, a.grid, dim3(kGemvThreads), a.lds, a.s, a.w, a.n_rows, a.nblk,
+                a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks);
 }
 
 template <int QT, bool XF16>
-static hipError_t gemv_dispatch_nt(int nt, bool align4, dim3 grid, hipStream_t s, const uint8_t *w, int n_rows,
-                                   int nblk, int64_t nb1, const void *X, int n_tokens, int k, float *Y) {
-  if (nt <= 1) return gemv_dispatch_align<QT, 1, XF16>(align4, grid, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y);
-  if (nt <= 2) return gemv_dispatch_align<QT, 2, XF16>(align4, grid, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y);
-  if (nt <= 4) return gemv_dispatch_align<QT, 4, XF16>(align4, grid, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y);
-  return gemv_dispatch_align<QT, 8, XF16>(align4, grid, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y);
+static hipError_t gemv_nt(int nt, bool align4, GemvLaunch a) {
+  // chunk_blocks: a multiple of 8, as many blocks as fit the LDS budget for NT slots.
+  auto chunk = [&](int NT) {
+    int cb = kXLdsBudget / (64 * NT);
+    cb -= cb & 7;  // chunks hold whole 8-block groups
+    a.chunk_blocks = a.nblk <= cb ? a.nblk : cb;
+    a.lds = static_cast<size_t>(a.chunk_blocks) * 64 * NT;
+  };
+  if (nt <= 1) { chunk(1); return gemv_go<QT, 1, XF16>(align4, a); }
+  if (nt <= 2) { chunk(2); return gemv_go<QT, 2, XF16>(align4, a); }
+  if (nt <= 4) { chunk(4); return gemv_go<QT, 4, XF16>(align4, a); }
+  chunk(8);
+  return gemv_go<QT, 8, XF16>(align4, a);
 }
 
-hipError_t launch_gemv(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
-                       int64_t n_tokens, float *Y, hipStream_t stream) {
-  const uint8_t *w = static_cast<const uint8_t *>(W);
+hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X,
+                               bool x_f16, int64_t n_tokens, float *Y, hipStream_t stream) {
+  GemvLaunch a;
+  a.grid = dim3(static_cast<unsigned>((n_rows + 15) / 16));
+  a.lds = 0;
+  a.s = stream;
+  a.w = static_cast<const uint8_t *>(W);
+  a.n_rows = static_cast<int>(n_rows);
+  a.nblk = static_cast<int>(k / 32);
+  a.nb1 = nb1;
+  a.X = X;
+  a.n_tokens = static_cast<int>(n_tokens);
+  a.k = static_cast<int>(k);
+  a.Y = Y;
+  a.chunk_blocks = a.nblk;
   const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0);
-  const dim3 grid(static_cast<unsigned>((n_rows + 15) / 16));
-  const int nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows), nt = static_cast<int>(n_tokens),
-            kk = static_cast<int>(k);
-  if (qtype == QMM_TYPE_Q4_0) {
-    if (x_f16) return gemv_dispatch_nt<QMM_TYPE_Q4_0, true>(nt, align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y);
-    return gemv_dispatch_nt<QMM_TYPE_Q4_0, false>(nt, align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y);
-  }
-  if (x_f16) return gemv_dispatch_nt<QMM_TYPE_Q8_0, true>(nt, align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y);
-  return gemv_dispatch_nt<QMM_TYPE_Q8_0, false>(nt, align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y);
+  const int nt = a.n_tokens;
+  if (qtype == QMM_TYPE_Q4_0)
+    return x_f16 ? gemv_nt<QMM_TYPE_Q4_0, true>(nt, align4, a) : gemv_nt<QMM_TYPE_Q4_0, false>(nt, align4, a);
+  return x_f16 ? gemv_nt<QMM_TYPE_Q8_0, true>(nt, align4, a) : gemv_nt<QMM_TYPE_Q8_0, false>(nt, align4, a);
 }
 
 }  // namespace qmm

@@ -27,9 +27,23 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
 hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,
                           hipStream_t stream);
 
-// Decode kernel, 1 <= n_tokens <= QMM_GEMV_MAX_TOKENS.
-hipError_t launch_gemv(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
-                       int64_t n_tokens, float *Y, hipStream_t stream);
+// One MUL_MAT of a (possibly batched) call.
+struct MatmulDesc {
+  const void *W;
+  int qtype;
+  int64_t n_rows, k, nb1;
+  const void *X;
+  bool x_f16;
+  int64_t n_tokens;
+  float *Y;
+};
+
+// Decode kernels, 1 <= n_tokens <= QMM_GEMV_MAX_TOKENS. launch_gemv_batch runs
+// `count` independent MUL_MATs, grouping those the streaming kernel can take
+// into shared launches; the rest go one by one to the general kernel.
+hipError_t launch_gemv_batch(const MatmulDesc *d, int count, hipStream_t stream);
+hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X,
+                               bool x_f16, int64_t n_tokens, float *Y, hipStream_t stream);
 
 // Matrix-core kernel, any n_tokens >= 1.
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,

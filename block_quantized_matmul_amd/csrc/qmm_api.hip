@@ -15,6 +15,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <vector>
+
 #include "common.h"
 #include "launch.h"
 
@@ -86,8 +88,8 @@ const char *qmm_status_string(int status) {
   }
 }
 
-int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, const void *X,
-                    int x_type, int64_t n_tokens, float *Y, int path, void *stream) {
+static int check_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                        const void *X, int x_type, int64_t n_tokens, const float *Y, int path) {
   if (X == nullptr || Y == nullptr) return QMM_ERR_NULL;
   int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
   if (st != QMM_OK) return st;
@@ -96,6 +98,13 @@ int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int
   if (path != QMM_PATH_AUTO && path != QMM_PATH_GEMV && path != QMM_PATH_GEMM) return QMM_ERR_PATH;
   if (path == QMM_PATH_GEMV && n_tokens > QMM_GEMV_MAX_TOKENS) return QMM_ERR_PATH;
   if (!aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+  return QMM_OK;
+}
+
+int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, const void *X,
+                    int x_type, int64_t n_tokens, float *Y, int path, void *stream) {
+  const int st = check_matmul(W, ggml_type, n_rows, k, row_stride_bytes, X, x_type, n_tokens, Y, path);
+  if (st != QMM_OK) return st;
   if (n_rows == 0 || n_tokens == 0) return QMM_OK;
 
   const bool gemv = path == QMM_PATH_GEMV || (path == QMM_PATH_AUTO && n_tokens <= QMM_GEMV_MAX_TOKENS);
@@ -105,9 +114,11 @@ int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int
     fprintf(stderr, "qmm: %s %s rows=%lld k=%lld nb1=%lld tokens=%lld x=%s align4=%d\n", gemv ? "gemv" : "gemm",
             type_name(ggml_type), (long long)n_rows, (long long)k, (long long)row_stride_bytes, (long long)n_tokens,
             x_f16 ? "f16" : "f32", (int)(aligned(W, 4) && row_stride_bytes % 4 == 0));
-  hipError_t e = gemv ? qmm::launch_gemv(W, ggml_type, n_rows, k, row_stride_bytes, X, x_f16, n_tokens, Y, s)
-                      : qmm::launch_gemm(W, ggml_type, n_rows, k, row_stride_bytes, X, x_f16, n_tokens, Y, s);
-  return status_of(e);
+  if (gemv) {
+    const qmm::MatmulDesc d{W, ggml_type, n_rows, k, row_stride_bytes, X, x_f16, n_tokens, Y};
+    return status_of(qmm::launch_gemv_batch(&d, 1, s));
+  }
+  return status_of(qmm::launch_gemm(W, ggml_type, n_rows, k, row_stride_bytes, X, x_f16, n_tokens, Y, s));
 }
 
 int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, const float *X,
@@ -118,6 +129,36 @@ int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t 
 int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                    const uint16_t *X, int64_t n_tokens, float *Y, void *stream) {
   return qmm_matmul_path(W, ggml_type, n_rows, k, row_stride_bytes, X, QMM_X_F16, n_tokens, Y, QMM_PATH_AUTO, stream);
+}
+
+int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream) {
+  if (count < 0) return QMM_ERR_SHAPE;
+  if (count == 0) return QMM_OK;
+  if (descs == nullptr) return QMM_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    const qmm_matmul_desc &d = descs[i];
+    const int st = check_matmul(d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X, d.x_type, d.n_tokens, d.Y,
+                                QMM_PATH_AUTO);
+    if (st != QMM_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<qmm::MatmulDesc> gemv;
+  gemv.reserve(count);
+  for (int i = 0; i < count; ++i) {
+    const qmm_matmul_desc &d = descs[i];
+    if (d.n_rows == 0 || d.n_tokens == 0) continue;
+    const bool x_f16 = d.x_type == QMM_X_F16;
+    if (d.n_tokens <= QMM_GEMV_MAX_TOKENS) {
+      gemv.push_back(qmm::MatmulDesc{d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X, x_f16, d.n_tokens, d.Y});
+    } else {
+      const hipError_t e =
+          qmm::launch_gemm(d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X, x_f16, d.n_tokens, d.Y, s);
+      if (e != hipSuccess) return QMM_ERR_HIP;
+    }
+  }
+  if (trace_on()) fprintf(stderr, "qmm: batch of %d (%zu decode-sized)\n", count, gemv.size());
+  if (gemv.empty()) return QMM_OK;
+  return status_of(qmm::launch_gemv_batch(gemv.data(), static_cast<int>(gemv.size()), s));
 }
 
 int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, float *out,

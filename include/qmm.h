@@ -130,6 +130,35 @@ int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
 int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                     const void *X, int x_type, int64_t n_tokens, float *Y, int path, void *stream);
 
+/* One MUL_MAT of a qmm_matmul_batch call; fields as in qmm_matmul_path. */
+typedef struct qmm_matmul_desc {
+  const void *W;
+  int ggml_type;
+  int64_t n_rows;
+  int64_t k;
+  int64_t row_stride_bytes;
+  const void *X;
+  int x_type; /* QMM_X_F32 or QMM_X_F16 */
+  int64_t n_tokens;
+  float *Y;
+} qmm_matmul_desc;
+
+/*
+ * qmm_matmul_batch - `count` independent MUL_MATs enqueued on one stream, as
+ * if each were passed to qmm_matmul_path with QMM_PATH_AUTO. A model issues
+ * several MUL_MATs that share an input and do not depend on each other
+ * ([Bind] section 3.2: a layer's attn_q/k/v, or ffn_gate and ffn_up); the
+ * decode-sized ones (n_tokens <= QMM_GEMV_MAX_TOKENS) with 16-byte-aligned
+ * layouts are grouped into shared launches, which removes the per-launch
+ * fixed cost that dominates small decode matmuls. `descs` is a host array
+ * read only during the call. Every descriptor is validated before anything is
+ * launched; on failure the status of the first invalid descriptor is
+ * returned and nothing is enqueued. Outputs must not overlap any input or
+ * each other. count == 0 is a no-op; count < 0 or descs == NULL with
+ * count > 0 returns QMM_ERR_NULL / QMM_ERR_SHAPE.
+ */
+int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream);
+
 /*
  * qmm_dequantize - the block decoder alone ([Bind] section 2.3 layout,
  * [Arch] reconstruction equation): out[r][i] = fp32(d) * fp32(q - z) for

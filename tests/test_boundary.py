@@ -35,8 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize",
-                            "qmm_row_bytes", "qmm_supports", "qmm_status_string"])
+    assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
+                            "qmm_dequantize", "qmm_row_bytes", "qmm_supports", "qmm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -131,3 +131,23 @@ def test_binding_refuses_cpu_tensors():
         qmm.qmm_matmul(W, Q4, 64, X, Y=torch.empty((1, 4)))
     with pytest.raises(TypeError):
         qmm.qmm_dequantize(W, Q4, 64, out=torch.empty((4, 64)))
+
+
+def test_batch_validation(L):
+    D = qmm.qmm_matmul_desc
+    ok = D(0x10000, Q4, 16, 64, 36, 0x20000, qmm.QMM_X_F32, 0, 0x30000)   # zero tokens: valid, no launch
+    bad_stride = D(0x10000, Q4, 16, 64, 35, 0x20000, qmm.QMM_X_F32, 1, 0x30000)
+    bad_type = D(0x10000, 5, 16, 64, 36, 0x20000, qmm.QMM_X_F32, 1, 0x30000)
+    bad_x = D(0x10000, Q4, 16, 64, 36, 0x20000, 3, 1, 0x30000)
+    arr = (D * 3)(ok, ok, ok)
+    assert L.qmm_matmul_batch(arr, 3, NULL) == qmm.QMM_OK
+    assert L.qmm_matmul_batch(arr, 0, NULL) == qmm.QMM_OK
+    assert L.qmm_matmul_batch(None, 0, NULL) == qmm.QMM_OK
+    assert L.qmm_matmul_batch(None, 2, NULL) == qmm.QMM_ERR_NULL
+    assert L.qmm_matmul_batch(arr, -1, NULL) == qmm.QMM_ERR_SHAPE
+    # the first invalid descriptor's status is returned, nothing launched
+    assert L.qmm_matmul_batch((D * 3)(ok, bad_stride, bad_type), 3, NULL) == qmm.QMM_ERR_STRIDE
+    assert L.qmm_matmul_batch((D * 2)(bad_type, bad_stride), 2, NULL) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul_batch((D * 1)(bad_x), 1, NULL) == qmm.QMM_ERR_TYPE
+    nullw = D(0, Q4, 16, 64, 36, 0x20000, qmm.QMM_X_F32, 1, 0x30000)
+    assert L.qmm_matmul_batch((D * 2)(ok, nullw), 2, NULL) == qmm.QMM_ERR_NULL

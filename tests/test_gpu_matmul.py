@@ -36,7 +36,8 @@ def _parity(W, qtype, k, X, path, offset=0, what=""):
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8])
 def test_gemv_ragged(qtype, xdt, n):
     for rows, k, extra, offset in ((1, 32, 0, 0), (37, 96, 0, 0), (37, 96, 2, 2), (300, 512, 4, 0),
-                                   (17, 4096, 256, 0), (33, 11008, 0, 2)):
+                                   (300, 512, 16, 0), (17, 4096, 256, 0), (33, 11008, 0, 2), (17, 11008, 0, 0),
+                                   (45, 2048, 0, 4)):
         W, X = _inputs(qtype, rows, k, n, extra, xdt=xdt)
         _parity(W, qtype, k, X, GEMV, offset, f"gemv rows={rows} k={k}")
 
@@ -199,3 +200,73 @@ def test_config5_stack_layers_sampled(n_tokens):
         toks = rng.integers(0, case.n_tokens, m)
         y_ref, s = O.matmul_sampled(W, case.qtype, case.rows, case.k, case.nb1, X, toks, rows)
         assert O.within_tolerance(Y[toks, rows], y_ref, s).all(), case.name
+
+
+# ------------------------------------------------------------ batched calls and graph replay
+def _batch_specs():
+    # (type, rows, k, n_tokens, x dtype): streaming-eligible, general-kernel and matrix-core entries,
+    # in an order that forces several launch groups
+    return [(Q4, 300, 4096, 1, np.float32), (Q4, 4096, 512, 1, np.float32), (Q4, 129, 11008, 1, np.float32),
+            (Q8, 77, 1024, 1, np.float32), (Q4, 40, 96, 1, np.float32), (Q4, 33, 4096, 3, np.float32),
+            (Q4, 64, 2048, 8, np.float16), (Q8, 50, 4096, 20, np.float16), (Q4, 16, 256, 2, np.float32)] + \
+           [(Q4, 16 * (i + 1), 256 * (1 + i % 3), 1, np.float32) for i in range(20)]
+
+
+def _batch_items(specs, seed=0):
+    import torch
+    from gpu_util import dev
+    host, items = [], []
+    for i, (qt, rows, k, n, xdt) in enumerate(specs):
+        W, X = _inputs(qt, rows, k, n, seed=seed + i, xdt=xdt)
+        Wd, Xd = dev(W), dev(X)
+        Y = torch.full((n, rows), float("nan"), dtype=torch.float32, device="cuda")
+        host.append((W, X, qt, k))
+        items.append((Wd, qt, k, Xd, Y))
+    return host, items
+
+
+def test_batch_matches_single_calls_and_oracle():
+    import torch
+    specs = _batch_specs()
+    host, items = _batch_items(specs)
+    say(f"batch of {len(items)}")
+    qmm.qmm_matmul_batch(items)
+    torch.cuda.synchronize()
+    for (W, X, qt, k), (_, _, _, _, Y) in zip(host, items):
+        y = Y.cpu().numpy()
+        assert_bitwise(y, run_matmul(W, qt, k, X, AUTO), f"batch vs single {W.shape}")
+        assert_close_to_oracle(y, W, qt, k, X, f"batch {W.shape}")
+
+
+def test_graph_replay_matches_eager():
+    """A captured graph (batched call + single calls) replayed several times,
+    with eager work in between, reproduces the eager results every time."""
+    import torch
+    host, items = _batch_items(_batch_specs()[:9], seed=100)
+    W0, qt0, k0, X0, _ = items[0]
+    Ys = torch.empty((X0.shape[0], W0.shape[0]), dtype=torch.float32, device="cuda")
+    Yg = torch.empty((40, W0.shape[0]), dtype=torch.float32, device="cuda")
+    Xg = torch.randn((40, k0), dtype=torch.float32, device="cuda")
+
+    def work():
+        qmm.qmm_matmul_batch(items)
+        qmm.qmm_matmul(W0, qt0, k0, X0, Y=Ys)
+        qmm.qmm_matmul(W0, qt0, k0, Xg, Y=Yg)
+
+    say("graph capture")
+    work()
+    torch.cuda.synchronize()
+    ref = [it[4].clone() for it in items] + [Ys.clone(), Yg.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(3):
+        for t in [it[4] for it in items] + [Ys, Yg]:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        out = [it[4] for it in items] + [Ys, Yg]
+        for a, b in zip(out, ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        _ = (Xg * 2).sum().item()  # unrelated eager work between replays
