@@ -9,7 +9,7 @@
 // per block and multiply-add them with activations in registers).
 //
 // Design (MI355X, gfx950). The kernel is bound by HBM: every weight byte is
-// read exactly once. One workgroup owns 16 rows; its 4 wavefronts split the
+// read exactly once. One workgroup owns 16 rows; its 8 wavefronts split the
 // row's blocks into contiguous ranges and meet in LDS at the end, in a fixed
 // order (no atomics, so results are bitwise reproducible).
 //
@@ -40,7 +40,7 @@
 
 namespace qmm {
 
-constexpr int kGemvWaves = 4;  // k split 4 ways, as in the streaming kernel
+constexpr int kGemvWaves = kKSplit;  // k split as in the streaming kernel
 constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kRing = 8;                  // weight units in flight per wavefront
 constexpr int kXLdsBudget = 64 * 1024;    // bytes of LDS for staged activations

@@ -7,6 +7,12 @@
 
 namespace qmm {
 
+// Both decode kernels give a 16-row group to one workgroup whose wavefronts
+// split k into this many contiguous ranges of 8-block groups and add their
+// partial sums in wavefront order; sharing the split makes their results
+// bitwise identical wherever both apply.
+constexpr int kKSplit = 8;
+
 // B-operand: this lane's 8 exact codes (q - z) of one block.
 template <int QT> __device__ __forceinline__ half8_t gemv_codes(uint32_t q0, uint32_t q1);
 template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q4_0>(uint32_t q0, uint32_t) {

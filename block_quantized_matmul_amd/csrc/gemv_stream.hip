@@ -9,9 +9,9 @@
 //
 // Design (MI355X, gfx950): the kernel is an HBM stream, so its structure
 // copies that of a plain streaming read as closely as it can.
-//  * A workgroup owns one 16-row group of one matrix; a launch has one
-//    workgroup per row group of every matrix in the batch (the hardware
-//    balances them across the CUs). Its 4 wavefronts split k into
+//  * A workgroup owns one 16-row group of one matrix; a launch's grid is
+//    (row groups of its largest matrix) x (matrices), and the hardware
+//    balances the workgroups across the CUs. Its 8 wavefronts split k into
 //    contiguous ranges of quads (8 blocks: 144 bytes Q4_0 / 272 bytes Q8_0
 //    per row, a whole number of 16-byte chunks) and stream them
 //    independently; they meet once, at the end, to add their partial sums in
@@ -37,7 +37,7 @@
 
 namespace qmm {
 
-constexpr int kRWaves = 4;  // wavefronts per workgroup (one 16-row group, k split 4 ways)
+constexpr int kRWaves = kKSplit;  // wavefronts per workgroup (one 16-row group, k split kKSplit ways)
 constexpr int kRThreads = 64 * kRWaves;
 constexpr int kRMaxMats = 16;
 
@@ -49,7 +49,7 @@ template <int QT, int NT> struct RCfg {
   static constexpr int row_stride = quad_chunks * 16;
   static constexpr int w_loads = (16 * quad_chunks + 63) / 64;       // loads per lane for the 16 rows
   // stages per round, sized so a round's registers stay near 64 VGPRs (the
-  // kernel then fits 4 wavefronts per SIMD, i.e. 4 workgroups per CU)
+  // kernel then fits 4 wavefronts per SIMD, i.e. 2 workgroups per CU)
   static constexpr int stage_vgprs = 4 * w_loads + NT * 4;
   static constexpr int depth = (64 / stage_vgprs) < 1 ? 1 : (64 / stage_vgprs > 6 ? 6 : 64 / stage_vgprs);
   static constexpr int w_lds = 16 * row_stride;
@@ -57,25 +57,34 @@ template <int QT, int NT> struct RCfg {
   static constexpr int lds_per_wave = w_lds + x_lds;
 };
 
-// Descriptor table of a launch, as arrays so that finding a workgroup's
-// matrix is one wide scalar load of rg_end plus one round of independent
-// scalar loads of that matrix's fields.
+// One matrix of a launch: 64 bytes, so a workgroup fetches all of it with a
+// single 16-dword scalar load and one wait (field by field, the compiler
+// places each scalar load next to its use, which serialises several memory
+// round trips before the first weight load can be issued).
+struct RMat {
+  const uint8_t *W;
+  const void *X;
+  float *Y;
+  int64_t nb1;
+  int n_rows, nblk, n_tokens, k;
+  int pad[4];
+};
+static_assert(sizeof(RMat) == 64, "one scalar load per matrix record");
+
+// Descriptor table of a launch. Workgroup (x, y) takes row group x of matrix
+// y; the grid is as wide as the largest matrix, and workgroups past a smaller
+// matrix's last row group return at once.
 struct RBatch {
-  int rg_end[kRMaxMats];  // row groups of matrix i and all before it
-  int count, total_rg;
-  const uint8_t *W[kRMaxMats];
-  const void *X[kRMaxMats];
-  float *Y[kRMaxMats];
-  int64_t nb1[kRMaxMats];
-  int n_rows[kRMaxMats], nblk[kRMaxMats], n_tokens[kRMaxMats], k[kRMaxMats];
+  RMat m[kRMaxMats];
 };
 
-// The batch is the kernel's first argument, so it sits at the start of the
-// kernel-argument segment; reading it through that constant address-space
-// pointer gives uniform scalar loads (indexing the by-value parameter with a
+typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
+template <class T> using GPtr = const __attribute__((address_space(1))) T *;
+// The batch is the kernel's only argument, so it sits at the start of the
+// kernel-argument segment; a record is read through that constant
+// address-space pointer as one vector (indexing the by-value parameter with a
 // run-time index would copy the whole table to scratch).
-typedef const __attribute__((address_space(4))) RBatch *KBatch;
-static_assert(offsetof(RBatch, rg_end) == 0, "descriptor table must lead the batch");
+typedef const __attribute__((address_space(4))) u32x16_t *KRec;
 
 template <int QT, int NT, bool XF16> struct RRegs {
   u32x4_t w[RCfg<QT, NT>::w_loads];
@@ -83,31 +92,31 @@ template <int QT, int NT, bool XF16> struct RRegs {
 };
 
 template <int QT, int NT, bool XF16>
-__global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
+__global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
     const RBatch batch) {
   (void)batch;  // read through the kernel-argument pointer
   using C = RCfg<QT, NT>;
   constexpr int QC = C::quad_chunks;
   constexpr int D = C::depth;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const KBatch B = (KBatch)__builtin_amdgcn_kernarg_segment_ptr();
+  const u32x16_t rec = ((KRec)__builtin_amdgcn_kernarg_segment_ptr())[blockIdx.y];
+  auto ptr = [&](int i) { return (static_cast<uint64_t>(rec[i + 1]) << 32) | rec[i]; };
+  const int n_rows = static_cast<int>(rec[8]);
+  const int rg = blockIdx.x;
+  if (rg * 16 >= n_rows) return;  // whole workgroup: past this matrix's rows
+  // The pointers are rebuilt from integers, so they are cast to the global
+  // address space explicitly (generic pointers would make every access a
+  // flat access, which also counts on the LDS counter and coarsens waits).
+  const GPtr<uint8_t> W = (GPtr<uint8_t>)ptr(0);
+  const GPtr<float> Xf = (GPtr<float>)ptr(2);
+  const GPtr<_Float16> Xh = (GPtr<_Float16>)ptr(2);
+  __attribute__((address_space(1))) float *Y = (__attribute__((address_space(1))) float *)ptr(4);
+  const int64_t nb1 = static_cast<int64_t>(ptr(6));
+  const int nblk = static_cast<int>(rec[9]), n_tokens = static_cast<int>(rec[10]), k = static_cast<int>(rec[11]);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = blockIdx.x;
-  int m = 0, rg_begin = 0;
-#pragma unroll
-  for (int i = 0; i < kRMaxMats - 1; ++i) {
-    const int e = B->rg_end[i];
-    if (rg >= e && i + 1 < B->count) {
-      m = i + 1;
-      rg_begin = e;
-    }
-  }
-  const uint8_t *W = B->W[m];
-  const int64_t nb1 = B->nb1[m];
-  const int n_rows = B->n_rows[m], nblk = B->nblk[m], n_tokens = B->n_tokens[m], k = B->k[m];
-  const int row0 = (rg - rg_begin) * 16;
+  const int row0 = rg * 16;
   // this wavefront's quads [q_lo, q_hi)
   const int qn = nblk >> 3;
   const int q_lo = (wave * qn) / kRWaves, q_hi = ((wave + 1) * qn) / kRWaves;
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
   // Lane-constant addressing: weight chunk c = 64 j + lane of a stage is row
   // c / QC, chunk c % QC; chunks past 16 * QC re-read chunk 0 of the stage
   // and are not stored. Rows past the end re-read the last row.
-  const uint8_t *wp[C::w_loads];
+  GPtr<uint8_t> wp[C::w_loads];
   int woff[C::w_loads];
 #pragma unroll
   for (int j = 0; j < C::w_loads; ++j) {
@@ -136,7 +145,6 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
   const int xb = lane >> 3, xj = lane & 7;
   const int xg = QT == QMM_TYPE_Q4_0 ? (xj & 3) : (xj >> 1);
   const int xh = QT == QMM_TYPE_Q4_0 ? 4 * (xj >> 2) : 4 * (xj & 1);
-  const void *Xm = B->X[m];
   int64_t xoff[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) xoff[t] = static_cast<int64_t>(min(t, n_tokens - 1)) * k + 32 * xb + 4 * xj;
@@ -145,13 +153,13 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
     const int qc = q;
 #pragma unroll
     for (int j = 0; j < C::w_loads; ++j)
-      r.w[j] = *reinterpret_cast<const u32x4_t *>(wp[j] + static_cast<int64_t>(qc) * (QC * 16));
+      r.w[j] = *(GPtr<u32x4_t>)(wp[j] + static_cast<int64_t>(qc) * (QC * 16));
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if constexpr (XF16)
-        r.x[t] = *reinterpret_cast<const half4_t *>(static_cast<const _Float16 *>(Xm) + xoff[t] + 256 * qc);
+        r.x[t] = *(GPtr<half4_t>)(Xh + xoff[t] + 256 * qc);
       else
-        r.x[t] = *reinterpret_cast<const float4_t *>(static_cast<const float *>(Xm) + xoff[t] + 256 * qc);
+        r.x[t] = *(GPtr<float4_t>)(Xf + xoff[t] + 256 * qc);
     }
   };
 
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
       if (q + i < q_hi) consume(st[i]);
   }
 
-  // Partial sums of the 4 wavefronts, added in wavefront order. D element e
+  // Partial sums of the wavefronts, added in wavefront order. D element e
   // of lane l: token 4 (l / 16) + e, row l % 16. The barrier waits on LDS
   // only; the ring's spare loads need not land first.
   constexpr int kRedLanes = NT > 4 ? 32 : 16;
@@ -230,25 +238,24 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
 #pragma unroll
     for (int w = 0; w < kRWaves; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
     const int row = row0 + r;
-    if (t < n_tokens && row < n_rows) B->Y[m][static_cast<int64_t>(t) * n_rows + row] = sum;
+    if (t < n_tokens && row < n_rows) Y[static_cast<int64_t>(t) * n_rows + row] = sum;
   }
 }
 
 // ------------------------------------------------------------------ host side
 
 template <int QT, int NT, bool XF16>
-static hipError_t r_go(const RBatch &B, hipStream_t s) {
-  const int grid = B.total_rg;
+static hipError_t r_go(const RBatch &B, int count, int max_rg, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kRWaves) * RCfg<QT, NT>::lds_per_wave + kRWaves * 32 * 4 * sizeof(float);
-  return launch(gemv_stream_kernel<QT, NT, XF16>, dim3(grid), dim3(kRThreads), lds, s, B);
+  return launch(gemv_stream_kernel<QT, NT, XF16>, dim3(max_rg, count), dim3(kRThreads), lds, s, B);
 }
 
 template <int QT, bool XF16>
-static hipError_t r_nt(int nt, const RBatch &B, hipStream_t s) {
-  if (nt <= 1) return r_go<QT, 1, XF16>(B, s);
-  if (nt <= 2) return r_go<QT, 2, XF16>(B, s);
-  if (nt <= 4) return r_go<QT, 4, XF16>(B, s);
-  return r_go<QT, 8, XF16>(B, s);
+static hipError_t r_nt(int nt, const RBatch &B, int count, int max_rg, hipStream_t s) {
+  if (nt <= 1) return r_go<QT, 1, XF16>(B, count, max_rg, s);
+  if (nt <= 2) return r_go<QT, 2, XF16>(B, count, max_rg, s);
+  if (nt <= 4) return r_go<QT, 4, XF16>(B, count, max_rg, s);
+  return r_go<QT, 8, XF16>(B, count, max_rg, s);
 }
 
 static int nt_slots(int64_t n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
@@ -258,12 +265,12 @@ static bool streamable(const MatmulDesc &d) {
   return reinterpret_cast<uintptr_t>(d.W) % 16 == 0 && d.nb1 % 16 == 0 && nblk % 8 == 0;
 }
 
-hipError_t launch_gemv_batch(const MatmulDesc *d, int count, hipStream_t stream) {
+hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t stream) {
   // Consecutive streamable descriptors with the same (type, activation type,
   // token-slot count) share a launch of up to kRMaxMats matrices; the rest
   // go one by one to the general kernel.
   int i = 0;
-  while (i < count) {
+  while (i < count_all) {
     if (!streamable(d[i])) {
       hipError_t e = launch_gemv_general(d[i].W, d[i].qtype, d[i].n_rows, d[i].k, d[i].nb1, d[i].X, d[i].x_f16,
                                          d[i].n_tokens, d[i].Y, stream);
@@ -274,29 +281,28 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count, hipStream_t stream)
     RBatch B{};
     const int qt = d[i].qtype, nt = nt_slots(d[i].n_tokens);
     const bool xf = d[i].x_f16;
-    int j = i, rg = 0;
-    while (j < count && B.count < kRMaxMats && streamable(d[j]) && d[j].qtype == qt && d[j].x_f16 == xf &&
+    int j = i, count = 0, max_rg = 0;
+    while (j < count_all && count < kRMaxMats && streamable(d[j]) && d[j].qtype == qt && d[j].x_f16 == xf &&
            nt_slots(d[j].n_tokens) == nt) {
-      const int c = B.count++;
-      B.W[c] = static_cast<const uint8_t *>(d[j].W);
-      B.X[c] = d[j].X;
-      B.Y[c] = d[j].Y;
-      B.nb1[c] = d[j].nb1;
-      B.n_rows[c] = static_cast<int>(d[j].n_rows);
-      B.nblk[c] = static_cast<int>(d[j].k / 32);
-      B.n_tokens[c] = static_cast<int>(d[j].n_tokens);
-      B.k[c] = static_cast<int>(d[j].k);
-      rg += static_cast<int>((d[j].n_rows + 15) / 16);
-      B.rg_end[c] = rg;
+      RMat &r = B.m[count++];
+      r.W = static_cast<const uint8_t *>(d[j].W);
+      r.X = d[j].X;
+      r.Y = d[j].Y;
+      r.nb1 = d[j].nb1;
+      r.n_rows = static_cast<int>(d[j].n_rows);
+      r.nblk = static_cast<int>(d[j].k / 32);
+      r.n_tokens = static_cast<int>(d[j].n_tokens);
+      r.k = static_cast<int>(d[j].k);
+      max_rg = max(max_rg, static_cast<int>((d[j].n_rows + 15) / 16));
       ++j;
     }
-    for (int c = B.count; c < kRMaxMats; ++c) B.rg_end[c] = rg;
-    B.total_rg = rg;
     hipError_t e;
     if (qt == QMM_TYPE_Q4_0)
-      e = xf ? r_nt<QMM_TYPE_Q4_0, true>(nt, B, stream) : r_nt<QMM_TYPE_Q4_0, false>(nt, B, stream);
+      e = xf ? r_nt<QMM_TYPE_Q4_0, true>(nt, B, count, max_rg, stream)
+             : r_nt<QMM_TYPE_Q4_0, false>(nt, B, count, max_rg, stream);
     else
-      e = xf ? r_nt<QMM_TYPE_Q8_0, true>(nt, B, stream) : r_nt<QMM_TYPE_Q8_0, false>(nt, B, stream);
+      e = xf ? r_nt<QMM_TYPE_Q8_0, true>(nt, B, count, max_rg, stream)
+             : r_nt<QMM_TYPE_Q8_0, false>(nt, B, count, max_rg, stream);
     if (e != hipSuccess) return e;
     i = j;
   }
