@@ -13,8 +13,9 @@ One step = the whole hot path over one batch of synthetic input:
             matrix-core (GEMM) kernel, one launch per MUL_MAT.
 Each pass is captured once into a HIP graph (its launches are exactly the C
 entry points' launches) and replayed; HIP events on the launch stream time
-every pass. Inputs are resident in HBM before the timed region starts. The
-decode pass with one launch per MUL_MAT (qmm_matmul) is timed beside it.
+every pass. Inputs are resident in HBM before the timed region starts. With
+--per-call, the decode pass with one launch per MUL_MAT (qmm_matmul) is timed
+after the steps as well.
 
 Prints ONE JSON line. `value` is the decode pass's achieved HBM bandwidth:
 algorithmic bytes (weight blocks + activations + outputs) per pass / pass
@@ -27,7 +28,7 @@ since they were taken. The CPU oracle is timed on a bounded sample of the
 same decode workload.
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--layers 32]
-                  [--cpu-layers 8] [--no-cpu-baseline] [--copy-calibration]
+                  [--cpu-layers 12] [--no-cpu-baseline] [--per-call] [--copy-calibration]
   python bench.py --summarize-trace DIR      (rocprofv3 -f csv kernel trace)
   python bench.py --only PASS [--steps K] [--layers L] [--copy-calibration]
   python bench.py --summarize-counters DIR... (rocprofv3 -f csv --pmc runs)
@@ -84,7 +85,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the decode pass the oracle times")
+    ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the decode pass the oracle times")
+    ap.add_argument("--per-call", action="store_true",
+                    help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run one plain {COPY_CAL_BYTES >> 20} MiB device copy (for counter calibration)")
     ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill"),
@@ -293,6 +296,8 @@ def main():
             qmm.qmm_matmul_x16(W[i], c.qtype, c.k, X2[i], Y=Y2[i % 7])
 
     passes = {"decode": decode_pass, "decode_per_call": decode_per_call_pass, "prefill": prefill_pass}
+    if not args.per_call and args.only != "decode_per_call":
+        del passes["decode_per_call"]
     launches = {"decode": len(groups), "decode_per_call": n, "prefill": n}
     if args.only:
         f = passes[args.only]
@@ -309,8 +314,9 @@ def main():
     for f in passes.values():
         f()
     torch.cuda.synchronize()
-    refs = [y.clone() for y in Y1 + Y1b + Y2]
-    if not all(torch.equal(a, b) for a, b in zip(Y1, Y1b)):
+    outs = Y1 + (Y1b if "decode_per_call" in passes else []) + Y2
+    refs = [y.clone() for y in outs]
+    if "decode_per_call" in passes and not all(torch.equal(a, b) for a, b in zip(Y1, Y1b)):
         raise RuntimeError("batched and per-call decode outputs differ")
     graphs = {}
     for name, f in passes.items():
@@ -337,23 +343,25 @@ def main():
         ev[s][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the per-call decode pass is timed after the steps, outside the step clock
-    for s in range(K):
-        ev[s][3].record()
-        graphs["decode_per_call"].replay()
-        ev[s][4].record()
-    torch.cuda.synchronize()
-    span = {"decode": (0, 1), "prefill": (1, 2), "decode_per_call": (3, 4)}
+    span = {"decode": (0, 1), "prefill": (1, 2)}
+    if "decode_per_call" in graphs:
+        # timed after the steps, outside the step clock
+        for s in range(K):
+            ev[s][3].record()
+            graphs["decode_per_call"].replay()
+            ev[s][4].record()
+        torch.cuda.synchronize()
+        span["decode_per_call"] = (3, 4)
     ms = {name: sorted(ev[s][a].elapsed_time(ev[s][b]) for s in range(K))[K // 2] for name, (a, b) in span.items()}
 
-    for a, b in zip(Y1 + Y1b + Y2, refs):
+    for a, b in zip(outs, refs):
         if not torch.equal(a, b):
             raise RuntimeError("graph replay output differs from the eager run")
 
     dec_bytes = sum(c.w_bytes() + c.n_tokens * c.k * 4 + c.n_tokens * c.rows * 4 for c in dec)
     pre_flops = sum(2.0 * c.rows * c.k * c.n_tokens for c in pre)
     gbs = dec_bytes / (ms["decode"] * 1e-3) / 1e9
-    gbs_pc = dec_bytes / (ms["decode_per_call"] * 1e-3) / 1e9
+
     tfl = pre_flops / (ms["prefill"] * 1e-3) / 1e12
     us_launch = {k: ms[k] * 1e3 / launches[k] for k in ms}
 
@@ -396,15 +404,17 @@ def main():
         "decode": {"ms_per_pass": round(ms["decode"], 4), "launches": launches["decode"],
                    "us_per_launch": round(us_launch["decode"], 3), "GB_per_s": round(gbs, 2),
                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_pass": dec_bytes},
-        "decode_per_call": {"ms_per_pass": round(ms["decode_per_call"], 4), "launches": n,
-                            "us_per_launch": round(us_launch["decode_per_call"], 3), "GB_per_s": round(gbs_pc, 2),
-                            "frac_of_hbm_peak": round(gbs_pc / HBM_PEAK_GBS, 4)},
         "prefill": {"ms_per_pass": round(ms["prefill"], 4), "launches": n,
                     "us_per_launch": round(us_launch["prefill"], 3), "TFLOP_per_s": round(tfl, 2),
                     "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4), "flops_per_pass": pre_flops},
         "roofline": r_dec,
         "roofline_prefill": r_pre,
     }
+    if "decode_per_call" in ms:
+        gbs_pc = dec_bytes / (ms["decode_per_call"] * 1e-3) / 1e9
+        out["decode_per_call"] = {"ms_per_pass": round(ms["decode_per_call"], 4), "launches": n,
+                                  "us_per_launch": round(us_launch["decode_per_call"], 3),
+                                  "GB_per_s": round(gbs_pc, 2), "frac_of_hbm_peak": round(gbs_pc / HBM_PEAK_GBS, 4)}
     if cpu_layers:
         import oracle.qmm_oracle as O
         log("timing the CPU oracle on a sample")

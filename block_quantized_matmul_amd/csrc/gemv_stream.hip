@@ -91,6 +91,107 @@ template <int QT, int NT, bool XF16> struct RRegs {
   typename std::conditional<XF16, half4_t, float4_t>::type x[NT];
 };
 
+// Lane-constant placement of a stage. Weight chunk c = 64 j + lane of the 16
+// rows is row c / QC, chunk c % QC of that row; chunks past 16 * QC re-read
+// chunk 0 and are not stored (woff < 0). The activation piece of a lane is
+// block lane / 8 of the quad, elements 4 (lane % 8) .. +3, for every token
+// slot.
+template <int QT, int NT> struct RLane {
+  int wrow[RCfg<QT, NT>::w_loads];   // row within the group
+  int wcol[RCfg<QT, NT>::w_loads];   // byte offset within the row's quad
+  int woff[RCfg<QT, NT>::w_loads];   // LDS byte offset, or -1
+  int xb, xg, xh;                    // activation piece: block, operand lane group, half offset
+
+  __device__ __forceinline__ explicit RLane(int lane) {
+    constexpr int QC = RCfg<QT, NT>::quad_chunks;
+#pragma unroll
+    for (int j = 0; j < RCfg<QT, NT>::w_loads; ++j) {
+      const int c = 64 * j + lane;
+      const bool ok = c < 16 * QC;
+      wrow[j] = ok ? c / QC : 0;
+      wcol[j] = ok ? 16 * (c % QC) : 0;
+      woff[j] = ok ? wrow[j] * RCfg<QT, NT>::row_stride + wcol[j] : -1;
+    }
+    xb = lane >> 3;
+    const int xj = lane & 7;
+    xg = QT == QMM_TYPE_Q4_0 ? (xj & 3) : (xj >> 1);
+    xh = QT == QMM_TYPE_Q4_0 ? 4 * (xj >> 2) : 4 * (xj & 1);
+  }
+};
+
+// Consume one stage: copy the weights into the wavefront's LDS area (wl) and
+// the activations, as fp16 in MFMA operand order, into xs; then run the 8
+// blocks (4 pairs) through the matrix cores into acc.
+template <int QT, int NT, bool XF16>
+__device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RLane<QT, NT> &L, unsigned char *wl,
+                                          half8_t *xs, int lane, float acc[4]) {
+  using C = RCfg<QT, NT>;
+#pragma unroll
+  for (int j = 0; j < C::w_loads; ++j)
+    if (L.woff[j] >= 0) *reinterpret_cast<u32x4_t *>(wl + L.woff[j]) = r.w[j];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    half4_t h;
+    if constexpr (XF16) {
+      h = r.x[t];
+    } else {
+      const half2_t a = cvt_half2(r.x[t].x, r.x[t].y), b = cvt_half2(r.x[t].z, r.x[t].w);
+      h = half4_t{a.x, a.y, b.x, b.y};
+    }
+    *reinterpret_cast<half4_t *>(reinterpret_cast<_Float16 *>(xs + (4 * L.xb + L.xg) * NT + t) + L.xh) = h;
+  }
+  const int r16 = lane & 15, g = lane >> 4;
+  const unsigned char *rb0 = wl + r16 * C::row_stride;
+  const int slot = min(r16, NT - 1);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {  // pairs of blocks in the quad
+    const unsigned char *rb = rb0 + u * (2 * Block<QT>::bytes);
+    // A-operand rows past the NT token slots repeat the last slot (no
+    // divergent reads; their results are never stored)
+    const half8_t xe = xs[(4 * (2 * u) + g) * NT + slot];
+    const half8_t xo = xs[(4 * (2 * u + 1) + g) * NT + slot];
+    auto ld = [&](int off) { return *reinterpret_cast<const uint32_t *>(rb + off); };
+    if constexpr (QT == QMM_TYPE_Q4_0) {
+      const uint32_t a0 = ld(4 * g), a1 = ld(4 * g + 4), b = ld(20 + 4 * g), d0 = ld(0), d1 = ld(16);
+      gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), 0), d0 & 0xFFFFu);
+      gemv_block<NT>(acc, xo, gemv_codes<QT>(b, 0), d1 >> 16);
+    } else {
+      const uint32_t a0 = ld(8 * g), a1 = ld(8 * g + 4), a2 = ld(8 * g + 8);
+      const uint32_t b0 = ld(36 + 8 * g), b1 = ld(40 + 8 * g), d0 = ld(0), d1 = ld(32);
+      gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), shift16(a1, a2)), d0 & 0xFFFFu);
+      gemv_block<NT>(acc, xo, gemv_codes<QT>(b0, b1), d1 >> 16);
+    }
+  }
+}
+
+// Partial sums of the wavefronts, added in wavefront order. D element e of
+// lane l: token 4 (l / 16) + e, row l % 16. The barrier waits on LDS only, so
+// weight loads in flight need not land first.
+template <int NT>
+__device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const float acc[4],
+                                         __attribute__((address_space(1))) float *Y, int row0, int n_rows,
+                                         int n_tokens) {
+  constexpr int kRedLanes = NT > 4 ? 32 : 16;
+  if (lane < kRedLanes) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(wave * 32 + lane) * 4 + e] = acc[e];
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (threadIdx.x < 16 * NT) {
+    const int r = threadIdx.x & 15;
+    const int t = threadIdx.x >> 4;
+    const int src = r + 16 * (t >> 2);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRWaves; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
+    const int row = row0 + r;
+    if (t < n_tokens && row < n_rows) Y[static_cast<int64_t>(t) * n_rows + row] = sum;
+  }
+}
+
 template <int QT, int NT, bool XF16>
 __global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
     const RBatch batch) {
@@ -124,86 +225,31 @@ __global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
   unsigned char *wl = smem + wave * C::lds_per_wave;
   half8_t *xs = reinterpret_cast<half8_t *>(wl + C::w_lds);
   float *red = reinterpret_cast<float *>(smem + kRWaves * C::lds_per_wave);
-  const int r16 = lane & 15, g = lane >> 4;
+  const RLane<QT, NT> L(lane);
 
-  // Lane-constant addressing: weight chunk c = 64 j + lane of a stage is row
-  // c / QC, chunk c % QC; chunks past 16 * QC re-read chunk 0 of the stage
-  // and are not stored. Rows past the end re-read the last row.
+  // Rows past the end re-read the last row; token slots past n_tokens
+  // re-read the last token (their results are never stored).
   GPtr<uint8_t> wp[C::w_loads];
-  int woff[C::w_loads];
 #pragma unroll
-  for (int j = 0; j < C::w_loads; ++j) {
-    const int c = 64 * j + lane;
-    const bool ok = c < 16 * QC;
-    const int row = ok ? c / QC : 0, cc = ok ? c % QC : 0;
-    wp[j] = W + static_cast<int64_t>(min(row0 + row, n_rows - 1)) * nb1 + 16 * cc;
-    woff[j] = ok ? row * C::row_stride + 16 * cc : -1;
-  }
-  // Activation piece of this lane: block lane / 8 of the stage, elements
-  // 4 (lane % 8) .. +3, for every token slot (slots past n_tokens re-read the
-  // last token; their results are never stored).
-  const int xb = lane >> 3, xj = lane & 7;
-  const int xg = QT == QMM_TYPE_Q4_0 ? (xj & 3) : (xj >> 1);
-  const int xh = QT == QMM_TYPE_Q4_0 ? 4 * (xj >> 2) : 4 * (xj & 1);
+  for (int j = 0; j < C::w_loads; ++j)
+    wp[j] = W + static_cast<int64_t>(min(row0 + L.wrow[j], n_rows - 1)) * nb1 + L.wcol[j];
   int64_t xoff[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) xoff[t] = static_cast<int64_t>(min(t, n_tokens - 1)) * k + 32 * xb + 4 * xj;
+  for (int t = 0; t < NT; ++t) xoff[t] = static_cast<int64_t>(min(t, n_tokens - 1)) * k + 32 * L.xb + 4 * (lane & 7);
 
   auto issue = [&](RRegs<QT, NT, XF16> &r, int q) {
-    const int qc = q;
 #pragma unroll
-    for (int j = 0; j < C::w_loads; ++j)
-      r.w[j] = *(GPtr<u32x4_t>)(wp[j] + static_cast<int64_t>(qc) * (QC * 16));
+    for (int j = 0; j < C::w_loads; ++j) r.w[j] = *(GPtr<u32x4_t>)(wp[j] + static_cast<int64_t>(q) * (QC * 16));
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if constexpr (XF16)
-        r.x[t] = *(GPtr<half4_t>)(Xh + xoff[t] + 256 * qc);
+        r.x[t] = *(GPtr<half4_t>)(Xh + xoff[t] + 256 * q);
       else
-        r.x[t] = *(GPtr<float4_t>)(Xf + xoff[t] + 256 * qc);
+        r.x[t] = *(GPtr<float4_t>)(Xf + xoff[t] + 256 * q);
     }
   };
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](const RRegs<QT, NT, XF16> &r) {
-#pragma unroll
-    for (int j = 0; j < C::w_loads; ++j)
-      if (woff[j] >= 0) *reinterpret_cast<u32x4_t *>(wl + woff[j]) = r.w[j];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      half4_t h;
-      if constexpr (XF16) {
-        h = r.x[t];
-      } else {
-        const half2_t a = cvt_half2(r.x[t].x, r.x[t].y), b = cvt_half2(r.x[t].z, r.x[t].w);
-        h = half4_t{a.x, a.y, b.x, b.y};
-      }
-      *reinterpret_cast<half4_t *>(reinterpret_cast<_Float16 *>(xs + (4 * xb + xg) * NT + t) + xh) = h;
-    }
-    const unsigned char *rb0 = wl + r16 * C::row_stride;
-    const int slot = min(r16, NT - 1);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {  // pairs of blocks in the quad
-      const unsigned char *rb = rb0 + u * (2 * Block<QT>::bytes);
-      // only the NT token slots read activations; other A-operand rows stay zero
-      half8_t xe = {}, xo = {};
-      if (r16 < NT) {
-        xe = xs[(4 * (2 * u) + g) * NT + slot];
-        xo = xs[(4 * (2 * u + 1) + g) * NT + slot];
-      }
-      auto ld = [&](int off) { return *reinterpret_cast<const uint32_t *>(rb + off); };
-      if constexpr (QT == QMM_TYPE_Q4_0) {
-        const uint32_t a0 = ld(4 * g), a1 = ld(4 * g + 4), b = ld(20 + 4 * g), d0 = ld(0), d1 = ld(16);
-        gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), 0), d0 & 0xFFFFu);
-        gemv_block<NT>(acc, xo, gemv_codes<QT>(b, 0), d1 >> 16);
-      } else {
-        const uint32_t a0 = ld(8 * g), a1 = ld(8 * g + 4), a2 = ld(8 * g + 8);
-        const uint32_t b0 = ld(36 + 8 * g), b1 = ld(40 + 8 * g), d0 = ld(0), d1 = ld(32);
-        gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), shift16(a1, a2)), d0 & 0xFFFFu);
-        gemv_block<NT>(acc, xo, gemv_codes<QT>(b0, b1), d1 >> 16);
-      }
-    }
-  };
-
   // Rounds of up to D stages: all loads of a round are issued at once (the
   // whole wavefront's share of k in one round for the common shapes), then
   // the stages are consumed in order. Other wavefronts on the CU overlap
@@ -215,31 +261,9 @@ __global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
       if (q + i < q_hi) issue(st[i], q + i);
 #pragma unroll
     for (int i = 0; i < D; ++i)
-      if (q + i < q_hi) consume(st[i]);
+      if (q + i < q_hi) r_consume<QT, NT, XF16>(st[i], L, wl, xs, lane, acc);
   }
-
-  // Partial sums of the wavefronts, added in wavefront order. D element e
-  // of lane l: token 4 (l / 16) + e, row l % 16. The barrier waits on LDS
-  // only; the ring's spare loads need not land first.
-  constexpr int kRedLanes = NT > 4 ? 32 : 16;
-  if (lane < kRedLanes) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[(wave * 32 + lane) * 4 + e] = acc[e];
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (threadIdx.x < 16 * NT) {
-    const int r = threadIdx.x & 15;
-    const int t = threadIdx.x >> 4;
-    const int src = r + 16 * (t >> 2);
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kRWaves; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
-    const int row = row0 + r;
-    if (t < n_tokens && row < n_rows) Y[static_cast<int64_t>(t) * n_rows + row] = sum;
-  }
+  r_reduce<NT>(red, wave, lane, acc, Y, row0, n_rows, n_tokens);
 }
 
 // ------------------------------------------------------------------ host side
