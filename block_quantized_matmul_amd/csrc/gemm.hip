@@ -11,14 +11,20 @@
 //
 // Design (MI355X, gfx950). The path is a dense contraction, so it runs on
 // v_mfma_f32_16x16x32_f16 with fp32 accumulation. A 256-thread workgroup owns
-// a 128-row x 128-token output tile and walks k in stages of 128 (four
-// blocks). Each stage: the quantised blocks of 128 rows (9 KiB for Q4_0) and
-// the activation tile are fetched into registers while the previous stage is
-// on the matrix cores; then the blocks are decoded to fp16 d * (q - z) (exact
-// integer code, one fp16 rounding of the product) and written with the fp16
-// activations into padded LDS tiles; four wavefronts each run a 64 x 64
-// sub-tile as 4 x 4 MFMA tiles. Weights never exist in dequantised form
-// outside LDS.
+// a 128-row x 128-token output tile; its four wavefronts each compute 64 x 64
+// as 4 x 4 MFMA tiles. k advances in stages of 64 (two blocks):
+//  * staging: each thread loads half of one row's two blocks (5 or 9
+//    dwords inside the pair) and half of one token's 64 activations, two
+//    stages ahead of their use, decodes the blocks to fp16 d * (q - z) (exact
+//    integer code, one fp16 rounding of the product) and stores weights and
+//    activations into LDS;
+//  * LDS is double-buffered, so the stores of stage s + 1 (and their decode
+//    arithmetic) overlap the MFMAs of stage s, with one LDS-only barrier per
+//    stage; the 144-byte row pitch (an odd multiple of 16 bytes) keeps the
+//    16-byte stores and the MFMA operand reads free of bank conflicts;
+//  * two workgroups fit a CU (72 KiB of LDS each), so one's loads and
+//    barriers overlap the other's matrix work.
+// Weights never exist in dequantised form outside LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -26,14 +32,10 @@ namespace qmm {
 
 constexpr int kBM = 128;  // weight rows per tile
 constexpr int kBN = 128;  // tokens per tile
-constexpr int kBK = 128;  // k per stage (4 blocks)
-constexpr int kLdsStride = kBK + 8;  // halves; 16-byte pad breaks LDS bank conflicts
+constexpr int kBK = 64;   // k per stage (2 blocks)
+constexpr int kPitch = kBK + 8;  // halves per LDS row: 144 bytes
 constexpr int kGemmThreads = 256;
-
-// Decoded pair of blocks (the codes of block j as dwords, its scale bits).
-template <int QT> struct PairCodes;
-template <> struct PairCodes<QMM_TYPE_Q4_0> { uint32_t d[2]; uint32_t q[2][4]; };
-template <> struct PairCodes<QMM_TYPE_Q8_0> { uint32_t d[2]; uint32_t q[2][8]; };
+static_assert(kGemmThreads == 2 * kBM && kGemmThreads == 2 * kBN, "two staging threads per row and per token");
 
 template <int QT>
 __device__ __forceinline__ void load_block_u16(const uint8_t *p, uint32_t &d, uint32_t *q) {
@@ -41,47 +43,6 @@ __device__ __forceinline__ void load_block_u16(const uint8_t *p, uint32_t &d, ui
   d = ld_u16(p);
 #pragma unroll
   for (int i = 0; i < nq; ++i) q[i] = ld_u16(p + 2 + 4 * i) | (ld_u16(p + 4 + 4 * i) << 16);
-}
-
-// Blocks blk0 and blk0 + 1 of the row at rp; blocks at or past nblk read as
-// zero codes with zero scale.
-template <int QT, bool ALIGN4>
-__device__ __forceinline__ PairCodes<QT> load_pair(const uint8_t *rp, int blk0, int nblk) {
-  constexpr int BB = Block<QT>::bytes;
-  constexpr int nq = QT == QMM_TYPE_Q4_0 ? 4 : 8;
-  PairCodes<QT> c;
-  const uint8_t *p = rp + static_cast<int64_t>(blk0) * BB;
-  if (ALIGN4 && blk0 + 1 < nblk) {
-    // 2 * BB bytes from a 4-byte-aligned address: block 0 = dwords 0.., its
-    // codes start 2 bytes in; block 1 starts at byte BB (2 mod 4), its codes
-    // at BB + 2 (aligned).
-    constexpr int ndw = 2 * BB / 4;  // 9 (Q4_0) or 17 (Q8_0)
-    uint32_t w[ndw];
-#pragma unroll
-    for (int i = 0; i + 4 <= ndw; i += 4) {
-      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(p + 4 * i);
-      w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
-    }
-    w[ndw - 1] = ld_u32(p + 4 * (ndw - 1));
-    c.d[0] = w[0] & 0xFFFFu;
-#pragma unroll
-    for (int i = 0; i < nq; ++i) c.q[0][i] = shift16(w[i], w[i + 1]);
-    c.d[1] = w[nq] >> 16;
-#pragma unroll
-    for (int i = 0; i < nq; ++i) c.q[1][i] = w[nq + 1 + i];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (blk0 + j < nblk) {
-        load_block_u16<QT>(p + j * BB, c.d[j], c.q[j]);
-      } else {
-        c.d[j] = 0;
-#pragma unroll
-        for (int i = 0; i < nq; ++i) c.q[j][i] = 0;
-      }
-    }
-  }
-  return c;
 }
 
 // Decode one block to 32 fp16 weights fl16(d * (q - z)) in element order and
@@ -115,56 +76,141 @@ __device__ __forceinline__ void store_block_f16(_Float16 *dst, uint32_t d_bits, 
   for (int i = 0; i < 4; ++i) o[i] = u32x4_t{as_u32(h[4 * i]), as_u32(h[4 * i + 1]), as_u32(h[4 * i + 2]), as_u32(h[4 * i + 3])};
 }
 
-// Activation slice of one thread: 64 consecutive k values of one token.
-template <bool XF16> struct XRaw;
-template <> struct XRaw<true> { u32x4_t v[8]; };
-template <> struct XRaw<false> { float4_t v[16]; };
+// One staging thread's half of a stage's pair of blocks (h = 0: block 2 s,
+// h = 1: block 2 s + 1), as raw dwords. With 4-byte-aligned rows and a whole
+// pair, half 0 is the pair's first nq + 1 dwords (scale = low half of w[0],
+// codes = bytes 2.. = w shifted by 16 bits) and half 1 its last nq + 1 dwords
+// (scale = high half of w[0], codes = w[1..]); all lie inside the pair. The
+// loaded dwords are not touched until the stage is stored, so the loads stay
+// in flight (any arithmetic on them right after the load would wait for it).
+template <int QT> struct HalfRaw {
+  static constexpr int nq = QT == QMM_TYPE_Q4_0 ? 4 : 8;
+  uint32_t w[nq + 1];
+};
 
+template <int QT>
+__device__ __forceinline__ HalfRaw<QT> load_half_pair(const uint8_t *rp, int st, int h) {
+  constexpr int nq = HalfRaw<QT>::nq;
+  constexpr int BB = Block<QT>::bytes;
+  const uint8_t *p = rp + static_cast<int64_t>(st) * (2 * BB) + (h ? (BB - 2) : 0);  // 4-byte aligned
+  HalfRaw<QT> r;
+#pragma unroll
+  for (int i = 0; i + 4 <= nq + 1; i += 4) {
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(p + 4 * i);
+    r.w[i] = v.x; r.w[i + 1] = v.y; r.w[i + 2] = v.z; r.w[i + 3] = v.w;
+  }
+  r.w[nq] = ld_u32(p + 4 * nq);
+  return r;
+}
+
+// Block blk of the row with 16-bit loads (any even row stride), in the
+// layout of half 1 (scale in the high half of w[0], codes in w[1..]); a block
+// at or past nblk reads as zero codes with a zero scale.
+template <int QT>
+__device__ __forceinline__ HalfRaw<QT> load_half_u16(const uint8_t *rp, int blk, int nblk) {
+  constexpr int nq = HalfRaw<QT>::nq;
+  HalfRaw<QT> r;
+  if (blk < nblk) {
+    uint32_t d;
+    load_block_u16<QT>(rp + static_cast<int64_t>(blk) * Block<QT>::bytes, d, r.w + 1);
+    r.w[0] = d << 16;
+  } else {
+#pragma unroll
+    for (int i = 0; i <= nq; ++i) r.w[i] = 0;
+  }
+  return r;
+}
+
+// Decode a half (layout of half 0 if first_layout, else of half 1) and
+// store its 32 fp16 weights. first_layout may differ between lanes.
+template <int QT>
+__device__ __forceinline__ void store_half(_Float16 *dst, const HalfRaw<QT> &r, bool first_layout) {
+  constexpr int nq = HalfRaw<QT>::nq;
+  uint32_t q[nq];
+  const uint32_t d = first_layout ? (r.w[0] & 0xFFFFu) : (r.w[0] >> 16);
+#pragma unroll
+  for (int i = 0; i < nq; ++i) q[i] = first_layout ? shift16(r.w[i], r.w[i + 1]) : r.w[i + 1];
+  store_block_f16<QT>(dst, d, q);
+}
+
+// Activations of one stage (128 tokens x 64 k) as 16-byte pieces spread so
+// that consecutive lanes read consecutive pieces of one token's row: a
+// wavefront's load covers whole 128-byte runs of a few rows instead of one
+// piece of 64 different rows (which costs the address unit a cache line per
+// lane). fp16: piece c = 256 i + tid (i < 4) is token c / 8, elements
+// 8 (c % 8) .. +7; fp32: piece c = 256 i + tid (i < 8) is token c / 16,
+// elements 4 (c % 16) .. +3.
+template <bool XF16> struct XPieces;
+template <> struct XPieces<true> { u32x4_t v[4]; };
+template <> struct XPieces<false> { float4_t v[8]; };
+
+template <bool XF16> struct XMap {
+  static constexpr int n = XF16 ? 4 : 8;         // pieces per thread
+  static constexpr int per_tok = XF16 ? 8 : 16;  // pieces per token row of a stage
+  static constexpr int elems = XF16 ? 8 : 4;     // elements per piece
+};
+
+// Token rows are clamped to the last token; k0 + elements past k (the
+// missing second block of an odd count) read as zeros when `tail`.
 template <bool XF16>
-__device__ __forceinline__ XRaw<XF16> load_x(const void *X, int tok, bool tok_ok, int k, int k0) {
-  XRaw<XF16> r;
-  constexpr int per32 = XF16 ? 4 : 8;  // vectors per 32 elements
+__device__ __forceinline__ XPieces<XF16> load_x_pieces(const void *X, int tok0, int n_tokens, int k, int k0, int tid,
+                                                       bool tail) {
+  using M = XMap<XF16>;
+  XPieces<XF16> r;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const bool ok = tok_ok && (k0 + 32 * c < k);
-#pragma unroll
-    for (int i = 0; i < per32; ++i) {
-      if constexpr (XF16) {
-        const u32x4_t *p = reinterpret_cast<const u32x4_t *>(static_cast<const _Float16 *>(X) +
-                                                             static_cast<int64_t>(tok) * k + k0 + 32 * c) + i;
-        r.v[c * per32 + i] = ok ? *p : u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-        const float4_t *p = reinterpret_cast<const float4_t *>(static_cast<const float *>(X) +
-                                                               static_cast<int64_t>(tok) * k + k0 + 32 * c) + i;
-        r.v[c * per32 + i] = ok ? *p : float4_t{0.f, 0.f, 0.f, 0.f};
-      }
+  for (int i = 0; i < M::n; ++i) {
+    const int c = 256 * i + tid;
+    const int tok = min(tok0 + c / M::per_tok, n_tokens - 1);
+    const int e = k0 + M::elems * (c % M::per_tok);
+    const int64_t off = static_cast<int64_t>(tok) * k + e;
+    if (!tail || e < k) {
+      if constexpr (XF16)
+        r.v[i] = *reinterpret_cast<const u32x4_t *>(static_cast<const _Float16 *>(X) + off);
+      else
+        r.v[i] = *reinterpret_cast<const float4_t *>(static_cast<const float *>(X) + off);
+    } else {
+      if constexpr (XF16)
+        r.v[i] = u32x4_t{0u, 0u, 0u, 0u};
+      else
+        r.v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
   return r;
 }
 
 template <bool XF16>
-__device__ __forceinline__ void store_x(_Float16 *dst, const XRaw<XF16> &r) {
-  u32x4_t *o = reinterpret_cast<u32x4_t *>(dst);
-  if constexpr (XF16) {
+__device__ __forceinline__ void store_x_pieces(_Float16 *xs, const XPieces<XF16> &r, int tid) {
+  using M = XMap<XF16>;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = r.v[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4_t a = r.v[2 * i], b = r.v[2 * i + 1];
-      o[i] = u32x4_t{as_u32(cvt_half2(a.x, a.y)), as_u32(cvt_half2(a.z, a.w)), as_u32(cvt_half2(b.x, b.y)),
-                     as_u32(cvt_half2(b.z, b.w))};
+  for (int i = 0; i < M::n; ++i) {
+    const int c = 256 * i + tid;
+    _Float16 *dst = xs + (c / M::per_tok) * kPitch + M::elems * (c % M::per_tok);
+    if constexpr (XF16) {
+      *reinterpret_cast<u32x4_t *>(dst) = r.v[i];
+    } else {
+      const float4_t f = r.v[i];
+      *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(cvt_half2(f.x, f.y)), as_u32(cvt_half2(f.z, f.w))};
     }
   }
 }
 
+// Workgroup barrier that waits for LDS accesses only: __syncthreads() would
+// also wait for the global loads of later stages, which are meant to stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int QT, bool XF16, bool ALIGN4>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
-                                                            int64_t nb1, const void *__restrict__ X, int n_tokens,
-                                                            int k, float *__restrict__ Y, bool y_vec4, int row_tiles) {
-  __shared__ __attribute__((aligned(16))) _Float16 Ws[kBM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) _Float16 Xs[kBN * kLdsStride];
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
+                                                               int64_t nb1, const void *__restrict__ X, int n_tokens,
+                                                               int k, float *__restrict__ Y, bool y_vec4,
+                                                               int row_tiles) {
+  __shared__ __attribute__((aligned(16))) _Float16 Ws[2][kBM * kPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 Xs[2][kBN * kPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -174,12 +220,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
   const int row0 = static_cast<int>(blockIdx.x % row_tiles) * kBM;
   const int tok0 = static_cast<int>(blockIdx.x / row_tiles) * kBN;
 
-  // Staging roles: thread -> (row, pair of blocks) and (token, 64-wide half of the stage).
-  const int srow = tid >> 1, spair = tid & 1;
+  // Weight staging: thread -> (row, half of the stage's block pair). The two
+  // halves of a row sit in adjacent lanes, so each load instruction touches
+  // 32 rows rather than 64; with the 144-byte pitch the 16-byte stores of 8
+  // lanes (4 rows x 2 halves) still cover 8 distinct bank groups. Rows past
+  // the end re-read the last one.
+  const int srow = tid >> 1, sh = tid & 1;
   const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
-  const int stok = tid >> 1, shalf = tid & 1;
-  const bool stok_ok = tok0 + stok < n_tokens;
-  const int stok_c = min(tok0 + stok, n_tokens - 1);
+  const int wofs = srow * kPitch + 32 * sh;
 
   float4_t acc[4][4];
 #pragma unroll
@@ -187,34 +235,77 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t *__res
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int n_stages = (nblk + 3) / 4;
-  PairCodes<QT> wraw = load_pair<QT, ALIGN4>(rp, 2 * spair, nblk);
-  XRaw<XF16> xraw = load_x<XF16>(X, stok_c, stok_ok, k, 64 * shalf);
-
-  for (int s = 0; s < n_stages; ++s) {
-    __syncthreads();  // everyone is done reading the previous stage
-    store_block_f16<QT>(Ws + srow * kLdsStride + 64 * spair, wraw.d[0], wraw.q[0]);
-    store_block_f16<QT>(Ws + srow * kLdsStride + 64 * spair + 32, wraw.d[1], wraw.q[1]);
-    store_x<XF16>(Xs + stok * kLdsStride + 64 * shalf, xraw);
-    __syncthreads();
-    if (s + 1 < n_stages) {
-      wraw = load_pair<QT, ALIGN4>(rp, 4 * (s + 1) + 2 * spair, nblk);
-      xraw = load_x<XF16>(X, stok_c, stok_ok, k, kBK * (s + 1) + 64 * shalf);
-    }
+  struct Stage {
+    HalfRaw<QT> w;
+    XPieces<XF16> x;
+  };
+  // Stages with a whole pair of blocks; an odd block count leaves one more.
+  const int n_full = nblk / 2;
+  auto load = [&](Stage &r, int st) {
+    if constexpr (ALIGN4)
+      r.w = load_half_pair<QT>(rp, st, sh);
+    else
+      r.w = load_half_u16<QT>(rp, 2 * st + sh, nblk);
+    r.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * st, tid, false);
+  };
+  auto store = [&](int buf, const Stage &r) {
+    store_half<QT>(Ws[buf] + wofs, r.w, ALIGN4 && sh == 0);
+    store_x_pieces<XF16>(Xs[buf], r.x, tid);
+  };
+  // operands: A (weights) row 64 wm + 16 i + lane % 16, B (activations)
+  // token 64 wn + 16 j + lane % 16; elements 8 (lane / 16) .. +7 of the k step
+  const int aofs = (64 * wm + (lane & 15)) * kPitch + 8 * (lane >> 4);
+  const int bofs = (64 * wn + (lane & 15)) * kPitch + 8 * (lane >> 4);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 32) {
       half8_t a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const half8_t *>(Ws + (64 * wm + 16 * i + (lane & 15)) * kLdsStride + kk + 8 * (lane >> 4));
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const half8_t *>(Ws[buf] + aofs + 16 * i * kPitch + kk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const half8_t *>(Xs + (64 * wn + 16 * j + (lane & 15)) * kLdsStride + kk + 8 * (lane >> 4));
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const half8_t *>(Xs[buf] + bofs + 16 * j * kPitch + kk);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  if (n_full > 0) {
+    // Two register sets hold stages loaded two stages ahead of their use;
+    // stage s + 1 is stored into the other LDS buffer while stage s is on the
+    // matrix cores. Loads past the last whole stage re-read it (unconditional
+    // loads keep the wait counts exact); such data is stored but never used.
+    const int last = n_full - 1;
+    Stage r0, r1;
+    load(r0, 0);
+    load(r1, min(1, last));
+    store(0, r0);
+    load(r0, min(2, last));
+    lds_barrier();
+    int s = 0;
+    for (; s + 1 < n_full; s += 2) {
+      compute(0);               // stage s
+      store(1, r1);             // stage s + 1
+      load(r1, min(s + 3, last));
+      lds_barrier();
+      compute(1);               // stage s + 1
+      store(0, r0);             // stage s + 2 (a copy of the last stage at the end)
+      load(r0, min(s + 4, last));
+      lds_barrier();
+    }
+    if (s < n_full) compute(0);  // odd count of whole stages: the last one
+  }
+  if (nblk & 1) {
+    // the last, single block: half 0 loads it, half 1 stores zeros
+    const int buf = n_full & 1;
+    Stage t;
+    t.w = load_half_u16<QT>(rp, 2 * n_full + sh, nblk);
+    t.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * n_full, tid, true);
+    store_half<QT>(Ws[buf] + wofs, t.w, false);
+    store_x_pieces<XF16>(Xs[buf], t.x, tid);
+    lds_barrier();
+    compute(buf);
   }
 
   // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
