@@ -9,7 +9,7 @@
 // per block and multiply-add them with activations in registers).
 //
 // Design (MI355X, gfx950). The kernel is bound by HBM: every weight byte is
-// read exactly once. One workgroup owns 16 rows; its 8 wavefronts split the
+// read exactly once. One workgroup owns 16 rows; its 8 or 16 wavefronts split the
 // row's blocks into contiguous ranges and meet in LDS at the end, in a fixed
 // order (no atomics, so results are bitwise reproducible).
 //
@@ -40,8 +40,6 @@
 
 namespace qmm {
 
-constexpr int kGemvWaves = kKSplit;  // k split as in the streaming kernel
-constexpr int kGemvThreads = 64 * kGemvWaves;
 constexpr int kRing = 8;                  // weight units in flight per wavefront
 constexpr int kXLdsBudget = 64 * 1024;    // bytes of LDS for staged activations
 
@@ -115,12 +113,12 @@ __device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4
 }
 
 // Dynamic LDS: the staged activations of one chunk, chunk_blocks * 64 * NT bytes.
-template <int QT, int NT, bool XF16, bool ALIGN4>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
+template <int QT, int NT, bool XF16, bool ALIGN4, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
                                                             int64_t nb1, const void *__restrict__ X, int n_tokens,
                                                             int k, float *__restrict__ Y, int chunk_blocks) {
   extern __shared__ __attribute__((aligned(16))) half8_t xs[];
-  __shared__ float red[kGemvWaves][NT > 4 ? 32 : 16][4];
+  __shared__ float red[WAVES][NT > 4 ? 32 : 16][4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
@@ -145,8 +143,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__res
     const int upg = ALIGN4 ? 4 : 8;  // units per 8-block group
     const int span = ((b_hi - b_lo) & 7) == 0 ? upg : 1;
     const int ng = nu / span;
-    const int u0 = ubase + span * static_cast<int>((static_cast<int64_t>(wave) * ng) / kGemvWaves);
-    const int u1 = ubase + span * static_cast<int>((static_cast<int64_t>(wave + 1) * ng) / kGemvWaves);
+    const int u0 = ubase + span * static_cast<int>((static_cast<int64_t>(wave) * ng) / WAVES);
+    const int u1 = ubase + span * static_cast<int>((static_cast<int64_t>(wave + 1) * ng) / WAVES);
     const bool has_units = u0 < u1;
 
     // Weight loads go out first, so the activation staging below overlaps
@@ -158,7 +156,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__res
       for (int i = 0; i < kRing; ++i) ring[i] = gemv_load<QT, ALIGN4>(rp, min(u0 + i, u1 - 1), g);
     }
     if (b_lo > 0) __syncthreads();  // previous chunk's activations no longer read
-    gemv_stage_x<QT, NT, XF16, kGemvThreads>(xs, X, n_tokens, k, b_lo, b_hi);
+    gemv_stage_x<QT, NT, XF16, 64 * WAVES>(xs, X, n_tokens, k, b_lo, b_hi);
     __syncthreads();
 
     if (has_units) {
@@ -173,7 +171,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__res
         }
       }
     }
-    if (ALIGN4 && ((b_hi - b_lo) & 1) && wave == kGemvWaves - 1) {
+    if (ALIGN4 && ((b_hi - b_lo) & 1) && wave == WAVES - 1) {
       // Odd block count in this chunk (only the last one): the final block
       // starts 4-byte aligned; 16-bit loads.
       const GemvRaw<QT, false> t = gemv_load<QT, false>(rp, b_hi - 1, g);
@@ -193,7 +191,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const uint8_t *__res
     const int src = r + 16 * (t >> 2);
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGemvWaves; ++w) s += red[w][src][t & 3];
+    for (int w = 0; w < WAVES; ++w) s += red[w][src][t & 3];
     const int orow = row0 + r;
     if (t < n_tokens && orow < n_rows) Y[static_cast<int64_t>(t) * n_rows + orow] = s;
   }
@@ -219,15 +217,21 @@ template <typename K> static hipError_t allow_lds(K kernel) {
   return e;
 }
 
-template <int QT, int NT, bool XF16>
-static hipError_t gemv_go(bool align4, const GemvLaunch &a) {
-  hipError_t e = allow_lds(align4 ? gemv_kernel<QT, NT, XF16, true> : gemv_kernel<QT, NT, XF16, false>);
+template <int QT, int NT, bool XF16, int WAVES>
+static hipError_t gemv_go_w(bool align4, const GemvLaunch &a) {
+  hipError_t e = allow_lds(align4 ? gemv_kernel<QT, NT, XF16, true, WAVES> : gemv_kernel<QT, NT, XF16, false, WAVES>);
   if (e != hipSuccess) return e;
   if (align4)
-    return launch(gemv_kernel<QT, NT, XF16, true>, a.grid, dim3(kGemvThreads), a.lds, a.s, a.w, a.n_rows, a.nblk,
+    return launch(gemv_kernel<QT, NT, XF16, true, WAVES>, a.grid, dim3(64 * WAVES), a.lds, a.s, a.w, a.n_rows, a.nblk,
                   a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks);
-  return launch(gemv_kernel<QT, NT, XF16, false>, a.grid, dim3(kGemvThreads), a.lds, a.s, a.w, a.n_rows, a.nblk,
+  return launch(gemv_kernel<QT, NT, XF16, false, WAVES>, a.grid, dim3(64 * WAVES), a.lds, a.s, a.w, a.n_rows, a.nblk,
                 a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks);
+}
+
+template <int QT, int NT, bool XF16>
+static hipError_t gemv_go(bool align4, const GemvLaunch &a) {
+  return k_split_for(a.grid.x, device_cus()) == kKSplitSmall ? gemv_go_w<QT, NT, XF16, kKSplitSmall>(align4, a)
+                                                             : gemv_go_w<QT, NT, XF16, kKSplitLarge>(align4, a);
 }
 
 template <int QT, bool XF16>

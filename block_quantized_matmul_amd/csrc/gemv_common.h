@@ -8,10 +8,18 @@
 namespace qmm {
 
 // Both decode kernels give a 16-row group to one workgroup whose wavefronts
-// split k into this many contiguous ranges of 8-block groups and add their
-// partial sums in wavefront order; sharing the split makes their results
-// bitwise identical wherever both apply.
-constexpr int kKSplit = 8;
+// split k into contiguous ranges of 8-block groups and add their partial sums
+// in wavefront order. A launch with no more row groups than the GPU has CUs
+// (one workgroup per CU) uses 16 wavefronts, halving each one's share and so
+// the compute left after its data arrives; larger launches use 8, which lets
+// two workgroups share a CU and overlap. Both kernels take the same split for
+// the same launch size, so their results are bitwise identical wherever both
+// apply.
+constexpr int kKSplitSmall = 16;
+constexpr int kKSplitLarge = 8;
+__host__ inline int k_split_for(int64_t row_groups, int cus) {
+  return cus > 0 && row_groups <= cus ? kKSplitSmall : kKSplitLarge;
+}
 
 // B-operand: this lane's 8 exact codes (q - z) of one block.
 template <int QT> __device__ __forceinline__ half8_t gemv_codes(uint32_t q0, uint32_t q1);

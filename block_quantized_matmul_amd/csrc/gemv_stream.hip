@@ -11,7 +11,8 @@
 // copies that of a plain streaming read as closely as it can.
 //  * A workgroup owns one 16-row group of one matrix; a launch's grid is
 //    (row groups of its largest matrix) x (matrices), and the hardware
-//    balances the workgroups across the CUs. Its 8 wavefronts split k into
+//    balances the workgroups across the CUs. Its 8 or 16 wavefronts (see
+//    k_split_for) split k into
 //    contiguous ranges of quads (8 blocks: 144 bytes Q4_0 / 272 bytes Q8_0
 //    per row, a whole number of 16-byte chunks) and stream them
 //    independently; they meet once, at the end, to add their partial sums in
@@ -37,8 +38,6 @@
 
 namespace qmm {
 
-constexpr int kRWaves = kKSplit;  // wavefronts per workgroup (one 16-row group, k split kKSplit ways)
-constexpr int kRThreads = 64 * kRWaves;
 constexpr int kRMaxMats = 16;
 
 template <int QT, int NT> struct RCfg {
@@ -167,7 +166,7 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
 // Partial sums of the wavefronts, added in wavefront order. D element e of
 // lane l: token 4 (l / 16) + e, row l % 16. The barrier waits on LDS only, so
 // weight loads in flight need not land first.
-template <int NT>
+template <int NT, int WAVES>
 __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const float acc[4],
                                          __attribute__((address_space(1))) float *Y, int row0, int n_rows,
                                          int n_tokens) {
@@ -186,14 +185,14 @@ __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const f
     const int src = r + 16 * (t >> 2);
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kRWaves; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
+    for (int w = 0; w < WAVES; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
     const int row = row0 + r;
     if (t < n_tokens && row < n_rows) Y[static_cast<int64_t>(t) * n_rows + row] = sum;
   }
 }
 
-template <int QT, int NT, bool XF16>
-__global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
+template <int QT, int NT, bool XF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 4) void gemv_stream_kernel(
     const RBatch batch) {
   (void)batch;  // read through the kernel-argument pointer
   using C = RCfg<QT, NT>;
@@ -220,11 +219,11 @@ __global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
   const int row0 = rg * 16;
   // this wavefront's quads [q_lo, q_hi)
   const int qn = nblk >> 3;
-  const int q_lo = (wave * qn) / kRWaves, q_hi = ((wave + 1) * qn) / kRWaves;
+  const int q_lo = (wave * qn) / WAVES, q_hi = ((wave + 1) * qn) / WAVES;
 
   unsigned char *wl = smem + wave * C::lds_per_wave;
   half8_t *xs = reinterpret_cast<half8_t *>(wl + C::w_lds);
-  float *red = reinterpret_cast<float *>(smem + kRWaves * C::lds_per_wave);
+  float *red = reinterpret_cast<float *>(smem + WAVES * C::lds_per_wave);
   const RLane<QT, NT> L(lane);
 
   // Rows past the end re-read the last row; token slots past n_tokens
@@ -263,23 +262,29 @@ __global__ __launch_bounds__(kRThreads, 4) void gemv_stream_kernel(
     for (int i = 0; i < D; ++i)
       if (q + i < q_hi) r_consume<QT, NT, XF16>(st[i], L, wl, xs, lane, acc);
   }
-  r_reduce<NT>(red, wave, lane, acc, Y, row0, n_rows, n_tokens);
+  r_reduce<NT, WAVES>(red, wave, lane, acc, Y, row0, n_rows, n_tokens);
 }
 
 // ------------------------------------------------------------------ host side
 
+template <int QT, int NT, bool XF16, int WAVES>
+static hipError_t r_go_w(const RBatch &B, int count, int max_rg, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(WAVES) * RCfg<QT, NT>::lds_per_wave + WAVES * 32 * 4 * sizeof(float);
+  return launch(gemv_stream_kernel<QT, NT, XF16, WAVES>, dim3(max_rg, count), dim3(64 * WAVES), lds, s, B);
+}
+
 template <int QT, int NT, bool XF16>
-static hipError_t r_go(const RBatch &B, int count, int max_rg, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(kRWaves) * RCfg<QT, NT>::lds_per_wave + kRWaves * 32 * 4 * sizeof(float);
-  return launch(gemv_stream_kernel<QT, NT, XF16>, dim3(max_rg, count), dim3(kRThreads), lds, s, B);
+static hipError_t r_go(const RBatch &B, int count, int max_rg, int waves, hipStream_t s) {
+  return waves == kKSplitSmall ? r_go_w<QT, NT, XF16, kKSplitSmall>(B, count, max_rg, s)
+                               : r_go_w<QT, NT, XF16, kKSplitLarge>(B, count, max_rg, s);
 }
 
 template <int QT, bool XF16>
-static hipError_t r_nt(int nt, const RBatch &B, int count, int max_rg, hipStream_t s) {
-  if (nt <= 1) return r_go<QT, 1, XF16>(B, count, max_rg, s);
-  if (nt <= 2) return r_go<QT, 2, XF16>(B, count, max_rg, s);
-  if (nt <= 4) return r_go<QT, 4, XF16>(B, count, max_rg, s);
-  return r_go<QT, 8, XF16>(B, count, max_rg, s);
+static hipError_t r_nt(int nt, const RBatch &B, int count, int max_rg, int waves, hipStream_t s) {
+  if (nt <= 1) return r_go<QT, 1, XF16>(B, count, max_rg, waves, s);
+  if (nt <= 2) return r_go<QT, 2, XF16>(B, count, max_rg, waves, s);
+  if (nt <= 4) return r_go<QT, 4, XF16>(B, count, max_rg, waves, s);
+  return r_go<QT, 8, XF16>(B, count, max_rg, waves, s);
 }
 
 static int nt_slots(int64_t n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
@@ -306,6 +311,7 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t str
     const int qt = d[i].qtype, nt = nt_slots(d[i].n_tokens);
     const bool xf = d[i].x_f16;
     int j = i, count = 0, max_rg = 0;
+    int64_t total_rg = 0;
     while (j < count_all && count < kRMaxMats && streamable(d[j]) && d[j].qtype == qt && d[j].x_f16 == xf &&
            nt_slots(d[j].n_tokens) == nt) {
       RMat &r = B.m[count++];
@@ -318,15 +324,17 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t str
       r.n_tokens = static_cast<int>(d[j].n_tokens);
       r.k = static_cast<int>(d[j].k);
       max_rg = max(max_rg, static_cast<int>((d[j].n_rows + 15) / 16));
+      total_rg += (d[j].n_rows + 15) / 16;
       ++j;
     }
+    const int waves = k_split_for(total_rg, device_cus());
     hipError_t e;
     if (qt == QMM_TYPE_Q4_0)
-      e = xf ? r_nt<QMM_TYPE_Q4_0, true>(nt, B, count, max_rg, stream)
-             : r_nt<QMM_TYPE_Q4_0, false>(nt, B, count, max_rg, stream);
+      e = xf ? r_nt<QMM_TYPE_Q4_0, true>(nt, B, count, max_rg, waves, stream)
+             : r_nt<QMM_TYPE_Q4_0, false>(nt, B, count, max_rg, waves, stream);
     else
-      e = xf ? r_nt<QMM_TYPE_Q8_0, true>(nt, B, count, max_rg, stream)
-             : r_nt<QMM_TYPE_Q8_0, false>(nt, B, count, max_rg, stream);
+      e = xf ? r_nt<QMM_TYPE_Q8_0, true>(nt, B, count, max_rg, waves, stream)
+             : r_nt<QMM_TYPE_Q8_0, false>(nt, B, count, max_rg, waves, stream);
     if (e != hipSuccess) return e;
     i = j;
   }

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <tuple>
 #include <utility>
 
@@ -22,6 +23,18 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
         return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, shmem, stream);
       },
       values);
+}
+
+// CUs of the current device (read once per device; 0 if HIP cannot tell).
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,

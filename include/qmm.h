@@ -154,7 +154,10 @@ typedef struct qmm_matmul_desc {
  * read only during the call. Every descriptor is validated before anything is
  * launched; on failure the status of the first invalid descriptor is
  * returned and nothing is enqueued. Outputs must not overlap any input or
- * each other. count == 0 is a no-op; count < 0 or descs == NULL with
+ * each other. Results are reproducible for a given batch; a MUL_MAT in a batch
+ * may differ in its last bits from the same MUL_MAT called alone, because the
+ * decode kernel splits k according to the size of its launch (both are within
+ * the stated error bound). count == 0 is a no-op; count < 0 or descs == NULL with
  * count > 0 returns QMM_ERR_NULL / QMM_ERR_SHAPE.
  */
 int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream);
