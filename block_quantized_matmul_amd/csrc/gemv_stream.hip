@@ -51,6 +51,13 @@ template <int QT, int NT> struct RCfg {
   // kernel then fits 4 wavefronts per SIMD, i.e. 2 workgroups per CU)
   static constexpr int stage_vgprs = 4 * w_loads + NT * 4;
   static constexpr int depth = (64 / stage_vgprs) < 1 ? 1 : (64 / stage_vgprs > 6 ? 6 : 64 / stage_vgprs);
+  // With 8 wavefronts per workgroup (launches larger than the GPU), Q4_0
+  // with one or two tokens takes rounds of 2 stages (the whole share for
+  // k = 4096) so the kernel fits in ~60 VGPRs and 6-8 wavefronts per SIMD:
+  // more workgroups per CU overlap one another's loads and compute.
+  static constexpr bool lean = QT == QMM_TYPE_Q4_0 && NT <= 2;
+  static constexpr int depth_large = lean ? 2 : depth;
+  static constexpr int waves_per_simd_large = !lean ? 4 : (NT == 1 ? 8 : 6);
   static constexpr int w_lds = 16 * row_stride;
   static constexpr int x_lds = 8 * 4 * NT * 16;                      // 8 blocks x 4 lane groups x NT slots x 8 halves
   static constexpr int lds_per_wave = w_lds + x_lds;
@@ -192,12 +199,12 @@ __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const f
 }
 
 template <int QT, int NT, bool XF16, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 4) void gemv_stream_kernel(
+__global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::waves_per_simd_large : 4)) void gemv_stream_kernel(
     const RBatch batch) {
   (void)batch;  // read through the kernel-argument pointer
   using C = RCfg<QT, NT>;
   constexpr int QC = C::quad_chunks;
-  constexpr int D = C::depth;
+  constexpr int D = WAVES == kKSplitLarge ? C::depth_large : C::depth;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const u32x16_t rec = ((KRec)__builtin_amdgcn_kernarg_segment_ptr())[blockIdx.y];
   auto ptr = [&](int i) { return (static_cast<uint64_t>(rec[i + 1]) << 32) | rec[i]; };
