@@ -26,6 +26,8 @@ SOURCES = ["qmm_api.hip", "dequant.hip", "gemv.hip", "gemv_stream.hip", "gemm.hi
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # let the hardware preload the first kernel arguments into scalar registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

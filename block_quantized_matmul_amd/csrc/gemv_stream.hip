@@ -86,11 +86,13 @@ struct RBatch {
 
 typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
 template <class T> using GPtr = const __attribute__((address_space(1))) T *;
-// The batch is the kernel's only argument, so it sits at the start of the
-// kernel-argument segment; a record is read through that constant
-// address-space pointer as one vector (indexing the by-value parameter with a
-// run-time index would copy the whole table to scratch).
+// A record is read through the kernel-argument segment pointer as one vector
+// (indexing the by-value parameter with a run-time index would copy the whole
+// table to scratch).
 typedef const __attribute__((address_space(4))) u32x16_t *KRec;
+// Byte offset of the table in the kernel-argument segment: it follows
+// matrix 0's eight scalar arguments (48 bytes) and two 8-byte pads.
+constexpr int kRTableOffset = 64;
 
 template <int QT, int NT, bool XF16> struct RRegs {
   u32x4_t w[RCfg<QT, NT>::w_loads];
@@ -200,26 +202,46 @@ __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const f
 
 template <int QT, int NT, bool XF16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::waves_per_simd_large : 4)) void gemv_stream_kernel(
-    const RBatch batch) {
+    const uint8_t *W0, const void *X0, float *Y0, int64_t nb1_0, int n_rows0, int nblk0, int n_tokens0, int k0,
+    int64_t, int64_t, const RBatch batch) {
   (void)batch;  // read through the kernel-argument pointer
   using C = RCfg<QT, NT>;
   constexpr int QC = C::quad_chunks;
   constexpr int D = WAVES == kKSplitLarge ? C::depth_large : C::depth;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const u32x16_t rec = ((KRec)__builtin_amdgcn_kernarg_segment_ptr())[blockIdx.y];
-  auto ptr = [&](int i) { return (static_cast<uint64_t>(rec[i + 1]) << 32) | rec[i]; };
-  const int n_rows = static_cast<int>(rec[8]);
+  // Matrix 0's fields are scalar arguments, which the hardware preloads into
+  // scalar registers when the wavefront starts (kernel-argument preloading),
+  // so its loads are issued without a memory round trip for the descriptor.
+  // Other matrices read their record from the table that follows them.
+  uint64_t wp0, xp0, yp0;
+  int64_t nb1;
+  int n_rows, nblk, n_tokens, k;
+  if (blockIdx.y == 0) {
+    wp0 = reinterpret_cast<uint64_t>(W0);
+    xp0 = reinterpret_cast<uint64_t>(X0);
+    yp0 = reinterpret_cast<uint64_t>(Y0);
+    nb1 = nb1_0;
+    n_rows = n_rows0, nblk = nblk0, n_tokens = n_tokens0, k = k0;
+  } else {
+    typedef const __attribute__((address_space(4))) char *KBytes;
+    const u32x16_t rec = ((KRec)((KBytes)__builtin_amdgcn_kernarg_segment_ptr() + kRTableOffset))[blockIdx.y];
+    auto ptr = [&](int i) { return (static_cast<uint64_t>(rec[i + 1]) << 32) | rec[i]; };
+    wp0 = ptr(0);
+    xp0 = ptr(2);
+    yp0 = ptr(4);
+    nb1 = static_cast<int64_t>(ptr(6));
+    n_rows = static_cast<int>(rec[8]), nblk = static_cast<int>(rec[9]), n_tokens = static_cast<int>(rec[10]),
+    k = static_cast<int>(rec[11]);
+  }
   const int rg = blockIdx.x;
   if (rg * 16 >= n_rows) return;  // whole workgroup: past this matrix's rows
-  // The pointers are rebuilt from integers, so they are cast to the global
+  // The pointers may be rebuilt from integers, so they are cast to the global
   // address space explicitly (generic pointers would make every access a
   // flat access, which also counts on the LDS counter and coarsens waits).
-  const GPtr<uint8_t> W = (GPtr<uint8_t>)ptr(0);
-  const GPtr<float> Xf = (GPtr<float>)ptr(2);
-  const GPtr<_Float16> Xh = (GPtr<_Float16>)ptr(2);
-  __attribute__((address_space(1))) float *Y = (__attribute__((address_space(1))) float *)ptr(4);
-  const int64_t nb1 = static_cast<int64_t>(ptr(6));
-  const int nblk = static_cast<int>(rec[9]), n_tokens = static_cast<int>(rec[10]), k = static_cast<int>(rec[11]);
+  const GPtr<uint8_t> W = (GPtr<uint8_t>)wp0;
+  const GPtr<float> Xf = (GPtr<float>)xp0;
+  const GPtr<_Float16> Xh = (GPtr<_Float16>)xp0;
+  __attribute__((address_space(1))) float *Y = (__attribute__((address_space(1))) float *)yp0;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -277,7 +299,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
 template <int QT, int NT, bool XF16, int WAVES>
 static hipError_t r_go_w(const RBatch &B, int count, int max_rg, hipStream_t s) {
   const size_t lds = static_cast<size_t>(WAVES) * RCfg<QT, NT>::lds_per_wave + WAVES * 32 * 4 * sizeof(float);
-  return launch(gemv_stream_kernel<QT, NT, XF16, WAVES>, dim3(max_rg, count), dim3(64 * WAVES), lds, s, B);
+  const RMat &m0 = B.m[0];
+  return launch(gemv_stream_kernel<QT, NT, XF16, WAVES>, dim3(max_rg, count), dim3(64 * WAVES), lds, s, m0.W, m0.X,
+                m0.Y, m0.nb1, m0.n_rows, m0.nblk, m0.n_tokens, m0.k, int64_t{0}, int64_t{0}, B);
 }
 
 template <int QT, int NT, bool XF16>
