@@ -22,6 +22,8 @@
 //    arithmetic) overlap the MFMAs of stage s, with one LDS-only barrier per
 //    stage; the 144-byte row pitch (an odd multiple of 16 bytes) keeps the
 //    16-byte stores and the MFMA operand reads free of bank conflicts;
+//  * within a stage the MFMAs are interleaved with the decode, the LDS
+//    stores and the loads of the next stages (interleave_stage);
 //  * two workgroups fit a CU (72 KiB of LDS each), so one's loads and
 //    barriers overlap the other's matrix work.
 // Weights never exist in dequantised form outside LDS.
@@ -204,6 +206,27 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Instruction order for one pipelined stage (32 MFMAs, the next stage's
+// decode and LDS stores, its global loads): the first operand reads, then
+// each MFMA followed by two VALU instructions of the decode, with an LDS
+// store, an operand read and a global load spread between them. A wavefront
+// issues in order, so without this the 32 MFMAs go out back to back and the
+// decode waits behind them; interleaved, the decode runs while the matrix
+// cores work.
+__device__ __forceinline__ void interleave_stage() {
+  constexpr int kDsRead = 0x100, kDsWrite = 0x200, kMfma = 0x008, kValu = 0x002, kVmemRead = 0x020;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, 2, 0);
+    if ((i & 3) == 0) __builtin_amdgcn_sched_group_barrier(kDsWrite, 1, 0);
+    if ((i & 3) == 2) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    if ((i & 7) == 5) __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
+  }
+}
+
 template <int QT, bool XF16, bool ALIGN4>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
                                                                int64_t nb1, const void *__restrict__ X, int n_tokens,
@@ -288,10 +311,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
       compute(0);               // stage s
       store(1, r1);             // stage s + 1
       load(r1, min(s + 3, last));
+      interleave_stage();
       lds_barrier();
       compute(1);               // stage s + 1
       store(0, r0);             // stage s + 2 (a copy of the last stage at the end)
       load(r0, min(s + 4, last));
+      interleave_stage();
       lds_barrier();
     }
     if (s < n_full) compute(0);  // odd count of whole stages: the last one
