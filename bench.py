@@ -316,8 +316,12 @@ def main():
     torch.cuda.synchronize()
     outs = Y1 + (Y1b if "decode_per_call" in passes else []) + Y2
     refs = [y.clone() for y in outs]
-    if "decode_per_call" in passes and not all(torch.equal(a, b) for a, b in zip(Y1, Y1b)):
-        raise RuntimeError("batched and per-call decode outputs differ")
+    if "decode_per_call" in passes:
+        # a batched launch may split k differently from a single call, so the
+        # two agree within rounding, not bitwise
+        for a, b in zip(Y1, Y1b):
+            if not torch.allclose(a, b, rtol=2e-3, atol=1e-4 * float(b.abs().max())):
+                raise RuntimeError("batched and per-call decode outputs differ beyond rounding")
     graphs = {}
     for name, f in passes.items():
         graphs[name] = torch.cuda.CUDAGraph()
