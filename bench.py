@@ -158,7 +158,7 @@ def summarize_counters(dirs):
     factor = {}
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
         cal = [v for (k, c), vs in agg.items() if c == cn and "copyBuffer" in k for v in vs
-               if v * 1024 > COPY_CAL_BYTES / 2]
+               if v * 1024 > COPY_CAL_BYTES / 4]
         if cal:
             factor[cn] = COPY_CAL_BYTES / (statistics.mean(cal) * 1024)
             print(f"CALIBRATION {cn}: copy of {COPY_CAL_BYTES} bytes counts {statistics.mean(cal) * 1024:.0f} "

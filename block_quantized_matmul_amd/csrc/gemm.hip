@@ -37,6 +37,8 @@ constexpr int kBN = 128;  // tokens per tile
 constexpr int kBK = 64;   // k per stage (2 blocks)
 constexpr int kPitch = kBK + 8;  // halves per LDS row: 144 bytes
 constexpr int kGemmThreads = 256;
+constexpr int kXcds = 8;       // XCDs of the GPU; workgroups are dealt to them round-robin
+constexpr int kGroupRows = 8;  // row tiles per group of the tile order
 static_assert(kGemmThreads == 2 * kBM && kGemmThreads == 2 * kBN, "two staging threads per row and per token");
 
 template <int QT>
@@ -239,9 +241,21 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  // 1-D grid: consecutive workgroups walk the row tiles of one token tile.
-  const int row0 = static_cast<int>(blockIdx.x % row_tiles) * kBM;
-  const int tok0 = static_cast<int>(blockIdx.x / row_tiles) * kBN;
+  // Tile of this workgroup. Workgroups go to the 8 XCDs round-robin, so
+  // XCD x = blockIdx % 8 takes a contiguous range of tile numbers (a plain
+  // 1-D order for the remainder); within it, tiles run over groups of
+  // kGroupRows row tiles, row tile fastest, so the workgroups of one XCD share
+  // weight rows and activation tokens in its L2.
+  const int n_tiles = static_cast<int>(gridDim.x);
+  const int bid = static_cast<int>(blockIdx.x);
+  const int per_xcd = n_tiles / kXcds;
+  const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
+  const int tok_tiles = n_tiles / row_tiles;
+  const int in_group = kGroupRows * tok_tiles;
+  const int first_row = (lin / in_group) * kGroupRows;
+  const int group_rows = min(row_tiles - first_row, kGroupRows);
+  const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
+  const int tok0 = ((lin % in_group) / group_rows) * kBN;
 
   // Weight staging: thread -> (row, half of the stage's block pair). The two
   // halves of a row sit in adjacent lanes, so each load instruction touches
