@@ -93,6 +93,8 @@ typedef const __attribute__((address_space(4))) u32x16_t *KRec;
 // Byte offset of the table in the kernel-argument segment: it follows
 // matrix 0's eight scalar arguments (48 bytes) and two 8-byte pads.
 constexpr int kRTableOffset = 64;
+// Fourth word of a buffer resource: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int QT, int NT, bool XF16> struct RRegs {
   u32x4_t w[RCfg<QT, NT>::w_loads];
@@ -235,12 +237,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   }
   const int rg = blockIdx.x;
   if (rg * 16 >= n_rows) return;  // whole workgroup: past this matrix's rows
-  // The pointers may be rebuilt from integers, so they are cast to the global
-  // address space explicitly (generic pointers would make every access a
-  // flat access, which also counts on the LDS counter and coarsens waits).
-  const GPtr<uint8_t> W = (GPtr<uint8_t>)wp0;
-  const GPtr<float> Xf = (GPtr<float>)xp0;
-  const GPtr<_Float16> Xh = (GPtr<_Float16>)xp0;
+  // The output pointer may be rebuilt from integers, so it is cast to the
+  // global address space explicitly (a generic pointer would make the store a
+  // flat access).
   __attribute__((address_space(1))) float *Y = (__attribute__((address_space(1))) float *)yp0;
 
   const int lane = threadIdx.x & 63;
@@ -255,25 +254,37 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   float *red = reinterpret_cast<float *>(smem + WAVES * C::lds_per_wave);
   const RLane<QT, NT> L(lane);
 
-  // Rows past the end re-read the last row; token slots past n_tokens
-  // re-read the last token (their results are never stored).
-  GPtr<uint8_t> wp[C::w_loads];
+  // Weights and activations are read through buffer resources: a uniform
+  // base with 32-bit per-lane offsets (one multiply per load slot, once) and
+  // the quad's offset in a scalar register, so advancing a stage costs no
+  // vector instructions. A raw buffer read at or past num_records returns
+  // zero, so rows past n_rows need no clamp (their results are never stored).
+  // Token slots past n_tokens re-read the last token.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void *>(wp0), 0, static_cast<int>(static_cast<uint32_t>(n_rows * nb1)), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void *>(xp0), 0, static_cast<int>(static_cast<uint32_t>(n_tokens * k * (XF16 ? 2 : 4))),
+      kRsrcWord3);
+  uint32_t wv[C::w_loads];
 #pragma unroll
   for (int j = 0; j < C::w_loads; ++j)
-    wp[j] = W + static_cast<int64_t>(min(row0 + L.wrow[j], n_rows - 1)) * nb1 + L.wcol[j];
-  int64_t xoff[NT];
+    wv[j] = static_cast<uint32_t>(row0 + L.wrow[j]) * static_cast<uint32_t>(nb1) + static_cast<uint32_t>(L.wcol[j]);
+  uint32_t xv[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) xoff[t] = static_cast<int64_t>(min(t, n_tokens - 1)) * k + 32 * L.xb + 4 * (lane & 7);
+  for (int t = 0; t < NT; ++t)
+    xv[t] = (static_cast<uint32_t>(min(t, n_tokens - 1) * k) + 32 * L.xb + 4 * (lane & 7)) * (XF16 ? 2 : 4);
 
   auto issue = [&](RRegs<QT, NT, XF16> &r, int q) {
+    const int wq = q * (QC * 16), xq = q * 256 * (XF16 ? 2 : 4);
 #pragma unroll
-    for (int j = 0; j < C::w_loads; ++j) r.w[j] = *(GPtr<u32x4_t>)(wp[j] + static_cast<int64_t>(q) * (QC * 16));
+    for (int j = 0; j < C::w_loads; ++j)
+      r.w[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wres, wv[j], wq, 0));
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if constexpr (XF16)
-        r.x[t] = *(GPtr<half4_t>)(Xh + xoff[t] + 256 * q);
+        r.x[t] = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(xres, xv[t], xq, 0));
       else
-        r.x[t] = *(GPtr<float4_t>)(Xf + xoff[t] + 256 * q);
+        r.x[t] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xv[t], xq, 0));
     }
   };
 
@@ -322,7 +333,10 @@ static int nt_slots(int64_t n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8
 
 static bool streamable(const MatmulDesc &d) {
   const int64_t nblk = d.k / 32;
-  return reinterpret_cast<uintptr_t>(d.W) % 16 == 0 && d.nb1 % 16 == 0 && nblk % 8 == 0;
+  // buffer offsets are 32-bit: the matrix and the activations must span less than 4 GiB
+  const int64_t xbytes = d.n_tokens * d.k * (d.x_f16 ? 2 : 4);
+  return reinterpret_cast<uintptr_t>(d.W) % 16 == 0 && d.nb1 % 16 == 0 && nblk % 8 == 0 &&
+         d.n_rows * d.nb1 < (int64_t{1} << 32) && xbytes < (int64_t{1} << 32);
 }
 
 hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t stream) {
