@@ -102,30 +102,31 @@ template <int QT, int NT, bool XF16> struct RRegs {
 };
 
 // Lane-constant placement of a stage. Weight chunk c = 64 j + lane of the 16
-// rows is row c / QC, chunk c % QC of that row; chunks past 16 * QC re-read
-// chunk 0 and are not stored (woff < 0). The activation piece of a lane is
-// block lane / 8 of the quad, elements 4 (lane % 8) .. +3, for every token
-// slot.
+// rows is row c / QC, chunk c % QC of that row: byte (c / QC) nb1 + 16 (c % QC)
+// of the row group, and 16 c in the wavefront's LDS copy (rows of 16 QC
+// bytes, unpadded); chunks past 16 * QC re-read chunk 0 and are not stored
+// (woff < 0). The activation piece of a lane is block lane / 8 of the quad,
+// elements 4 (lane % 8) .. +3, staged at LDS byte xw (token slot 0).
 template <int QT, int NT> struct RLane {
-  int wrow[RCfg<QT, NT>::w_loads];   // row within the group
-  int wcol[RCfg<QT, NT>::w_loads];   // byte offset within the row's quad
-  int woff[RCfg<QT, NT>::w_loads];   // LDS byte offset, or -1
-  int xb, xg, xh;                    // activation piece: block, operand lane group, half offset
+  int woff[RCfg<QT, NT>::w_loads];
+  uint32_t wv[RCfg<QT, NT>::w_loads];
+  int xw;
 
-  __device__ __forceinline__ explicit RLane(int lane) {
+  __device__ __forceinline__ RLane(int lane, uint32_t nb1) {
     constexpr int QC = RCfg<QT, NT>::quad_chunks;
 #pragma unroll
     for (int j = 0; j < RCfg<QT, NT>::w_loads; ++j) {
       const int c = 64 * j + lane;
       const bool ok = c < 16 * QC;
-      wrow[j] = ok ? c / QC : 0;
-      wcol[j] = ok ? 16 * (c % QC) : 0;
-      woff[j] = ok ? wrow[j] * RCfg<QT, NT>::row_stride + wcol[j] : -1;
+      const uint32_t r = static_cast<uint32_t>(c) / QC;
+      woff[j] = ok ? 16 * c : -1;
+      // r nb1 + 16 (c - QC r) with one 24-bit multiply-add (nb1 < 2^24)
+      wv[j] = ok ? __umul24(r, nb1 - 16 * QC) + 16 * c : 0;
     }
-    xb = lane >> 3;
-    const int xj = lane & 7;
-    xg = QT == QMM_TYPE_Q4_0 ? (xj & 3) : (xj >> 1);
-    xh = QT == QMM_TYPE_Q4_0 ? 4 * (xj >> 2) : 4 * (xj & 1);
+    const int xb = lane >> 3, xj = lane & 7;
+    const int xg = QT == QMM_TYPE_Q4_0 ? (xj & 3) : (xj >> 1);
+    const int xh = QT == QMM_TYPE_Q4_0 ? 4 * (xj >> 2) : 4 * (xj & 1);
+    xw = (4 * xb + xg) * NT * 16 + 2 * xh;
   }
 };
 
@@ -148,7 +149,7 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
       const half2_t a = cvt_half2(r.x[t].x, r.x[t].y), b = cvt_half2(r.x[t].z, r.x[t].w);
       h = half4_t{a.x, a.y, b.x, b.y};
     }
-    *reinterpret_cast<half4_t *>(reinterpret_cast<_Float16 *>(xs + (4 * L.xb + L.xg) * NT + t) + L.xh) = h;
+    *reinterpret_cast<half4_t *>(reinterpret_cast<unsigned char *>(xs) + L.xw + 16 * t) = h;
   }
   const int r16 = lane & 15, g = lane >> 4;
   const unsigned char *rb0 = wl + r16 * C::row_stride;
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   unsigned char *wl = smem + wave * C::lds_per_wave;
   half8_t *xs = reinterpret_cast<half8_t *>(wl + C::w_lds);
   float *red = reinterpret_cast<float *>(smem + WAVES * C::lds_per_wave);
-  const RLane<QT, NT> L(lane);
+  const RLane<QT, NT> L(lane, static_cast<uint32_t>(nb1));
 
   // Weights and activations are read through buffer resources: a uniform
   // base with 32-bit per-lane offsets (one multiply per load slot, once) and
@@ -268,11 +269,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   uint32_t wv[C::w_loads];
 #pragma unroll
   for (int j = 0; j < C::w_loads; ++j)
-    wv[j] = static_cast<uint32_t>(row0 + L.wrow[j]) * static_cast<uint32_t>(nb1) + static_cast<uint32_t>(L.wcol[j]);
+    wv[j] = static_cast<uint32_t>(row0) * static_cast<uint32_t>(nb1) + L.wv[j];
   uint32_t xv[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    xv[t] = (static_cast<uint32_t>(min(t, n_tokens - 1) * k) + 32 * L.xb + 4 * (lane & 7)) * (XF16 ? 2 : 4);
+  for (int t = 0; t < NT; ++t) xv[t] = (static_cast<uint32_t>(min(t, n_tokens - 1) * k) + 4 * lane) * (XF16 ? 2 : 4);
 
   auto issue = [&](RRegs<QT, NT, XF16> &r, int q) {
     const int wq = q * (QC * 16), xq = q * 256 * (XF16 ? 2 : 4);
@@ -333,10 +333,11 @@ static int nt_slots(int64_t n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8
 
 static bool streamable(const MatmulDesc &d) {
   const int64_t nblk = d.k / 32;
-  // buffer offsets are 32-bit: the matrix and the activations must span less than 4 GiB
+  // buffer offsets are 32-bit (the matrix and the activations must span less
+  // than 4 GiB) and the per-lane row offsets use a 24-bit multiply
   const int64_t xbytes = d.n_tokens * d.k * (d.x_f16 ? 2 : 4);
   return reinterpret_cast<uintptr_t>(d.W) % 16 == 0 && d.nb1 % 16 == 0 && nblk % 8 == 0 &&
-         d.n_rows * d.nb1 < (int64_t{1} << 32) && xbytes < (int64_t{1} << 32);
+         d.n_rows * d.nb1 < (int64_t{1} << 32) && d.nb1 < (int64_t{1} << 24) && xbytes < (int64_t{1} << 32);
 }
 
 hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t stream) {
