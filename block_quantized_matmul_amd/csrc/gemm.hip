@@ -20,11 +20,12 @@
 //    activations into LDS;
 //  * LDS is double-buffered, so the stores of stage s + 1 (and their decode
 //    arithmetic) overlap the MFMAs of stage s, with one LDS-only barrier per
-//    stage; the 144-byte row pitch (an odd multiple of 16 bytes) keeps the
-//    16-byte stores and the MFMA operand reads free of bank conflicts;
+//    stage; rows of 128 bytes with their 16-byte chunks permuted by
+//    row (lds_at) keep the stores and the MFMA operand reads free of bank
+//    conflicts;
 //  * within a stage the MFMAs are interleaved with the decode, the LDS
 //    stores and the loads of the next stages (interleave_stage);
-//  * two workgroups fit a CU (72 KiB of LDS each), so one's loads and
+//  * two workgroups fit a CU (64 KiB of LDS each), so one's loads and
 //    barriers overlap the other's matrix work.
 // Weights never exist in dequantised form outside LDS.
 #include "common.h"
@@ -35,7 +36,12 @@ namespace qmm {
 constexpr int kBM = 128;  // weight rows per tile
 constexpr int kBN = 128;  // tokens per tile
 constexpr int kBK = 64;   // k per stage (2 blocks)
-constexpr int kPitch = kBK + 8;  // halves per LDS row: 144 bytes
+// LDS tiles are 128 rows x 64 halves, 128 bytes per row without padding;
+// 16-byte chunk c of row r sits at chunk position c ^ (r % 8). On gfx950 this
+// keeps the MFMA operand reads (row lane % 16, chunk lane / 16 + 4 h) and
+// both staging stores free of LDS bank conflicts, which a padded 144-byte
+// pitch does not for the reads (measured: twice the LDS cycles per read).
+__device__ __forceinline__ int lds_at(int row, int chunk) { return row * kBK + 8 * (chunk ^ (row & 7)); }
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;       // XCDs of the GPU; workgroups are dealt to them round-robin
 constexpr int kGroupRows = 8;  // row tiles per group of the tile order
@@ -50,9 +56,9 @@ __device__ __forceinline__ void load_block_u16(const uint8_t *p, uint32_t &d, ui
 }
 
 // Decode one block to 32 fp16 weights fl16(d * (q - z)) in element order and
-// store them at dst (16-byte aligned LDS).
+// store them as chunks c0 .. c0 + 3 of LDS tile row `row`.
 template <int QT>
-__device__ __forceinline__ void store_block_f16(_Float16 *dst, uint32_t d_bits, const uint32_t *q) {
+__device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0, uint32_t d_bits, const uint32_t *q) {
   const _Float16 dh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d_bits));
   const half2_t d2 = {dh, dh};
   half2_t h[16];
@@ -75,9 +81,10 @@ __device__ __forceinline__ void store_block_f16(_Float16 *dst, uint32_t d_bits, 
       h[2 * i + 1] = u[1] * d2;
     }
   }
-  u32x4_t *o = reinterpret_cast<u32x4_t *>(dst);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = u32x4_t{as_u32(h[4 * i]), as_u32(h[4 * i + 1]), as_u32(h[4 * i + 2]), as_u32(h[4 * i + 3])};
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4_t *>(tile + lds_at(row, c0 + i)) =
+        u32x4_t{as_u32(h[4 * i]), as_u32(h[4 * i + 1]), as_u32(h[4 * i + 2]), as_u32(h[4 * i + 3])};
 }
 
 // One staging thread's half of a stage's pair of blocks (h = 0: block 2 s,
@@ -126,15 +133,16 @@ __device__ __forceinline__ HalfRaw<QT> load_half_u16(const uint8_t *rp, int blk,
 }
 
 // Decode a half (layout of half 0 if first_layout, else of half 1) and
-// store its 32 fp16 weights. first_layout may differ between lanes.
+// store its 32 fp16 weights as chunks c0 .. c0 + 3 of tile row `row`.
+// first_layout may differ between lanes.
 template <int QT>
-__device__ __forceinline__ void store_half(_Float16 *dst, const HalfRaw<QT> &r, bool first_layout) {
+__device__ __forceinline__ void store_half(_Float16 *tile, int row, int c0, const HalfRaw<QT> &r, bool first_layout) {
   constexpr int nq = HalfRaw<QT>::nq;
   uint32_t q[nq];
   const uint32_t d = first_layout ? (r.w[0] & 0xFFFFu) : (r.w[0] >> 16);
 #pragma unroll
   for (int i = 0; i < nq; ++i) q[i] = first_layout ? shift16(r.w[i], r.w[i + 1]) : r.w[i + 1];
-  store_block_f16<QT>(dst, d, q);
+  store_block_f16<QT>(tile, row, c0, d, q);
 }
 
 // Activations of one stage (128 tokens x 64 k) as 16-byte pieces spread so
@@ -188,7 +196,8 @@ __device__ __forceinline__ void store_x_pieces(_Float16 *xs, const XPieces<XF16>
 #pragma unroll
   for (int i = 0; i < M::n; ++i) {
     const int c = 256 * i + tid;
-    _Float16 *dst = xs + (c / M::per_tok) * kPitch + M::elems * (c % M::per_tok);
+    const int tok = c / M::per_tok, e = M::elems * (c % M::per_tok);
+    _Float16 *dst = xs + lds_at(tok, e >> 3) + (e & 7);
     if constexpr (XF16) {
       *reinterpret_cast<u32x4_t *>(dst) = r.v[i];
     } else {
@@ -234,8 +243,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
                                                                int64_t nb1, const void *__restrict__ X, int n_tokens,
                                                                int k, float *__restrict__ Y, bool y_vec4,
                                                                int row_tiles) {
-  __shared__ __attribute__((aligned(16))) _Float16 Ws[2][kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) _Float16 Xs[2][kBN * kPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 Ws[2][kBM * kBK];
+  __shared__ __attribute__((aligned(16))) _Float16 Xs[2][kBN * kBK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -259,12 +268,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
 
   // Weight staging: thread -> (row, half of the stage's block pair). The two
   // halves of a row sit in adjacent lanes, so each load instruction touches
-  // 32 rows rather than 64; with the 144-byte pitch the 16-byte stores of 8
-  // lanes (4 rows x 2 halves) still cover 8 distinct bank groups. Rows past
-  // the end re-read the last one.
+  // 32 rows rather than 64. Rows past the end re-read the last one.
   const int srow = tid >> 1, sh = tid & 1;
   const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
-  const int wofs = srow * kPitch + 32 * sh;
 
   float4_t acc[4][4];
 #pragma unroll
@@ -286,21 +292,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
     r.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * st, tid, false);
   };
   auto store = [&](int buf, const Stage &r) {
-    store_half<QT>(Ws[buf] + wofs, r.w, ALIGN4 && sh == 0);
+    store_half<QT>(Ws[buf], srow, 4 * sh, r.w, ALIGN4 && sh == 0);
     store_x_pieces<XF16>(Xs[buf], r.x, tid);
   };
   // operands: A (weights) row 64 wm + 16 i + lane % 16, B (activations)
-  // token 64 wn + 16 j + lane % 16; elements 8 (lane / 16) .. +7 of the k step
-  const int aofs = (64 * wm + (lane & 15)) * kPitch + 8 * (lane >> 4);
-  const int bofs = (64 * wn + (lane & 15)) * kPitch + 8 * (lane >> 4);
+  // token 64 wn + 16 j + lane % 16; elements 8 (lane / 16) .. +7 of k step
+  // h (chunk lane / 16 + 4 h); rows 16 apart share the chunk swizzle.
+  int aofs[2], bofs[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    aofs[h] = lds_at(64 * wm + (lane & 15), (lane >> 4) + 4 * h);
+    bofs[h] = lds_at(64 * wn + (lane & 15), (lane >> 4) + 4 * h);
+  }
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
+    for (int h = 0; h < 2; ++h) {
       half8_t a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const half8_t *>(Ws[buf] + aofs + 16 * i * kPitch + kk);
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const half8_t *>(Ws[buf] + aofs[h] + 16 * i * kBK);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const half8_t *>(Xs[buf] + bofs + 16 * j * kPitch + kk);
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const half8_t *>(Xs[buf] + bofs[h] + 16 * j * kBK);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
     Stage t;
     t.w = load_half_u16<QT>(rp, 2 * n_full + sh, nblk);
     t.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * n_full, tid, true);
-    store_half<QT>(Ws[buf] + wofs, t.w, false);
+    store_half<QT>(Ws[buf], srow, 4 * sh, t.w, false);
     store_x_pieces<XF16>(Xs[buf], t.x, tid);
     lds_barrier();
     compute(buf);
