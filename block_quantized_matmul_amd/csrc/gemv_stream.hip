@@ -42,10 +42,13 @@ constexpr int kRMaxMats = 16;
 
 template <int QT, int NT> struct RCfg {
   static constexpr int quad_chunks = QT == QMM_TYPE_Q4_0 ? 9 : 17;  // 16-byte chunks per row per quad
-  // LDS bytes per row: unpadded, so a stage is stored as one contiguous run
-  // (chunk c at 16 c) and the per-row dword reads of 16 rows (stride 36 or 68
-  // dwords) fall in distinct banks.
-  static constexpr int row_stride = quad_chunks * 16;
+  // LDS bytes per row of the stage copy. Unpadded (chunk c at 16 c, one
+  // 16-byte store per chunk) for up to 2 tokens. With 4 or 8 tokens, whose
+  // activation traffic makes LDS the tighter resource, rows are padded by 8
+  // bytes (stride 38 or 70 dwords): the per-row dword reads of a half
+  // wavefront then fall in distinct banks (at 36 or 68 they conflict 2-way on
+  // gfx950), at the price of two 8-byte stores per chunk.
+  static constexpr int row_stride = quad_chunks * 16 + (NT >= 4 ? 8 : 0);
   static constexpr int w_loads = (16 * quad_chunks + 63) / 64;       // loads per lane for the 16 rows
   // stages per round, sized so a round's registers stay near 64 VGPRs (the
   // kernel then fits 4 wavefronts per SIMD, i.e. 2 workgroups per CU)
@@ -103,8 +106,8 @@ template <int QT, int NT, bool XF16> struct RRegs {
 
 // Lane-constant placement of a stage. Weight chunk c = 64 j + lane of the 16
 // rows is row c / QC, chunk c % QC of that row: byte (c / QC) nb1 + 16 (c % QC)
-// of the row group, and 16 c in the wavefront's LDS copy (rows of 16 QC
-// bytes, unpadded); chunks past 16 * QC re-read chunk 0 and are not stored
+// of the row group, and byte (c / QC) row_stride + 16 (c % QC) of the
+// wavefront's LDS copy; chunks past 16 * QC re-read chunk 0 and are not stored
 // (woff < 0). The activation piece of a lane is block lane / 8 of the quad,
 // elements 4 (lane % 8) .. +3, staged at LDS byte xw (token slot 0).
 template <int QT, int NT> struct RLane {
@@ -119,7 +122,7 @@ template <int QT, int NT> struct RLane {
       const int c = 64 * j + lane;
       const bool ok = c < 16 * QC;
       const uint32_t r = static_cast<uint32_t>(c) / QC;
-      woff[j] = ok ? 16 * c : -1;
+      woff[j] = ok ? static_cast<int>(r) * RCfg<QT, NT>::row_stride + 16 * (c - QC * static_cast<int>(r)) : -1;
       // r nb1 + 16 (c - QC r) with one 24-bit multiply-add (nb1 < 2^24)
       wv[j] = ok ? __umul24(r, nb1 - 16 * QC) + 16 * c : 0;
     }
@@ -139,7 +142,14 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
   using C = RCfg<QT, NT>;
 #pragma unroll
   for (int j = 0; j < C::w_loads; ++j)
-    if (L.woff[j] >= 0) *reinterpret_cast<u32x4_t *>(wl + L.woff[j]) = r.w[j];
+    if (L.woff[j] >= 0) {
+      if constexpr (C::row_stride % 16 == 0) {
+        *reinterpret_cast<u32x4_t *>(wl + L.woff[j]) = r.w[j];
+      } else {
+        *reinterpret_cast<u32x2_t *>(wl + L.woff[j]) = u32x2_t{r.w[j].x, r.w[j].y};
+        *reinterpret_cast<u32x2_t *>(wl + L.woff[j] + 8) = u32x2_t{r.w[j].z, r.w[j].w};
+      }
+    }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     half4_t h;
