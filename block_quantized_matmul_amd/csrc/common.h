@@ -28,6 +28,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float float4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef _Float16 half4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int QT> struct Block;
 template <> struct Block<QMM_TYPE_Q4_0> { static constexpr int bytes = 18; };

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         v[2 * j + 1] = d * static_cast<float>(static_cast<int8_t>(two >> 8));
       }
     }
-    float4_t *o = reinterpret_cast<float4_t *>(out + blk * 32 + 8 * part);
+    float4_a4 *o = reinterpret_cast<float4_a4 *>(out + blk * 32 + 8 * part);
     o[0] = float4_t{v[0], v[1], v[2], v[3]};
     o[1] = float4_t{v[4], v[5], v[6], v[7]};
   }

@@ -177,9 +177,9 @@ __device__ __forceinline__ XPieces<XF16> load_x_pieces(const void *X, int tok0, 
     const int64_t off = static_cast<int64_t>(tok) * k + e;
     if (!tail || e < k) {
       if constexpr (XF16)
-        r.v[i] = *reinterpret_cast<const u32x4_t *>(static_cast<const _Float16 *>(X) + off);
+        r.v[i] = *reinterpret_cast<const u32x4_a4 *>(static_cast<const _Float16 *>(X) + off);
       else
-        r.v[i] = *reinterpret_cast<const float4_t *>(static_cast<const float *>(X) + off);
+        r.v[i] = *reinterpret_cast<const float4_a4 *>(static_cast<const float *>(X) + off);
     } else {
       if constexpr (XF16)
         r.v[i] = u32x4_t{0u, 0u, 0u, 0u};

@@ -50,9 +50,9 @@ __device__ __forceinline__ void gemv_stage_x(half8_t *xs, const void *X, int n_t
     const int64_t src = static_cast<int64_t>(t) * k + 32 * (b_lo + bb) + 4 * j;
     half4_t h;
     if constexpr (XF16) {
-      h = *reinterpret_cast<const half4_t *>(static_cast<const _Float16 *>(X) + src);
+      h = *reinterpret_cast<const half4_a4 *>(static_cast<const _Float16 *>(X) + src);
     } else {
-      const float4_t f = *reinterpret_cast<const float4_t *>(static_cast<const float *>(X) + src);
+      const float4_t f = *reinterpret_cast<const float4_a4 *>(static_cast<const float *>(X) + src);
       const half2_t a = cvt_half2(f.x, f.y), b = cvt_half2(f.z, f.w);
       h = half4_t{a.x, a.y, b.x, b.y};
     }

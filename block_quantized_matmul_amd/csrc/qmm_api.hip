@@ -81,7 +81,7 @@ const char *qmm_status_string(int status) {
     case QMM_ERR_TYPE: return "QMM_ERR_TYPE: unsupported weight or activation type";
     case QMM_ERR_SHAPE: return "QMM_ERR_SHAPE: k must be a positive multiple of 32; sizes must be in [0, 2^31)";
     case QMM_ERR_STRIDE: return "QMM_ERR_STRIDE: row stride must be even and cover the row's blocks";
-    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte, X 16-byte, Y 4-byte, out 16-byte alignment";
+    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte, X, Y and out 4-byte alignment";
     case QMM_ERR_HIP: return "QMM_ERR_HIP: the HIP runtime rejected the kernel launch";
     case QMM_ERR_PATH: return "QMM_ERR_PATH: unknown path, or GEMV forced with more than 8 tokens";
     default: return "unknown qmm status";
@@ -97,7 +97,7 @@ static int check_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k,
   if (n_tokens < 0 || n_tokens > kMaxDim) return QMM_ERR_SHAPE;
   if (path != QMM_PATH_AUTO && path != QMM_PATH_GEMV && path != QMM_PATH_GEMM) return QMM_ERR_PATH;
   if (path == QMM_PATH_GEMV && n_tokens > QMM_GEMV_MAX_TOKENS) return QMM_ERR_PATH;
-  if (!aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+  if (!aligned(X, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
   return QMM_OK;
 }
 
@@ -166,7 +166,7 @@ int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
   if (out == nullptr) return QMM_ERR_NULL;
   int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
   if (st != QMM_OK) return st;
-  if (!aligned(out, 16)) return QMM_ERR_ALIGN;
+  if (!aligned(out, 4)) return QMM_ERR_ALIGN;
   if (n_rows == 0) return QMM_OK;
   if (trace_on())
     fprintf(stderr, "qmm: dequant %s rows=%lld k=%lld nb1=%lld\n", type_name(ggml_type), (long long)n_rows,

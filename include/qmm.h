@@ -104,7 +104,7 @@ extern "C" {
  *   n_rows           ne1 of W (>= 0)
  *   k                ne0 of W and of X; positive multiple of 32
  *   row_stride_bytes nb1 of W; even and >= qmm_row_bytes(ggml_type, k)
- *   X                device pointer, fp32 [n_tokens][k], 16-byte aligned
+ *   X                device pointer, fp32 [n_tokens][k], 4-byte aligned
  *   n_tokens         ne1 of X (>= 0)
  *   Y                device pointer, fp32 [n_tokens][n_rows], 4-byte aligned
  *   stream           hipStream_t or NULL
@@ -116,7 +116,7 @@ int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t 
 
 /*
  * qmm_matmul_x16 - as qmm_matmul, but X holds fp16 (IEEE binary16 bit
- * patterns) activations [n_tokens][k], 16-byte aligned.
+ * patterns) activations [n_tokens][k], 4-byte aligned.
  */
 int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                    const uint16_t *X, int64_t n_tokens, float *Y, void *stream);
@@ -165,7 +165,7 @@ int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream);
 /*
  * qmm_dequantize - the block decoder alone ([Bind] section 2.3 layout,
  * [Arch] reconstruction equation): out[r][i] = fp32(d) * fp32(q - z) for
- * element i of row r. out is fp32 [n_rows][k], 16-byte aligned, caller-owned.
+ * element i of row r. out is fp32 [n_rows][k], 4-byte aligned, caller-owned.
  * The result is bit-exact (NaN scales give NaN). n_rows == 0 is a no-op.
  */
 int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,

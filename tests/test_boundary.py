@@ -97,7 +97,7 @@ def test_validation_codes(L):
     assert _mm(L, nb1=34) == E.QMM_ERR_STRIDE
     assert _mm(L, t=Q8, nb1=36) == E.QMM_ERR_STRIDE
     assert _mm(L, W=ctypes.c_void_p(0x10001)) == E.QMM_ERR_ALIGN
-    assert _mm(L, X=ctypes.c_void_p(0x20004)) == E.QMM_ERR_ALIGN
+    assert _mm(L, X=ctypes.c_void_p(0x20002)) == E.QMM_ERR_ALIGN
     assert _mm(L, Y=ctypes.c_void_p(0x30002)) == E.QMM_ERR_ALIGN
     assert _mm(L, path=3) == E.QMM_ERR_PATH
     assert _mm(L, path=qmm.QMM_PATH_GEMV, n=9) == E.QMM_ERR_PATH
@@ -120,7 +120,7 @@ def test_dequantize_validation(L):
     assert L.qmm_dequantize(P, 9, 4, 64, 36, P2, NULL) == qmm.QMM_ERR_TYPE
     assert L.qmm_dequantize(P, Q4, 4, 63, 36, P2, NULL) == qmm.QMM_ERR_SHAPE
     assert L.qmm_dequantize(P, Q4, 4, 64, 30, P2, NULL) == qmm.QMM_ERR_STRIDE
-    assert L.qmm_dequantize(P, Q4, 4, 64, 36, ctypes.c_void_p(0x20008), NULL) == qmm.QMM_ERR_ALIGN
+    assert L.qmm_dequantize(P, Q4, 4, 64, 36, ctypes.c_void_p(0x20002), NULL) == qmm.QMM_ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -66,3 +66,23 @@ def test_strides_alignment_and_ragged(qtype, k, extra, offset):
         W2 = W.copy()
         W2[:, nb1 - extra:] ^= 0xFF
         _check(W2, qtype, k, offset, what=f"k={k} pad={extra} refilled")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_dword_aligned_output(qtype):
+    """out only 4-byte aligned (the weakest alignment the boundary accepts)."""
+    import torch
+    from gpu_util import place_weights
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64(300 + qtype))
+    rows, k = 37, 160
+    nb1 = synth.dense_row_bytes(qtype, k) + 2
+    W = synth.make_weights(qtype, rows, k, nb1, rng)
+    say(f"dequant dword-aligned out type={qtype}")
+    _keep, Wd = place_weights(W)
+    flat = torch.zeros(rows * k + 8, dtype=torch.float32, device="cuda")
+    out = flat[1:1 + rows * k].view(rows, k)
+    assert out.data_ptr() % 16 == 4
+    qmm.qmm_dequantize(Wd, qtype, k, n_rows=rows, row_stride_bytes=nb1, out=out)
+    torch.cuda.synchronize()
+    assert_bitwise(out.cpu().numpy(), O.dequantize(W, qtype, rows, k, nb1), "dword-aligned out")

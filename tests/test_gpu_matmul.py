@@ -8,6 +8,8 @@ import pytest
 import block_quantized_matmul_amd as qmm
 import oracle.qmm_oracle as O
 from block_quantized_matmul_amd import synth
+import gpu_util
+import torch
 from gpu_util import assert_bitwise, assert_close_to_oracle, run_matmul, say
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +66,37 @@ def test_dispatch_and_cross_check(qtype):
         assert_bitwise(ya, expect, f"auto n={n}")
         assert_close_to_oracle(yg, W, qtype, 1024, X, f"gemm n={n}")
         assert_close_to_oracle(ya, W, qtype, 1024, X, f"auto n={n}")
+
+
+def _dword_aligned_copy(a: np.ndarray, dtype) -> tuple:
+    """a on the GPU starting 4 bytes past a 16-byte boundary (the weakest
+    alignment the boundary accepts for X, Y and out). Returns (keepalive, view)."""
+    per = 4 // np.dtype(dtype).itemsize
+    flat = torch.zeros(a.size + 16, dtype=torch.float32 if dtype == np.float32 else torch.float16, device="cuda")
+    view = flat[per:per + a.size]
+    view.copy_(torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda())
+    assert view.data_ptr() % 16 == 4
+    return flat, view.view(a.shape)
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("xdt", [np.float32, np.float16])
+@pytest.mark.parametrize("path,n", [(GEMV, 1), (GEMV, 8), (GEMM, 40)])
+def test_dword_aligned_activations_and_outputs(qtype, xdt, path, n):
+    """X and Y only 4-byte aligned: the same results, bit for bit, as with
+    16-byte-aligned buffers, for a streamable and a general weight layout."""
+    for rows, k, extra in ((64, 512, 0), (70, 1024, 10)):
+        W, X = _inputs(qtype, rows, k, n, extra, xdt=xdt)
+        say(f"dword-aligned X/Y type={qtype} x={np.dtype(xdt).name} path={path} n={n} rows={rows} k={k} pad={extra}")
+        want = run_matmul(W, qtype, k, X, path)
+        _keep, Wd = gpu_util.place_weights(W)
+        _kx, Xd = _dword_aligned_copy(X, xdt)
+        _ky, Yd = _dword_aligned_copy(np.zeros((n, rows), np.float32), np.float32)
+        qmm.qmm_matmul_path(Wd, qtype, k, Xd, n_rows=rows, row_stride_bytes=W.shape[1], n_tokens=n, Y=Yd, path=path)
+        torch.cuda.synchronize()
+        got = Yd.cpu().numpy()
+        assert_bitwise(got, want, "dword-aligned X/Y")
+        assert_close_to_oracle(got, W, qtype, k, X, "dword-aligned X/Y")
 
 
 # ------------------------------------------------------------ closed-form invariants
