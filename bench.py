@@ -85,6 +85,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-get-rows", action="store_true", help="skip the GET_ROWS (token-embedding gather) line")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
@@ -189,6 +190,63 @@ def traffic_from_profiles(kernel):
                 if m and m.group(1) == kernel and m.group(3) == h:
                     return int(m.group(2))
     return None
+
+
+# ---------------------------------------------------------------- GET_ROWS
+
+GET_ROWS_IDS = 2048
+
+
+def time_get_rows(torch, qmm, synth, with_oracle=False):
+    """GET_ROWS of one prefill ubatch (2048 token ids) from the model's
+    32000x4096 Q4_0 token-embedding matrix: back-to-back launches in a graph,
+    rotating over >= 1 GiB of matrix copies so the gathered rows come from
+    HBM. Algorithmic bytes: the gathered rows' blocks, the ids and the fp32
+    output (HBM-bound decoder)."""
+    import numpy as np
+    rows, k, qt = 32000, 4096, synth.TYPE_Q4_0
+    nb1 = synth.dense_row_bytes(qt, k)
+    rng = np.random.Generator(np.random.PCG64(4242))
+    W0 = torch.from_numpy(synth.make_weights(qt, rows, k, nb1, rng)).cuda()
+    copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    ids = torch.from_numpy(rng.integers(0, rows, size=GET_ROWS_IDS).astype(np.int32)).cuda()
+    out = torch.empty((GET_ROWS_IDS, k), dtype=torch.float32, device="cuda")
+    reps = 4 * copies
+
+    def run():
+        for i in range(reps):
+            qmm.qmm_get_rows(Ws[i % copies], qt, k, ids, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(5):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    us = sorted(ts)[2]
+    byts = GET_ROWS_IDS * (nb1 + 4 + 4 * k)
+    gbs = byts / (us * 1e-6) / 1e9
+    res = {"workload": f"{GET_ROWS_IDS} ids into a {rows}x{k} Q4_0 matrix", "us_per_launch": round(us, 3),
+           "algorithmic_bytes_per_launch": byts, "GB_per_s": round(gbs, 2),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "kernel": "dequant_kernel", "bound": "hbm"}
+    if with_oracle:
+        # the oracle as it stands (it dequantises the whole matrix, then gathers), once, on the host
+        import oracle.qmm_oracle as O
+        Wh, idh = W0.cpu().numpy(), ids.cpu().numpy()
+        t0 = time.perf_counter()
+        O.get_rows(Wh, qt, rows, k, nb1, idh)
+        res["cpu_oracle_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+    return res
 
 
 # ---------------------------------------------------------------- workload
@@ -419,6 +477,8 @@ def main():
         out["decode_per_call"] = {"ms_per_pass": round(ms["decode_per_call"], 4), "launches": n,
                                   "us_per_launch": round(us_launch["decode_per_call"], 3),
                                   "GB_per_s": round(gbs_pc, 2), "frac_of_hbm_peak": round(gbs_pc / HBM_PEAK_GBS, 4)}
+    if not args.no_get_rows:
+        out["get_rows"] = time_get_rows(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if cpu_layers:
         import oracle.qmm_oracle as O
         log("timing the CPU oracle on a sample")

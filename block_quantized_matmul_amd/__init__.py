@@ -61,7 +61,9 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_path.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, vp]
         L.qmm_dequantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
         L.qmm_matmul_batch.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp]
-        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch"):
+        L.qmm_get_rows.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
+        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch",
+                  "qmm_get_rows"):
             getattr(L, f).restype = i32
         L.qmm_row_bytes.argtypes = [i32, i64]
         L.qmm_row_bytes.restype = i64
@@ -160,6 +162,24 @@ def qmm_dequantize(W, ggml_type, k, n_rows=None, row_stride_bytes=None, out=None
                               _stream(stream))
     if st != QMM_OK:
         raise QmmError(st, "qmm_dequantize")
+    return out
+
+
+def qmm_get_rows(W, ggml_type, k, ids, n_rows=None, row_stride_bytes=None, out=None, stream=None):
+    """GET_ROWS: fp32 [len(ids)][k], row i = dequantised row ids[i] of W
+    (C: qmm_get_rows; an index outside [0, n_rows) gives a row of NaNs).
+    ids is a contiguous int32 GPU tensor."""
+    import torch
+    n_rows, nb1 = _weights_geometry(W, n_rows, row_stride_bytes)
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise TypeError("ids must be a contiguous 1-D int32 tensor")
+    n_ids = int(ids.shape[0])
+    if out is None:
+        out = torch.empty((n_ids, int(k)), dtype=torch.float32, device=W.device)
+    st = lib().qmm_get_rows(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(ids, "ids"), n_ids,
+                            _gpu_ptr(out, "out"), _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_get_rows")
     return out
 
 

@@ -1,8 +1,12 @@
-// Block decoder: out[r][i] = fp32(d) * fp32(q - z), bit-exact.
+// Block decoder: out[r][i] = fp32(d) * fp32(q - z), bit-exact, for every row
+// of W or for the rows an index vector selects (GET_ROWS).
 //
 // [Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3 (block
 // layout); [Arch] "llama.cpp 源码完全拆解(一)：整体架构与模块全景", section
-// "权重装载：GGUF、mmap 与 4 bit 块" (w_hat = s (q - z)).
+// "权重装载：GGUF、mmap 与 4 bit 块" (w_hat = s (q - z)); GET_ROWS on a quantised
+// weight with an I32 index vector: [Load] "llama.cpp 源码完全拆解(三)：GGUF 装载、
+// mmap 与张量放置", section "第六步：能力校验" (the op the capability probe
+// builds for token-embedding tensors).
 //
 // One thread writes eight consecutive outputs (one quarter of a block), so a
 // wavefront stores 2 KiB of contiguous fp32 with 16-byte stores. HBM-bound:
@@ -12,15 +16,26 @@
 
 namespace qmm {
 
+// Output row r is W's row ids[r] (or r when ids is null); an index outside
+// [0, n_rows) gives a row of quiet NaNs and reads nothing.
 template <int QT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ W, int64_t n_quarters, int nblk,
-                                                      int64_t nb1, float *__restrict__ out) {
+                                                      int64_t nb1, const int32_t *__restrict__ ids, int64_t n_rows,
+                                                      float *__restrict__ out) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n_quarters; t += stride) {
     const int part = static_cast<int>(t & 3);  // elements [8 part, 8 part + 8)
     const int64_t blk = t >> 2;
-    const int64_t row = blk / nblk;
-    const int b = static_cast<int>(blk - row * nblk);
+    const int64_t orow = blk / nblk;
+    const int b = static_cast<int>(blk - orow * nblk);
+    float4_a4 *o = reinterpret_cast<float4_a4 *>(out + blk * 32 + 8 * part);
+    const int64_t row = ids ? static_cast<int64_t>(ids[orow]) : orow;
+    if (row < 0 || row >= n_rows) {
+      const float nan = __builtin_bit_cast(float, 0x7FC00000u);
+      o[0] = float4_t{nan, nan, nan, nan};
+      o[1] = float4_t{nan, nan, nan, nan};
+      continue;
+    }
     const uint8_t *p = W + row * nb1 + static_cast<int64_t>(b) * Block<QT>::bytes;
     const float d = half_bits_to_float(ld_u16(p));
     float v[8];
@@ -43,22 +58,33 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         v[2 * j + 1] = d * static_cast<float>(static_cast<int8_t>(two >> 8));
       }
     }
-    float4_a4 *o = reinterpret_cast<float4_a4 *>(out + blk * 32 + 8 * part);
     o[0] = float4_t{v[0], v[1], v[2], v[3]};
     o[1] = float4_t{v[4], v[5], v[6], v[7]};
   }
 }
 
-hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,
-                          hipStream_t stream) {
+static hipError_t decode_rows(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const int32_t *ids,
+                              int64_t n_out, float *out, hipStream_t stream) {
   const int nblk = static_cast<int>(k / 32);
-  const int64_t quarters = n_rows * nblk * 4;
+  const int64_t quarters = n_out * nblk * 4;
   const int64_t want = (quarters + 255) / 256;
   const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
   const uint8_t *w = static_cast<const uint8_t *>(W);
   if (qtype == QMM_TYPE_Q4_0)
-    return launch(dequant_kernel<QMM_TYPE_Q4_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, out);
-  return launch(dequant_kernel<QMM_TYPE_Q8_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, out);
+    return launch(dequant_kernel<QMM_TYPE_Q4_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, ids, n_rows,
+                  out);
+  return launch(dequant_kernel<QMM_TYPE_Q8_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, ids, n_rows,
+                out);
+}
+
+hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,
+                          hipStream_t stream) {
+  return decode_rows(W, qtype, n_rows, k, nb1, nullptr, n_rows, out, stream);
+}
+
+hipError_t launch_get_rows(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const int32_t *ids,
+                           int64_t n_ids, float *out, hipStream_t stream) {
+  return decode_rows(W, qtype, n_rows, k, nb1, ids, n_ids, out, stream);
 }
 
 }  // namespace qmm

@@ -39,6 +39,8 @@ inline int device_cus() {
 
 hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,
                           hipStream_t stream);
+hipError_t launch_get_rows(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const int32_t *ids,
+                           int64_t n_ids, float *out, hipStream_t stream);
 
 // One MUL_MAT of a (possibly batched) call.
 struct MatmulDesc {

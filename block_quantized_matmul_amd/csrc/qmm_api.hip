@@ -174,4 +174,19 @@ int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
   return status_of(qmm::launch_dequant(W, ggml_type, n_rows, k, row_stride_bytes, out, static_cast<hipStream_t>(stream)));
 }
 
+int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                 const int32_t *ids, int64_t n_ids, float *out, void *stream) {
+  if (ids == nullptr || out == nullptr) return QMM_ERR_NULL;
+  int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
+  if (st != QMM_OK) return st;
+  if (n_ids < 0 || n_ids > kMaxDim) return QMM_ERR_SHAPE;
+  if (!aligned(ids, 4) || !aligned(out, 4)) return QMM_ERR_ALIGN;
+  if (n_ids == 0) return QMM_OK;
+  if (trace_on())
+    fprintf(stderr, "qmm: get_rows %s rows=%lld k=%lld nb1=%lld ids=%lld\n", type_name(ggml_type), (long long)n_rows,
+            (long long)k, (long long)row_stride_bytes, (long long)n_ids);
+  return status_of(qmm::launch_get_rows(W, ggml_type, n_rows, k, row_stride_bytes, ids, n_ids, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -172,6 +172,24 @@ int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
                    float *out, void *stream);
 
 /*
+ * qmm_get_rows - GET_ROWS on a quantised weight: out[i][j] = the dequantised
+ * element j of row ids[i] of W, bit-exact as in qmm_dequantize (the op the
+ * capability probe builds for token-embedding tensors with an I32 index
+ * vector, [Load] section 第六步).
+ *   W, ggml_type, n_rows, k, row_stride_bytes  as in qmm_matmul
+ *   ids      device pointer, int32 [n_ids], 4-byte aligned, caller-owned
+ *   n_ids    number of rows to gather (>= 0; 0 is a no-op)
+ *   out      device pointer, fp32 [n_ids][k], 4-byte aligned, caller-owned
+ *   stream   hipStream_t or NULL
+ * An index outside [0, n_rows) cannot be checked on the host (ids are device
+ * data): its output row is filled with quiet NaNs and nothing is read for it.
+ * Returns QMM_OK, or the status of the first failed check (QMM_ERR_NULL,
+ * _TYPE, _SHAPE, _STRIDE, _ALIGN) without launching, or QMM_ERR_HIP.
+ */
+int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                 const int32_t *ids, int64_t n_ids, float *out, void *stream);
+
+/*
  * qmm_row_bytes - the dense row stride (k / 32) * block bytes, i.e. nb[1]
  * without padding ([Graph] ggml_tensor stride comment). Negative status code
  * for an unknown type or a k that is not a positive multiple of 32.

@@ -141,6 +141,21 @@ def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
         return d32 * c
 
 
+def get_rows(W, qtype: int, n_rows: int, k: int, nb1: int, ids) -> np.ndarray:
+    """GET_ROWS on a quantised weight: fp32 [len(ids)][k], row i = the
+    dequantised row ids[i] of W ([Load] section "第六步：能力校验": the op
+    built for a weight with an I32 index vector). An index outside
+    [0, n_rows) has no row to take; its output row is NaN (the library's
+    documented reading, since device-side indices cannot be validated).
+    """
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.full((ids.size, k), np.nan, dtype=np.float32)
+    ok = (ids >= 0) & (ids < n_rows)
+    if n_rows > 0 and ok.any():
+        out[ok] = dequantize(W, qtype, n_rows, k, nb1)[ids[ok]]
+    return out
+
+
 def _activations_f64(X, k: int) -> np.ndarray:
     X = np.asarray(X)
     if X.dtype not in (np.float32, np.float16):

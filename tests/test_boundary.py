@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
-                            "qmm_dequantize", "qmm_row_bytes", "qmm_supports", "qmm_status_string"])
+                            "qmm_dequantize", "qmm_get_rows", "qmm_row_bytes", "qmm_supports",
+                            "qmm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -121,6 +122,21 @@ def test_dequantize_validation(L):
     assert L.qmm_dequantize(P, Q4, 4, 63, 36, P2, NULL) == qmm.QMM_ERR_SHAPE
     assert L.qmm_dequantize(P, Q4, 4, 64, 30, P2, NULL) == qmm.QMM_ERR_STRIDE
     assert L.qmm_dequantize(P, Q4, 4, 64, 36, ctypes.c_void_p(0x20002), NULL) == qmm.QMM_ERR_ALIGN
+
+
+def test_get_rows_validation(L):
+    A = ctypes.c_void_p(0x40000)  # fake 16-byte-aligned index pointer
+    assert L.qmm_get_rows(NULL, Q4, 4, 64, 36, A, 3, P2, NULL) == qmm.QMM_ERR_NULL
+    assert L.qmm_get_rows(P, Q4, 4, 64, 36, NULL, 3, P2, NULL) == qmm.QMM_ERR_NULL
+    assert L.qmm_get_rows(P, Q4, 4, 64, 36, A, 3, NULL, NULL) == qmm.QMM_ERR_NULL
+    assert L.qmm_get_rows(P, 9, 4, 64, 36, A, 3, P2, NULL) == qmm.QMM_ERR_TYPE
+    assert L.qmm_get_rows(P, Q4, 4, 63, 36, A, 3, P2, NULL) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_get_rows(P, Q4, 4, 64, 36, A, -1, P2, NULL) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_get_rows(P, Q4, 4, 64, 30, A, 3, P2, NULL) == qmm.QMM_ERR_STRIDE
+    assert L.qmm_get_rows(P, Q4, 4, 64, 36, ctypes.c_void_p(0x40002), 3, P2, NULL) == qmm.QMM_ERR_ALIGN
+    assert L.qmm_get_rows(P, Q4, 4, 64, 36, A, 3, ctypes.c_void_p(0x20002), NULL) == qmm.QMM_ERR_ALIGN
+    # zero indices: nothing is launched
+    assert L.qmm_get_rows(P, Q4, 4, 64, 36, A, 0, P2, NULL) == qmm.QMM_OK
 
 
 def test_binding_refuses_cpu_tensors():

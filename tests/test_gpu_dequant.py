@@ -86,3 +86,23 @@ def test_dword_aligned_output(qtype):
     qmm.qmm_dequantize(Wd, qtype, k, n_rows=rows, row_stride_bytes=nb1, out=out)
     torch.cuda.synchronize()
     assert_bitwise(out.cpu().numpy(), O.dequantize(W, qtype, rows, k, nb1), "dword-aligned out")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("rows,k,extra,offset", [(300, 256, 0, 0), (77, 96, 6, 2), (2000, 4096, 256, 0)])
+def test_get_rows(qtype, rows, k, extra, offset):
+    """GET_ROWS bit-exact against the oracle: repeated indices, the first and
+    last row, and out-of-range indices (rows of NaN)."""
+    import torch
+    from gpu_util import place_weights
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([400, qtype, rows, k]))
+    nb1 = synth.dense_row_bytes(qtype, k) + extra
+    W = synth.make_weights(qtype, rows, k, nb1, rng)
+    ids = rng.integers(0, rows, size=512).astype(np.int32)
+    ids[:6] = [0, rows - 1, 0, -1, rows, np.iinfo(np.int32).min]
+    say(f"get_rows type={qtype} rows={rows} k={k} nb1={nb1} offset={offset} n_ids={ids.size}")
+    _keep, Wd = place_weights(W, offset)
+    out = qmm.qmm_get_rows(Wd, qtype, k, torch.from_numpy(ids).cuda(), n_rows=rows, row_stride_bytes=nb1)
+    torch.cuda.synchronize()
+    assert_bitwise(out.cpu().numpy(), O.get_rows(W, qtype, rows, k, nb1, ids), "get_rows")

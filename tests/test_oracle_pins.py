@@ -67,6 +67,23 @@ def test_golden_block(fname, qtype):
     assert s[0, 0] == np.sum(np.abs(want))
 
 
+def test_get_rows_gathers_golden_rows():
+    """Row selection checked against the golden blocks' printed elements:
+    W = [Q4_0 golden block; the same block with its scale negated]."""
+    g = read_golden("q4_0_block.txt")
+    raw = _hex_bytes(g["bytes"])
+    neg = raw.copy()
+    neg[1] ^= 0x80  # sign bit of the binary16 scale
+    W = np.vstack([raw, neg])
+    want0 = np.array([float(v) for v in g["elements"]], dtype=np.float32)
+    out = O.get_rows(W, Q4, 2, 32, raw.size, [1, 0, 0, -1, 2])
+    assert out.shape == (5, 32)
+    assert np.array_equal(out[0], -want0)
+    assert np.array_equal(out[1], want0) and np.array_equal(out[2], want0)
+    assert np.isnan(out[3]).all() and np.isnan(out[4]).all()
+    assert O.get_rows(W, Q4, 2, 32, raw.size, []).shape == (0, 32)
+
+
 # ---------------------------------------------------------------- codes, position by position
 def test_q4_0_every_code_at_every_position():
     # d = 1.0 (0x3c00); every element code 8 (weight 0) except one position.
