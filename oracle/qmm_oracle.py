@@ -182,6 +182,42 @@ def matmul(W, qtype: int, n_rows: int, k: int, nb1: int, X):
     return y, s
 
 
+def matmul_id(W, qtype: int, n_experts: int, n_rows: int, k: int, nb1: int, nb2: int, X, ids):
+    """MUL_MAT_ID: expert-routed MUL_MAT ([Load] section "第六步：能力校验":
+    ggml_mul_mat_id(ctx, w, b, ids) with w the stacked experts, b F32
+    [ne0 = k, n_ids_used, n_tokens] and ids I32 [n_ids_used, n_tokens]).
+
+    W  : uint8 [n_experts][nb2]; expert e's row r starts at byte r * nb1 of
+         W[e] (nb2 >= n_rows * nb1).
+    X  : [n_tokens][x_slots][k], x_slots = n_ids (one activation row per
+         selected expert, the pages' shape) or 1 (one row shared by all).
+    ids: int [n_tokens][n_ids].
+    Returns (y, s), float64 [n_tokens][n_ids][n_rows]: for token t and slot i
+    the MUL_MAT of expert ids[t][i] with X[t][i] (or X[t][0]). An id outside
+    [0, n_experts) selects no expert; its row is NaN (the library's reading).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    X = np.asarray(X)
+    n_tokens, n_ids = ids.shape
+    if X.ndim != 3 or X.shape[0] != n_tokens or X.shape[1] not in (1, n_ids) or X.shape[2] != k:
+        raise ValueError("X must be [n_tokens][1 or n_ids][k]")
+    W = np.asarray(W, dtype=np.uint8)
+    if W.shape != (n_experts, nb2) or nb2 < n_rows * nb1:
+        raise ValueError("W must be [n_experts][nb2] with nb2 >= n_rows * nb1")
+    y = np.full((n_tokens, n_ids, n_rows), np.nan)
+    s = np.full((n_tokens, n_ids, n_rows), np.nan)
+    for t in range(n_tokens):
+        for i in range(n_ids):
+            e = ids[t, i]
+            if not 0 <= e < n_experts:
+                continue
+            We = W[e, :n_rows * nb1].reshape(n_rows, nb1)
+            xr = X[t, i if X.shape[1] > 1 else 0].reshape(1, k)
+            yt, st = matmul(We, qtype, n_rows, k, nb1, xr)
+            y[t, i], s[t, i] = yt[0], st[0]
+    return y, s
+
+
 def matmul_sampled(W, qtype: int, n_rows: int, k: int, nb1: int, X, tokens, rows):
     """y and s for the listed (token, row) pairs only, each as a plain fp64
     dot product of one dequantised row with one activation row."""

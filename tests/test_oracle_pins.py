@@ -175,6 +175,44 @@ def test_brute_force_fraction(qtype, k):
             assert abs(Fraction(s[t, r]) - se) <= Fraction(bound), (r, t)
 
 
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("x_slots", [1, 2])
+def test_matmul_id_brute_force_fraction(qtype, x_slots):
+    """MUL_MAT_ID against exact rational sums over hand-decoded blocks of the
+    selected expert, with a repeated and an invalid expert id."""
+    rng = np.random.Generator(np.random.PCG64(77 + qtype + x_slots))
+    n_exp, rows, k, n_ids, ntok = 3, 3, 64, 2, 3
+    nb1 = O.row_bytes(qtype, k) + 2
+    nb2 = rows * nb1 + 4
+    W = np.zeros((n_exp, nb2), np.uint8)
+    for e in range(n_exp):
+        W[e, :rows * nb1] = synth.make_weights(qtype, rows, k, nb1, rng, d_lo=-2.0, d_hi=2.0).reshape(-1)
+        W[e, rows * nb1:] = rng.integers(0, 256, size=nb2 - rows * nb1, dtype=np.uint8)
+    X = (rng.standard_normal((ntok, x_slots, k)) * 4).astype(np.float32)
+    ids = np.array([[2, 0], [1, 1], [0, 3]])
+    y, s = O.matmul_id(W, qtype, n_exp, rows, k, nb1, nb2, X, ids)
+    assert np.isnan(y[2, 1]).all()
+    bpb = O.BLOCK_BYTES[qtype]
+    for t in range(ntok):
+        for i in range(n_ids):
+            e = ids[t, i]
+            if e >= n_exp:
+                continue
+            xs = [Fraction(float(v)) for v in X[t, i if x_slots > 1 else 0]]
+            for r in range(rows):
+                row = W[e, r * nb1:(r + 1) * nb1]
+                w = []
+                for b in range(k // 32):
+                    w += _decode_block_by_hand(row[b * bpb:(b + 1) * bpb], qtype)
+                ye = sum(wi * xi for wi, xi in zip(w, xs))
+                se = sum(abs(wi * xi) for wi, xi in zip(w, xs))
+                bound = k * 2.0 ** -52 * float(se)
+                assert abs(Fraction(y[t, i, r]) - ye) <= Fraction(bound), (t, i, r)
+                assert abs(Fraction(s[t, i, r]) - se) <= Fraction(bound), (t, i, r)
+    if x_slots == 1:
+        assert np.array_equal(y[1, 0], y[1, 1])  # same expert, same activation row
+
+
 # ---------------------------------------------------------------- invariants
 def _case(qtype, rows=37, k=160, nb1_extra=10, ntok=5, seed=7):
     rng = np.random.Generator(np.random.PCG64(seed))
