@@ -62,8 +62,9 @@ def lib() -> ctypes.CDLL:
         L.qmm_dequantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
         L.qmm_matmul_batch.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp]
         L.qmm_get_rows.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
+        L.qmm_matmul_id.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
         for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch",
-                  "qmm_get_rows"):
+                  "qmm_get_rows", "qmm_matmul_id"):
             getattr(L, f).restype = i32
         L.qmm_row_bytes.argtypes = [i32, i64]
         L.qmm_row_bytes.restype = i64
@@ -181,6 +182,40 @@ def qmm_get_rows(W, ggml_type, k, ids, n_rows=None, row_stride_bytes=None, out=N
     if st != QMM_OK:
         raise QmmError(st, "qmm_get_rows")
     return out
+
+
+def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stride_bytes=None,
+                  expert_stride_bytes=None, Y=None, stream=None):
+    """MUL_MAT_ID (C: qmm_matmul_id): Y[t][i] = MUL_MAT(expert ids[t][i], X[t][i or 0]).
+
+    W is a contiguous uint8 [n_experts][n_rows][nb1] GPU tensor, or any uint8
+    GPU tensor with the four geometry arguments given. X is a contiguous fp32
+    [n_tokens][x_slots][k] tensor (x_slots 1 or n_ids), ids a contiguous int32
+    [n_tokens][n_ids] tensor; Y (fp32 [n_tokens][n_ids][n_rows]) is allocated
+    if None. An id outside [0, n_experts) gives a row of NaNs."""
+    import torch
+    if W.dtype != torch.uint8:
+        raise TypeError("W must be a uint8 tensor of raw blocks")
+    if None in (n_experts, n_rows, row_stride_bytes, expert_stride_bytes):
+        if W.dim() != 3 or not W.is_contiguous():
+            raise ValueError("pass the geometry for a W that is not a contiguous [experts][rows][nb1] tensor")
+        n_experts, n_rows, row_stride_bytes = W.shape
+        expert_stride_bytes = n_rows * row_stride_bytes
+    if X.dtype != torch.float32 or X.dim() != 3 or not X.is_contiguous():
+        raise TypeError("X must be a contiguous float32 [n_tokens][x_slots][k] tensor")
+    if ids.dtype != torch.int32 or ids.dim() != 2 or not ids.is_contiguous():
+        raise TypeError("ids must be a contiguous int32 [n_tokens][n_ids] tensor")
+    n_tokens, n_ids = int(ids.shape[0]), int(ids.shape[1])
+    if int(X.shape[0]) != n_tokens or int(X.shape[2]) != int(k):
+        raise ValueError("X must be [n_tokens][x_slots][k] with the n_tokens of ids")
+    if Y is None:
+        Y = torch.empty((n_tokens, n_ids, int(n_rows)), dtype=torch.float32, device=X.device)
+    st = lib().qmm_matmul_id(_gpu_ptr(W, "W"), int(ggml_type), int(n_experts), int(n_rows), int(k),
+                             int(row_stride_bytes), int(expert_stride_bytes), _gpu_ptr(X, "X"), int(X.shape[1]),
+                             _gpu_ptr(ids, "ids"), n_ids, n_tokens, _gpu_ptr(Y, "Y"), _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_matmul_id")
+    return Y
 
 
 def qmm_matmul_batch(items, stream=None):

@@ -113,12 +113,38 @@ __device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4
 }
 
 // Dynamic LDS: the staged activations of one chunk, chunk_blocks * 64 * NT bytes.
+// Expert routing (MUL_MAT_ID) when ids is not null: workgroup row y serves
+// pair p = pair0 + blockIdx.y = (token p / n_ids, slot p % n_ids), whose
+// matrix is expert ids[p] of the stack (stride nb2), activation row
+// X[token][slot] (X[token][0] when x_slots == 1, fp32) and output Y[p]; an
+// id outside [0, n_experts) gives a row of NaNs.
+struct GemvRoute {
+  const int32_t *ids;
+  int64_t nb2;
+  int n_experts, n_ids, x_slots, pair0;
+};
+
 template <int QT, int NT, bool XF16, bool ALIGN4, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
                                                             int64_t nb1, const void *__restrict__ X, int n_tokens,
-                                                            int k, float *__restrict__ Y, int chunk_blocks) {
+                                                            int k, float *__restrict__ Y, int chunk_blocks,
+                                                            GemvRoute route) {
   extern __shared__ __attribute__((aligned(16))) half8_t xs[];
   __shared__ float red[WAVES][NT > 4 ? 32 : 16][4];
+  if (route.ids != nullptr) {
+    const int p = route.pair0 + static_cast<int>(blockIdx.y);
+    const int e = __builtin_amdgcn_readfirstlane(route.ids[p]);
+    const int t = p / route.n_ids, slot = p - t * route.n_ids;
+    Y += static_cast<int64_t>(p) * n_rows;
+    if (e < 0 || e >= route.n_experts) {
+      const int row = static_cast<int>(blockIdx.x) * 16 + static_cast<int>(threadIdx.x);
+      if (threadIdx.x < 16 && row < n_rows) Y[row] = __builtin_bit_cast(float, 0x7FC00000u);
+      return;
+    }
+    W += static_cast<int64_t>(e) * route.nb2;
+    X = static_cast<const float *>(X) + (static_cast<int64_t>(t) * route.x_slots + (route.x_slots > 1 ? slot : 0)) * k;
+    n_tokens = 1;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
@@ -208,6 +234,7 @@ struct GemvLaunch {
   int n_tokens, k;
   float *Y;
   int chunk_blocks;
+  GemvRoute route;
 };
 
 // Allow the kernel more than the default dynamic LDS (once per instantiation).
@@ -223,15 +250,16 @@ static hipError_t gemv_go_w(bool align4, const GemvLaunch &a) {
   if (e != hipSuccess) return e;
   if (align4)
     return launch(gemv_kernel<QT, NT, XF16, true, WAVES>, a.grid, dim3(64 * WAVES), a.lds, a.s, a.w, a.n_rows, a.nblk,
-                  a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks);
+                  a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks, a.route);
   return launch(gemv_kernel<QT, NT, XF16, false, WAVES>, a.grid, dim3(64 * WAVES), a.lds, a.s, a.w, a.n_rows, a.nblk,
-                a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks);
+                a.nb1, a.X, a.n_tokens, a.k, a.Y, a.chunk_blocks, a.route);
 }
 
 template <int QT, int NT, bool XF16>
 static hipError_t gemv_go(bool align4, const GemvLaunch &a) {
-  return k_split_for(a.grid.x, device_cus()) == kKSplitSmall ? gemv_go_w<QT, NT, XF16, kKSplitSmall>(align4, a)
-                                                             : gemv_go_w<QT, NT, XF16, kKSplitLarge>(align4, a);
+  const int64_t groups = static_cast<int64_t>(a.grid.x) * (a.route.ids ? a.grid.y : 1);
+  return k_split_for(groups, device_cus()) == kKSplitSmall ? gemv_go_w<QT, NT, XF16, kKSplitSmall>(align4, a)
+                                                           : gemv_go_w<QT, NT, XF16, kKSplitLarge>(align4, a);
 }
 
 template <int QT, bool XF16>
@@ -250,6 +278,36 @@ static hipError_t gemv_nt(int nt, bool align4, GemvLaunch a) {
   return gemv_go<QT, 8, XF16>(align4, a);
 }
 
+hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
+                                  int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids, int64_t n_ids,
+                                  int64_t n_tokens, float *Y, hipStream_t stream) {
+  const int64_t pairs = n_tokens * n_ids;
+  constexpr int64_t kMaxY = 65535;  // grid rows per launch
+  const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0) && (nb2 % 4 == 0);
+  for (int64_t p0 = 0; p0 < pairs; p0 += kMaxY) {
+    GemvLaunch a;
+    const unsigned count = static_cast<unsigned>(pairs - p0 < kMaxY ? pairs - p0 : kMaxY);
+    a.grid = dim3(static_cast<unsigned>((n_rows + 15) / 16), count);
+    a.lds = 0;
+    a.s = stream;
+    a.w = static_cast<const uint8_t *>(W);
+    a.n_rows = static_cast<int>(n_rows);
+    a.nblk = static_cast<int>(k / 32);
+    a.nb1 = nb1;
+    a.X = X;
+    a.n_tokens = 1;
+    a.k = static_cast<int>(k);
+    a.Y = Y;
+    a.chunk_blocks = a.nblk;
+    a.route = GemvRoute{ids, nb2, static_cast<int>(n_experts), static_cast<int>(n_ids), static_cast<int>(x_slots),
+                        static_cast<int>(p0)};
+    hipError_t e = qtype == QMM_TYPE_Q4_0 ? gemv_nt<QMM_TYPE_Q4_0, false>(1, align4, a)
+                                           : gemv_nt<QMM_TYPE_Q8_0, false>(1, align4, a);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X,
                                bool x_f16, int64_t n_tokens, float *Y, hipStream_t stream) {
   GemvLaunch a;
@@ -265,6 +323,7 @@ hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t
   a.k = static_cast<int>(k);
   a.Y = Y;
   a.chunk_blocks = a.nblk;
+  a.route = GemvRoute{nullptr, 0, 0, 0, 0, 0};
   const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0);
   const int nt = a.n_tokens;
   if (qtype == QMM_TYPE_Q4_0)

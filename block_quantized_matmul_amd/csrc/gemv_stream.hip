@@ -96,6 +96,19 @@ typedef const __attribute__((address_space(4))) u32x16_t *KRec;
 // Byte offset of the table in the kernel-argument segment: it follows
 // matrix 0's eight scalar arguments (48 bytes) and two 8-byte pads.
 constexpr int kRTableOffset = 64;
+
+// Routing record of an expert-routed launch (MUL_MAT_ID), in the table's
+// second slot: pair p = pair0 + blockIdx.y is (token p / n_ids, slot
+// p % n_ids); its matrix is expert ids[p] of the stack (expert stride nb2),
+// its activation row X[token][slot] (X[token][0] when x_slots == 1), its
+// output Y[p].
+struct RRoute {
+  const int32_t *ids;
+  int64_t nb2;
+  int n_experts, n_ids, x_slots, pair0;
+  int pad[8];
+};
+static_assert(sizeof(RRoute) == 64, "one table slot");
 // Fourth word of a buffer resource: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -213,7 +226,7 @@ __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const f
   }
 }
 
-template <int QT, int NT, bool XF16, int WAVES>
+template <int QT, int NT, bool XF16, int WAVES, bool IDS = false>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::waves_per_simd_large : 4)) void gemv_stream_kernel(
     const uint8_t *W0, const void *X0, float *Y0, int64_t nb1_0, int n_rows0, int nblk0, int n_tokens0, int k0,
     int64_t, int64_t, const RBatch batch) {
@@ -229,7 +242,32 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   uint64_t wp0, xp0, yp0;
   int64_t nb1;
   int n_rows, nblk, n_tokens, k;
-  if (blockIdx.y == 0) {
+  if constexpr (IDS) {
+    // Expert-routed: matrix 0's fields describe expert 0 of the stack and
+    // the shared X and Y; the routing record selects this pair's expert.
+    typedef const __attribute__((address_space(4))) char *KBytes;
+    const u32x16_t rec = ((KRec)((KBytes)__builtin_amdgcn_kernarg_segment_ptr() + kRTableOffset))[1];
+    const GPtr<int32_t> ids = (GPtr<int32_t>)((static_cast<uint64_t>(rec[1]) << 32) | rec[0]);
+    const int64_t nb2 = static_cast<int64_t>((static_cast<uint64_t>(rec[3]) << 32) | rec[2]);
+    const int n_experts = static_cast<int>(rec[4]), n_ids = static_cast<int>(rec[5]);
+    const int x_slots = static_cast<int>(rec[6]);
+    const int p = static_cast<int>(rec[7]) + static_cast<int>(blockIdx.y);
+    const int e = __builtin_amdgcn_readfirstlane(ids[p]);
+    const int t = p / n_ids, slot = p - t * n_ids;
+    nb1 = nb1_0;
+    n_rows = n_rows0, nblk = nblk0, n_tokens = 1, k = k0;
+    yp0 = reinterpret_cast<uint64_t>(Y0) + static_cast<uint64_t>(p) * static_cast<uint64_t>(n_rows) * 4;
+    if (e < 0 || e >= n_experts) {
+      // no such expert: this pair's rows are NaN
+      const int row = static_cast<int>(blockIdx.x) * 16 + static_cast<int>(threadIdx.x);
+      if (threadIdx.x < 16 && row < n_rows)
+        reinterpret_cast<__attribute__((address_space(1))) float *>(yp0)[row] = __builtin_bit_cast(float, 0x7FC00000u);
+      return;
+    }
+    wp0 = reinterpret_cast<uint64_t>(W0) + static_cast<uint64_t>(e) * static_cast<uint64_t>(nb2);
+    xp0 = reinterpret_cast<uint64_t>(X0) +
+          (static_cast<uint64_t>(t) * x_slots + (x_slots > 1 ? slot : 0)) * static_cast<uint64_t>(k) * 4;
+  } else if (blockIdx.y == 0) {
     wp0 = reinterpret_cast<uint64_t>(W0);
     xp0 = reinterpret_cast<uint64_t>(X0);
     yp0 = reinterpret_cast<uint64_t>(Y0);
@@ -348,6 +386,64 @@ static bool streamable(const MatmulDesc &d) {
   const int64_t xbytes = d.n_tokens * d.k * (d.x_f16 ? 2 : 4);
   return reinterpret_cast<uintptr_t>(d.W) % 16 == 0 && d.nb1 % 16 == 0 && nblk % 8 == 0 &&
          d.n_rows * d.nb1 < (int64_t{1} << 32) && d.nb1 < (int64_t{1} << 24) && xbytes < (int64_t{1} << 32);
+}
+
+static RMat record(const MatmulDesc &d) {
+  RMat r{};
+  r.W = static_cast<const uint8_t *>(d.W);
+  r.X = d.X;
+  r.Y = d.Y;
+  r.nb1 = d.nb1;
+  r.n_rows = static_cast<int>(d.n_rows);
+  r.nblk = static_cast<int>(d.k / 32);
+  r.n_tokens = static_cast<int>(d.n_tokens);
+  r.k = static_cast<int>(d.k);
+  return r;
+}
+
+template <int QT, int WAVES>
+static hipError_t id_go_w(const RBatch &B, int count, int rg, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(WAVES) * RCfg<QT, 1>::lds_per_wave + WAVES * 32 * 4 * sizeof(float);
+  const RMat &m0 = B.m[0];
+  return launch(gemv_stream_kernel<QT, 1, false, WAVES, true>, dim3(rg, count), dim3(64 * WAVES), lds, s, m0.W, m0.X,
+                m0.Y, m0.nb1, m0.n_rows, m0.nblk, m0.n_tokens, m0.k, int64_t{0}, int64_t{0}, B);
+}
+
+bool id_streamable(const void *W, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2) {
+  return reinterpret_cast<uintptr_t>(W) % 16 == 0 && nb1 % 16 == 0 && nb2 % 16 == 0 && (k / 32) % 8 == 0 &&
+         n_rows * nb1 < (int64_t{1} << 32) && nb1 < (int64_t{1} << 24) && k * 4 < (int64_t{1} << 32);
+}
+
+hipError_t launch_gemv_id_stream(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
+                                 int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids, int64_t n_ids,
+                                 int64_t n_tokens, float *Y, hipStream_t stream) {
+  RBatch B{};
+  B.m[0] = record(MatmulDesc{W, qtype, n_rows, k, nb1, X, false, 1, Y});
+  RRoute route{};
+  route.ids = ids;
+  route.nb2 = nb2;
+  route.n_experts = static_cast<int>(n_experts);
+  route.n_ids = static_cast<int>(n_ids);
+  route.x_slots = static_cast<int>(x_slots);
+  const int64_t pairs = n_tokens * n_ids;
+  const int rg = static_cast<int>((n_rows + 15) / 16);
+  const int waves = k_split_for(pairs * rg, device_cus());
+  constexpr int64_t kMaxY = 65535;  // grid rows per launch
+  for (int64_t p0 = 0; p0 < pairs; p0 += kMaxY) {
+    route.pair0 = static_cast<int>(p0);
+    static_assert(sizeof(RRoute) == sizeof(RMat), "routing record fills one table slot");
+    __builtin_memcpy(&B.m[1], &route, sizeof(RRoute));
+    const int count = static_cast<int>(pairs - p0 < kMaxY ? pairs - p0 : kMaxY);
+    hipError_t e;
+    if (qtype == QMM_TYPE_Q4_0)
+      e = waves == kKSplitSmall ? id_go_w<QMM_TYPE_Q4_0, kKSplitSmall>(B, count, rg, stream)
+                                : id_go_w<QMM_TYPE_Q4_0, kKSplitLarge>(B, count, rg, stream);
+    else
+      e = waves == kKSplitSmall ? id_go_w<QMM_TYPE_Q8_0, kKSplitSmall>(B, count, rg, stream)
+                                : id_go_w<QMM_TYPE_Q8_0, kKSplitLarge>(B, count, rg, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t stream) {

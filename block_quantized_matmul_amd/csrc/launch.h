@@ -60,6 +60,18 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count, hipStream_t stream)
 hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X,
                                bool x_f16, int64_t n_tokens, float *Y, hipStream_t stream);
 
+// Expert-routed decode (MUL_MAT_ID): one single-token product per
+// (token, slot) pair, against expert ids[pair] of a stack of n_experts
+// matrices expert_stride bytes apart. The streaming kernel takes stacks that
+// id_streamable accepts, the general kernel any valid layout.
+bool id_streamable(const void *W, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2);
+hipError_t launch_gemv_id_stream(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
+                                 int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids, int64_t n_ids,
+                                 int64_t n_tokens, float *Y, hipStream_t stream);
+hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
+                                  int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids, int64_t n_ids,
+                                  int64_t n_tokens, float *Y, hipStream_t stream);
+
 // Matrix-core kernel, any n_tokens >= 1.
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
                        int64_t n_tokens, float *Y, hipStream_t stream);

@@ -189,4 +189,31 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
                                         static_cast<hipStream_t>(stream)));
 }
 
+int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                  int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *stream) {
+  if (X == nullptr || ids == nullptr || Y == nullptr) return QMM_ERR_NULL;
+  int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
+  if (st != QMM_OK) return st;
+  if (n_experts < 0 || n_experts > kMaxDim || n_ids < 0 || n_tokens < 0) return QMM_ERR_SHAPE;
+  if (n_ids > 0 && n_tokens > kMaxDim / n_ids) return QMM_ERR_SHAPE;  // pair index is an int
+  if (x_slots != 1 && x_slots != n_ids) return QMM_ERR_SHAPE;
+  if (expert_stride_bytes % 2 != 0 || expert_stride_bytes < n_rows * row_stride_bytes) return QMM_ERR_STRIDE;
+  if (!aligned(X, 4) || !aligned(ids, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+  if (n_rows == 0 || n_ids == 0 || n_tokens == 0) return QMM_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool streaming = qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
+  if (trace_on())
+    fprintf(stderr, "qmm: matmul_id %s %s experts=%lld rows=%lld k=%lld nb1=%lld nb2=%lld ids=%lld tokens=%lld\n",
+            streaming ? "stream" : "general", type_name(ggml_type), (long long)n_experts, (long long)n_rows,
+            (long long)k, (long long)row_stride_bytes, (long long)expert_stride_bytes, (long long)n_ids,
+            (long long)n_tokens);
+  if (streaming)
+    return status_of(qmm::launch_gemv_id_stream(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
+                                                expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));
+  return status_of(qmm::launch_gemv_id_general(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
+                                              expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));
+}
+
 }  // extern "C"

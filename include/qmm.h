@@ -190,6 +190,37 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
                  const int32_t *ids, int64_t n_ids, float *out, void *stream);
 
 /*
+ * qmm_matmul_id - MUL_MAT_ID, the expert-routed MUL_MAT that serves MoE
+ * expert routing (and adapter routing): for every token t and slot i,
+ *   Y[t][i][r] = sum_j dequant(W_e)[r][j] * X[t][s][j],  e = ids[t][i],
+ * with s = i when x_slots == n_ids and s = 0 when x_slots == 1 (one
+ * activation row shared by all slots). This is the op the capability probe
+ * builds with activations F32 [k, n_ids, tokens] and ids I32 [n_ids, tokens]
+ * ([Load] section 第六步, the GGML_OP_MUL_MAT_ID case).
+ *   W                    device pointer to n_experts matrices, each n_rows rows
+ *                        of row_stride_bytes, expert e at e * expert_stride_bytes
+ *                        (2-byte aligned, caller-owned, read only)
+ *   ggml_type, k, row_stride_bytes  as in qmm_matmul
+ *   n_experts            matrices in the stack (>= 0)
+ *   expert_stride_bytes  even, >= n_rows * row_stride_bytes
+ *   X                    device pointer, fp32 [n_tokens][x_slots][k], 4-byte aligned
+ *   x_slots              1 or n_ids
+ *   ids                  device pointer, int32 [n_tokens][n_ids], 4-byte aligned
+ *   n_ids, n_tokens      >= 0, n_ids * n_tokens < 2^31; 0 is a no-op
+ *   Y                    device pointer, fp32 [n_tokens][n_ids][n_rows], 4-byte aligned
+ *   stream               hipStream_t or NULL
+ * Every pair is a single-token product on the decode kernels, so weight
+ * traffic grows with n_tokens * n_ids (the decode case, not a grouped
+ * prefill GEMM). An id outside [0, n_experts) cannot be checked on the host:
+ * that pair's output row is filled with quiet NaNs and nothing is read for it.
+ * Returns QMM_OK, or the status of the first failed check (QMM_ERR_NULL,
+ * _TYPE, _SHAPE, _STRIDE, _ALIGN) without launching, or QMM_ERR_HIP.
+ */
+int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                  int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *stream);
+
+/*
  * qmm_row_bytes - the dense row stride (k / 32) * block bytes, i.e. nb[1]
  * without padding ([Graph] ggml_tensor stride comment). Negative status code
  * for an unknown type or a k that is not a positive multiple of 32.

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
-                            "qmm_dequantize", "qmm_get_rows", "qmm_row_bytes", "qmm_supports",
+                            "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_row_bytes", "qmm_supports",
                             "qmm_status_string"])
 
 
@@ -137,6 +137,37 @@ def test_get_rows_validation(L):
     assert L.qmm_get_rows(P, Q4, 4, 64, 36, A, 3, ctypes.c_void_p(0x20002), NULL) == qmm.QMM_ERR_ALIGN
     # zero indices: nothing is launched
     assert L.qmm_get_rows(P, Q4, 4, 64, 36, A, 0, P2, NULL) == qmm.QMM_OK
+
+
+def _mid(L, W=P, t=Q4, ne=8, rows=16, k=64, nb1=36, nb2=576, X=P2, xs=2, ids=ctypes.c_void_p(0x40000), n_ids=2,
+         n=3, Y=P3):
+    return L.qmm_matmul_id(W, t, ne, rows, k, nb1, nb2, X, xs, ids, n_ids, n, Y, NULL)
+
+
+def test_matmul_id_validation(L):
+    # nothing below is launched: every call fails a host check or is empty
+    assert _mid(L, W=NULL) == qmm.QMM_ERR_NULL
+    assert _mid(L, X=NULL) == qmm.QMM_ERR_NULL
+    assert _mid(L, ids=NULL) == qmm.QMM_ERR_NULL
+    assert _mid(L, Y=NULL) == qmm.QMM_ERR_NULL
+    assert _mid(L, t=7) == qmm.QMM_ERR_TYPE
+    assert _mid(L, k=48) == qmm.QMM_ERR_SHAPE
+    assert _mid(L, ne=-1) == qmm.QMM_ERR_SHAPE
+    assert _mid(L, n_ids=-1, xs=1) == qmm.QMM_ERR_SHAPE
+    assert _mid(L, n=-1) == qmm.QMM_ERR_SHAPE
+    assert _mid(L, xs=3) == qmm.QMM_ERR_SHAPE            # x_slots must be 1 or n_ids
+    assert _mid(L, n_ids=1 << 16, xs=1, n=1 << 16) == qmm.QMM_ERR_SHAPE  # 2^32 pairs
+    assert _mid(L, nb1=35) == qmm.QMM_ERR_STRIDE
+    assert _mid(L, nb2=575) == qmm.QMM_ERR_STRIDE         # below n_rows * nb1
+    assert _mid(L, nb2=577) == qmm.QMM_ERR_STRIDE         # odd
+    assert _mid(L, W=ctypes.c_void_p(0x10001)) == qmm.QMM_ERR_ALIGN
+    assert _mid(L, X=ctypes.c_void_p(0x20002)) == qmm.QMM_ERR_ALIGN
+    assert _mid(L, ids=ctypes.c_void_p(0x40002)) == qmm.QMM_ERR_ALIGN
+    assert _mid(L, Y=ctypes.c_void_p(0x30002)) == qmm.QMM_ERR_ALIGN
+    # empty calls succeed without a launch
+    assert _mid(L, n=0) == qmm.QMM_OK
+    assert _mid(L, n_ids=0, xs=1) == qmm.QMM_OK
+    assert _mid(L, rows=0, nb2=0) == qmm.QMM_OK
 
 
 def test_binding_refuses_cpu_tensors():
