@@ -86,6 +86,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-get-rows", action="store_true", help="skip the GET_ROWS (token-embedding gather) line")
+    ap.add_argument("--no-matmul-id", action="store_true", help="skip the MUL_MAT_ID (routed expert FFN) lines")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
@@ -246,6 +247,96 @@ def time_get_rows(torch, qmm, synth, with_oracle=False):
         t0 = time.perf_counter()
         O.get_rows(Wh, qt, rows, k, nb1, idh)
         res["cpu_oracle_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+    return res
+
+
+# ---------------------------------------------------------------- MUL_MAT_ID
+
+MOE_EXPERTS, MOE_ROWS, MOE_K, MOE_USED = 8, 14336, 4096, 2
+MOE_PREFILL_TOKENS = 512
+
+
+def _graph_time(torch, run, reps):
+    """Median over 5 replays of a graph of `reps` launches: microseconds per launch."""
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(5):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return sorted(ts)[2]
+
+
+def time_matmul_id(torch, qmm, synth, with_oracle=False):
+    """MUL_MAT_ID on a routed FFN projection: 8 experts of 14336x4096 Q4_0,
+    2 selected per token (seeded random routing), activations shared by the
+    slots. Decode (1 token, per-pair decode kernel) and the probe's 512-token
+    batch (grouped: routing kernel + matrix-core tiles), each as back-to-back
+    launches in a graph over >= 1.1 GiB of expert-stack copies, a different
+    routing per launch, so the weights come from HBM."""
+    import numpy as np
+    E, rows, k, used, qt = MOE_EXPERTS, MOE_ROWS, MOE_K, MOE_USED, synth.TYPE_Q4_0
+    nb1 = synth.dense_row_bytes(qt, k)
+    rng = np.random.Generator(np.random.PCG64(4343))
+    Wh = synth.make_weights(qt, E * rows, k, nb1, rng)
+    W0 = torch.from_numpy(Wh).cuda().view(E, rows, nb1)
+    copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    res = {"workload": f"{E} experts of {rows}x{k} Q4_0, {used} selected per token"}
+
+    def routing(n_tokens):
+        return np.stack([rng.permutation(E)[:used] for _ in range(n_tokens)]).astype(np.int32)
+
+    # decode
+    reps = 4 * copies
+    ids_d = [torch.from_numpy(routing(1)).cuda() for _ in range(reps)]
+    Xd = torch.from_numpy(synth.make_activations(1, k, rng)).cuda().view(1, 1, k)
+    Yd = torch.empty((1, used, rows), dtype=torch.float32, device="cuda")
+
+    def run_d():
+        for i in range(reps):
+            qmm.qmm_matmul_id(Ws[i % copies], qt, k, Xd, ids_d[i], Y=Yd)
+
+    us = _graph_time(torch, run_d, reps)
+    byts = used * rows * nb1 + 4 * k + 4 * used + 4 * used * rows
+    gbs = byts / (us * 1e-6) / 1e9
+    res["decode"] = {"tokens": 1, "us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": byts,
+                     "GB_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "kernel": "gemv_stream_kernel", "bound": "hbm"}
+    # prefill-sized batch
+    T = MOE_PREFILL_TOKENS
+    reps_p = copies
+    ids_p = [torch.from_numpy(routing(T)).cuda() for _ in range(reps_p)]
+    Xp = torch.from_numpy(synth.make_activations(T, k, rng)).cuda().view(T, 1, k)
+    Yp = torch.empty((T, used, rows), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qmm.qmm_matmul_id_workspace_bytes(E, used, T), dtype=torch.uint8, device="cuda")
+
+    def run_p():
+        for i in range(reps_p):
+            qmm.qmm_matmul_id(Ws[i % copies], qt, k, Xp, ids_p[i], Y=Yp, workspace=ws)
+
+    us_p = _graph_time(torch, run_p, reps_p)
+    flops = 2 * T * used * rows * k
+    tfl = flops / (us_p * 1e-6) / 1e12
+    res["prefill"] = {"tokens": T, "us_per_launch": round(us_p, 3), "flops_per_launch": flops,
+                      "TFLOP_per_s": round(tfl, 2), "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
+                      "kernel": "route_kernel + gemm_kernel (routed)", "bound": "mfma"}
+    if with_oracle:
+        # the oracle as it stands, once, on the host: the decode call
+        import oracle.qmm_oracle as O
+        idh = ids_d[0].cpu().numpy()
+        t0 = time.perf_counter()
+        O.matmul_id(Wh.reshape(E, rows * nb1), qt, E, rows, k, nb1, rows * nb1, Xd.cpu().numpy(), idh)
+        res["decode"]["cpu_oracle_us"] = round((time.perf_counter() - t0) * 1e6, 1)
     return res
 
 
@@ -479,6 +570,8 @@ def main():
                                   "GB_per_s": round(gbs_pc, 2), "frac_of_hbm_peak": round(gbs_pc / HBM_PEAK_GBS, 4)}
     if not args.no_get_rows:
         out["get_rows"] = time_get_rows(torch, qmm, synth, with_oracle=bool(cpu_layers))
+    if not args.no_matmul_id:
+        out["matmul_id"] = time_matmul_id(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if cpu_layers:
         import oracle.qmm_oracle as O
         log("timing the CPU oracle on a sample")

@@ -28,6 +28,7 @@ QMM_ERR_STRIDE = -4
 QMM_ERR_ALIGN = -5
 QMM_ERR_HIP = -6
 QMM_ERR_PATH = -7
+QMM_ERR_WORKSPACE = -8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 
@@ -62,7 +63,9 @@ def lib() -> ctypes.CDLL:
         L.qmm_dequantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
         L.qmm_matmul_batch.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp]
         L.qmm_get_rows.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
-        L.qmm_matmul_id.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
+        L.qmm_matmul_id.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp, i64, vp]
+        L.qmm_matmul_id_workspace_bytes.argtypes = [i64, i64, i64]
+        L.qmm_matmul_id_workspace_bytes.restype = i64
         for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch",
                   "qmm_get_rows", "qmm_matmul_id"):
             getattr(L, f).restype = i32
@@ -184,8 +187,12 @@ def qmm_get_rows(W, ggml_type, k, ids, n_rows=None, row_stride_bytes=None, out=N
     return out
 
 
+def qmm_matmul_id_workspace_bytes(n_experts: int, n_ids: int, n_tokens: int) -> int:
+    return int(lib().qmm_matmul_id_workspace_bytes(int(n_experts), int(n_ids), int(n_tokens)))
+
+
 def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stride_bytes=None,
-                  expert_stride_bytes=None, Y=None, stream=None):
+                  expert_stride_bytes=None, Y=None, workspace=None, stream=None):
     """MUL_MAT_ID (C: qmm_matmul_id): Y[t][i] = MUL_MAT(expert ids[t][i], X[t][i or 0]).
 
     W is a contiguous uint8 [n_experts][n_rows][nb1] GPU tensor, or any uint8
@@ -196,7 +203,7 @@ def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stri
     import torch
     if W.dtype != torch.uint8:
         raise TypeError("W must be a uint8 tensor of raw blocks")
-    if None in (n_experts, n_rows, row_stride_bytes, expert_stride_bytes):
+    if any(v is None for v in (n_experts, n_rows, row_stride_bytes, expert_stride_bytes)):
         if W.dim() != 3 or not W.is_contiguous():
             raise ValueError("pass the geometry for a W that is not a contiguous [experts][rows][nb1] tensor")
         n_experts, n_rows, row_stride_bytes = W.shape
@@ -210,9 +217,17 @@ def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stri
         raise ValueError("X must be [n_tokens][x_slots][k] with the n_tokens of ids")
     if Y is None:
         Y = torch.empty((n_tokens, n_ids, int(n_rows)), dtype=torch.float32, device=X.device)
+    need = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens)
+    if need < 0:
+        raise QmmError(need, "qmm_matmul_id_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws = _gpu_ptr(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().qmm_matmul_id(_gpu_ptr(W, "W"), int(ggml_type), int(n_experts), int(n_rows), int(k),
                              int(row_stride_bytes), int(expert_stride_bytes), _gpu_ptr(X, "X"), int(X.shape[1]),
-                             _gpu_ptr(ids, "ids"), n_ids, n_tokens, _gpu_ptr(Y, "Y"), _stream(stream))
+                             _gpu_ptr(ids, "ids"), n_ids, n_tokens, _gpu_ptr(Y, "Y"), ws, ws_bytes,
+                             _stream(stream))
     if st != QMM_OK:
         raise QmmError(st, "qmm_matmul_id")
     return Y

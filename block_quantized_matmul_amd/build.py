@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmm.so")
 
-SOURCES = ["qmm_api.hip", "dequant.hip", "gemv.hip", "gemv_stream.hip", "gemm.hip"]
+SOURCES = ["qmm_api.hip", "dequant.hip", "gemv.hip", "gemv_stream.hip", "gemm.hip", "route.hip"]
 
 # Packed fp32 VALU forms are disabled for every HIP translation unit; the
 # host pass does not know the feature and warns, which is harmless.

@@ -34,7 +34,7 @@
 namespace qmm {
 
 constexpr int kBM = 128;  // weight rows per tile
-constexpr int kBN = 128;  // tokens per tile
+constexpr int kBN = kTileTokens;  // tokens per tile (128)
 constexpr int kBK = 64;   // k per stage (2 blocks)
 // LDS tiles are 128 rows x 64 halves, 128 bytes per row without padding;
 // 16-byte chunk c of row r sits at chunk position c ^ (r % 8). On gfx950 this
@@ -207,6 +207,24 @@ __device__ __forceinline__ void store_x_pieces(_Float16 *xs, const XPieces<XF16>
   }
 }
 
+// The routed form: piece i of a thread belongs to token slot c / per_tok of
+// the tile, whose activation row starts at xrow[i] (gathered once per tile).
+template <bool XF16>
+__device__ __forceinline__ XPieces<XF16> load_x_rows(const float *const *xrow, int k, int k0, int tid, bool tail) {
+  static_assert(!XF16, "routed activations are fp32");
+  using M = XMap<XF16>;
+  XPieces<XF16> r;
+#pragma unroll
+  for (int i = 0; i < M::n; ++i) {
+    const int e = k0 + M::elems * (tid % M::per_tok);
+    if (!tail || e < k)
+      r.v[i] = *reinterpret_cast<const float4_a4 *>(xrow[i] + e);
+    else
+      r.v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  return r;
+}
+
 // Workgroup barrier that waits for LDS accesses only: __syncthreads() would
 // also wait for the global loads of later stages, which are meant to stay in
 // flight across it.
@@ -238,11 +256,23 @@ __device__ __forceinline__ void interleave_stage() {
   }
 }
 
-template <int QT, bool XF16, bool ALIGN4>
+// Expert routing (MUL_MAT_ID): token tile t of the grid is tiles[t] =
+// (expert, first entry, count) of `list`, the (token, slot) pairs grouped by
+// expert; entry j of the tile is pair p = list[first + j], whose activation
+// row is X[p / n_ids][x_slots > 1 ? p % n_ids : 0] and output row Y[p]. A
+// tile with count 0 is empty.
+struct GemmRoute {
+  const int32_t *list;
+  const int32_t *tiles;  // 4 ints per tile
+  int64_t nb2;
+  int n_ids, x_slots;
+};
+
+template <int QT, bool XF16, bool ALIGN4, bool ROUTED = false>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
                                                                int64_t nb1, const void *__restrict__ X, int n_tokens,
                                                                int k, float *__restrict__ Y, bool y_vec4,
-                                                               int row_tiles) {
+                                                               int row_tiles, GemmRoute route) {
   __shared__ __attribute__((aligned(16))) _Float16 Ws[2][kBM * kBK];
   __shared__ __attribute__((aligned(16))) _Float16 Xs[2][kBN * kBK];
 
@@ -264,7 +294,28 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
   const int first_row = (lin / in_group) * kGroupRows;
   const int group_rows = min(row_tiles - first_row, kGroupRows);
   const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
-  const int tok0 = ((lin % in_group) / group_rows) * kBN;
+  int tok0 = ((lin % in_group) / group_rows) * kBN;
+
+  int list0 = 0;
+  const float *xrow[XMap<XF16>::n];
+  if constexpr (ROUTED) {
+    const int *td = route.tiles + 4 * (tok0 / kBN);
+    const int e = __builtin_amdgcn_readfirstlane(td[0]);
+    list0 = __builtin_amdgcn_readfirstlane(td[1]);
+    n_tokens = __builtin_amdgcn_readfirstlane(td[2]);
+    if (n_tokens == 0) return;  // whole workgroup: an unused tile
+    W += static_cast<int64_t>(e) * route.nb2;
+    tok0 = 0;
+    using M = XMap<XF16>;
+#pragma unroll
+    for (int i = 0; i < M::n; ++i) {
+      const int slot = min((256 * i + tid) / M::per_tok, n_tokens - 1);
+      const int p = route.list[list0 + slot];
+      const int t = p / route.n_ids;
+      const int64_t xr = static_cast<int64_t>(t) * route.x_slots + (route.x_slots > 1 ? p - t * route.n_ids : 0);
+      xrow[i] = static_cast<const float *>(X) + xr * k;
+    }
+  }
 
   // Weight staging: thread -> (row, half of the stage's block pair). The two
   // halves of a row sit in adjacent lanes, so each load instruction touches
@@ -289,7 +340,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
       r.w = load_half_pair<QT>(rp, st, sh);
     else
       r.w = load_half_u16<QT>(rp, 2 * st + sh, nblk);
-    r.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * st, tid, false);
+    if constexpr (ROUTED)
+      r.x = load_x_rows<XF16>(xrow, k, kBK * st, tid, false);
+    else
+      r.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * st, tid, false);
   };
   auto store = [&](int buf, const Stage &r) {
     store_half<QT>(Ws[buf], srow, 4 * sh, r.w, ALIGN4 && sh == 0);
@@ -351,7 +405,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
     const int buf = n_full & 1;
     Stage t;
     t.w = load_half_u16<QT>(rp, 2 * n_full + sh, nblk);
-    t.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * n_full, tid, true);
+    if constexpr (ROUTED)
+      t.x = load_x_rows<XF16>(xrow, k, kBK * n_full, tid, true);
+    else
+      t.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * n_full, tid, true);
     store_half<QT>(Ws[buf], srow, 4 * sh, t.w, false);
     store_x_pieces<XF16>(Xs[buf], t.x, tid);
     lds_barrier();
@@ -364,7 +421,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
   for (int j = 0; j < 4; ++j) {
     const int tok = tok0 + 64 * wn + 16 * j + (lane & 15);
     if (tok >= n_tokens) continue;
-    float *yrow = Y + static_cast<int64_t>(tok) * n_rows;
+    const int64_t yr = ROUTED ? route.list[list0 + tok] : tok;
+    float *yrow = Y + yr * n_rows;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = row0 + 64 * wm + 16 * i + 4 * (lane >> 4);
@@ -382,11 +440,36 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__
 template <int QT, bool XF16>
 static hipError_t gemm_dispatch(bool align4, dim3 grid, hipStream_t s, const uint8_t *w, int n_rows, int nblk,
                                 int64_t nb1, const void *X, int n_tokens, int k, float *Y, bool y_vec4, int row_tiles) {
+  const GemmRoute none{nullptr, nullptr, 0, 0, 0};
   if (align4)
     return launch(gemm_kernel<QT, XF16, true>, grid, dim3(kGemmThreads), 0, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y,
-                  y_vec4, row_tiles);
+                  y_vec4, row_tiles, none);
   return launch(gemm_kernel<QT, XF16, false>, grid, dim3(kGemmThreads), 0, s, w, n_rows, nblk, nb1, X, n_tokens, k, Y,
-                y_vec4, row_tiles);
+                y_vec4, row_tiles, none);
+}
+
+hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
+                              const float *X, int64_t x_slots, int64_t n_ids, const int32_t *list,
+                              const int32_t *tiles, int64_t max_tiles, float *Y, hipStream_t stream) {
+  const uint8_t *w = static_cast<const uint8_t *>(W);
+  const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0) && (nb2 % 4 == 0);
+  const bool y_vec4 = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && (n_rows % 4 == 0);
+  const int64_t row_tiles = (n_rows + kBM - 1) / kBM;
+  if (row_tiles * max_tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(row_tiles * max_tiles));
+  const GemmRoute route{list, tiles, nb2, static_cast<int>(n_ids), static_cast<int>(x_slots)};
+  const int rt = static_cast<int>(row_tiles), nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows),
+            kk = static_cast<int>(k);
+  const dim3 block(kGemmThreads);
+  if (qtype == QMM_TYPE_Q4_0)
+    return align4 ? launch(gemm_kernel<QMM_TYPE_Q4_0, false, true, true>, grid, block, 0, stream, w, nr, nblk, nb1,
+                           static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route)
+                  : launch(gemm_kernel<QMM_TYPE_Q4_0, false, false, true>, grid, block, 0, stream, w, nr, nblk, nb1,
+                           static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route);
+  return align4 ? launch(gemm_kernel<QMM_TYPE_Q8_0, false, true, true>, grid, block, 0, stream, w, nr, nblk, nb1,
+                         static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route)
+                : launch(gemm_kernel<QMM_TYPE_Q8_0, false, false, true>, grid, block, 0, stream, w, nr, nblk, nb1,
+                         static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route);
 }
 
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,

@@ -72,6 +72,21 @@ hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, i
                                   int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids, int64_t n_ids,
                                   int64_t n_tokens, float *Y, hipStream_t stream);
 
+// Grouped expert-routed product for many tokens: a routing kernel buckets the
+// pairs by expert into the workspace (route_workspace_bytes of it), then the
+// matrix-core kernel runs tiles of kTileTokens pairs of one expert. Experts
+// are counted in LDS, so n_experts <= kRouteMaxExperts.
+constexpr int kTileTokens = 128;
+constexpr int kRouteMaxExperts = 4096;
+int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs);
+int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs);
+hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k,
+                                    int64_t nb1, int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids,
+                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace, hipStream_t stream);
+hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
+                              const float *X, int64_t x_slots, int64_t n_ids, const int32_t *list,
+                              const int32_t *tiles, int64_t max_tiles, float *Y, hipStream_t stream);
+
 // Matrix-core kernel, any n_tokens >= 1.
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
                        int64_t n_tokens, float *Y, hipStream_t stream);

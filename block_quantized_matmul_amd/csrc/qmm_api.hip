@@ -84,6 +84,7 @@ const char *qmm_status_string(int status) {
     case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte, X, Y and out 4-byte alignment";
     case QMM_ERR_HIP: return "QMM_ERR_HIP: the HIP runtime rejected the kernel launch";
     case QMM_ERR_PATH: return "QMM_ERR_PATH: unknown path, or GEMV forced with more than 8 tokens";
+    case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or smaller than qmm_matmul_id_workspace_bytes";
     default: return "unknown qmm status";
   }
 }
@@ -189,26 +190,57 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
                                         static_cast<hipStream_t>(stream)));
 }
 
+// The grouped (bucket-by-expert) path serves calls with more tokens than the
+// decode kernels take and enough pairs per expert to amortise a matrix-core
+// tile: a selected expert costs about as much as 3 to 4 single-token passes
+// over its weights whatever its pair count (up to 128), so below an average
+// of 4 pairs per expert the per-pair decode route is faster. It needs the
+// workspace and counts experts in LDS.
+static bool id_grouped(int64_t n_experts, int64_t n_ids, int64_t n_tokens) {
+  const int64_t pairs = n_ids * n_tokens;
+  const int64_t used = n_experts < pairs ? n_experts : pairs;
+  return n_tokens > QMM_GEMV_MAX_TOKENS && n_experts <= qmm::kRouteMaxExperts && pairs >= 4 * used;
+}
+
+int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t n_tokens) {
+  if (n_experts < 0 || n_experts > kMaxDim || n_ids < 0 || n_tokens < 0) return QMM_ERR_SHAPE;
+  if (n_ids > 0 && n_tokens > kMaxDim / n_ids) return QMM_ERR_SHAPE;
+  if (n_ids == 0 || !id_grouped(n_experts, n_ids, n_tokens)) return 0;
+  return qmm::route_workspace_bytes(n_experts, n_ids * n_tokens);
+}
+
 int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
                   int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
-                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *stream) {
+                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                  int64_t workspace_bytes, void *stream) {
   if (X == nullptr || ids == nullptr || Y == nullptr) return QMM_ERR_NULL;
   int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
   if (st != QMM_OK) return st;
-  if (n_experts < 0 || n_experts > kMaxDim || n_ids < 0 || n_tokens < 0) return QMM_ERR_SHAPE;
-  if (n_ids > 0 && n_tokens > kMaxDim / n_ids) return QMM_ERR_SHAPE;  // pair index is an int
+  const int64_t need = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens);
+  if (need < 0) return static_cast<int>(need);
   if (x_slots != 1 && x_slots != n_ids) return QMM_ERR_SHAPE;
   if (expert_stride_bytes % 2 != 0 || expert_stride_bytes < n_rows * row_stride_bytes) return QMM_ERR_STRIDE;
   if (!aligned(X, 4) || !aligned(ids, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
   if (n_rows == 0 || n_ids == 0 || n_tokens == 0) return QMM_OK;
+  const bool grouped = id_grouped(n_experts, n_ids, n_tokens);
+  if (grouped) {
+    if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return QMM_ERR_ALIGN;
+    const int64_t row_tiles = (n_rows + 127) / 128;
+    if (row_tiles * qmm::route_max_tiles(n_experts, n_ids * n_tokens) > kMaxDim) return QMM_ERR_SHAPE;
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool streaming = qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
+  const bool streaming = !grouped && qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
   if (trace_on())
     fprintf(stderr, "qmm: matmul_id %s %s experts=%lld rows=%lld k=%lld nb1=%lld nb2=%lld ids=%lld tokens=%lld\n",
-            streaming ? "stream" : "general", type_name(ggml_type), (long long)n_experts, (long long)n_rows,
-            (long long)k, (long long)row_stride_bytes, (long long)expert_stride_bytes, (long long)n_ids,
-            (long long)n_tokens);
+            grouped ? "grouped" : streaming ? "stream" : "general", type_name(ggml_type), (long long)n_experts,
+            (long long)n_rows, (long long)k, (long long)row_stride_bytes, (long long)expert_stride_bytes,
+            (long long)n_ids, (long long)n_tokens);
+  if (grouped)
+    return status_of(qmm::launch_matmul_id_grouped(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
+                                                   expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y,
+                                                   workspace, s));
   if (streaming)
     return status_of(qmm::launch_gemv_id_stream(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
                                                 expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));

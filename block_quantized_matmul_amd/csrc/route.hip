@@ -1,0 +1,128 @@
+// Grouped MUL_MAT_ID for many tokens: the (token, slot) pairs are bucketed by
+// expert on the GPU, then the matrix-core kernel runs one tile per (weight
+// row tile, 128 pairs of one expert), so each selected expert's weights are
+// read once per token tile instead of once per pair.
+//
+// What is computed: the expert-routed MUL_MAT of [Load] "llama.cpp 源码完全拆解
+// (三)：GGUF 装载、mmap 与张量放置", section "第六步：能力校验" (the probe's
+// GGML_OP_MUL_MAT_ID case: activations F32 [k, n_ids, 512], ids I32
+// [n_ids, 512]); the 512-token batch is what makes grouping pay.
+//
+// Routing (one 1024-thread workgroup, ids are device data): count the pairs
+// per expert in LDS, scan the counts into list offsets and token-tile
+// offsets, write the tile table (expert, first list entry, count) padded
+// with empty tiles up to the host's bound, then place every pair in its
+// expert's bucket. Pairs whose id names no expert go after the valid ones
+// and get rows of NaN. Within a bucket the order depends on LDS atomics; a
+// pair's result does not, because every output element is the same
+// fixed-order sum whichever column of a tile its pair occupies.
+#include "common.h"
+#include "launch.h"
+
+namespace qmm {
+
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kPerThread = kRouteMaxExperts / kRouteThreads;
+static_assert(kRouteMaxExperts % kRouteThreads == 0, "experts split evenly over the threads");
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__restrict__ ids, int n_pairs,
+                                                              int n_experts, int max_tiles,
+                                                              int32_t *__restrict__ list, int32_t *__restrict__ tiles,
+                                                              float *__restrict__ Y, int n_rows) {
+  __shared__ int cnt[kRouteMaxExperts];
+  __shared__ int cur[kRouteMaxExperts];
+  __shared__ int scan_c[2][kRouteThreads];
+  __shared__ int scan_t[2][kRouteThreads];
+  __shared__ int bad_cur;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kRouteMaxExperts; e += kRouteThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < n_pairs; p += kRouteThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < n_experts) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // Thread tid owns experts [kPerThread tid, kPerThread (tid + 1)): its pair
+  // and tile sums, then an inclusive scan over the threads (Hillis-Steele).
+  int c_own = 0, t_own = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int c = cnt[kPerThread * tid + i];
+    c_own += c;
+    t_own += (c + kTileTokens - 1) / kTileTokens;
+  }
+  scan_c[0][tid] = c_own;
+  scan_t[0][tid] = t_own;
+  __syncthreads();
+  int src = 0;
+  for (int d = 1; d < kRouteThreads; d *= 2) {
+    const int dst = src ^ 1;
+    scan_c[dst][tid] = scan_c[src][tid] + (tid >= d ? scan_c[src][tid - d] : 0);
+    scan_t[dst][tid] = scan_t[src][tid] + (tid >= d ? scan_t[src][tid - d] : 0);
+    __syncthreads();
+    src = dst;
+  }
+  int off = scan_c[src][tid] - c_own, toff = scan_t[src][tid] - t_own;
+  const int n_valid = scan_c[src][kRouteThreads - 1], n_tiles = scan_t[src][kRouteThreads - 1];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int e = kPerThread * tid + i, c = cnt[e];
+    cur[e] = off;
+    for (int j = 0; j * kTileTokens < c; ++j, ++toff) {
+      int32_t *t = tiles + 4 * static_cast<int64_t>(toff);
+      t[0] = e;
+      t[1] = off + j * kTileTokens;
+      t[2] = min(kTileTokens, c - j * kTileTokens);
+      t[3] = 0;
+    }
+    off += c;
+  }
+  for (int i = n_tiles + tid; i < max_tiles; i += kRouteThreads) {
+    int32_t *t = tiles + 4 * static_cast<int64_t>(i);
+    t[0] = 0, t[1] = 0, t[2] = 0, t[3] = 0;  // empty: its workgroups exit at once
+  }
+  if (tid == 0) bad_cur = n_valid;
+  __syncthreads();
+
+  for (int p = tid; p < n_pairs; p += kRouteThreads) {
+    const int e = ids[p];
+    const int pos = (e >= 0 && e < n_experts) ? atomicAdd(&cur[e], 1) : atomicAdd(&bad_cur, 1);
+    list[pos] = p;
+  }
+  __syncthreads();  // the bucket writes above are visible to the whole workgroup
+  for (int i = n_valid; i < n_pairs; ++i) {
+    float *y = Y + static_cast<int64_t>(list[i]) * n_rows;
+    for (int r = tid; r < n_rows; r += kRouteThreads) y[r] = __builtin_bit_cast(float, 0x7FC00000u);
+  }
+}
+
+}  // namespace
+
+int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs) {
+  // sum over experts of ceil(count / tile) <= n_pairs / tile + (experts used)
+  return (n_pairs + kTileTokens - 1) / kTileTokens + (n_experts < n_pairs ? n_experts : n_pairs);
+}
+
+int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs) {
+  return (n_pairs * 4 + 15) / 16 * 16 + 16 * route_max_tiles(n_experts, n_pairs);
+}
+
+hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k,
+                                    int64_t nb1, int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids,
+                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                                    hipStream_t stream) {
+  const int64_t n_pairs = n_tokens * n_ids;
+  const int64_t max_tiles = route_max_tiles(n_experts, n_pairs);
+  int32_t *list = static_cast<int32_t *>(workspace);
+  int32_t *tiles = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + (n_pairs * 4 + 15) / 16 * 16);
+  hipError_t e = launch(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, static_cast<int>(n_pairs),
+                        static_cast<int>(n_experts), static_cast<int>(max_tiles), list, tiles, Y,
+                        static_cast<int>(n_rows));
+  if (e != hipSuccess) return e;
+  return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, x_slots, n_ids, list, tiles, max_tiles, Y, stream);
+}
+
+}  // namespace qmm

@@ -94,6 +94,7 @@ extern "C" {
 #define QMM_ERR_ALIGN (-5)  /* pointer alignment requirement not met */
 #define QMM_ERR_HIP (-6)    /* HIP reported an error for the launch */
 #define QMM_ERR_PATH (-7)   /* unknown path, or GEMV forced with too many tokens */
+#define QMM_ERR_WORKSPACE (-8) /* workspace NULL or smaller than the call needs */
 
 /*
  * qmm_matmul - Y = MUL_MAT(W, X) with fp32 activations ([Bind] section 2.3,
@@ -208,17 +209,34 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
  *   ids                  device pointer, int32 [n_tokens][n_ids], 4-byte aligned
  *   n_ids, n_tokens      >= 0, n_ids * n_tokens < 2^31; 0 is a no-op
  *   Y                    device pointer, fp32 [n_tokens][n_ids][n_rows], 4-byte aligned
+ *   workspace            device scratch of at least
+ *                        qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens)
+ *                        bytes, 4-byte aligned, caller-owned; may be NULL when
+ *                        that size is 0. Its contents are overwritten; two
+ *                        calls in flight must not share one.
  *   stream               hipStream_t or NULL
- * Every pair is a single-token product on the decode kernels, so weight
- * traffic grows with n_tokens * n_ids (the decode case, not a grouped
- * prefill GEMM). An id outside [0, n_experts) cannot be checked on the host:
- * that pair's output row is filled with quiet NaNs and nothing is read for it.
+ * Up to QMM_GEMV_MAX_TOKENS tokens (decode), and whenever the pairs average
+ * fewer than 4 per expert, every pair is a single-token product on the
+ * decode kernels. Otherwise (with at most 4096 experts) a routing kernel
+ * buckets the pairs by expert in the workspace and the matrix-core kernel
+ * runs 128 pairs of one expert per tile. An id outside
+ * [0, n_experts) cannot be checked on the host: that pair's output row is
+ * filled with quiet NaNs and nothing is read for it.
  * Returns QMM_OK, or the status of the first failed check (QMM_ERR_NULL,
- * _TYPE, _SHAPE, _STRIDE, _ALIGN) without launching, or QMM_ERR_HIP.
+ * _TYPE, _SHAPE, _STRIDE, _ALIGN, _WORKSPACE) without launching, or
+ * QMM_ERR_HIP.
  */
 int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
                   int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
-                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *stream);
+                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                  int64_t workspace_bytes, void *stream);
+
+/*
+ * qmm_matmul_id_workspace_bytes - the workspace qmm_matmul_id needs for these
+ * sizes (0 when the call takes the decode kernels), or QMM_ERR_SHAPE for
+ * negative or too large sizes.
+ */
+int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t n_tokens);
 
 /*
  * qmm_row_bytes - the dense row stride (k / 32) * block bytes, i.e. nb[1]

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
-                            "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_row_bytes", "qmm_supports",
+                            "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_workspace_bytes", "qmm_row_bytes", "qmm_supports",
                             "qmm_status_string"])
 
 
@@ -140,8 +140,8 @@ def test_get_rows_validation(L):
 
 
 def _mid(L, W=P, t=Q4, ne=8, rows=16, k=64, nb1=36, nb2=576, X=P2, xs=2, ids=ctypes.c_void_p(0x40000), n_ids=2,
-         n=3, Y=P3):
-    return L.qmm_matmul_id(W, t, ne, rows, k, nb1, nb2, X, xs, ids, n_ids, n, Y, NULL)
+         n=3, Y=P3, ws=NULL, ws_bytes=0):
+    return L.qmm_matmul_id(W, t, ne, rows, k, nb1, nb2, X, xs, ids, n_ids, n, Y, ws, ws_bytes, NULL)
 
 
 def test_matmul_id_validation(L):
@@ -164,10 +164,31 @@ def test_matmul_id_validation(L):
     assert _mid(L, X=ctypes.c_void_p(0x20002)) == qmm.QMM_ERR_ALIGN
     assert _mid(L, ids=ctypes.c_void_p(0x40002)) == qmm.QMM_ERR_ALIGN
     assert _mid(L, Y=ctypes.c_void_p(0x30002)) == qmm.QMM_ERR_ALIGN
+    # more tokens than the decode kernels take: the grouped path needs a workspace
+    need = L.qmm_matmul_id_workspace_bytes(8, 2, 64)
+    assert need >= 64 * 2 * 4 + 16 * 8
+    assert _mid(L, n=64, ws=NULL, ws_bytes=need) == qmm.QMM_ERR_WORKSPACE
+    assert _mid(L, n=64, ws=ctypes.c_void_p(0x50000), ws_bytes=need - 1) == qmm.QMM_ERR_WORKSPACE
+    assert _mid(L, n=64, ws=ctypes.c_void_p(0x50002), ws_bytes=need) == qmm.QMM_ERR_ALIGN
+    assert _mid(L, n=64, ws=ctypes.c_void_p(0x50000), ws_bytes=need, k=48) == qmm.QMM_ERR_SHAPE
     # empty calls succeed without a launch
     assert _mid(L, n=0) == qmm.QMM_OK
     assert _mid(L, n_ids=0, xs=1) == qmm.QMM_OK
     assert _mid(L, rows=0, nb2=0) == qmm.QMM_OK
+
+
+def test_matmul_id_workspace_sizes(L):
+    W = L.qmm_matmul_id_workspace_bytes
+    assert W(8, 2, 1) == 0 and W(8, 2, 8) == 0           # decode: per-pair kernels
+    assert W(8, 0, 512) == 0
+    assert W(5000, 2, 512) == 0                          # too many experts to bucket in LDS
+    assert W(8, 2, 15) == 0 and W(8, 2, 16) > 0          # under / at 4 pairs per expert
+    assert W(64, 8, 9) == 0 and W(64, 8, 32) > 0
+    # 1024 pairs in up to 8 + 8 tiles of 128, plus the pair list
+    assert W(8, 2, 512) == 1024 * 4 + 16 * (8 + 8)
+    assert W(2, 1, 9) == 48 + 16 * (1 + 2)
+    assert W(-1, 2, 512) == qmm.QMM_ERR_SHAPE
+    assert W(8, 1 << 16, 1 << 16) == qmm.QMM_ERR_SHAPE
 
 
 def test_binding_refuses_cpu_tensors():

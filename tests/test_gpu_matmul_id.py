@@ -110,3 +110,95 @@ def test_matmul_id_mixtral_sized_sampled(qtype):
         y_ref, s = O.matmul_sampled(We, qtype, rows, k, nb1, X[0], np.zeros_like(rsamp), rsamp)
         ok = O.within_tolerance(Y[0, i, rsamp], y_ref, s)
         assert ok.all(), f"expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
+
+
+def _skewed_ids(rng, n_tokens, n_ids, n_experts):
+    """Routing with an uneven load: expert 1 takes about half the pairs (more
+    than one 128-pair tile at 300 tokens), expert n_experts - 1 none, and
+    two ids name no expert."""
+    ids = rng.integers(0, n_experts - 1, size=(n_tokens, n_ids)).astype(np.int32)
+    ids[rng.random((n_tokens, n_ids)) < 0.5] = 1
+    ids[0, 0] = -1
+    ids[n_tokens - 1, n_ids - 1] = n_experts
+    return ids
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("layout", ["aligned", "padded"])
+@pytest.mark.parametrize("shared_x", [False, True])
+@pytest.mark.parametrize("n_tokens,n_experts", [(9, 4), (300, 8)])
+def test_matmul_id_grouped(qtype, layout, shared_x, n_tokens, n_experts):
+    """More tokens than the decode kernels take: pairs bucketed by expert,
+    matrix-core tiles. Every token is checked at 9 tokens; a sample at 300."""
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([503, qtype, n_tokens, int(shared_x), len(layout)]))
+    n_ids, rows, k = 2, 200, 544   # 17 blocks: an odd block count, a ragged row tile
+    assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0, "not the grouped path"
+    dense = synth.dense_row_bytes(qtype, k)
+    if layout == "aligned":
+        nb1, nb2, offset = dense, rows * dense + 64, 0
+    else:                    # 2-byte-aligned stack and rows: the halfword weight loads
+        nb1, nb2, offset = dense + 2, rows * (dense + 2) + 6, 2
+    W = _stack(qtype, n_experts, rows, k, nb1, nb2, rng)
+    xs = 1 if shared_x else n_ids
+    X = synth.make_activations(n_tokens * xs, k, rng, np.float32).reshape(n_tokens, xs, k)
+    ids = _skewed_ids(rng, n_tokens, n_ids, n_experts)
+    say(f"matmul_id grouped {layout} type={qtype} tokens={n_tokens} x_slots={xs}")
+    Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
+    sample = np.arange(n_tokens) if n_tokens <= 16 else \
+        np.unique(np.concatenate([[0, 1, n_tokens - 1], rng.integers(0, n_tokens, 40)]))
+    y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X[sample], ids[sample])
+    _check(Y[sample], y_ref, s, f"matmul_id grouped {layout}")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_matmul_id_grouped_repeatable_and_agrees_with_decode(qtype):
+    """The bucket order inside an expert varies from run to run; the results
+    must not (bitwise). Each token's rows also agree, within tolerance, with
+    the same token routed alone through the decode kernels."""
+    rng = np.random.Generator(np.random.PCG64([504, qtype]))
+    n_experts, n_ids, rows, k, n_tokens = 16, 4, 256, 1024, 200
+    nb1 = synth.dense_row_bytes(qtype, k)
+    nb2 = rows * nb1
+    W = _stack(qtype, n_experts, rows, k, nb1, nb2, rng)
+    X = synth.make_activations(n_tokens * n_ids, k, rng, np.float32).reshape(n_tokens, n_ids, k)
+    ids = rng.integers(0, n_experts, size=(n_tokens, n_ids)).astype(np.int32)
+    import block_quantized_matmul_amd as qmm
+    assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0, "not the grouped path"
+    say(f"matmul_id grouped twice type={qtype} tokens={n_tokens}")
+    Y1 = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
+    Y2 = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
+    assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32)), "grouped MUL_MAT_ID is not repeatable"
+    for t in (0, 77, n_tokens - 1):
+        Yd = _run(W, qtype, n_experts, rows, k, nb1, nb2, X[t:t + 1], ids[t:t + 1])
+        y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X[t:t + 1], ids[t:t + 1])
+        _check(Yd, y_ref, s, "decode route")
+        _check(Y1[t:t + 1], y_ref, s, "grouped route")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_matmul_id_mixtral_prefill_sampled(qtype):
+    """512 tokens through 8 experts of 14336 x 4096, 2 selected per token
+    (the probe's batch at a routed-FFN shape, the grouped bench case);
+    sampled (token, slot, row) outputs against the oracle."""
+    import torch
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([505, qtype]))
+    n_experts, rows, k, n_ids, n_tokens = 8, 14336, 4096, 2, 512
+    nb1 = synth.dense_row_bytes(qtype, k)
+    Wn = synth.make_weights(qtype, n_experts * rows, k, nb1, rng)
+    X = synth.make_activations(n_tokens, k, rng, np.float32).reshape(n_tokens, 1, k)
+    ids = np.stack([rng.permutation(n_experts)[:n_ids] for _ in range(n_tokens)]).astype(np.int32)
+    say(f"matmul_id prefill experts={n_experts} rows={rows} k={k} tokens={n_tokens} type={qtype}")
+    W = dev(Wn.reshape(n_experts, rows, nb1))
+    Y = qmm.qmm_matmul_id(W, qtype, k, dev(X), dev(ids))
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    for t in (0, 255, 511):
+        rsamp = np.unique(np.concatenate([[0, 127, 128, rows - 1], rng.integers(0, rows, 60)]))
+        for i in range(n_ids):
+            e = ids[t, i]
+            We = Wn[e * rows:(e + 1) * rows]
+            y_ref, s = O.matmul_sampled(We, qtype, rows, k, nb1, X[t], np.zeros_like(rsamp), rsamp)
+            ok = O.within_tolerance(Y[t, i, rsamp], y_ref, s)
+            assert ok.all(), f"token {t} expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
