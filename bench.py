@@ -64,9 +64,12 @@ COPY_CAL_BYTES = 1 << 30        # size of the plain copy used to calibrate count
 CSRC = os.path.join(ROOT, "block_quantized_matmul_amd", "csrc")
 KERNELS = {
     # name fragment in the kernel symbol -> sources the kernel is built from
-    "gemv_stream_kernel": ("gemv_stream.hip", "gemv_common.h", "common.h"),
-    "gemm_kernel": ("gemm.hip", "common.h"),
+    "gemv_stream_kernel": ("gemv_stream.hip", "gemv_common.h", "common.h", "launch.h"),
+    "gemm_kernel": ("gemm.hip", "common.h", "launch.h"),
 }
+# Template arguments of the plain (MUL_MAT) instantiations; the expert-routed
+# (MUL_MAT_ID) ones carry one more, which the demangled name shows.
+KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -118,6 +121,13 @@ def _short(name):
     return re.sub(r"\(.*", "", name).replace("void ", "")
 
 
+def _routed(name, kern):
+    """True for the expert-routed instantiation of `kern` (one template
+    argument more than the plain one)."""
+    m = re.search(re.escape(kern) + r"<([^>]*)>", name)
+    return bool(m) and len(m.group(1).split(",")) > KERNEL_TARGS[kern]
+
+
 def _col(row, *names):
     for n in names:
         if n in row:
@@ -136,9 +146,11 @@ def summarize_trace(d):
         print(f"{k[:58]:58s} {gx:9d} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
               f"{min(v):9.2f} {max(v):9.2f}")
     for kern in KERNELS:
-        v = [x for (k, _), xs in by.items() if kern in k for x in xs]
-        if v:
-            print(f"ALL {kern}: calls {len(v)} avg_us {statistics.mean(v):.3f} source_sha256 {source_hash(kern)}")
+        for routed, tag in ((False, ""), (True, " routed")):
+            v = [x for (k, _), xs in by.items() if kern in k and _routed(k, kern) == routed for x in xs]
+            if v:
+                print(f"ALL {kern}{tag}: calls {len(v)} avg_us {statistics.mean(v):.3f} "
+                      f"source_sha256 {source_hash(kern)}")
 
 
 def summarize_counters(dirs):
@@ -168,7 +180,7 @@ def summarize_counters(dirs):
     for kern in KERNELS:
         total = 0.0
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-            v = [x for (k, c), xs in agg.items() if kern in k and c == cn for x in xs]
+            v = [x for (k, c), xs in agg.items() if kern in k and not _routed(k, kern) and c == cn for x in xs]
             if not v or cn not in factor:
                 total = None
                 break
