@@ -18,10 +18,11 @@ from dataclasses import dataclass
 import numpy as np
 
 TYPE_Q4_0 = 2
+TYPE_Q4_1 = 3
 TYPE_Q8_0 = 8
 QK = 32
-BLOCK_BYTES = {TYPE_Q4_0: 18, TYPE_Q8_0: 34}
-TYPE_NAMES = {TYPE_Q4_0: "q4_0", TYPE_Q8_0: "q8_0"}
+BLOCK_BYTES = {TYPE_Q4_0: 18, TYPE_Q4_1: 20, TYPE_Q8_0: 34}
+TYPE_NAMES = {TYPE_Q4_0: "q4_0", TYPE_Q4_1: "q4_1", TYPE_Q8_0: "q8_0"}
 
 N_EMBD = 4096
 N_FF = 11008
@@ -76,16 +77,24 @@ def assemble_rows(d_bits: np.ndarray, code_bytes: np.ndarray, nb1: int,
 def make_weights(qtype: int, rows: int, k: int, nb1: int | None, rng: np.random.Generator,
                  d_lo: float = 0.001, d_hi: float = 0.05) -> np.ndarray:
     """Random quantised rows: d = fp16(U[d_lo, d_hi]) (round to nearest even);
-    Q4_0 code bytes uniform 0..255 (both nibbles uniform 0..15); Q8_0 codes
+    Q4_0 code bytes uniform 0..255 (both nibbles uniform 0..15); Q4_1 the
+    same code bytes after a minimum m = fp16(-U[6, 9] * |d draw|) (blocks spanning
+    about [-7.5 d, 7.5 d], as a min/max quantiser makes them); Q8_0 codes
     uniform integers in [-127, 127]; padding bytes uniform 0..255."""
     if k % QK:
         raise ValueError("k must be a multiple of 32")
     nblk = k // QK
     dense = dense_row_bytes(qtype, k)
     nb1 = dense if nb1 is None else nb1
-    d_bits = rng.uniform(d_lo, d_hi, size=(rows, nblk)).astype(np.float16).view(np.uint16)
+    d_draw = rng.uniform(d_lo, d_hi, size=(rows, nblk))
+    d_bits = d_draw.astype(np.float16).view(np.uint16)
     if qtype == TYPE_Q4_0:
         codes = rng.integers(0, 256, size=(rows, nblk, 16), dtype=np.uint8)
+    elif qtype == TYPE_Q4_1:
+        m_bits = (-rng.uniform(6.0, 9.0, size=(rows, nblk)) * np.abs(d_draw)).astype(np.float16).view(np.uint16)
+        codes = np.empty((rows, nblk, 18), dtype=np.uint8)
+        codes[:, :, 0:2] = m_bits.view(np.uint8).reshape(rows, nblk, 2)  # little-endian
+        codes[:, :, 2:] = rng.integers(0, 256, size=(rows, nblk, 16), dtype=np.uint8)
     elif qtype == TYPE_Q8_0:
         codes = rng.integers(-127, 128, size=(rows, nblk, 32), dtype=np.int8).view(np.uint8)
     else:

@@ -1,4 +1,4 @@
-"""Plain CPU oracle for block-quantized MUL_MAT on GGUF Q4_0 / Q8_0 weights.
+"""Plain CPU oracle for block-quantized MUL_MAT on GGUF Q4_0 / Q4_1 / Q8_0 weights.
 
 TEST INFRASTRUCTURE. Only the tests, the package entry point's smoke check and
 the benchmark's CPU-baseline leg may import this module. The library never
@@ -14,8 +14,9 @@ Sources (the pages are cited by title and section):
           section "权重装载：GGUF、mmap 与 4 bit 块": the uniform block
           quantisation equation q(w) = clip(round(w/s) + z, qmin, qmax) with
           reconstruction w_hat = s (q - z), the error-variance equation, the
-          legacy-family paragraph (32 weights per block, one shared scale) and
-          the quality table (Q8_0 row: 46.87 % smaller than F16).
+          legacy-family paragraph (32 weights per block, one shared scale,
+          Q4_1 with an extra minimum offset) and the quality table (Q8_0
+          row: 46.87 % smaller than F16).
   [Graph] "llama.cpp 源码完全拆解(二)：ggml 计算图与内存分配器", section
           "ggml_tensor：一个图节点的全部字段" (nb[0] = block bytes,
           nb[1] = nb[0] * ne[0] / block_size + padding, ne[0] contiguous).
@@ -31,7 +32,11 @@ Readings taken where the pages are silent (also listed in the design notes):
     z = 0 and signed int8 codes, so w = d * q.
   * Q8_0 block = fp16 d followed by 32 int8 codes (34 bytes); 34/32 bytes per
     weight is exactly the table's 46.87 % reduction versus 16-bit weights.
-  * The scale d is stored little-endian as IEEE-754 binary16.
+  * Q4_1 block = fp16 d, fp16 m (the minimum offset), then the 16 code
+    bytes in Q4_0's nibble order (20 bytes); 4-bit codes 0..15 with
+    w = d * q + m, the reconstruction with the stored minimum in place of
+    the zero point.
+  * The scale d (and Q4_1's m) is stored little-endian as IEEE-754 binary16.
   * Activations X are [n_tokens][k] with k contiguous; Y is [n_tokens][n_rows]
     with rows contiguous, fully overwritten.
   * Dequantisation is to fp32 (the product d * (q - z) is exact in fp32 for
@@ -46,17 +51,22 @@ import numpy as np
 
 # Type ids follow ggml's enumeration (the pages name the types, not the ids).
 TYPE_Q4_0 = 2
+TYPE_Q4_1 = 3
 TYPE_Q8_0 = 8
 
 QK = 32  # weights per block for both legacy types ([Arch] legacy-family paragraph)
 
 BLOCK_BYTES = {
-    TYPE_Q4_0: 2 + QK // 2,  # ggml_half d + uint8_t qs[16]  ([Bind] section 2.3)
-    TYPE_Q8_0: 2 + QK,       # ggml_half d + int8 qs[32]     (reading, see header)
+    TYPE_Q4_0: 2 + QK // 2,      # ggml_half d + uint8_t qs[16]  ([Bind] section 2.3)
+    TYPE_Q4_1: 2 + 2 + QK // 2,  # d, the minimum m, qs[16]      (reading, see header)
+    TYPE_Q8_0: 2 + QK,           # ggml_half d + int8 qs[32]     (reading, see header)
 }
 
-ZERO_POINT = {TYPE_Q4_0: 8, TYPE_Q8_0: 0}
-CODE_RANGE = {TYPE_Q4_0: (0, 15), TYPE_Q8_0: (-128, 127)}
+ZERO_POINT = {TYPE_Q4_0: 8, TYPE_Q4_1: 0, TYPE_Q8_0: 0}
+CODE_RANGE = {TYPE_Q4_0: (0, 15), TYPE_Q4_1: (0, 15), TYPE_Q8_0: (-128, 127)}
+HAS_MIN = {TYPE_Q4_0: False, TYPE_Q4_1: True, TYPE_Q8_0: False}
+# bytes before the codes: d, and m where the type has one
+CODE_OFFSET = {TYPE_Q4_0: 2, TYPE_Q4_1: 4, TYPE_Q8_0: 2}
 
 
 # --------------------------------------------------------------------------
@@ -118,8 +128,8 @@ def block_scales_and_codes(W, qtype: int, n_rows: int, k: int, nb1: int):
     blocks = W[:, : nblk * bpb].reshape(n_rows, nblk, bpb)
     d_bits = blocks[:, :, 0].astype(np.uint32) | (blocks[:, :, 1].astype(np.uint32) << 8)
     d = half_bits_to_double(d_bits)
-    payload = blocks[:, :, 2:]
-    if qtype == TYPE_Q4_0:
+    payload = blocks[:, :, CODE_OFFSET[qtype]:]
+    if qtype in (TYPE_Q4_0, TYPE_Q4_1):
         low = (payload & 0x0F).astype(np.int64)   # element j      <- low nibble of byte j
         high = (payload >> 4).astype(np.int64)    # element j + 16 <- high nibble of byte j
         q = np.concatenate([low, high], axis=2)   # [n_rows, nblk, 32]
@@ -128,17 +138,36 @@ def block_scales_and_codes(W, qtype: int, n_rows: int, k: int, nb1: int):
     return d, q.reshape(n_rows, k)
 
 
-def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
-    """Weights as fp32 [n_rows][k]: w = fp32(d) * fp32(q - z).
+def block_mins(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
+    """The minimum offset m of every block (float64 [n_rows, k/32]): the
+    binary16 after d in a Q4_1 block; zero for types without one."""
+    W = _check_layout(W, qtype, n_rows, k, nb1)
+    nblk = k // QK
+    if not HAS_MIN[qtype]:
+        return np.zeros((n_rows, nblk))
+    bpb = BLOCK_BYTES[qtype]
+    blocks = W[:, : nblk * bpb].reshape(n_rows, nblk, bpb)
+    m_bits = blocks[:, :, 2].astype(np.uint32) | (blocks[:, :, 3].astype(np.uint32) << 8)
+    return half_bits_to_double(m_bits)
 
-    z = 8 for Q4_0 and 0 for Q8_0. The multiply is a single IEEE fp32
-    multiply; for finite d it is exact, so this is the bit-exact target.
+
+def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
+    """Weights as fp32 [n_rows][k]: w = fp32(d) * fp32(q - z), plus fp32(m)
+    for Q4_1.
+
+    z = 8 for Q4_0 and 0 for Q4_1 and Q8_0. The multiply is a single IEEE
+    fp32 multiply; for finite d it is exact (an 11-bit significand times a
+    code of at most 8 bits). Q4_1 then adds m with one fp32 rounding, so
+    w = fp32(d q + m) exactly rounded. This is the bit-exact target.
     """
     d, q = block_scales_and_codes(W, qtype, n_rows, k, nb1)
     c = (q - ZERO_POINT[qtype]).astype(np.float32)
     d32 = np.repeat(d.astype(np.float32), QK, axis=1)
     with np.errstate(invalid="ignore", over="ignore"):
-        return d32 * c
+        w = d32 * c
+        if HAS_MIN[qtype]:
+            w = w + np.repeat(block_mins(W, qtype, n_rows, k, nb1).astype(np.float32), QK, axis=1)
+        return w
 
 
 def get_rows(W, qtype: int, n_rows: int, k: int, nb1: int, ids) -> np.ndarray:
@@ -274,11 +303,20 @@ def quantize_codes(w, d, qtype: int) -> np.ndarray:
 def quantize(w, qtype: int) -> np.ndarray:
     """Quantise fp32 weights [n_rows][k] into dense rows of blocks (uint8
     [n_rows][row_bytes]). Scale choice: d = fp16(amax / 7) for Q4_0 and
-    fp16(amax / 127) for Q8_0, so |w / d| stays inside the code range."""
+    fp16(amax / 127) for Q8_0, so |w / d| stays inside the code range; for
+    Q4_1, m = fp16(block minimum) and d = fp16((max - min) / 15), codes
+    q = clip(round((w - m) / d), 0, 15)."""
     w = np.asarray(w, dtype=np.float32)
     n_rows, k = w.shape
     nblk = k // QK
     wb = w.reshape(n_rows, nblk, QK).astype(np.float64)
+    if qtype == TYPE_Q4_1:
+        lo, hi = np.min(wb, axis=2), np.max(wb, axis=2)
+        d16 = ((hi - lo) / 15.0).astype(np.float16)
+        m16 = lo.astype(np.float16)
+        d = d16.astype(np.float64)[:, :, None]
+        q = quantize_codes(wb - m16.astype(np.float64)[:, :, None], d, qtype)
+        return pack_blocks(d16.view(np.uint16), q, qtype, m16.view(np.uint16))
     amax = np.max(np.abs(wb), axis=2)
     div = 7.0 if qtype == TYPE_Q4_0 else 127.0
     d16 = (amax / div).astype(np.float16)
@@ -287,19 +325,25 @@ def quantize(w, qtype: int) -> np.ndarray:
     return pack_blocks(d16.view(np.uint16), q, qtype)
 
 
-def pack_blocks(d_bits, q, qtype: int) -> np.ndarray:
-    """Lay out blocks: d as little-endian binary16, then the codes (Q4_0: code
-    of element j in the low nibble and of element j + 16 in the high nibble of
-    byte j; Q8_0: 32 int8 codes). q has shape [n_rows, nblk, 32]."""
+def pack_blocks(d_bits, q, qtype: int, m_bits=None) -> np.ndarray:
+    """Lay out blocks: d as little-endian binary16, Q4_1's m likewise, then the
+    codes (Q4_0 / Q4_1: code of element j in the low nibble and of element
+    j + 16 in the high nibble of byte j; Q8_0: 32 int8 codes). q has shape
+    [n_rows, nblk, 32]."""
     d_bits = np.asarray(d_bits, dtype=np.uint16)
     q = np.asarray(q, dtype=np.int64)
     n_rows, nblk = d_bits.shape
     bpb = BLOCK_BYTES[qtype]
+    c0 = CODE_OFFSET[qtype]
     out = np.zeros((n_rows, nblk, bpb), dtype=np.uint8)
     out[:, :, 0] = d_bits & 0xFF
     out[:, :, 1] = d_bits >> 8
-    if qtype == TYPE_Q4_0:
-        out[:, :, 2:] = (q[:, :, :16] | (q[:, :, 16:] << 4)).astype(np.uint8)
+    if HAS_MIN[qtype]:
+        m_bits = np.asarray(m_bits, dtype=np.uint16)
+        out[:, :, 2] = m_bits & 0xFF
+        out[:, :, 3] = m_bits >> 8
+    if qtype in (TYPE_Q4_0, TYPE_Q4_1):
+        out[:, :, c0:] = (q[:, :, :16] | (q[:, :, 16:] << 4)).astype(np.uint8)
     else:
-        out[:, :, 2:] = q.astype(np.int8).view(np.uint8)
+        out[:, :, c0:] = q.astype(np.int8).view(np.uint8)
     return out.reshape(n_rows, nblk * bpb)
