@@ -6,11 +6,15 @@
 // of byte j, element j + 16 in the high nibble); Q8_0 = binary16 d + 32 int8.
 // Reconstruction ([Arch] = "llama.cpp 源码完全拆解(一)：整体架构与模块全景",
 // section "权重装载：GGUF、mmap 与 4 bit 块"): w = d * (q - z), z = 8 for Q4_0
-// and 0 for Q8_0.
+// and 0 for Q8_0. Q4_1, the legacy type with a minimum offset (same page,
+// the paragraph on the three quantisation families): binary16 d, binary16 m,
+// then Q4_0's 16 nibble bytes; w = d * q + m with unsigned codes 0..15.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "qmm.h"
 
@@ -33,7 +37,25 @@ typedef _Float16 half4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int QT> struct Block;
 template <> struct Block<QMM_TYPE_Q4_0> { static constexpr int bytes = 18; };
+template <> struct Block<QMM_TYPE_Q4_1> { static constexpr int bytes = 20; };
 template <> struct Block<QMM_TYPE_Q8_0> { static constexpr int bytes = 34; };
+
+// nibbles: 4-bit codes in Q4_0's byte order; has_min: a binary16 m follows d;
+// codes: byte offset of the codes in the block; zero: the zero point z.
+template <int QT> struct QTraits {
+  static constexpr bool nibbles = QT != QMM_TYPE_Q8_0;
+  static constexpr bool has_min = QT == QMM_TYPE_Q4_1;
+  static constexpr int codes = has_min ? 4 : 2;
+  static constexpr int zero = QT == QMM_TYPE_Q4_0 ? 8 : 0;
+};
+
+// Calls f(std::integral_constant<int, QT>) for the run-time type id (one of
+// the three the library accepts; the entry points validate it first).
+template <class F> __host__ inline auto by_qtype(int qtype, F f) {
+  if (qtype == QMM_TYPE_Q4_0) return f(std::integral_constant<int, QMM_TYPE_Q4_0>{});
+  if (qtype == QMM_TYPE_Q4_1) return f(std::integral_constant<int, QMM_TYPE_Q4_1>{});
+  return f(std::integral_constant<int, QMM_TYPE_Q8_0>{});
+}
 
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
 __device__ __forceinline__ uint32_t ld_u32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
@@ -64,21 +86,23 @@ constexpr uint32_t kSelB23 = 0x00070006u;  // halves (1024 + byte2, 1024 + byte3
 __device__ __forceinline__ half2_t bytes01_plus_1024(uint32_t v) { return as_half2(__builtin_amdgcn_perm(v, kMagic64, kSelB01)); }
 __device__ __forceinline__ half2_t bytes23_plus_1024(uint32_t v) { return as_half2(__builtin_amdgcn_perm(v, kMagic64, kSelB23)); }
 
-// Four Q4_0 code bytes qs[j..j+3] -> eight exact fp16 values (q - 8):
+// Four nibble code bytes qs[j..j+3] -> eight exact fp16 values (q - Z):
 //   out[0] = (e_j, e_j+1), out[1] = (e_j+2, e_j+3)          (low nibbles)
 //   out[2] = (e_j+16, e_j+17), out[3] = (e_j+18, e_j+19)    (high nibbles)
-// Low nibble n: 1024 + n - 1032 = n - 8. High nibble m (kept in place, so the
-// byte is 16 m): (1024 + 16 m) / 16 - 72 = m - 8. Both steps are exact.
+// Low nibble n: 1024 + n - (1024 + Z) = n - Z. High nibble m (kept in place,
+// so the byte is 16 m): (1024 + 16 m) / 16 - (64 + Z) = m - Z. Both steps
+// are exact. Z = 8 for Q4_0, 0 for Q4_1.
+template <int Z = 8>
 __device__ __forceinline__ void q4_unpack(uint32_t qs, half2_t out[4]) {
-  const half2_t m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const half2_t mlo = {(_Float16)(-1024.0f - Z), (_Float16)(-1024.0f - Z)};
   const half2_t s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2_t m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const half2_t mhi = {(_Float16)(-64.0f - Z), (_Float16)(-64.0f - Z)};
   const uint32_t lo = qs & 0x0F0F0F0Fu;
   const uint32_t hi = qs & 0xF0F0F0F0u;
-  out[0] = bytes01_plus_1024(lo) + m1032;
-  out[1] = bytes23_plus_1024(lo) + m1032;
-  out[2] = bytes01_plus_1024(hi) * s16 + m72;
-  out[3] = bytes23_plus_1024(hi) * s16 + m72;
+  out[0] = bytes01_plus_1024(lo) + mlo;
+  out[1] = bytes23_plus_1024(lo) + mlo;
+  out[2] = bytes01_plus_1024(hi) * s16 + mhi;
+  out[3] = bytes23_plus_1024(hi) * s16 + mhi;
 }
 
 // Four Q8_0 int8 codes -> four exact fp16 values: (c ^ 0x80) = c + 128 as an

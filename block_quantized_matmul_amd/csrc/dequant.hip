@@ -1,5 +1,6 @@
-// Block decoder: out[r][i] = fp32(d) * fp32(q - z), bit-exact, for every row
-// of W or for the rows an index vector selects (GET_ROWS).
+// Block decoder: out[r][i] = fp32(d) * fp32(q - z) (Q4_1: fp32(d) * q + m,
+// one rounding), bit-exact, for every row of W or for the rows an index
+// vector selects (GET_ROWS).
 //
 // [Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3 (block
 // layout); [Arch] "llama.cpp 源码完全拆解(一)：整体架构与模块全景", section
@@ -10,7 +11,7 @@
 //
 // One thread writes eight consecutive outputs (one quarter of a block), so a
 // wavefront stores 2 KiB of contiguous fp32 with 16-byte stores. HBM-bound:
-// 18 (or 34) bytes read and 128 bytes written per block.
+// 18, 20 or 34 bytes read and 128 bytes written per block.
 #include "common.h"
 #include "launch.h"
 
@@ -39,15 +40,22 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const uint8_t *p = W + row * nb1 + static_cast<int64_t>(b) * Block<QT>::bytes;
     const float d = half_bits_to_float(ld_u16(p));
     float v[8];
-    if constexpr (QT == QMM_TYPE_Q4_0) {
+    if constexpr (QTraits<QT>::nibbles) {
       // part 0/1: low nibbles of qs[0..7] / qs[8..15]; part 2/3: high nibbles.
-      const uint8_t *q = p + 2 + 8 * (part & 1);
+      constexpr int Z = QTraits<QT>::zero;
+      const uint8_t *q = p + QTraits<QT>::codes + 8 * (part & 1);
       const int shift = (part & 2) ? 4 : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t two = ld_u16(q + 2 * j);
-        v[2 * j] = d * static_cast<float>(static_cast<int>((two >> shift) & 0xF) - 8);
-        v[2 * j + 1] = d * static_cast<float>(static_cast<int>((two >> (8 + shift)) & 0xF) - 8);
+        v[2 * j] = d * static_cast<float>(static_cast<int>((two >> shift) & 0xF) - Z);
+        v[2 * j + 1] = d * static_cast<float>(static_cast<int>((two >> (8 + shift)) & 0xF) - Z);
+      }
+      if constexpr (QTraits<QT>::has_min) {
+        // d * q is exact, so adding m rounds once, as one fma would
+        const float m = half_bits_to_float(ld_u16(p + 2));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __fadd_rn(v[j], m);
       }
     } else {
       const uint8_t *q = p + 2 + 8 * part;
@@ -70,11 +78,10 @@ static hipError_t decode_rows(const void *W, int qtype, int64_t n_rows, int64_t 
   const int64_t want = (quarters + 255) / 256;
   const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
   const uint8_t *w = static_cast<const uint8_t *>(W);
-  if (qtype == QMM_TYPE_Q4_0)
-    return launch(dequant_kernel<QMM_TYPE_Q4_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, ids, n_rows,
-                  out);
-  return launch(dequant_kernel<QMM_TYPE_Q8_0>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, ids, n_rows,
-                out);
+  return by_qtype(qtype, [&](auto qt) {
+    return launch(dequant_kernel<decltype(qt)::value>, dim3(grid), dim3(256), 0, stream, w, quarters, nblk, nb1, ids,
+                  n_rows, out);
+  });
 }
 
 hipError_t launch_dequant(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, float *out,

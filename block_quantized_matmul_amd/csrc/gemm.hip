@@ -47,16 +47,22 @@ constexpr int kXcds = 8;       // XCDs of the GPU; workgroups are dealt to them 
 constexpr int kGroupRows = 8;  // row tiles per group of the tile order
 static_assert(kGemmThreads == 2 * kBM && kGemmThreads == 2 * kBN, "two staging threads per row and per token");
 
+// d (and m, in the high half, for a type with a minimum) and the code dwords
+// of one block, with 16-bit loads.
 template <int QT>
 __device__ __forceinline__ void load_block_u16(const uint8_t *p, uint32_t &d, uint32_t *q) {
-  constexpr int nq = QT == QMM_TYPE_Q4_0 ? 4 : 8;
+  constexpr int nq = QTraits<QT>::nibbles ? 4 : 8;
+  constexpr int c = QTraits<QT>::codes;
   d = ld_u16(p);
+  if constexpr (QTraits<QT>::has_min) d |= ld_u16(p + 2) << 16;
 #pragma unroll
-  for (int i = 0; i < nq; ++i) q[i] = ld_u16(p + 2 + 4 * i) | (ld_u16(p + 4 + 4 * i) << 16);
+  for (int i = 0; i < nq; ++i) q[i] = ld_u16(p + c + 4 * i) | (ld_u16(p + c + 2 + 4 * i) << 16);
 }
 
-// Decode one block to 32 fp16 weights fl16(d * (q - z)) in element order and
-// store them as chunks c0 .. c0 + 3 of LDS tile row `row`.
+// Decode one block to 32 fp16 weights fl16(d * (q - z)) (Q4_1: fl16(d q + m),
+// one fp16 fma, a single rounding of the exact value) in element order and
+// store them as chunks c0 .. c0 + 3 of LDS tile row `row`. d_bits holds d in
+// its low half and, for Q4_1, m in its high half.
 template <int QT>
 __device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0, uint32_t d_bits, const uint32_t *q) {
   const _Float16 dh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d_bits));
@@ -66,11 +72,23 @@ __device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half2_t u[4];
-      q4_unpack(q[i], u);
+      q4_unpack<8>(q[i], u);
       h[2 * i] = u[0] * d2;      // elements 4i, 4i+1
       h[2 * i + 1] = u[1] * d2;  // 4i+2, 4i+3
       h[8 + 2 * i] = u[2] * d2;  // 16+4i, 17+4i
       h[9 + 2 * i] = u[3] * d2;  // 18+4i, 19+4i
+    }
+  } else if constexpr (QT == QMM_TYPE_Q4_1) {
+    const _Float16 mh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d_bits >> 16));
+    const half2_t m2 = {mh, mh};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2_t u[4];
+      q4_unpack<0>(q[i], u);
+      h[2 * i] = __builtin_elementwise_fma(u[0], d2, m2);
+      h[2 * i + 1] = __builtin_elementwise_fma(u[1], d2, m2);
+      h[8 + 2 * i] = __builtin_elementwise_fma(u[2], d2, m2);
+      h[9 + 2 * i] = __builtin_elementwise_fma(u[3], d2, m2);
     }
   } else {
 #pragma unroll
@@ -94,8 +112,10 @@ __device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0,
 // (scale = high half of w[0], codes = w[1..]); all lie inside the pair. The
 // loaded dwords are not touched until the stage is stored, so the loads stay
 // in flight (any arithmetic on them right after the load would wait for it).
+// Q4_1 blocks (20 bytes) are dword-aligned in a pair: both halves are one
+// whole block, d|m in w[0] and the codes in w[1..4].
 template <int QT> struct HalfRaw {
-  static constexpr int nq = QT == QMM_TYPE_Q4_0 ? 4 : 8;
+  static constexpr int nq = QTraits<QT>::nibbles ? 4 : 8;
   uint32_t w[nq + 1];
 };
 
@@ -103,7 +123,8 @@ template <int QT>
 __device__ __forceinline__ HalfRaw<QT> load_half_pair(const uint8_t *rp, int st, int h) {
   constexpr int nq = HalfRaw<QT>::nq;
   constexpr int BB = Block<QT>::bytes;
-  const uint8_t *p = rp + static_cast<int64_t>(st) * (2 * BB) + (h ? (BB - 2) : 0);  // 4-byte aligned
+  constexpr int h1 = QTraits<QT>::has_min ? BB : BB - 2;  // half 1 starts here, 4-byte aligned
+  const uint8_t *p = rp + static_cast<int64_t>(st) * (2 * BB) + (h ? h1 : 0);
   HalfRaw<QT> r;
 #pragma unroll
   for (int i = 0; i + 4 <= nq + 1; i += 4) {
@@ -124,7 +145,7 @@ __device__ __forceinline__ HalfRaw<QT> load_half_u16(const uint8_t *rp, int blk,
   if (blk < nblk) {
     uint32_t d;
     load_block_u16<QT>(rp + static_cast<int64_t>(blk) * Block<QT>::bytes, d, r.w + 1);
-    r.w[0] = d << 16;
+    r.w[0] = QTraits<QT>::has_min ? d : d << 16;
   } else {
 #pragma unroll
     for (int i = 0; i <= nq; ++i) r.w[i] = 0;
@@ -139,6 +160,12 @@ template <int QT>
 __device__ __forceinline__ void store_half(_Float16 *tile, int row, int c0, const HalfRaw<QT> &r, bool first_layout) {
   constexpr int nq = HalfRaw<QT>::nq;
   uint32_t q[nq];
+  if constexpr (QTraits<QT>::has_min) {  // one layout for both halves
+#pragma unroll
+    for (int i = 0; i < nq; ++i) q[i] = r.w[i + 1];
+    store_block_f16<QT>(tile, row, c0, r.w[0], q);
+    return;
+  }
   const uint32_t d = first_layout ? (r.w[0] & 0xFFFFu) : (r.w[0] >> 16);
 #pragma unroll
   for (int i = 0; i < nq; ++i) q[i] = first_layout ? shift16(r.w[i], r.w[i + 1]) : r.w[i + 1];
@@ -461,15 +488,13 @@ hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t 
   const int rt = static_cast<int>(row_tiles), nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows),
             kk = static_cast<int>(k);
   const dim3 block(kGemmThreads);
-  if (qtype == QMM_TYPE_Q4_0)
-    return align4 ? launch(gemm_kernel<QMM_TYPE_Q4_0, false, true, true>, grid, block, 0, stream, w, nr, nblk, nb1,
+  return by_qtype(qtype, [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    return align4 ? launch(gemm_kernel<QT, false, true, true>, grid, block, 0, stream, w, nr, nblk, nb1,
                            static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route)
-                  : launch(gemm_kernel<QMM_TYPE_Q4_0, false, false, true>, grid, block, 0, stream, w, nr, nblk, nb1,
+                  : launch(gemm_kernel<QT, false, false, true>, grid, block, 0, stream, w, nr, nblk, nb1,
                            static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route);
-  return align4 ? launch(gemm_kernel<QMM_TYPE_Q8_0, false, true, true>, grid, block, 0, stream, w, nr, nblk, nb1,
-                         static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route)
-                : launch(gemm_kernel<QMM_TYPE_Q8_0, false, false, true>, grid, block, 0, stream, w, nr, nblk, nb1,
-                         static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route);
+  });
 }
 
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
@@ -483,12 +508,11 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
   const int rt = static_cast<int>(row_tiles);
   const int nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows), nt = static_cast<int>(n_tokens),
             kk = static_cast<int>(k);
-  if (qtype == QMM_TYPE_Q4_0) {
-    if (x_f16) return gemm_dispatch<QMM_TYPE_Q4_0, true>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
-    return gemm_dispatch<QMM_TYPE_Q4_0, false>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
-  }
-  if (x_f16) return gemm_dispatch<QMM_TYPE_Q8_0, true>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
-  return gemm_dispatch<QMM_TYPE_Q8_0, false>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
+  return by_qtype(qtype, [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    if (x_f16) return gemm_dispatch<QT, true>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
+    return gemm_dispatch<QT, false>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
+  });
 }
 
 }  // namespace qmm

@@ -30,7 +30,7 @@
 // of lane l.
 //
 // Weight access (row start 4-byte aligned): a unit is a pair of blocks (36
-// bytes Q4_0, 68 bytes Q8_0). The four lanes of a row load overlapping dword
+// bytes Q4_0, 40 bytes Q4_1, 68 bytes Q8_0). The four lanes of a row load overlapping dword
 // windows that together cover the pair once; the two scales are forwarded
 // from the lanes that loaded them with ds_bpermute. Rows whose start is only
 // 2-byte aligned take 16-bit loads, one block per unit.
@@ -48,9 +48,13 @@ template <int QT, bool ALIGN4> struct GemvRaw;
 template <> struct GemvRaw<QMM_TYPE_Q4_0, true> { u32x2_t a; uint32_t b; };
 // Q8_0 pair: dwords 2g .. 2g + 2 (even block) and 9 + 2g .. 10 + 2g (odd block).
 template <> struct GemvRaw<QMM_TYPE_Q8_0, true> { uint32_t a0, a1, a2; u32x2_t b; };
+// Q4_1 pair (40 bytes, both blocks dword-aligned): dwords g, g + 1 (even
+// block: d|m in dword 0, codes in dwords 1..4) and 5 + g, 6 + g (odd block).
+template <> struct GemvRaw<QMM_TYPE_Q4_1, true> { u32x2_t a, b; };
 // Single block, 16-bit loads: scale bits and the lane's code dwords.
 template <> struct GemvRaw<QMM_TYPE_Q4_0, false> { uint32_t d, q; };
 template <> struct GemvRaw<QMM_TYPE_Q8_0, false> { uint32_t d, q0, q1; };
+template <> struct GemvRaw<QMM_TYPE_Q4_1, false> { uint32_t d, q; };  // d = d | m << 16
 
 template <int QT, bool ALIGN4>
 __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int u, int g) {
@@ -60,6 +64,9 @@ __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int 
     if constexpr (QT == QMM_TYPE_Q4_0) {
       r.a = ld_u32x2(p + 4 * g);
       r.b = ld_u32(p + 20 + 4 * g);
+    } else if constexpr (QT == QMM_TYPE_Q4_1) {
+      r.a = ld_u32x2(p + 4 * g);
+      r.b = ld_u32x2(p + 20 + 4 * g);
     } else {
       const u32x3_a4 a = *reinterpret_cast<const u32x3_a4 *>(p + 8 * g);
       r.a0 = a.x;
@@ -72,6 +79,9 @@ __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int 
     r.d = ld_u16(p);
     if constexpr (QT == QMM_TYPE_Q4_0) {
       r.q = ld_u16(p + 2 + 4 * g) | (ld_u16(p + 4 + 4 * g) << 16);
+    } else if constexpr (QT == QMM_TYPE_Q4_1) {
+      r.d |= ld_u16(p + 2) << 16;
+      r.q = ld_u16(p + 4 + 4 * g) | (ld_u16(p + 6 + 4 * g) << 16);
     } else {
       r.q0 = ld_u16(p + 2 + 8 * g) | (ld_u16(p + 4 + 8 * g) << 16);
       r.q1 = ld_u16(p + 6 + 8 * g) | (ld_u16(p + 8 + 8 * g) << 16);
@@ -95,6 +105,13 @@ __device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4
       const uint32_t dd = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * (r16 + 48), static_cast<int>(r.a.y)));
       gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(r.a.x, r.a.y), 0), de & 0xFFFFu);
       gemv_block<NT>(acc, xo, gemv_codes<QT>(r.b, 0), dd >> 16);
+    } else if constexpr (QT == QMM_TYPE_Q4_1) {
+      // d|m of each block: dword 0 / dword 5 of the pair, held by lane g = 0
+      // of the row (a.x / b.x).
+      const uint32_t de = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * r16, static_cast<int>(r.a.x)));
+      const uint32_t dd = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * r16, static_cast<int>(r.b.x)));
+      gemv_block_min<NT>(acc, xe, gemv_codes<QT>(r.a.y, 0), de);
+      gemv_block_min<NT>(acc, xo, gemv_codes<QT>(r.b.y, 0), dd);
     } else {
       // Even block: scale = low half of dword 0 (lane g = 0's a0); odd block
       // starts at byte 34: scale = high half of dword 8 (lane g = 3's a2).
@@ -107,6 +124,8 @@ __device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4
     const half8_t x = xs[(4 * (u - b_lo) + g) * NT + xslot];
     if constexpr (QT == QMM_TYPE_Q4_0)
       gemv_block<NT>(acc, x, gemv_codes<QT>(r.q, 0), r.d);
+    else if constexpr (QT == QMM_TYPE_Q4_1)
+      gemv_block_min<NT>(acc, x, gemv_codes<QT>(r.q, 0), r.d);
     else
       gemv_block<NT>(acc, x, gemv_codes<QT>(r.q0, r.q1), r.d);
   }
@@ -301,8 +320,7 @@ hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, i
     a.chunk_blocks = a.nblk;
     a.route = GemvRoute{ids, nb2, static_cast<int>(n_experts), static_cast<int>(n_ids), static_cast<int>(x_slots),
                         static_cast<int>(p0)};
-    hipError_t e = qtype == QMM_TYPE_Q4_0 ? gemv_nt<QMM_TYPE_Q4_0, false>(1, align4, a)
-                                           : gemv_nt<QMM_TYPE_Q8_0, false>(1, align4, a);
+    hipError_t e = by_qtype(qtype, [&](auto qt) { return gemv_nt<decltype(qt)::value, false>(1, align4, a); });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -326,9 +344,10 @@ hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t
   a.route = GemvRoute{nullptr, 0, 0, 0, 0, 0};
   const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0);
   const int nt = a.n_tokens;
-  if (qtype == QMM_TYPE_Q4_0)
-    return x_f16 ? gemv_nt<QMM_TYPE_Q4_0, true>(nt, align4, a) : gemv_nt<QMM_TYPE_Q4_0, false>(nt, align4, a);
-  return x_f16 ? gemv_nt<QMM_TYPE_Q8_0, true>(nt, align4, a) : gemv_nt<QMM_TYPE_Q8_0, false>(nt, align4, a);
+  return by_qtype(qtype, [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    return x_f16 ? gemv_nt<QT, true>(nt, align4, a) : gemv_nt<QT, false>(nt, align4, a);
+  });
 }
 
 }  // namespace qmm

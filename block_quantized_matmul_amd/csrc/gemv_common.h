@@ -25,7 +25,12 @@ __host__ inline int k_split_for(int64_t row_groups, int cus) {
 template <int QT> __device__ __forceinline__ half8_t gemv_codes(uint32_t q0, uint32_t q1);
 template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q4_0>(uint32_t q0, uint32_t) {
   half2_t h[4];
-  q4_unpack(q0, h);
+  q4_unpack<8>(q0, h);
+  return make_half8(h[0], h[1], h[2], h[3]);
+}
+template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q4_1>(uint32_t q0, uint32_t) {
+  half2_t h[4];
+  q4_unpack<0>(q0, h);
   return make_half8(h[0], h[1], h[2], h[3]);
 }
 template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q8_0>(uint32_t q0, uint32_t q1) {
@@ -38,7 +43,7 @@ template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q8_0>(uint32_
 // Staged activations: for chunk-relative block bb, lane group g and token t,
 // the 8 fp16 values of the A operand live at xs[(4 bb + g) * NT + t], in the
 // element order the B operand uses:
-//   Q4_0: elements 4g..4g+3 then 16+4g..16+4g+3;  Q8_0: elements 8g..8g+7.
+//   Q4_0, Q4_1: elements 4g..4g+3 then 16+4g..16+4g+3;  Q8_0: elements 8g..8g+7.
 template <int QT, int NT, bool XF16, int THREADS>
 __device__ __forceinline__ void gemv_stage_x(half8_t *xs, const void *X, int n_tokens, int k, int b_lo, int b_hi) {
   const int nb = b_hi - b_lo;
@@ -56,8 +61,8 @@ __device__ __forceinline__ void gemv_stage_x(half8_t *xs, const void *X, int n_t
       const half2_t a = cvt_half2(f.x, f.y), b = cvt_half2(f.z, f.w);
       h = half4_t{a.x, a.y, b.x, b.y};
     }
-    const int g = QT == QMM_TYPE_Q4_0 ? (j & 3) : (j >> 1);
-    const int half_off = QT == QMM_TYPE_Q4_0 ? 4 * (j >> 2) : 4 * (j & 1);
+    const int g = QTraits<QT>::nibbles ? (j & 3) : (j >> 1);
+    const int half_off = QTraits<QT>::nibbles ? 4 * (j >> 2) : 4 * (j & 1);
     *reinterpret_cast<half4_t *>(reinterpret_cast<_Float16 *>(xs + (4 * bb + g) * NT + t) + half_off) = h;
   }
 }
@@ -70,6 +75,33 @@ __device__ __forceinline__ void gemv_block(float acc[4], half8_t xop, half8_t wo
   constexpr int E = NT < 4 ? NT : 4;
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(d, part[e], acc[e]);
+}
+
+// A block with a minimum offset (Q4_1): sum_i (d q_i + m) x_i =
+// d * sum_i q_i x_i + m * sum_i x_i. The second sum comes from one more MFMA
+// with an all-ones B operand (every column then holds the block's sum of the
+// fp16 activations of each token slot); dm_bits = d | m << 16.
+template <int NT>
+__device__ __forceinline__ void gemv_block_min(float acc[4], half8_t xop, half8_t wop, uint32_t dm_bits) {
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const _Float16 one = static_cast<_Float16>(1.0f);
+  const half8_t ones = {one, one, one, one, one, one, one, one};
+  const float4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, zero, 0, 0, 0);
+  const float4_t sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, ones, zero, 0, 0, 0);
+  const float d = half_bits_to_float(dm_bits & 0xFFFFu), m = half_bits_to_float(dm_bits >> 16);
+  constexpr int E = NT < 4 ? NT : 4;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(m, sx[e], __builtin_fmaf(d, part[e], acc[e]));
+}
+
+// One block's contribution for any type: dm_bits = d (low half) and, for a
+// type with a minimum, m (high half).
+template <int QT, int NT>
+__device__ __forceinline__ void gemv_any_block(float acc[4], half8_t xop, half8_t wop, uint32_t dm_bits) {
+  if constexpr (QTraits<QT>::has_min)
+    gemv_block_min<NT>(acc, xop, wop, dm_bits);
+  else
+    gemv_block<NT>(acc, xop, wop, dm_bits & 0xFFFFu);
 }
 
 }  // namespace qmm

@@ -13,8 +13,8 @@
 //    (row groups of its largest matrix) x (matrices), and the hardware
 //    balances the workgroups across the CUs. Its 8 or 16 wavefronts (see
 //    k_split_for) split k into
-//    contiguous ranges of quads (8 blocks: 144 bytes Q4_0 / 272 bytes Q8_0
-//    per row, a whole number of 16-byte chunks) and stream them
+//    contiguous ranges of quads (8 blocks: 144 bytes Q4_0, 160 Q4_1, 272
+//    Q8_0 per row, a whole number of 16-byte chunks) and stream them
 //    independently; they meet once, at the end, to add their partial sums in
 //    a fixed order through LDS (no atomics: results are reproducible, and
 //    identical to the general kernel's, which splits k the same way).
@@ -24,7 +24,9 @@
 //    register set. A wavefront issues the loads of a round of stages at once
 //    and then consumes them in order (the wait counter is exact).
 //  * Consuming a stage copies it into the wavefront's private LDS area (the
-//    activations converted to fp16 in MFMA operand order) and runs 8 MFMAs.
+//    activations converted to fp16 in MFMA operand order) and runs 8 MFMAs
+//    (16 for Q4_1, whose second MFMA per block sums the activations for the
+//    minimum term).
 // Several matrices per launch remove the fixed per-launch cost that
 // dominates decode-sized matmuls (a launch plus its ramp costs about as much
 // as streaming ten megabytes).
@@ -41,7 +43,8 @@ namespace qmm {
 constexpr int kRMaxMats = 16;
 
 template <int QT, int NT> struct RCfg {
-  static constexpr int quad_chunks = QT == QMM_TYPE_Q4_0 ? 9 : 17;  // 16-byte chunks per row per quad
+  // 16-byte chunks per row per quad of 8 blocks (144, 160 or 272 bytes)
+  static constexpr int quad_chunks = Block<QT>::bytes / 2;
   // LDS bytes per row of the stage copy. Unpadded (chunk c at 16 c, one
   // 16-byte store per chunk) for up to 2 tokens. With 4 or 8 tokens, whose
   // activation traffic makes LDS the tighter resource, rows are padded by 8
@@ -58,7 +61,7 @@ template <int QT, int NT> struct RCfg {
   // with one or two tokens takes rounds of 2 stages (the whole share for
   // k = 4096) so the kernel fits in ~60 VGPRs and 6-8 wavefronts per SIMD:
   // more workgroups per CU overlap one another's loads and compute.
-  static constexpr bool lean = QT == QMM_TYPE_Q4_0 && NT <= 2;
+  static constexpr bool lean = QTraits<QT>::nibbles && NT <= 2;
   static constexpr int depth_large = lean ? 2 : depth;
   static constexpr int waves_per_simd_large = !lean ? 4 : (NT == 1 ? 8 : 6);
   static constexpr int w_lds = 16 * row_stride;
@@ -140,8 +143,8 @@ template <int QT, int NT> struct RLane {
       wv[j] = ok ? __umul24(r, nb1 - 16 * QC) + 16 * c : 0;
     }
     const int xb = lane >> 3, xj = lane & 7;
-    const int xg = QT == QMM_TYPE_Q4_0 ? (xj & 3) : (xj >> 1);
-    const int xh = QT == QMM_TYPE_Q4_0 ? 4 * (xj >> 2) : 4 * (xj & 1);
+    const int xg = QTraits<QT>::nibbles ? (xj & 3) : (xj >> 1);
+    const int xh = QTraits<QT>::nibbles ? 4 * (xj >> 2) : 4 * (xj & 1);
     xw = (4 * xb + xg) * NT * 16 + 2 * xh;
   }
 };
@@ -189,6 +192,11 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
       const uint32_t a0 = ld(4 * g), a1 = ld(4 * g + 4), b = ld(20 + 4 * g), d0 = ld(0), d1 = ld(16);
       gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), 0), d0 & 0xFFFFu);
       gemv_block<NT>(acc, xo, gemv_codes<QT>(b, 0), d1 >> 16);
+    } else if constexpr (QT == QMM_TYPE_Q4_1) {
+      // blocks at bytes 0 and 20 of the pair: d|m dword, then 4 code dwords
+      const uint32_t a = ld(4 + 4 * g), b = ld(24 + 4 * g), dm0 = ld(0), dm1 = ld(20);
+      gemv_block_min<NT>(acc, xe, gemv_codes<QT>(a, 0), dm0);
+      gemv_block_min<NT>(acc, xo, gemv_codes<QT>(b, 0), dm1);
     } else {
       const uint32_t a0 = ld(8 * g), a1 = ld(8 * g + 4), a2 = ld(8 * g + 8);
       const uint32_t b0 = ld(36 + 8 * g), b1 = ld(40 + 8 * g), d0 = ld(0), d1 = ld(32);
@@ -435,12 +443,11 @@ hipError_t launch_gemv_id_stream(const void *W, int qtype, int64_t n_experts, in
     __builtin_memcpy(&B.m[1], &route, sizeof(RRoute));
     const int count = static_cast<int>(pairs - p0 < kMaxY ? pairs - p0 : kMaxY);
     hipError_t e;
-    if (qtype == QMM_TYPE_Q4_0)
-      e = waves == kKSplitSmall ? id_go_w<QMM_TYPE_Q4_0, kKSplitSmall>(B, count, rg, stream)
-                                : id_go_w<QMM_TYPE_Q4_0, kKSplitLarge>(B, count, rg, stream);
-    else
-      e = waves == kKSplitSmall ? id_go_w<QMM_TYPE_Q8_0, kKSplitSmall>(B, count, rg, stream)
-                                : id_go_w<QMM_TYPE_Q8_0, kKSplitLarge>(B, count, rg, stream);
+    e = by_qtype(qtype, [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
+      return waves == kKSplitSmall ? id_go_w<QT, kKSplitSmall>(B, count, rg, stream)
+                                   : id_go_w<QT, kKSplitLarge>(B, count, rg, stream);
+    });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -480,13 +487,11 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t str
       ++j;
     }
     const int waves = k_split_for(total_rg, device_cus());
-    hipError_t e;
-    if (qt == QMM_TYPE_Q4_0)
-      e = xf ? r_nt<QMM_TYPE_Q4_0, true>(nt, B, count, max_rg, waves, stream)
-             : r_nt<QMM_TYPE_Q4_0, false>(nt, B, count, max_rg, waves, stream);
-    else
-      e = xf ? r_nt<QMM_TYPE_Q8_0, true>(nt, B, count, max_rg, waves, stream)
-             : r_nt<QMM_TYPE_Q8_0, false>(nt, B, count, max_rg, waves, stream);
+    const hipError_t e = by_qtype(qt, [&](auto q) {
+      constexpr int QT = decltype(q)::value;
+      return xf ? r_nt<QT, true>(nt, B, count, max_rg, waves, stream)
+                : r_nt<QT, false>(nt, B, count, max_rg, waves, stream);
+    });
     if (e != hipSuccess) return e;
     i = j;
   }

@@ -14,7 +14,9 @@
  *   [Arch]  "llama.cpp 源码完全拆解(一)：整体架构与模块全景", section
  *           "权重装载：GGUF、mmap 与 4 bit 块": block reconstruction
  *           w_hat = s (q - z); legacy types (Q4_0 ... Q8_0) use 32 weights per
- *           block with one shared scale; the quantised matmul kernels decode
+ *           block with one shared scale, Q4_1 with an extra minimum offset
+ *           (the paragraph on the three quantisation families); the
+ *           quantised matmul kernels decode
  *           scale and integer weights per block and multiply-add them with the
  *           activations in registers, with no separate fp16 restore step.
  *   [Graph] "llama.cpp 源码完全拆解(二)：ggml 计算图与内存分配器", section
@@ -31,7 +33,10 @@
  *   W  weights, n_rows rows; row r starts at W + r * row_stride_bytes and holds
  *      k / 32 consecutive blocks. Q4_0 block = 18 bytes: little-endian binary16
  *      d, then 16 bytes qs; element j (0..15) is the low nibble of qs[j],
- *      element j + 16 the high nibble; weight = d * (q - 8). Q8_0 block = 34
+ *      element j + 16 the high nibble; weight = d * (q - 8). Q4_1 block = 20
+ *      bytes: binary16 d, binary16 m, then 16 bytes qs in Q4_0's nibble
+ *      order; weight = d * q + m (unsigned codes; the layout of d, m and qs
+ *      is this library's reading of the minimum-offset type). Q8_0 block = 34
  *      bytes: binary16 d, then 32 int8 codes; weight = d * q. Bytes between
  *      the last block of a row and the next row (padding) are never read.
  *   X  activations [n_tokens][k], k contiguous (fp32, or fp16 for *_x16).
@@ -50,9 +55,11 @@
  * HIP rejects returns QMM_ERR_HIP. qmm_status_string() names every code.
  *
  * Numerics: dequantised weights are exact (fp32 d * (q - z) is exact for every
- * finite binary16 d). The matmul accumulates in fp32. Decode-sized calls
+ * finite binary16 d; Q4_1's d * q + m is that exact product plus m, rounded
+ * once to fp32). The matmul accumulates in fp32. Decode-sized calls
  * (n_tokens <= QMM_GEMV_MAX_TOKENS) round activations to fp16 and multiply
- * them by the exact integer codes, applying d in fp32 once per block; larger
+ * them by the exact integer codes, applying d in fp32 once per block (Q4_1:
+ * plus m times the block's sum of the fp16 activations); larger
  * calls round both the dequantised weights and the activations to fp16 for
  * the matrix cores. Every element satisfies
  *   |y - y_exact| <= 1e-3 * sum_i |w_i x_i| + 1e-5
@@ -72,6 +79,7 @@ extern "C" {
 
 /* Weight types; the values follow ggml's type enumeration. */
 #define QMM_TYPE_Q4_0 2
+#define QMM_TYPE_Q4_1 3
 #define QMM_TYPE_Q8_0 8
 
 /* Activation element types for qmm_matmul_path. */
@@ -101,7 +109,7 @@ extern "C" {
  * [Load] section 第六步, [Arch] section 权重装载).
  *   W                device pointer, 2-byte aligned, n_rows rows of
  *                    row_stride_bytes bytes (see layout above)
- *   ggml_type        QMM_TYPE_Q4_0 or QMM_TYPE_Q8_0
+ *   ggml_type        QMM_TYPE_Q4_0, QMM_TYPE_Q4_1 or QMM_TYPE_Q8_0
  *   n_rows           ne1 of W (>= 0)
  *   k                ne0 of W and of X; positive multiple of 32
  *   row_stride_bytes nb1 of W; even and >= qmm_row_bytes(ggml_type, k)

@@ -57,7 +57,10 @@ def test_row_bytes_and_supports(L):
     assert L.qmm_row_bytes(Q8, 4096) == 4352
     assert L.qmm_row_bytes(Q4, 11008) == 6192
     assert L.qmm_row_bytes(Q8, 32) == 34
-    assert L.qmm_row_bytes(3, 4096) == qmm.QMM_ERR_TYPE
+    assert L.qmm_row_bytes(qmm.QMM_TYPE_Q4_1, 4096) == 2560
+    assert L.qmm_supports(qmm.QMM_TYPE_Q4_1, 64, 40) == 1 and L.qmm_supports(qmm.QMM_TYPE_Q4_1, 64, 38) == 0
+    for bad_type in (0, 1, 4, 6, 7, 9, 12):
+        assert L.qmm_row_bytes(bad_type, 4096) == qmm.QMM_ERR_TYPE
     for bad_k in (0, -32, 48, 1 << 31):
         assert L.qmm_row_bytes(Q4, bad_k) == qmm.QMM_ERR_SHAPE
     assert L.qmm_supports(Q4, 4096, 2304) == 1
@@ -86,7 +89,7 @@ def test_validation_codes(L):
     assert _mm(L, X=NULL) == E.QMM_ERR_NULL
     assert _mm(L, Y=NULL) == E.QMM_ERR_NULL
     assert _mm(L, t=0) == E.QMM_ERR_TYPE
-    assert _mm(L, t=3) == E.QMM_ERR_TYPE
+    assert _mm(L, t=1) == E.QMM_ERR_TYPE
     assert _mm(L, xt=2) == E.QMM_ERR_TYPE
     assert _mm(L, k=0) == E.QMM_ERR_SHAPE
     assert _mm(L, k=40) == E.QMM_ERR_SHAPE

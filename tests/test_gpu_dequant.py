@@ -8,7 +8,7 @@ from block_quantized_matmul_amd import synth
 from gpu_util import assert_bitwise, run_dequant, say
 
 pytestmark = pytest.mark.gpu
-Q4, Q8 = O.TYPE_Q4_0, O.TYPE_Q8_0
+Q4, Q41, Q8 = O.TYPE_Q4_0, O.TYPE_Q4_1, O.TYPE_Q8_0
 
 
 def _check(Wnp, qtype, k, offset=0, what=""):
@@ -29,6 +29,22 @@ def test_every_scale_pattern(qtype):
     codes = rng.integers(0, 256, size=(rows, 32, payload), dtype=np.uint8)
     W = synth.assemble_rows(d, codes, synth.dense_row_bytes(qtype, k))
     _check(W, qtype, k, what="all scales")
+
+
+@pytest.mark.parametrize("which", ["d", "m"])
+def test_q4_1_every_scale_and_min_pattern(which):
+    # 65536 blocks: block i has d bits i (or m bits i), the other field and
+    # the code bytes seeded random.
+    rng = np.random.Generator(np.random.PCG64(110 + len(which)))
+    rows, k = 2048, 1024
+    pat = np.arange(65536, dtype=np.uint16).reshape(rows, 32)
+    other = rng.integers(0, 65536, size=(rows, 32)).astype(np.uint16)
+    d, m = (pat, other) if which == "d" else (other, pat)
+    payload = np.empty((rows, 32, 18), np.uint8)
+    payload[:, :, 0:2] = m.view(np.uint8).reshape(rows, 32, 2)
+    payload[:, :, 2:] = rng.integers(0, 256, size=(rows, 32, 16), dtype=np.uint8)
+    W = synth.assemble_rows(d, payload, synth.dense_row_bytes(Q41, k))
+    _check(W, Q41, k, what=f"all {which} patterns")
 
 
 @pytest.mark.parametrize("qtype", [Q4, Q8])
@@ -53,7 +69,7 @@ def test_config_weights(cfg):
         _check(case.weights(), case.qtype, case.k, what=case.name)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("k,extra,offset", [(32, 0, 0), (96, 0, 0), (96, 2, 2), (160, 6, 0), (512, 30, 2),
                                             (4096, 256, 0)])
 def test_strides_alignment_and_ragged(qtype, k, extra, offset):
@@ -68,7 +84,7 @@ def test_strides_alignment_and_ragged(qtype, k, extra, offset):
         _check(W2, qtype, k, offset, what=f"k={k} pad={extra} refilled")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 def test_dword_aligned_output(qtype):
     """out only 4-byte aligned (the weakest alignment the boundary accepts)."""
     import torch
@@ -88,7 +104,7 @@ def test_dword_aligned_output(qtype):
     assert_bitwise(out.cpu().numpy(), O.dequantize(W, qtype, rows, k, nb1), "dword-aligned out")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("rows,k,extra,offset", [(300, 256, 0, 0), (77, 96, 6, 2), (2000, 4096, 256, 0)])
 def test_get_rows(qtype, rows, k, extra, offset):
     """GET_ROWS bit-exact against the oracle: repeated indices, the first and

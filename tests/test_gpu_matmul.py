@@ -13,7 +13,7 @@ import torch
 from gpu_util import assert_bitwise, assert_close_to_oracle, run_matmul, say
 
 pytestmark = pytest.mark.gpu
-Q4, Q8 = O.TYPE_Q4_0, O.TYPE_Q8_0
+Q4, Q41, Q8 = O.TYPE_Q4_0, O.TYPE_Q4_1, O.TYPE_Q8_0
 GEMV, GEMM, AUTO = qmm.QMM_PATH_GEMV, qmm.QMM_PATH_GEMM, qmm.QMM_PATH_AUTO
 
 
@@ -33,7 +33,7 @@ def _parity(W, qtype, k, X, path, offset=0, what=""):
 
 
 # ------------------------------------------------------------ small shapes, every kernel variant
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8])
 def test_gemv_ragged(qtype, xdt, n):
@@ -44,7 +44,7 @@ def test_gemv_ragged(qtype, xdt, n):
         _parity(W, qtype, k, X, GEMV, offset, f"gemv rows={rows} k={k}")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("n", [1, 9, 16, 37, 128, 200])
 def test_gemm_ragged(qtype, xdt, n):
@@ -54,7 +54,7 @@ def test_gemm_ragged(qtype, xdt, n):
         _parity(W, qtype, k, X, GEMM, offset, f"gemm rows={rows} k={k}")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 def test_dispatch_and_cross_check(qtype):
     """AUTO picks GEMV up to 8 tokens; for n = 1..16 both kernels agree with
     the oracle (and therefore with each other) on the same inputs."""
@@ -79,7 +79,7 @@ def _dword_aligned_copy(a: np.ndarray, dtype) -> tuple:
     return flat, view.view(a.shape)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("path,n", [(GEMV, 1), (GEMV, 8), (GEMM, 40)])
 def test_dword_aligned_activations_and_outputs(qtype, xdt, path, n):
@@ -100,7 +100,7 @@ def test_dword_aligned_activations_and_outputs(qtype, xdt, path, n):
 
 
 # ------------------------------------------------------------ closed-form invariants
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("path,n", [(GEMV, 1), (GEMV, 8), (GEMM, 24)])
 def test_one_hot_activation(qtype, path, n):
     """x = e_j: every other product is an exact zero, so y equals the
@@ -114,12 +114,17 @@ def test_one_hot_activation(qtype, path, n):
     Y = run_matmul(W, qtype, k, X, path)
     w = O.dequantize(W, qtype, rows, k, W.shape[1])[:, cols].T
     if path == GEMM:
-        w = w.astype(np.float16).astype(np.float32)
+        # the matrix cores take fp16(d (q - z)) or, for Q4_1, fp16(d q + m):
+        # one rounding of the exact weight (exact in fp64)
+        d, q = O.block_scales_and_codes(W, qtype, rows, k, W.shape[1])
+        m = O.block_mins(W, qtype, rows, k, W.shape[1])
+        exact = np.repeat(d, 32, axis=1) * (q - O.ZERO_POINT[qtype]) + np.repeat(m, 32, axis=1)
+        w = exact[:, cols].T.astype(np.float16).astype(np.float32)
     # a zero weight may be -0.0 (negative d times code 0); sums give +0.0
     assert_bitwise(Y + np.float32(0.0), w + np.float32(0.0), "one-hot")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("path,n", [(GEMV, 3), (GEMM, 40)])
 def test_zero_codes_scaling_permutation_padding_determinism(qtype, path, n):
     rows, k = 150, 1024
