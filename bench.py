@@ -90,6 +90,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-get-rows", action="store_true", help="skip the GET_ROWS (token-embedding gather) line")
     ap.add_argument("--no-matmul-id", action="store_true", help="skip the MUL_MAT_ID (routed expert FFN) lines")
+    ap.add_argument("--no-q4-1", action="store_true", help="skip the Q4_1 lines")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
@@ -259,6 +260,47 @@ def time_get_rows(torch, qmm, synth, with_oracle=False):
         t0 = time.perf_counter()
         O.get_rows(Wh, qt, rows, k, nb1, idh)
         res["cpu_oracle_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+    return res
+
+
+# ---------------------------------------------------------------- Q4_1
+
+def time_q4_1(torch, qmm, synth, with_oracle=False):
+    """Q4_1 (the minimum-offset legacy type) on the 11008x4096 FFN projection:
+    decode (1 fp32 token) and prefill (2048 fp16 tokens), back-to-back launches
+    in a graph over >= 1.1 GiB of weight copies, so weights come from HBM."""
+    import numpy as np
+    rows, k, qt = 11008, 4096, synth.TYPE_Q4_1
+    rng = np.random.Generator(np.random.PCG64(4141))
+    Wh = synth.make_weights(qt, rows, k, None, rng)
+    W0 = torch.from_numpy(Wh).cuda()
+    copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    Xh = synth.make_activations(1, k, rng)
+    X1 = torch.from_numpy(Xh).cuda()
+    Y1 = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+    reps = 4 * copies
+    us = _graph_time(torch, lambda: [qmm.qmm_matmul(Ws[i % copies], qt, k, X1, Y=Y1) for i in range(reps)], reps)
+    byts = W0.numel() + 4 * k + 4 * rows
+    gbs = byts / (us * 1e-6) / 1e9
+    T = 2048
+    X2 = torch.from_numpy(synth.make_activations(T, k, rng, np.float16)).cuda()
+    Y2 = torch.empty((T, rows), dtype=torch.float32, device="cuda")
+    us2 = _graph_time(torch, lambda: [qmm.qmm_matmul_x16(Ws[i % copies], qt, k, X2, Y=Y2) for i in range(copies)],
+                      copies)
+    tfl = 2 * T * rows * k / (us2 * 1e-6) / 1e12
+    res = {"workload": f"{rows}x{k} Q4_1",
+           "decode": {"tokens": 1, "us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": byts,
+                      "GB_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                      "kernel": "gemv_stream_kernel", "bound": "hbm"},
+           "prefill": {"tokens": T, "us_per_launch": round(us2, 3), "TFLOP_per_s": round(tfl, 2),
+                       "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4), "kernel": "gemm_kernel",
+                       "bound": "mfma"}}
+    if with_oracle:
+        import oracle.qmm_oracle as O
+        t0 = time.perf_counter()
+        O.matmul(Wh, qt, rows, k, Wh.shape[1], Xh)
+        res["decode"]["cpu_oracle_us"] = round((time.perf_counter() - t0) * 1e6, 1)
     return res
 
 
@@ -584,6 +626,8 @@ def main():
         out["get_rows"] = time_get_rows(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if not args.no_matmul_id:
         out["matmul_id"] = time_matmul_id(torch, qmm, synth, with_oracle=bool(cpu_layers))
+    if not args.no_q4_1:
+        out["q4_1"] = time_q4_1(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if cpu_layers:
         import oracle.qmm_oracle as O
         log("timing the CPU oracle on a sample")
