@@ -202,3 +202,53 @@ def test_matmul_id_mixtral_prefill_sampled(qtype):
             y_ref, s = O.matmul_sampled(We, qtype, rows, k, nb1, X[t], np.zeros_like(rsamp), rsamp)
             ok = O.within_tolerance(Y[t, i, rsamp], y_ref, s)
             assert ok.all(), f"token {t} expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
+
+
+@pytest.mark.parametrize("n_experts,n_ids,n_tokens", [(256, 8, 128), (4096, 8, 2048), (4097, 2, 16)])
+def test_matmul_id_many_experts(n_experts, n_ids, n_tokens):
+    """Many small experts: 256 and 4096 (the most the grouped route counts in
+    LDS) take the grouped path, 4097 the per-pair one; sampled tokens against
+    the oracle."""
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([506, n_experts, n_ids]))
+    rows, k = 40, 64
+    nb1 = synth.dense_row_bytes(Q4, k)
+    nb2 = rows * nb1
+    W = _stack(Q4, n_experts, rows, k, nb1, nb2, rng)
+    X = synth.make_activations(n_tokens, k, rng).reshape(n_tokens, 1, k)
+    ids = rng.integers(0, n_experts, size=(n_tokens, n_ids)).astype(np.int32)
+    ids[1, :] = n_experts - 1
+    grouped = qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0
+    assert grouped == (n_experts <= 4096)
+    say(f"matmul_id experts={n_experts} n_ids={n_ids} tokens={n_tokens} grouped={grouped}")
+    Y = _run(W, Q4, n_experts, rows, k, nb1, nb2, X, ids)
+    sample = np.unique(np.concatenate([[0, 1, n_tokens - 1], rng.integers(0, n_tokens, 30)]))
+    y_ref, s = O.matmul_id(W, Q4, n_experts, rows, k, nb1, nb2, X[sample], ids[sample])
+    _check(Y[sample], y_ref, s, f"matmul_id experts={n_experts}")
+
+
+@pytest.mark.parametrize("n_experts", [0, 4])
+def test_matmul_id_grouped_no_valid_id(n_experts):
+    """Grouped path where no id names an expert (or there are none): every
+    output row is NaN, and nothing else is written."""
+    import torch
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([507, n_experts]))
+    rows, k, n_ids, n_tokens = 24, 64, 2, 40
+    nb1 = synth.dense_row_bytes(Q4, k)
+    nb2 = rows * nb1
+    W = _stack(Q4, max(n_experts, 1), rows, k, nb1, nb2, rng)
+    X = synth.make_activations(n_tokens, k, rng).reshape(n_tokens, 1, k)
+    ids = np.full((n_tokens, n_ids), n_experts, np.int32)
+    ids[::3, 0] = -7
+    assert n_experts == 0 or qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0
+    say(f"matmul_id no valid id experts={n_experts}")
+    from gpu_util import place_weights
+    _keep, Wd = place_weights(W)
+    Y = torch.zeros((n_tokens + 1, n_ids, rows), dtype=torch.float32, device="cuda")
+    qmm.qmm_matmul_id(Wd, Q4, k, dev(X), dev(ids), n_experts=n_experts, n_rows=rows, row_stride_bytes=nb1,
+                      expert_stride_bytes=nb2, Y=Y[:n_tokens])
+    torch.cuda.synchronize()
+    Yh = Y.cpu().numpy()
+    assert np.isnan(Yh[:n_tokens]).all()
+    assert (Yh[n_tokens] == 0).all()
