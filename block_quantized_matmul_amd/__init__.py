@@ -105,6 +105,31 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _check_span(t, dtype, n_elems, name):
+    """t must be a contiguous GPU tensor of `dtype` holding at least n_elems
+    elements: the C entry points trust the sizes they are given, so the
+    binding checks that the buffers behind them are large enough."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n_elems:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n_elems}")
+
+
+def _weights_span(ggml_type, k, n_rows, nb1, n_experts=1, nb2=0):
+    """Bytes of W the kernels may read: up to the end of the last row's blocks."""
+    if n_rows <= 0 or n_experts <= 0:
+        return 0
+    dense = qmm_row_bytes(ggml_type, k)
+    if dense < 0:
+        return 0  # the C call reports the type or shape error
+    return (n_experts - 1) * nb2 + (n_rows - 1) * nb1 + dense
+
+
 def _weights_geometry(W, n_rows, row_stride_bytes):
     import torch
     if W.dtype != torch.uint8:
@@ -134,6 +159,9 @@ def qmm_matmul_path(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_to
         n_tokens = X.shape[0]
     if Y is None:
         Y = torch.empty((int(n_tokens), n_rows), dtype=torch.float32, device=X.device)
+    _check_span(W, torch.uint8, _weights_span(ggml_type, k, n_rows, nb1), "W")
+    _check_span(X, X.dtype, int(n_tokens) * int(k), "X")
+    _check_span(Y, torch.float32, int(n_tokens) * n_rows, "Y")
     st = lib().qmm_matmul_path(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(X, "X"), x_type,
                                int(n_tokens), _gpu_ptr(Y, "Y"), int(path), _stream(stream))
     if st != QMM_OK:
@@ -163,6 +191,8 @@ def qmm_dequantize(W, ggml_type, k, n_rows=None, row_stride_bytes=None, out=None
     n_rows, nb1 = _weights_geometry(W, n_rows, row_stride_bytes)
     if out is None:
         out = torch.empty((n_rows, int(k)), dtype=torch.float32, device=W.device)
+    _check_span(W, torch.uint8, _weights_span(ggml_type, k, n_rows, nb1), "W")
+    _check_span(out, torch.float32, n_rows * int(k), "out")
     st = lib().qmm_dequantize(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(out, "out"),
                               _stream(stream))
     if st != QMM_OK:
@@ -181,6 +211,8 @@ def qmm_get_rows(W, ggml_type, k, ids, n_rows=None, row_stride_bytes=None, out=N
     n_ids = int(ids.shape[0])
     if out is None:
         out = torch.empty((n_ids, int(k)), dtype=torch.float32, device=W.device)
+    _check_span(W, torch.uint8, _weights_span(ggml_type, k, n_rows, nb1), "W")
+    _check_span(out, torch.float32, n_ids * int(k), "out")
     st = lib().qmm_get_rows(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(ids, "ids"), n_ids,
                             _gpu_ptr(out, "out"), _stream(stream))
     if st != QMM_OK:
@@ -218,6 +250,9 @@ def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stri
         raise ValueError("X must be [n_tokens][x_slots][k] with the n_tokens of ids")
     if Y is None:
         Y = torch.empty((n_tokens, n_ids, int(n_rows)), dtype=torch.float32, device=X.device)
+    _check_span(W, torch.uint8, _weights_span(ggml_type, k, int(n_rows), int(row_stride_bytes), int(n_experts),
+                                              int(expert_stride_bytes)), "W")
+    _check_span(Y, torch.float32, n_tokens * n_ids * int(n_rows), "Y")
     need = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens)
     if need < 0:
         raise QmmError(need, "qmm_matmul_id_workspace_bytes")
@@ -247,6 +282,8 @@ def qmm_matmul_batch(items, stream=None):
         rows, nb1 = _weights_geometry(W, None, None)
         if X.dtype not in (torch.float32, torch.float16):
             raise TypeError("X must be float32 or float16")
+        _check_span(X, X.dtype, int(X.shape[0]) * int(k), "X")
+        _check_span(Y, torch.float32, int(X.shape[0]) * rows, "Y")
         arr[i] = qmm_matmul_desc(_gpu_ptr(W, "W").value, int(t), rows, int(k), nb1, _gpu_ptr(X, "X").value,
                                  QMM_X_F16 if X.dtype == torch.float16 else QMM_X_F32, int(X.shape[0]),
                                  _gpu_ptr(Y, "Y").value)

@@ -324,3 +324,27 @@ def test_graph_replay_matches_eager():
         for a, b in zip(out, ref):
             assert torch.equal(a, b), f"replay {rep} differs"
         _ = (Xg * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_binding_rejects_short_buffers():
+    """The binding refuses buffers smaller than the sizes it passes to the C
+    ABI (which trusts them), before anything is launched."""
+    rows, k = 64, 256
+    W, X = _inputs(Q4, rows, k, 3)
+    Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
+    with pytest.raises(ValueError):
+        qmm.qmm_matmul(Wd, Q4, k, Xd, Y=torch.empty((3, rows - 1), device="cuda"))
+    with pytest.raises(ValueError):
+        qmm.qmm_matmul(Wd[:-1], Q4, k, Xd, n_rows=rows, row_stride_bytes=W.shape[1])
+    with pytest.raises(ValueError):
+        qmm.qmm_matmul(Wd, Q4, k, Xd[:2], n_tokens=3)
+    with pytest.raises(ValueError):
+        qmm.qmm_dequantize(Wd, Q4, k, out=torch.empty((rows, k - 1), device="cuda"))
+    ids = torch.zeros(5, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        qmm.qmm_get_rows(Wd, Q4, k, ids, out=torch.empty((4, k), device="cuda"))
+    with pytest.raises(ValueError):
+        qmm.qmm_matmul_id(Wd.view(2, rows // 2, -1), Q4, k, Xd.view(3, 1, k),
+                          torch.zeros((3, 2), dtype=torch.int32, device="cuda"),
+                          Y=torch.empty((3, 2, rows // 2 - 1), device="cuda"))
+    torch.cuda.synchronize()
