@@ -119,14 +119,19 @@ def _find(d, suffix):
 
 
 def _short(name):
+    name = name.replace("(anonymous namespace)::", "")
     return re.sub(r"\(.*", "", name).replace("void ", "")
 
 
 def _routed(name, kern):
-    """True for the expert-routed instantiation of `kern` (one template
-    argument more than the plain one)."""
+    """True for the expert-routed instantiation of `kern`: its last template
+    argument (the routing flag, which a demangled name may omit when it has
+    its default, false) is true."""
     m = re.search(re.escape(kern) + r"<([^>]*)>", name)
-    return bool(m) and len(m.group(1).split(",")) > KERNEL_TARGS[kern]
+    if not m:
+        return False
+    args = [a.strip() for a in m.group(1).split(",")]
+    return len(args) > KERNEL_TARGS[kern] and args[KERNEL_TARGS[kern]] == "true"
 
 
 def _col(row, *names):
@@ -147,11 +152,15 @@ def summarize_trace(d):
         print(f"{k[:58]:58s} {gx:9d} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
               f"{min(v):9.2f} {max(v):9.2f}")
     for kern in KERNELS:
-        for routed, tag in ((False, ""), (True, " routed")):
-            v = [x for (k, _), xs in by.items() if kern in k and _routed(k, kern) == routed for x in xs]
-            if v:
-                print(f"ALL {kern}{tag}: calls {len(v)} avg_us {statistics.mean(v):.3f} "
-                      f"source_sha256 {source_hash(kern)}")
+        groups = {}
+        for (k, _), xs in by.items():
+            m = re.search(re.escape(kern) + r"<(\d+)", k)
+            if m:
+                groups.setdefault((int(m.group(1)), _routed(k, kern)), []).extend(xs)
+        for (qt, routed), v in sorted(groups.items()):
+            tag = " routed" if routed else ""
+            print(f"ALL {kern} type {qt}{tag}: calls {len(v)} avg_us {statistics.mean(v):.3f} "
+                  f"source_sha256 {source_hash(kern)}")
 
 
 def summarize_counters(dirs):

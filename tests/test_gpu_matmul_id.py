@@ -252,3 +252,51 @@ def test_matmul_id_grouped_no_valid_id(n_experts):
     Yh = Y.cpu().numpy()
     assert np.isnan(Yh[:n_tokens]).all()
     assert (Yh[n_tokens] == 0).all()
+
+
+def test_matmul_id_graph_replay_with_new_routing():
+    """Decode and grouped MUL_MAT_ID captured in one graph and replayed with
+    new routing written into the captured ids buffers between replays (as a
+    serving loop would), with eager work in between: every replay equals an
+    eager call on the same routing."""
+    import torch
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64(508))
+    n_experts, rows, k, n_ids = 8, 136, 256, 2
+    nb1 = synth.dense_row_bytes(Q4, k)
+    W = dev(_stack(Q4, n_experts, rows, k, nb1, rows * nb1, rng).reshape(n_experts, rows, nb1))
+    Xd = dev(synth.make_activations(1, k, rng).reshape(1, 1, k))
+    Xp = dev(synth.make_activations(300, k, rng).reshape(300, 1, k))
+    ids_d = torch.zeros((1, n_ids), dtype=torch.int32, device="cuda")
+    ids_p = torch.zeros((300, n_ids), dtype=torch.int32, device="cuda")
+    Yd = torch.empty((1, n_ids, rows), dtype=torch.float32, device="cuda")
+    Yp = torch.empty((300, n_ids, rows), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, 300), dtype=torch.uint8, device="cuda")
+
+    def work():
+        qmm.qmm_matmul_id(W, Q4, k, Xd, ids_d, Y=Yd)
+        qmm.qmm_matmul_id(W, Q4, k, Xp, ids_p, Y=Yp, workspace=ws)
+
+    def routing(n):
+        return torch.from_numpy(np.stack([rng.permutation(n_experts)[:n_ids] for _ in range(n)]).astype(np.int32))
+
+    say("matmul_id graph capture")
+    work()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(3):
+        ids_d.copy_(routing(1).cuda())
+        ids_p.copy_(routing(300).cuda())
+        Yd.fill_(float("nan"))
+        Yp.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_d, got_p = Yd.clone(), Yp.clone()
+        work()  # eager, same routing
+        torch.cuda.synchronize()
+        assert torch.equal(got_d, Yd), f"decode replay {rep} differs"
+        assert torch.equal(got_p, Yp), f"grouped replay {rep} differs"
+        _ = (Xp * 2).sum().item()  # unrelated eager work between replays
