@@ -45,7 +45,7 @@ def _check(Y, y_ref, s, what):
 @pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 @pytest.mark.parametrize("layout", ["stream", "general"])
 @pytest.mark.parametrize("shared_x", [False, True])
-@pytest.mark.parametrize("n_tokens", [1, 3])
+@pytest.mark.parametrize("n_tokens", [1, 3, 9])
 def test_matmul_id_small(qtype, layout, shared_x, n_tokens):
     rng = np.random.Generator(np.random.PCG64([500, qtype, n_tokens, int(shared_x), len(layout)]))
     n_experts, n_ids, rows, k = 8, 2, 200, 512
@@ -62,6 +62,9 @@ def test_matmul_id_small(qtype, layout, shared_x, n_tokens):
     if n_tokens > 1:
         ids[1] = [-1, 0]                           # no expert, the first expert
         ids[2, 1] = n_experts                      # one past the last
+    if n_tokens == 9:  # more tokens than decode-sized, too few pairs per expert to group
+        import block_quantized_matmul_amd as qmm
+        assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) == 0
     say(f"matmul_id {layout} type={qtype} tokens={n_tokens} x_slots={X.shape[1]} ids={ids.tolist()}")
     Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
     y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
