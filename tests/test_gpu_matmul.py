@@ -55,6 +55,17 @@ def test_gemm_ragged(qtype, xdt, n):
 
 
 @pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+def test_gemm_full_size_tiles(qtype):
+    """More 128-row tiles than CUs: the 128-row tile variant (the ragged
+    tests above are small enough to take the 64-row one), with ragged rows
+    and tokens and an odd block count, every element against the oracle."""
+    rows, k, n = 4230, 288, 1030
+    assert ((rows + 127) // 128) * ((n + 127) // 128) > 256
+    W, X = _inputs(qtype, rows, k, n, xdt=np.float16)
+    _parity(W, qtype, k, X, GEMM, 0, "gemm 128-row tiles")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
 def test_dispatch_and_cross_check(qtype):
     """AUTO picks GEMV up to 8 tokens; for n = 1..16 both kernels agree with
     the oracle (and therefore with each other) on the same inputs."""
