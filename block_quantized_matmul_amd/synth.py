@@ -19,10 +19,12 @@ import numpy as np
 
 TYPE_Q4_0 = 2
 TYPE_Q4_1 = 3
+TYPE_Q5_0 = 6
+TYPE_Q5_1 = 7
 TYPE_Q8_0 = 8
 QK = 32
-BLOCK_BYTES = {TYPE_Q4_0: 18, TYPE_Q4_1: 20, TYPE_Q8_0: 34}
-TYPE_NAMES = {TYPE_Q4_0: "q4_0", TYPE_Q4_1: "q4_1", TYPE_Q8_0: "q8_0"}
+BLOCK_BYTES = {TYPE_Q4_0: 18, TYPE_Q4_1: 20, TYPE_Q5_0: 22, TYPE_Q5_1: 24, TYPE_Q8_0: 34}
+TYPE_NAMES = {TYPE_Q4_0: "q4_0", TYPE_Q4_1: "q4_1", TYPE_Q5_0: "q5_0", TYPE_Q5_1: "q5_1", TYPE_Q8_0: "q8_0"}
 
 N_EMBD = 4096
 N_FF = 11008
@@ -79,8 +81,10 @@ def make_weights(qtype: int, rows: int, k: int, nb1: int | None, rng: np.random.
     """Random quantised rows: d = fp16(U[d_lo, d_hi]) (round to nearest even);
     Q4_0 code bytes uniform 0..255 (both nibbles uniform 0..15); Q4_1 the
     same code bytes after a minimum m = fp16(-U[6, 9] * |d draw|) (blocks spanning
-    about [-7.5 d, 7.5 d], as a min/max quantiser makes them); Q8_0 codes
-    uniform integers in [-127, 127]; padding bytes uniform 0..255."""
+    about [-7.5 d, 7.5 d], as a min/max quantiser makes them); Q5_0 four
+    random bytes of fifth bits then the code bytes; Q5_1 a minimum
+    fp16(-U[12, 18] * |d draw|), then the same as Q5_0; Q8_0 codes uniform
+    integers in [-127, 127]; padding bytes uniform 0..255."""
     if k % QK:
         raise ValueError("k must be a multiple of 32")
     nblk = k // QK
@@ -95,6 +99,13 @@ def make_weights(qtype: int, rows: int, k: int, nb1: int | None, rng: np.random.
         codes = np.empty((rows, nblk, 18), dtype=np.uint8)
         codes[:, :, 0:2] = m_bits.view(np.uint8).reshape(rows, nblk, 2)  # little-endian
         codes[:, :, 2:] = rng.integers(0, 256, size=(rows, nblk, 16), dtype=np.uint8)
+    elif qtype in (TYPE_Q5_0, TYPE_Q5_1):
+        lead = 2 if qtype == TYPE_Q5_1 else 0
+        codes = np.empty((rows, nblk, lead + 20), dtype=np.uint8)
+        if lead:
+            m_bits = (-rng.uniform(12.0, 18.0, size=(rows, nblk)) * np.abs(d_draw)).astype(np.float16).view(np.uint16)
+            codes[:, :, 0:2] = m_bits.view(np.uint8).reshape(rows, nblk, 2)
+        codes[:, :, lead:] = rng.integers(0, 256, size=(rows, nblk, 20), dtype=np.uint8)
     elif qtype == TYPE_Q8_0:
         codes = rng.integers(-127, 128, size=(rows, nblk, 32), dtype=np.int8).view(np.uint8)
     else:

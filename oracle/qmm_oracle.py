@@ -1,4 +1,5 @@
-"""Plain CPU oracle for block-quantized MUL_MAT on GGUF Q4_0 / Q4_1 / Q8_0 weights.
+"""Plain CPU oracle for block-quantized MUL_MAT on GGUF Q4_0 / Q4_1 / Q5_0 / Q5_1 /
+Q8_0 weights.
 
 TEST INFRASTRUCTURE. Only the tests, the package entry point's smoke check and
 the benchmark's CPU-baseline leg may import this module. The library never
@@ -36,7 +37,12 @@ Readings taken where the pages are silent (also listed in the design notes):
     bytes in Q4_0's nibble order (20 bytes); 4-bit codes 0..15 with
     w = d * q + m, the reconstruction with the stored minimum in place of
     the zero point.
-  * The scale d (and Q4_1's m) is stored little-endian as IEEE-754 binary16.
+  * Q5_0 / Q5_1 (legacy types with 5-bit codes; the pages give neither the
+    packing nor the field order): d (and, for Q5_1, m as in Q4_1), then a
+    32-bit little-endian word whose bit j is the fifth bit of element j,
+    then the 16 nibble bytes in Q4_0's order holding the low four bits.
+    Codes 0..31; Q5_0 has z = 16 (w = d * (q - 16)), Q5_1 w = d * q + m.
+  * The scale d (and m) is stored little-endian as IEEE-754 binary16.
   * Activations X are [n_tokens][k] with k contiguous; Y is [n_tokens][n_rows]
     with rows contiguous, fully overwritten.
   * Dequantisation is to fp32 (the product d * (q - z) is exact in fp32 for
@@ -52,6 +58,8 @@ import numpy as np
 # Type ids follow ggml's enumeration (the pages name the types, not the ids).
 TYPE_Q4_0 = 2
 TYPE_Q4_1 = 3
+TYPE_Q5_0 = 6
+TYPE_Q5_1 = 7
 TYPE_Q8_0 = 8
 
 QK = 32  # weights per block for both legacy types ([Arch] legacy-family paragraph)
@@ -59,14 +67,20 @@ QK = 32  # weights per block for both legacy types ([Arch] legacy-family paragra
 BLOCK_BYTES = {
     TYPE_Q4_0: 2 + QK // 2,      # ggml_half d + uint8_t qs[16]  ([Bind] section 2.3)
     TYPE_Q4_1: 2 + 2 + QK // 2,  # d, the minimum m, qs[16]      (reading, see header)
+    TYPE_Q5_0: 2 + 4 + QK // 2,  # d, qh (fifth bits), qs[16]    (reading, see header)
+    TYPE_Q5_1: 2 + 2 + 4 + QK // 2,  # d, m, qh, qs[16]          (reading, see header)
     TYPE_Q8_0: 2 + QK,           # ggml_half d + int8 qs[32]     (reading, see header)
 }
 
-ZERO_POINT = {TYPE_Q4_0: 8, TYPE_Q4_1: 0, TYPE_Q8_0: 0}
-CODE_RANGE = {TYPE_Q4_0: (0, 15), TYPE_Q4_1: (0, 15), TYPE_Q8_0: (-128, 127)}
-HAS_MIN = {TYPE_Q4_0: False, TYPE_Q4_1: True, TYPE_Q8_0: False}
-# bytes before the codes: d, and m where the type has one
-CODE_OFFSET = {TYPE_Q4_0: 2, TYPE_Q4_1: 4, TYPE_Q8_0: 2}
+ZERO_POINT = {TYPE_Q4_0: 8, TYPE_Q4_1: 0, TYPE_Q5_0: 16, TYPE_Q5_1: 0, TYPE_Q8_0: 0}
+CODE_RANGE = {TYPE_Q4_0: (0, 15), TYPE_Q4_1: (0, 15), TYPE_Q5_0: (0, 31), TYPE_Q5_1: (0, 31),
+              TYPE_Q8_0: (-128, 127)}
+HAS_MIN = {TYPE_Q4_0: False, TYPE_Q4_1: True, TYPE_Q5_0: False, TYPE_Q5_1: True, TYPE_Q8_0: False}
+# byte offset of the 32-bit fifth-bit word (types with 5-bit codes)
+QH_OFFSET = {TYPE_Q5_0: 2, TYPE_Q5_1: 4}
+# bytes before the code bytes: d, m where the type has one, qh where it has one
+CODE_OFFSET = {TYPE_Q4_0: 2, TYPE_Q4_1: 4, TYPE_Q5_0: 6, TYPE_Q5_1: 8, TYPE_Q8_0: 2}
+NIBBLE_TYPES = (TYPE_Q4_0, TYPE_Q4_1, TYPE_Q5_0, TYPE_Q5_1)
 
 
 # --------------------------------------------------------------------------
@@ -129,10 +143,17 @@ def block_scales_and_codes(W, qtype: int, n_rows: int, k: int, nb1: int):
     d_bits = blocks[:, :, 0].astype(np.uint32) | (blocks[:, :, 1].astype(np.uint32) << 8)
     d = half_bits_to_double(d_bits)
     payload = blocks[:, :, CODE_OFFSET[qtype]:]
-    if qtype in (TYPE_Q4_0, TYPE_Q4_1):
+    if qtype in NIBBLE_TYPES:
         low = (payload & 0x0F).astype(np.int64)   # element j      <- low nibble of byte j
         high = (payload >> 4).astype(np.int64)    # element j + 16 <- high nibble of byte j
         q = np.concatenate([low, high], axis=2)   # [n_rows, nblk, 32]
+        if qtype in QH_OFFSET:
+            o = QH_OFFSET[qtype]
+            qh = np.zeros((n_rows, nblk), dtype=np.int64)
+            for b in range(4):                    # little-endian 32-bit word
+                qh |= blocks[:, :, o + b].astype(np.int64) << (8 * b)
+            bits = (qh[:, :, None] >> np.arange(32)) & 1   # bit j: fifth bit of element j
+            q = q | (bits << 4)
     else:
         q = payload.view(np.int8).astype(np.int64)
     return d, q.reshape(n_rows, k)
@@ -140,7 +161,7 @@ def block_scales_and_codes(W, qtype: int, n_rows: int, k: int, nb1: int):
 
 def block_mins(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
     """The minimum offset m of every block (float64 [n_rows, k/32]): the
-    binary16 after d in a Q4_1 block; zero for types without one."""
+    binary16 after d in a Q4_1 or Q5_1 block; zero for types without one."""
     W = _check_layout(W, qtype, n_rows, k, nb1)
     nblk = k // QK
     if not HAS_MIN[qtype]:
@@ -153,12 +174,13 @@ def block_mins(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
 
 def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
     """Weights as fp32 [n_rows][k]: w = fp32(d) * fp32(q - z), plus fp32(m)
-    for Q4_1.
+    for the types with a minimum (Q4_1, Q5_1).
 
-    z = 8 for Q4_0 and 0 for Q4_1 and Q8_0. The multiply is a single IEEE
-    fp32 multiply; for finite d it is exact (an 11-bit significand times a
-    code of at most 8 bits). Q4_1 then adds m with one fp32 rounding, so
-    w = fp32(d q + m) exactly rounded. This is the bit-exact target.
+    z = 8 for Q4_0, 16 for Q5_0 and 0 otherwise. The multiply is a single
+    IEEE fp32 multiply; for finite d it is exact (an 11-bit significand
+    times a code of at most 8 bits). Q4_1 / Q5_1 then add m with one fp32
+    rounding, so w = fp32(d q + m) exactly rounded. This is the bit-exact
+    target.
     """
     d, q = block_scales_and_codes(W, qtype, n_rows, k, nb1)
     c = (q - ZERO_POINT[qtype]).astype(np.float32)
@@ -302,23 +324,24 @@ def quantize_codes(w, d, qtype: int) -> np.ndarray:
 
 def quantize(w, qtype: int) -> np.ndarray:
     """Quantise fp32 weights [n_rows][k] into dense rows of blocks (uint8
-    [n_rows][row_bytes]). Scale choice: d = fp16(amax / 7) for Q4_0 and
-    fp16(amax / 127) for Q8_0, so |w / d| stays inside the code range; for
-    Q4_1, m = fp16(block minimum) and d = fp16((max - min) / 15), codes
-    q = clip(round((w - m) / d), 0, 15)."""
+    [n_rows][row_bytes]). Scale choice: d = fp16(amax / 7) for Q4_0,
+    fp16(amax / 15) for Q5_0 and fp16(amax / 127) for Q8_0, so |w / d| stays
+    inside the code range; for Q4_1 / Q5_1, m = fp16(block minimum) and
+    d = fp16((max - min) / qmax), codes q = clip(round((w - m) / d), 0, qmax)
+    with qmax = 15 / 31."""
     w = np.asarray(w, dtype=np.float32)
     n_rows, k = w.shape
     nblk = k // QK
     wb = w.reshape(n_rows, nblk, QK).astype(np.float64)
-    if qtype == TYPE_Q4_1:
+    if HAS_MIN[qtype]:
         lo, hi = np.min(wb, axis=2), np.max(wb, axis=2)
-        d16 = ((hi - lo) / 15.0).astype(np.float16)
+        d16 = ((hi - lo) / float(CODE_RANGE[qtype][1])).astype(np.float16)
         m16 = lo.astype(np.float16)
         d = d16.astype(np.float64)[:, :, None]
         q = quantize_codes(wb - m16.astype(np.float64)[:, :, None], d, qtype)
         return pack_blocks(d16.view(np.uint16), q, qtype, m16.view(np.uint16))
     amax = np.max(np.abs(wb), axis=2)
-    div = 7.0 if qtype == TYPE_Q4_0 else 127.0
+    div = {TYPE_Q4_0: 7.0, TYPE_Q5_0: 15.0, TYPE_Q8_0: 127.0}[qtype]
     d16 = (amax / div).astype(np.float16)
     d = d16.astype(np.float64)
     q = quantize_codes(wb, d[:, :, None], qtype)
@@ -326,10 +349,11 @@ def quantize(w, qtype: int) -> np.ndarray:
 
 
 def pack_blocks(d_bits, q, qtype: int, m_bits=None) -> np.ndarray:
-    """Lay out blocks: d as little-endian binary16, Q4_1's m likewise, then the
-    codes (Q4_0 / Q4_1: code of element j in the low nibble and of element
-    j + 16 in the high nibble of byte j; Q8_0: 32 int8 codes). q has shape
-    [n_rows, nblk, 32]."""
+    """Lay out blocks: d as little-endian binary16, m likewise (Q4_1, Q5_1),
+    the fifth bits as a little-endian 32-bit word (Q5_0, Q5_1), then the
+    codes (nibble types: low four bits of element j in the low nibble and of
+    element j + 16 in the high nibble of byte j; Q8_0: 32 int8 codes). q has
+    shape [n_rows, nblk, 32]."""
     d_bits = np.asarray(d_bits, dtype=np.uint16)
     q = np.asarray(q, dtype=np.int64)
     n_rows, nblk = d_bits.shape
@@ -342,8 +366,14 @@ def pack_blocks(d_bits, q, qtype: int, m_bits=None) -> np.ndarray:
         m_bits = np.asarray(m_bits, dtype=np.uint16)
         out[:, :, 2] = m_bits & 0xFF
         out[:, :, 3] = m_bits >> 8
-    if qtype in (TYPE_Q4_0, TYPE_Q4_1):
-        out[:, :, c0:] = (q[:, :, :16] | (q[:, :, 16:] << 4)).astype(np.uint8)
+    if qtype in NIBBLE_TYPES:
+        out[:, :, c0:] = ((q[:, :, :16] & 0xF) | ((q[:, :, 16:] & 0xF) << 4)).astype(np.uint8)
+        if qtype in QH_OFFSET:
+            qh = np.zeros((n_rows, nblk), dtype=np.int64)
+            for j in range(32):
+                qh |= ((q[:, :, j] >> 4) & 1) << j
+            for b in range(4):
+                out[:, :, QH_OFFSET[qtype] + b] = (qh >> (8 * b)) & 0xFF
     else:
         out[:, :, c0:] = q.astype(np.int8).view(np.uint8)
     return out.reshape(n_rows, nblk * bpb)

@@ -20,6 +20,7 @@ import oracle.qmm_oracle as O
 from block_quantized_matmul_amd import synth
 
 Q4, Q41, Q8 = O.TYPE_Q4_0, O.TYPE_Q4_1, O.TYPE_Q8_0
+Q50, Q51 = O.TYPE_Q5_0, O.TYPE_Q5_1
 
 
 def _hex_bytes(tokens):
@@ -50,7 +51,8 @@ def test_half_decode_specials_golden():
 
 
 # ---------------------------------------------------------------- hand-worked blocks
-@pytest.mark.parametrize("fname,qtype", [("q4_0_block.txt", Q4), ("q4_1_block.txt", Q41), ("q8_0_block.txt", Q8)])
+@pytest.mark.parametrize("fname,qtype", [("q4_0_block.txt", Q4), ("q4_1_block.txt", Q41), ("q5_0_block.txt", Q50),
+                                         ("q5_1_block.txt", Q51), ("q8_0_block.txt", Q8)])
 def test_golden_block(fname, qtype):
     g = read_golden(fname)
     raw = _hex_bytes(g["bytes"])
@@ -137,6 +139,29 @@ def test_q4_1_dequant_is_one_rounding_of_the_exact_value():
             abs(Fraction(float(w[i])) - exact) <= abs(exact) * Fraction(1, 2 ** 24), i
 
 
+@pytest.mark.parametrize("qtype", [Q50, Q51])
+def test_q5_every_code_at_every_position(qtype):
+    # d = 1.0; Q5_1 with m = -0.5. Every element code 16 (Q5_0: weight 0;
+    # Q5_1: 15.5) except one position, which takes every code 0..31.
+    lead = bytes([0x00, 0x3C]) + (bytes([0x00, 0xB8]) if qtype == Q51 else b"")
+    base = 16 if qtype == Q50 else 16 - 0.5
+    for pos in range(32):
+        for code in range(32):
+            codes = [16] * 32
+            codes[pos] = code
+            qh = sum(((c >> 4) & 1) << j for j, c in enumerate(codes))
+            qs = bytes((codes[j] & 0xF) | ((codes[j + 16] & 0xF) << 4) for j in range(16))
+            raw = np.frombuffer(lead + qh.to_bytes(4, "little") + qs, np.uint8).reshape(1, -1)
+            w = O.dequantize(raw, qtype, 1, 32, raw.shape[1])[0]
+            if qtype == Q50:
+                want = np.zeros(32, np.float32)
+                want[pos] = code - 16
+            else:
+                want = np.full(32, 15.5, np.float32)
+                want[pos] = code - 0.5
+            assert np.array_equal(w, want), (qtype, pos, code, base)
+
+
 def test_q8_0_every_code_at_every_position():
     for pos in range(32):
         for code in range(-128, 128):
@@ -177,6 +202,17 @@ def _decode_block_by_hand(raw, qtype):
     explicit byte/nibble loops for the codes."""
     d = Fraction(float(np.frombuffer(bytes(raw[:2]), np.float16)[0]))
     raw = [int(b) for b in raw]
+    if qtype in (Q50, Q51):
+        o = 2 if qtype == Q50 else 4
+        qh = raw[o] | (raw[o + 1] << 8) | (raw[o + 2] << 16) | (raw[o + 3] << 24)
+        q = [0] * 32
+        for j in range(16):
+            q[j] = (raw[o + 4 + j] & 0xF) | (((qh >> j) & 1) << 4)
+            q[j + 16] = (raw[o + 4 + j] >> 4) | (((qh >> (j + 16)) & 1) << 4)
+        if qtype == Q50:
+            return [d * (c - 16) for c in q]
+        m = Fraction(float(np.frombuffer(bytes(raw[2:4]), np.float16)[0]))
+        return [Fraction(float(np.float32(float(d * c + m)))) for c in q]
     if qtype == Q41:
         m = Fraction(float(np.frombuffer(bytes(raw[2:4]), np.float16)[0]))
         q = [0] * 32
@@ -195,7 +231,7 @@ def _decode_block_by_hand(raw, qtype):
     return [d * c for c in q]
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("k", [32, 64, 96])
 def test_brute_force_fraction(qtype, k):
     rng = np.random.Generator(np.random.PCG64(1234 + k + qtype))
@@ -218,7 +254,7 @@ def test_brute_force_fraction(qtype, k):
             assert abs(Fraction(s[t, r]) - se) <= Fraction(bound), (r, t)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q8])
 @pytest.mark.parametrize("x_slots", [1, 2])
 def test_matmul_id_brute_force_fraction(qtype, x_slots):
     """MUL_MAT_ID against exact rational sums over hand-decoded blocks of the
@@ -278,7 +314,7 @@ def test_zero_codes_give_zero(qtype):
     assert np.all(y == 0) and np.all(s == 0)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 def test_power_of_two_scaling_row_permutation_padding(qtype):
     W, X, rows, k, nb1 = _case(qtype)
     y, _ = O.matmul(W, qtype, rows, k, nb1, X)
@@ -296,7 +332,7 @@ def test_power_of_two_scaling_row_permutation_padding(qtype):
     assert np.array_equal(y4, y)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 def test_one_hot_activation_selects_a_column(qtype):
     W, _, rows, k, nb1 = _case(qtype)
     w = O.dequantize(W, qtype, rows, k, nb1)
@@ -307,7 +343,7 @@ def test_one_hot_activation_selects_a_column(qtype):
         assert np.array_equal(y[0], w[:, j].astype(np.float64))
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 def test_sampled_matches_full(qtype):
     W, X, rows, k, nb1 = _case(qtype)
     y, s = O.matmul(W, qtype, rows, k, nb1, X)
@@ -355,6 +391,29 @@ def test_quantise_error_bound_and_variance(qtype):
     assert 0.85 < ratio < 1.15, ratio
 
 
+@pytest.mark.parametrize("qtype", [Q50, Q51])
+def test_q5_round_trip_and_error_bound(qtype):
+    """Every code survives dequantise -> quantise, and a quantised block stays
+    within half a step (plus the binary16 rounding of d and m) of the
+    weights, with the uniform-quantiser error variance ([Arch])."""
+    codes = np.arange(32)
+    z = O.ZERO_POINT[qtype]
+    for dbits in (0x3C00, 0x2E66, 0x1234):
+        d = float(np.array([dbits], np.uint16).view(np.float16)[0])
+        w = (np.float32(d) * (codes - z).astype(np.float32)).astype(np.float64)
+        assert np.array_equal(O.quantize_codes(w, d, qtype), codes)
+    rng = np.random.default_rng(13)
+    w = rng.uniform(-1, 1, size=(64, 32 * 64)).astype(np.float32)
+    Wq = O.quantize(w, qtype)
+    wh = O.dequantize(Wq, qtype, 64, w.shape[1], Wq.shape[1]).astype(np.float64)
+    d = np.repeat(O.block_scales_and_codes(Wq, qtype, 64, w.shape[1], Wq.shape[1])[0], 32, axis=1)
+    m = np.repeat(O.block_mins(Wq, qtype, 64, w.shape[1], Wq.shape[1]), 32, axis=1)
+    err = wh - w
+    assert np.all(np.abs(err) <= d * (0.5 + 31 * 2.0 ** -10) + np.abs(m) * 2.0 ** -10 + 1e-7)
+    ratio = np.mean(err ** 2) / np.mean(d ** 2 / 12.0)
+    assert 0.85 < ratio < 1.15, ratio
+
+
 def test_q4_1_round_trip_and_error_bound():
     """Codes survive w = d q + m -> q; a min/max quantised block stays within
     half a step (plus the binary16 rounding of d and m) of the weights, with
@@ -384,6 +443,7 @@ def test_row_bytes_and_size_ratios():
     assert O.row_bytes(Q8, 4096) == 4352 and O.row_bytes(Q8, 11008) == 11696
     assert O.row_bytes(Q4, 512) == 288
     assert O.row_bytes(Q41, 4096) == 2560  # 20 bytes per 32 weights: 5 bits per weight
+    assert O.row_bytes(Q50, 4096) == 2816 and O.row_bytes(Q51, 4096) == 3072  # 5.5 and 6 bits
     # quality table of [Arch]: Q8_0 is 46.87 % smaller than F16
     assert abs((1 - O.BLOCK_BYTES[Q8] / 64) * 100 - 46.87) < 0.01
     # [Load] introduction: a 6B model is about 4 GB at 4 bits and 12 GB at 16 bits;
@@ -400,7 +460,8 @@ def test_row_bytes_and_size_ratios():
 def _pins_pass(dequant):
     """Golden blocks and the Q8_0 sign check against a candidate dequantiser."""
     try:
-        for fname, qtype in (("q4_0_block.txt", Q4), ("q4_1_block.txt", Q41), ("q8_0_block.txt", Q8)):
+        for fname, qtype in (("q4_0_block.txt", Q4), ("q4_1_block.txt", Q41), ("q5_0_block.txt", Q50),
+                             ("q5_1_block.txt", Q51), ("q8_0_block.txt", Q8)):
             g = read_golden(fname)
             raw = _hex_bytes(g["bytes"]).reshape(1, -1)
             want = np.array([float(v) for v in g["elements"]], np.float32)
@@ -463,4 +524,24 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(O, "block_mins", swapped_scale_and_min)
     assert not _pins_pass(O.dequantize), "m read from d's bytes"
     monkeypatch.setattr(O, "block_mins", orig_mins)
+    assert _pins_pass(O.dequantize)
+    # Q5: the fifth bits ignored, taken in reverse order, Q5_0 with z = 8
+    def no_fifth_bit(W, qtype, n_rows, k, nb1):
+        d, q = orig(W, qtype, n_rows, k, nb1)
+        return d, (q & 0xF if qtype in (Q50, Q51) else q)
+
+    def reversed_fifth_bits(W, qtype, n_rows, k, nb1):
+        d, q = orig(W, qtype, n_rows, k, nb1)
+        if qtype in (Q50, Q51):
+            hb = (q >> 4).reshape(n_rows, -1, 32)[:, :, ::-1].reshape(n_rows, k)
+            q = (q & 0xF) | (hb << 4)
+        return d, q
+
+    for bad in (no_fifth_bit, reversed_fifth_bits):
+        monkeypatch.setattr(O, "block_scales_and_codes", bad)
+        assert not _pins_pass(O.dequantize), bad.__name__
+    monkeypatch.setattr(O, "block_scales_and_codes", orig)
+    monkeypatch.setitem(O.ZERO_POINT, Q50, 8)
+    assert not _pins_pass(O.dequantize), "Q5_0 zero point 8"
+    monkeypatch.setitem(O.ZERO_POINT, Q50, 16)
     assert _pins_pass(O.dequantize)
