@@ -13,6 +13,8 @@ import os
 
 QMM_TYPE_Q4_0 = 2
 QMM_TYPE_Q4_1 = 3
+QMM_TYPE_Q5_0 = 6
+QMM_TYPE_Q5_1 = 7
 QMM_TYPE_Q8_0 = 8
 QMM_X_F32 = 0
 QMM_X_F16 = 1

@@ -9,6 +9,10 @@
 // and 0 for Q8_0. Q4_1, the legacy type with a minimum offset (same page,
 // the paragraph on the three quantisation families): binary16 d, binary16 m,
 // then Q4_0's 16 nibble bytes; w = d * q + m with unsigned codes 0..15.
+// Q5_0 / Q5_1 (the other legacy types; their packing is this library's
+// reading): d (and m for Q5_1), a 32-bit word whose bit j is the fifth bit
+// of element j, then 16 nibble bytes with the low four bits; codes 0..31,
+// w = d * (q - 16) for Q5_0 and d * q + m for Q5_1.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,15 +42,20 @@ typedef _Float16 half4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 template <int QT> struct Block;
 template <> struct Block<QMM_TYPE_Q4_0> { static constexpr int bytes = 18; };
 template <> struct Block<QMM_TYPE_Q4_1> { static constexpr int bytes = 20; };
+template <> struct Block<QMM_TYPE_Q5_0> { static constexpr int bytes = 22; };
+template <> struct Block<QMM_TYPE_Q5_1> { static constexpr int bytes = 24; };
 template <> struct Block<QMM_TYPE_Q8_0> { static constexpr int bytes = 34; };
 
-// nibbles: 4-bit codes in Q4_0's byte order; has_min: a binary16 m follows d;
-// codes: byte offset of the codes in the block; zero: the zero point z.
+// nibbles: (low) 4-bit codes in Q4_0's byte order; has_min: a binary16 m
+// follows d; has_qh: a 32-bit word of fifth bits follows (at byte qh);
+// codes: byte offset of the code bytes; zero: the zero point z.
 template <int QT> struct QTraits {
   static constexpr bool nibbles = QT != QMM_TYPE_Q8_0;
-  static constexpr bool has_min = QT == QMM_TYPE_Q4_1;
-  static constexpr int codes = has_min ? 4 : 2;
-  static constexpr int zero = QT == QMM_TYPE_Q4_0 ? 8 : 0;
+  static constexpr bool has_min = QT == QMM_TYPE_Q4_1 || QT == QMM_TYPE_Q5_1;
+  static constexpr bool has_qh = QT == QMM_TYPE_Q5_0 || QT == QMM_TYPE_Q5_1;
+  static constexpr int qh = has_min ? 4 : 2;
+  static constexpr int codes = 2 + (has_min ? 2 : 0) + (has_qh ? 4 : 0);
+  static constexpr int zero = QT == QMM_TYPE_Q4_0 ? 8 : QT == QMM_TYPE_Q5_0 ? 16 : 0;
 };
 
 // Calls f(std::integral_constant<int, QT>) for the run-time type id (one of
@@ -54,6 +63,8 @@ template <int QT> struct QTraits {
 template <class F> __host__ inline auto by_qtype(int qtype, F f) {
   if (qtype == QMM_TYPE_Q4_0) return f(std::integral_constant<int, QMM_TYPE_Q4_0>{});
   if (qtype == QMM_TYPE_Q4_1) return f(std::integral_constant<int, QMM_TYPE_Q4_1>{});
+  if (qtype == QMM_TYPE_Q5_0) return f(std::integral_constant<int, QMM_TYPE_Q5_0>{});
+  if (qtype == QMM_TYPE_Q5_1) return f(std::integral_constant<int, QMM_TYPE_Q5_1>{});
   return f(std::integral_constant<int, QMM_TYPE_Q8_0>{});
 }
 
@@ -103,6 +114,27 @@ __device__ __forceinline__ void q4_unpack(uint32_t qs, half2_t out[4]) {
   out[1] = bytes23_plus_1024(lo) + mlo;
   out[2] = bytes01_plus_1024(hi) * s16 + mhi;
   out[3] = bytes23_plus_1024(hi) * s16 + mhi;
+}
+
+// Four bits h (bit i for byte i) moved to bit 4 of each byte of a dword: the
+// multiply by 1 + 2^7 + 2^14 + 2^21 puts bit i at bit 8 i (among others that
+// the mask drops).
+__device__ __forceinline__ uint32_t spread4_to_bit4(uint32_t h) {
+  return ((__umul24(h, 0x00204081u)) & 0x01010101u) << 4;
+}
+
+// Four 5-bit code bytes qs[j0..j0+3] with their fifth bits from qh (bit j
+// for element j) -> eight exact fp16 values (q - Z), in q4_unpack's order:
+//   out[0..1] = elements j0..j0+3, out[2..3] = elements j0+16..j0+19.
+template <int Z>
+__device__ __forceinline__ void q5_unpack(uint32_t qs, uint32_t qh, int j0, half2_t out[4]) {
+  const half2_t mz = {(_Float16)(-1024.0f - Z), (_Float16)(-1024.0f - Z)};
+  const uint32_t lo = (qs & 0x0F0F0F0Fu) | spread4_to_bit4(__builtin_amdgcn_ubfe(qh, j0, 4));
+  const uint32_t hi = ((qs >> 4) & 0x0F0F0F0Fu) | spread4_to_bit4(__builtin_amdgcn_ubfe(qh, j0 + 16, 4));
+  out[0] = bytes01_plus_1024(lo) + mz;
+  out[1] = bytes23_plus_1024(lo) + mz;
+  out[2] = bytes01_plus_1024(hi) + mz;
+  out[3] = bytes23_plus_1024(hi) + mz;
 }
 
 // Four Q8_0 int8 codes -> four exact fp16 values: (c ^ 0x80) = c + 128 as an

@@ -1,5 +1,5 @@
-// Block decoder: out[r][i] = fp32(d) * fp32(q - z) (Q4_1: fp32(d) * q + m,
-// one rounding), bit-exact, for every row of W or for the rows an index
+// Block decoder: out[r][i] = fp32(d) * fp32(q - z) (Q4_1, Q5_1: fp32(d) * q
+// + m, one rounding), bit-exact, for every row of W or for the rows an index
 // vector selects (GET_ROWS).
 //
 // [Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3 (block
@@ -11,7 +11,7 @@
 //
 // One thread writes eight consecutive outputs (one quarter of a block), so a
 // wavefront stores 2 KiB of contiguous fp32 with 16-byte stores. HBM-bound:
-// 18, 20 or 34 bytes read and 128 bytes written per block.
+// 18 to 34 bytes read and 128 bytes written per block.
 #include "common.h"
 #include "launch.h"
 
@@ -45,11 +45,19 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
       constexpr int Z = QTraits<QT>::zero;
       const uint8_t *q = p + QTraits<QT>::codes + 8 * (part & 1);
       const int shift = (part & 2) ? 4 : 0;
+      // fifth bits of this part's elements 8 part .. 8 part + 7 (5-bit types)
+      uint32_t h5 = 0;
+      if constexpr (QTraits<QT>::has_qh) {
+        const uint8_t *qh = p + QTraits<QT>::qh;
+        h5 = ((ld_u16(qh) | (ld_u16(qh + 2) << 16)) >> (8 * part)) & 0xFFu;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t two = ld_u16(q + 2 * j);
-        v[2 * j] = d * static_cast<float>(static_cast<int>((two >> shift) & 0xF) - Z);
-        v[2 * j + 1] = d * static_cast<float>(static_cast<int>((two >> (8 + shift)) & 0xF) - Z);
+        const int c0 = static_cast<int>(((two >> shift) & 0xF) | (((h5 >> (2 * j)) & 1) << 4));
+        const int c1 = static_cast<int>(((two >> (8 + shift)) & 0xF) | (((h5 >> (2 * j + 1)) & 1) << 4));
+        v[2 * j] = d * static_cast<float>(c0 - Z);
+        v[2 * j + 1] = d * static_cast<float>(c1 - Z);
       }
       if constexpr (QTraits<QT>::has_min) {
         // d * q is exact, so adding m rounds once, as one fma would

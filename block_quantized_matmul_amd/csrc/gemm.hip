@@ -49,14 +49,17 @@ static_assert(kGemmThreads == 2 * kBM && kGemmThreads == 2 * kBN, "two staging t
 
 // d (and m, in the high half, for a type with a minimum) and the code dwords
 // of one block, with 16-bit loads.
+// (and the fifth-bit word, for a 5-bit type, in q[0] before the codes)
 template <int QT>
 __device__ __forceinline__ void load_block_u16(const uint8_t *p, uint32_t &d, uint32_t *q) {
   constexpr int nq = QTraits<QT>::nibbles ? 4 : 8;
   constexpr int c = QTraits<QT>::codes;
+  constexpr int h = QTraits<QT>::has_qh ? 1 : 0;
   d = ld_u16(p);
   if constexpr (QTraits<QT>::has_min) d |= ld_u16(p + 2) << 16;
+  if constexpr (QTraits<QT>::has_qh) q[0] = ld_u16(p + QTraits<QT>::qh) | (ld_u16(p + QTraits<QT>::qh + 2) << 16);
 #pragma unroll
-  for (int i = 0; i < nq; ++i) q[i] = ld_u16(p + c + 4 * i) | (ld_u16(p + c + 2 + 4 * i) << 16);
+  for (int i = 0; i < nq; ++i) q[h + i] = ld_u16(p + c + 4 * i) | (ld_u16(p + c + 2 + 4 * i) << 16);
 }
 
 // Decode one block to 32 fp16 weights fl16(d * (q - z)) (Q4_1: fl16(d q + m),
@@ -64,7 +67,8 @@ __device__ __forceinline__ void load_block_u16(const uint8_t *p, uint32_t &d, ui
 // store them as chunks c0 .. c0 + 3 of LDS tile row `row`. d_bits holds d in
 // its low half and, for Q4_1, m in its high half.
 template <int QT>
-__device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0, uint32_t d_bits, const uint32_t *q) {
+__device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0, uint32_t d_bits, const uint32_t *q,
+                                                uint32_t qh = 0) {
   const _Float16 dh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d_bits));
   const half2_t d2 = {dh, dh};
   half2_t h[16];
@@ -77,6 +81,23 @@ __device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0,
       h[2 * i + 1] = u[1] * d2;  // 4i+2, 4i+3
       h[8 + 2 * i] = u[2] * d2;  // 16+4i, 17+4i
       h[9 + 2 * i] = u[3] * d2;  // 18+4i, 19+4i
+    }
+  } else if constexpr (QTraits<QT>::has_qh) {
+    // 5-bit codes: fl16(d (q - z)), or fl16(d q + m) with one fp16 fma
+    const _Float16 mh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d_bits >> 16));
+    const half2_t m2 = {mh, mh};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half2_t u[4];
+      q5_unpack<QTraits<QT>::zero>(q[i], qh, 4 * i, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int at = e < 2 ? 2 * i + e : 8 + 2 * i + (e - 2);
+        if constexpr (QTraits<QT>::has_min)
+          h[at] = __builtin_elementwise_fma(u[e], d2, m2);
+        else
+          h[at] = u[e] * d2;
+      }
     }
   } else if constexpr (QT == QMM_TYPE_Q4_1) {
     const _Float16 mh = __builtin_bit_cast(_Float16, static_cast<uint16_t>(d_bits >> 16));
@@ -114,8 +135,10 @@ __device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0,
 // in flight (any arithmetic on them right after the load would wait for it).
 // Q4_1 blocks (20 bytes) are dword-aligned in a pair: both halves are one
 // whole block, d|m in w[0] and the codes in w[1..4].
+// 5-bit types add the fifth-bit word: w[0] scale (and m), w[1] fifth bits
+// (Q5_0 half 0: shifted by 16 bits like everything else), w[2..5] codes.
 template <int QT> struct HalfRaw {
-  static constexpr int nq = QTraits<QT>::nibbles ? 4 : 8;
+  static constexpr int nq = (QTraits<QT>::nibbles ? 4 : 8) + (QTraits<QT>::has_qh ? 1 : 0);
   uint32_t w[nq + 1];
 };
 
@@ -123,15 +146,21 @@ template <int QT>
 __device__ __forceinline__ HalfRaw<QT> load_half_pair(const uint8_t *rp, int st, int h) {
   constexpr int nq = HalfRaw<QT>::nq;
   constexpr int BB = Block<QT>::bytes;
-  constexpr int h1 = QTraits<QT>::has_min ? BB : BB - 2;  // half 1 starts here, 4-byte aligned
+  constexpr int h1 = BB % 4 == 0 ? BB : BB - 2;  // half 1 starts here, 4-byte aligned
   const uint8_t *p = rp + static_cast<int64_t>(st) * (2 * BB) + (h ? h1 : 0);
   HalfRaw<QT> r;
+  constexpr int NW = nq + 1;
 #pragma unroll
-  for (int i = 0; i + 4 <= nq + 1; i += 4) {
+  for (int i = 0; i + 4 <= NW; i += 4) {
     const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(p + 4 * i);
     r.w[i] = v.x; r.w[i + 1] = v.y; r.w[i + 2] = v.z; r.w[i + 3] = v.w;
   }
-  r.w[nq] = ld_u32(p + 4 * nq);
+  if constexpr (NW % 4 == 2) {
+    const u32x2_t v = ld_u32x2(p + 4 * (NW - 2));
+    r.w[NW - 2] = v.x; r.w[NW - 1] = v.y;
+  } else if constexpr (NW % 4 == 1) {
+    r.w[NW - 1] = ld_u32(p + 4 * (NW - 1));
+  }
   return r;
 }
 
@@ -145,7 +174,7 @@ __device__ __forceinline__ HalfRaw<QT> load_half_u16(const uint8_t *rp, int blk,
   if (blk < nblk) {
     uint32_t d;
     load_block_u16<QT>(rp + static_cast<int64_t>(blk) * Block<QT>::bytes, d, r.w + 1);
-    r.w[0] = QTraits<QT>::has_min ? d : d << 16;
+    r.w[0] = QTraits<QT>::has_min ? d : d << 16;  // the layout of half 1
   } else {
 #pragma unroll
     for (int i = 0; i <= nq; ++i) r.w[i] = 0;
@@ -163,13 +192,19 @@ __device__ __forceinline__ void store_half(_Float16 *tile, int row, int c0, cons
   if constexpr (QTraits<QT>::has_min) {  // one layout for both halves
 #pragma unroll
     for (int i = 0; i < nq; ++i) q[i] = r.w[i + 1];
-    store_block_f16<QT>(tile, row, c0, r.w[0], q);
+    if constexpr (QTraits<QT>::has_qh)
+      store_block_f16<QT>(tile, row, c0, r.w[0], q + 1, q[0]);
+    else
+      store_block_f16<QT>(tile, row, c0, r.w[0], q);
     return;
   }
   const uint32_t d = first_layout ? (r.w[0] & 0xFFFFu) : (r.w[0] >> 16);
 #pragma unroll
   for (int i = 0; i < nq; ++i) q[i] = first_layout ? shift16(r.w[i], r.w[i + 1]) : r.w[i + 1];
-  store_block_f16<QT>(tile, row, c0, d, q);
+  if constexpr (QTraits<QT>::has_qh)
+    store_block_f16<QT>(tile, row, c0, d, q + 1, q[0]);
+  else
+    store_block_f16<QT>(tile, row, c0, d, q);
 }
 
 // Activations of one stage (128 tokens x 64 k) as 16-byte pieces spread so

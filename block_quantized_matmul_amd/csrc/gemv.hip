@@ -30,7 +30,7 @@
 // of lane l.
 //
 // Weight access (row start 4-byte aligned): a unit is a pair of blocks (36
-// bytes Q4_0, 40 bytes Q4_1, 68 bytes Q8_0). The four lanes of a row load overlapping dword
+// bytes Q4_0, 40 Q4_1, 44 Q5_0, 48 Q5_1, 68 Q8_0). The four lanes of a row load overlapping dword
 // windows that together cover the pair once; the two scales are forwarded
 // from the lanes that loaded them with ds_bpermute. Rows whose start is only
 // 2-byte aligned take 16-bit loads, one block per unit.
@@ -51,10 +51,18 @@ template <> struct GemvRaw<QMM_TYPE_Q8_0, true> { uint32_t a0, a1, a2; u32x2_t b
 // Q4_1 pair (40 bytes, both blocks dword-aligned): dwords g, g + 1 (even
 // block: d|m in dword 0, codes in dwords 1..4) and 5 + g, 6 + g (odd block).
 template <> struct GemvRaw<QMM_TYPE_Q4_1, true> { u32x2_t a, b; };
+// Q5_0 pair (44 bytes; block 1 at byte 22): dwords 0-1 (d, fifth bits of
+// block 0), 1 + g, 2 + g (its codes start at byte 6), 5-6 (d in the high
+// half of dword 5, fifth bits in dword 6) and 7 + g (block 1's codes).
+template <> struct GemvRaw<QMM_TYPE_Q5_0, true> { u32x2_t h0, c0, h1; uint32_t c1; };
+// Q5_1 pair (48 bytes): dwords 0-1 (d|m, fifth bits), 2 + g, 6-7, 8 + g.
+template <> struct GemvRaw<QMM_TYPE_Q5_1, true> { u32x2_t h0, h1; uint32_t c0, c1; };
 // Single block, 16-bit loads: scale bits and the lane's code dwords.
 template <> struct GemvRaw<QMM_TYPE_Q4_0, false> { uint32_t d, q; };
 template <> struct GemvRaw<QMM_TYPE_Q8_0, false> { uint32_t d, q0, q1; };
 template <> struct GemvRaw<QMM_TYPE_Q4_1, false> { uint32_t d, q; };  // d = d | m << 16
+template <> struct GemvRaw<QMM_TYPE_Q5_0, false> { uint32_t d, h, q; };
+template <> struct GemvRaw<QMM_TYPE_Q5_1, false> { uint32_t d, h, q; };  // d = d | m << 16
 
 template <int QT, bool ALIGN4>
 __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int u, int g) {
@@ -67,6 +75,16 @@ __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int 
     } else if constexpr (QT == QMM_TYPE_Q4_1) {
       r.a = ld_u32x2(p + 4 * g);
       r.b = ld_u32x2(p + 20 + 4 * g);
+    } else if constexpr (QT == QMM_TYPE_Q5_0) {
+      r.h0 = ld_u32x2(p);
+      r.c0 = ld_u32x2(p + 4 + 4 * g);
+      r.h1 = ld_u32x2(p + 20);
+      r.c1 = ld_u32(p + 28 + 4 * g);
+    } else if constexpr (QT == QMM_TYPE_Q5_1) {
+      r.h0 = ld_u32x2(p);
+      r.c0 = ld_u32(p + 8 + 4 * g);
+      r.h1 = ld_u32x2(p + 24);
+      r.c1 = ld_u32(p + 32 + 4 * g);
     } else {
       const u32x3_a4 a = *reinterpret_cast<const u32x3_a4 *>(p + 8 * g);
       r.a0 = a.x;
@@ -82,6 +100,11 @@ __device__ __forceinline__ GemvRaw<QT, ALIGN4> gemv_load(const uint8_t *rp, int 
     } else if constexpr (QT == QMM_TYPE_Q4_1) {
       r.d |= ld_u16(p + 2) << 16;
       r.q = ld_u16(p + 4 + 4 * g) | (ld_u16(p + 6 + 4 * g) << 16);
+    } else if constexpr (QTraits<QT>::has_qh) {
+      constexpr int o = QTraits<QT>::qh, c = QTraits<QT>::codes;
+      if constexpr (QTraits<QT>::has_min) r.d |= ld_u16(p + 2) << 16;
+      r.h = ld_u16(p + o) | (ld_u16(p + o + 2) << 16);
+      r.q = ld_u16(p + c + 4 * g) | (ld_u16(p + c + 2 + 4 * g) << 16);
     } else {
       r.q0 = ld_u16(p + 2 + 8 * g) | (ld_u16(p + 4 + 8 * g) << 16);
       r.q1 = ld_u16(p + 6 + 8 * g) | (ld_u16(p + 8 + 8 * g) << 16);
@@ -112,6 +135,13 @@ __device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4
       const uint32_t dd = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * r16, static_cast<int>(r.b.x)));
       gemv_block_min<NT>(acc, xe, gemv_codes<QT>(r.a.y, 0), de);
       gemv_block_min<NT>(acc, xo, gemv_codes<QT>(r.b.y, 0), dd);
+    } else if constexpr (QT == QMM_TYPE_Q5_0) {
+      gemv_block<NT>(acc, xe, gemv_codes5<QT>(shift16(r.c0.x, r.c0.y), shift16(r.h0.x, r.h0.y), 4 * g),
+                     r.h0.x & 0xFFFFu);
+      gemv_block<NT>(acc, xo, gemv_codes5<QT>(r.c1, r.h1.y, 4 * g), r.h1.x >> 16);
+    } else if constexpr (QT == QMM_TYPE_Q5_1) {
+      gemv_block_min<NT>(acc, xe, gemv_codes5<QT>(r.c0, r.h0.y, 4 * g), r.h0.x);
+      gemv_block_min<NT>(acc, xo, gemv_codes5<QT>(r.c1, r.h1.y, 4 * g), r.h1.x);
     } else {
       // Even block: scale = low half of dword 0 (lane g = 0's a0); odd block
       // starts at byte 34: scale = high half of dword 8 (lane g = 3's a2).
@@ -126,6 +156,8 @@ __device__ __forceinline__ void gemv_unit(float acc[4], const GemvRaw<QT, ALIGN4
       gemv_block<NT>(acc, x, gemv_codes<QT>(r.q, 0), r.d);
     else if constexpr (QT == QMM_TYPE_Q4_1)
       gemv_block_min<NT>(acc, x, gemv_codes<QT>(r.q, 0), r.d);
+    else if constexpr (QTraits<QT>::has_qh)
+      gemv_any_block<QT, NT>(acc, x, gemv_codes5<QT>(r.q, r.h, 4 * g), r.d);
     else
       gemv_block<NT>(acc, x, gemv_codes<QT>(r.q0, r.q1), r.d);
   }

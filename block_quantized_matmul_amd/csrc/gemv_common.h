@@ -33,6 +33,13 @@ template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q4_1>(uint32_
   q4_unpack<0>(q0, h);
   return make_half8(h[0], h[1], h[2], h[3]);
 }
+// B-operand of a 5-bit type: the lane's code bytes qs[j0..j0+3] (elements
+// j0..j0+3 and j0+16..j0+19) with their fifth bits from qh.
+template <int QT> __device__ __forceinline__ half8_t gemv_codes5(uint32_t qs, uint32_t qh, int j0) {
+  half2_t h[4];
+  q5_unpack<QTraits<QT>::zero>(qs, qh, j0, h);
+  return make_half8(h[0], h[1], h[2], h[3]);
+}
 template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q8_0>(uint32_t q0, uint32_t q1) {
   half2_t lo[2], hi[2];
   q8_unpack(q0, lo);
@@ -43,7 +50,8 @@ template <> __device__ __forceinline__ half8_t gemv_codes<QMM_TYPE_Q8_0>(uint32_
 // Staged activations: for chunk-relative block bb, lane group g and token t,
 // the 8 fp16 values of the A operand live at xs[(4 bb + g) * NT + t], in the
 // element order the B operand uses:
-//   Q4_0, Q4_1: elements 4g..4g+3 then 16+4g..16+4g+3;  Q8_0: elements 8g..8g+7.
+//   Q4_0, Q4_1, Q5_0, Q5_1: elements 4g..4g+3 then 16+4g..16+4g+3;
+//   Q8_0: elements 8g..8g+7.
 template <int QT, int NT, bool XF16, int THREADS>
 __device__ __forceinline__ void gemv_stage_x(half8_t *xs, const void *X, int n_tokens, int k, int b_lo, int b_hi) {
   const int nb = b_hi - b_lo;

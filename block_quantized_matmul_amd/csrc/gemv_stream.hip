@@ -13,8 +13,9 @@
 //    (row groups of its largest matrix) x (matrices), and the hardware
 //    balances the workgroups across the CUs. Its 8 or 16 wavefronts (see
 //    k_split_for) split k into
-//    contiguous ranges of quads (8 blocks: 144 bytes Q4_0, 160 Q4_1, 272
-//    Q8_0 per row, a whole number of 16-byte chunks) and stream them
+//    contiguous ranges of quads (8 blocks: 144 bytes Q4_0, 160 Q4_1, 176
+//    Q5_0, 192 Q5_1, 272 Q8_0 per row, a whole number of 16-byte chunks) and
+//    stream them
 //    independently; they meet once, at the end, to add their partial sums in
 //    a fixed order through LDS (no atomics: results are reproducible, and
 //    identical to the general kernel's, which splits k the same way).
@@ -25,8 +26,8 @@
 //    and then consumes them in order (the wait counter is exact).
 //  * Consuming a stage copies it into the wavefront's private LDS area (the
 //    activations converted to fp16 in MFMA operand order) and runs 8 MFMAs
-//    (16 for Q4_1, whose second MFMA per block sums the activations for the
-//    minimum term).
+//    (16 for Q4_1 and Q5_1, whose second MFMA per block sums the activations
+//    for the minimum term).
 // Several matrices per launch remove the fixed per-launch cost that
 // dominates decode-sized matmuls (a launch plus its ramp costs about as much
 // as streaming ten megabytes).
@@ -57,11 +58,12 @@ template <int QT, int NT> struct RCfg {
   // kernel then fits 4 wavefronts per SIMD, i.e. 2 workgroups per CU)
   static constexpr int stage_vgprs = 4 * w_loads + NT * 4;
   static constexpr int depth = (64 / stage_vgprs) < 1 ? 1 : (64 / stage_vgprs > 6 ? 6 : 64 / stage_vgprs);
-  // With 8 wavefronts per workgroup (launches larger than the GPU), Q4_0
-  // with one or two tokens takes rounds of 2 stages (the whole share for
-  // k = 4096) so the kernel fits in ~60 VGPRs and 6-8 wavefronts per SIMD:
-  // more workgroups per CU overlap one another's loads and compute.
-  static constexpr bool lean = QTraits<QT>::nibbles && NT <= 2;
+  // With 8 wavefronts per workgroup (launches larger than the GPU), the
+  // nibble types (Q5_1 aside, whose decode needs more registers) with one or
+  // two tokens take rounds of 2 stages (the whole share for k = 4096) so the
+  // kernel fits in ~60 VGPRs and 6-8 wavefronts per SIMD: more workgroups
+  // per CU overlap one another's loads and compute.
+  static constexpr bool lean = QTraits<QT>::nibbles && !(QTraits<QT>::has_qh && QTraits<QT>::has_min) && NT <= 2;
   static constexpr int depth_large = lean ? 2 : depth;
   static constexpr int waves_per_simd_large = !lean ? 4 : (NT == 1 ? 8 : 6);
   static constexpr int w_lds = 16 * row_stride;
@@ -197,6 +199,18 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
       const uint32_t a = ld(4 + 4 * g), b = ld(24 + 4 * g), dm0 = ld(0), dm1 = ld(20);
       gemv_block_min<NT>(acc, xe, gemv_codes<QT>(a, 0), dm0);
       gemv_block_min<NT>(acc, xo, gemv_codes<QT>(b, 0), dm1);
+    } else if constexpr (QT == QMM_TYPE_Q5_0) {
+      // blocks at bytes 0 and 22: d, fifth-bit word, codes (block 0's start
+      // 2 bytes into a dword, block 1's are dword-aligned)
+      const uint32_t w0 = ld(0), w1 = ld(4), a0 = ld(4 + 4 * g), a1 = ld(8 + 4 * g);
+      const uint32_t w5 = ld(20), h1 = ld(24), b = ld(28 + 4 * g);
+      gemv_block<NT>(acc, xe, gemv_codes5<QT>(shift16(a0, a1), shift16(w0, w1), 4 * g), w0 & 0xFFFFu);
+      gemv_block<NT>(acc, xo, gemv_codes5<QT>(b, h1, 4 * g), w5 >> 16);
+    } else if constexpr (QT == QMM_TYPE_Q5_1) {
+      // blocks at bytes 0 and 24: d|m, fifth-bit word, 4 code dwords
+      const uint32_t dm0 = ld(0), h0 = ld(4), a = ld(8 + 4 * g), dm1 = ld(24), h1 = ld(28), b = ld(32 + 4 * g);
+      gemv_block_min<NT>(acc, xe, gemv_codes5<QT>(a, h0, 4 * g), dm0);
+      gemv_block_min<NT>(acc, xo, gemv_codes5<QT>(b, h1, 4 * g), dm1);
     } else {
       const uint32_t a0 = ld(8 * g), a1 = ld(8 * g + 4), a2 = ld(8 * g + 8);
       const uint32_t b0 = ld(36 + 8 * g), b1 = ld(40 + 8 * g), d0 = ld(0), d1 = ld(32);

@@ -28,6 +28,8 @@ int block_bytes(int type) {
   switch (type) {
     case QMM_TYPE_Q4_0: return 18;
     case QMM_TYPE_Q4_1: return 20;
+    case QMM_TYPE_Q5_0: return 22;
+    case QMM_TYPE_Q5_1: return 24;
     case QMM_TYPE_Q8_0: return 34;
     default: return 0;
   }
@@ -54,7 +56,15 @@ int check_weights(const void *W, int type, int64_t n_rows, int64_t k, int64_t nb
   return QMM_OK;
 }
 
-const char *type_name(int t) { return t == QMM_TYPE_Q4_0 ? "q4_0" : t == QMM_TYPE_Q4_1 ? "q4_1" : "q8_0"; }
+const char *type_name(int t) {
+  switch (t) {
+    case QMM_TYPE_Q4_0: return "q4_0";
+    case QMM_TYPE_Q4_1: return "q4_1";
+    case QMM_TYPE_Q5_0: return "q5_0";
+    case QMM_TYPE_Q5_1: return "q5_1";
+    default: return "q8_0";
+  }
+}
 
 int status_of(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 

@@ -36,7 +36,12 @@
  *      element j + 16 the high nibble; weight = d * (q - 8). Q4_1 block = 20
  *      bytes: binary16 d, binary16 m, then 16 bytes qs in Q4_0's nibble
  *      order; weight = d * q + m (unsigned codes; the layout of d, m and qs
- *      is this library's reading of the minimum-offset type). Q8_0 block = 34
+ *      is this library's reading of the minimum-offset type). Q5_0 block = 22
+ *      bytes: binary16 d, a little-endian 32-bit word whose bit j is the
+ *      fifth bit of element j, then 16 bytes qs with the low four bits in
+ *      Q4_0's nibble order; weight = d * (q - 16), codes 0..31. Q5_1 block =
+ *      24 bytes: d, m, the fifth-bit word, qs; weight = d * q + m (the
+ *      packing of both is this library's reading: the pages give none). Q8_0 block = 34
  *      bytes: binary16 d, then 32 int8 codes; weight = d * q. Bytes between
  *      the last block of a row and the next row (padding) are never read.
  *   X  activations [n_tokens][k], k contiguous (fp32, or fp16 for *_x16).
@@ -55,11 +60,11 @@
  * HIP rejects returns QMM_ERR_HIP. qmm_status_string() names every code.
  *
  * Numerics: dequantised weights are exact (fp32 d * (q - z) is exact for every
- * finite binary16 d; Q4_1's d * q + m is that exact product plus m, rounded
- * once to fp32). The matmul accumulates in fp32. Decode-sized calls
+ * finite binary16 d; the d * q + m of Q4_1 / Q5_1 is that exact product plus
+ * m, rounded once to fp32). The matmul accumulates in fp32. Decode-sized calls
  * (n_tokens <= QMM_GEMV_MAX_TOKENS) round activations to fp16 and multiply
- * them by the exact integer codes, applying d in fp32 once per block (Q4_1:
- * plus m times the block's sum of the fp16 activations); larger
+ * them by the exact integer codes, applying d in fp32 once per block (Q4_1,
+ * Q5_1: plus m times the block's sum of the fp16 activations); larger
  * calls round both the dequantised weights and the activations to fp16 for
  * the matrix cores. Every element satisfies
  *   |y - y_exact| <= 1e-3 * sum_i |w_i x_i| + 1e-5
@@ -80,6 +85,8 @@ extern "C" {
 /* Weight types; the values follow ggml's type enumeration. */
 #define QMM_TYPE_Q4_0 2
 #define QMM_TYPE_Q4_1 3
+#define QMM_TYPE_Q5_0 6
+#define QMM_TYPE_Q5_1 7
 #define QMM_TYPE_Q8_0 8
 
 /* Activation element types for qmm_matmul_path. */
@@ -109,7 +116,7 @@ extern "C" {
  * [Load] section 第六步, [Arch] section 权重装载).
  *   W                device pointer, 2-byte aligned, n_rows rows of
  *                    row_stride_bytes bytes (see layout above)
- *   ggml_type        QMM_TYPE_Q4_0, QMM_TYPE_Q4_1 or QMM_TYPE_Q8_0
+ *   ggml_type        QMM_TYPE_Q4_0, _Q4_1, _Q5_0, _Q5_1 or _Q8_0
  *   n_rows           ne1 of W (>= 0)
  *   k                ne0 of W and of X; positive multiple of 32
  *   row_stride_bytes nb1 of W; even and >= qmm_row_bytes(ggml_type, k)

@@ -59,7 +59,8 @@ def test_row_bytes_and_supports(L):
     assert L.qmm_row_bytes(Q8, 32) == 34
     assert L.qmm_row_bytes(qmm.QMM_TYPE_Q4_1, 4096) == 2560
     assert L.qmm_supports(qmm.QMM_TYPE_Q4_1, 64, 40) == 1 and L.qmm_supports(qmm.QMM_TYPE_Q4_1, 64, 38) == 0
-    for bad_type in (0, 1, 4, 6, 7, 9, 12):
+    assert L.qmm_row_bytes(qmm.QMM_TYPE_Q5_0, 4096) == 2816 and L.qmm_row_bytes(qmm.QMM_TYPE_Q5_1, 4096) == 3072
+    for bad_type in (0, 1, 4, 5, 9, 12):
         assert L.qmm_row_bytes(bad_type, 4096) == qmm.QMM_ERR_TYPE
     for bad_k in (0, -32, 48, 1 << 31):
         assert L.qmm_row_bytes(Q4, bad_k) == qmm.QMM_ERR_SHAPE
@@ -69,7 +70,7 @@ def test_row_bytes_and_supports(L):
     assert L.qmm_supports(Q4, 4096, 2303) == 0
     assert L.qmm_supports(Q4, 4096, 2302) == 0
     assert L.qmm_supports(Q8, 48, 100) == 0
-    assert L.qmm_supports(7, 4096, 4096) == 0
+    assert L.qmm_supports(5, 4096, 4096) == 0
 
 
 def test_status_strings(L):
@@ -153,7 +154,7 @@ def test_matmul_id_validation(L):
     assert _mid(L, X=NULL) == qmm.QMM_ERR_NULL
     assert _mid(L, ids=NULL) == qmm.QMM_ERR_NULL
     assert _mid(L, Y=NULL) == qmm.QMM_ERR_NULL
-    assert _mid(L, t=7) == qmm.QMM_ERR_TYPE
+    assert _mid(L, t=5) == qmm.QMM_ERR_TYPE
     assert _mid(L, k=48) == qmm.QMM_ERR_SHAPE
     assert _mid(L, ne=-1) == qmm.QMM_ERR_SHAPE
     assert _mid(L, n_ids=-1, xs=1) == qmm.QMM_ERR_SHAPE

@@ -9,6 +9,7 @@ from gpu_util import assert_bitwise, run_dequant, say
 
 pytestmark = pytest.mark.gpu
 Q4, Q41, Q8 = O.TYPE_Q4_0, O.TYPE_Q4_1, O.TYPE_Q8_0
+Q50, Q51 = O.TYPE_Q5_0, O.TYPE_Q5_1
 
 
 def _check(Wnp, qtype, k, offset=0, what=""):
@@ -69,7 +70,7 @@ def test_config_weights(cfg):
         _check(case.weights(), case.qtype, case.k, what=case.name)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("k,extra,offset", [(32, 0, 0), (96, 0, 0), (96, 2, 2), (160, 6, 0), (512, 30, 2),
                                             (4096, 256, 0)])
 def test_strides_alignment_and_ragged(qtype, k, extra, offset):
@@ -84,7 +85,7 @@ def test_strides_alignment_and_ragged(qtype, k, extra, offset):
         _check(W2, qtype, k, offset, what=f"k={k} pad={extra} refilled")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 def test_dword_aligned_output(qtype):
     """out only 4-byte aligned (the weakest alignment the boundary accepts)."""
     import torch
@@ -104,7 +105,7 @@ def test_dword_aligned_output(qtype):
     assert_bitwise(out.cpu().numpy(), O.dequantize(W, qtype, rows, k, nb1), "dword-aligned out")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("rows,k,extra,offset", [(300, 256, 0, 0), (77, 96, 6, 2), (2000, 4096, 256, 0)])
 def test_get_rows(qtype, rows, k, extra, offset):
     """GET_ROWS bit-exact against the oracle: repeated indices, the first and

@@ -14,6 +14,7 @@ from gpu_util import assert_bitwise, assert_close_to_oracle, run_matmul, say
 
 pytestmark = pytest.mark.gpu
 Q4, Q41, Q8 = O.TYPE_Q4_0, O.TYPE_Q4_1, O.TYPE_Q8_0
+Q50, Q51 = O.TYPE_Q5_0, O.TYPE_Q5_1
 GEMV, GEMM, AUTO = qmm.QMM_PATH_GEMV, qmm.QMM_PATH_GEMM, qmm.QMM_PATH_AUTO
 
 
@@ -33,7 +34,7 @@ def _parity(W, qtype, k, X, path, offset=0, what=""):
 
 
 # ------------------------------------------------------------ small shapes, every kernel variant
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8])
 def test_gemv_ragged(qtype, xdt, n):
@@ -44,7 +45,7 @@ def test_gemv_ragged(qtype, xdt, n):
         _parity(W, qtype, k, X, GEMV, offset, f"gemv rows={rows} k={k}")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("n", [1, 9, 16, 37, 128, 200])
 def test_gemm_ragged(qtype, xdt, n):
@@ -54,7 +55,7 @@ def test_gemm_ragged(qtype, xdt, n):
         _parity(W, qtype, k, X, GEMM, offset, f"gemm rows={rows} k={k}")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 def test_gemm_full_size_tiles(qtype):
     """More 128-row tiles than CUs: the 128-row tile variant (the ragged
     tests above are small enough to take the 64-row one), with ragged rows
@@ -65,7 +66,7 @@ def test_gemm_full_size_tiles(qtype):
     _parity(W, qtype, k, X, GEMM, 0, "gemm 128-row tiles")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 def test_dispatch_and_cross_check(qtype):
     """AUTO picks GEMV up to 8 tokens; for n = 1..16 both kernels agree with
     the oracle (and therefore with each other) on the same inputs."""
@@ -90,7 +91,7 @@ def _dword_aligned_copy(a: np.ndarray, dtype) -> tuple:
     return flat, view.view(a.shape)
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("path,n", [(GEMV, 1), (GEMV, 8), (GEMM, 40)])
 def test_dword_aligned_activations_and_outputs(qtype, xdt, path, n):
@@ -111,7 +112,7 @@ def test_dword_aligned_activations_and_outputs(qtype, xdt, path, n):
 
 
 # ------------------------------------------------------------ closed-form invariants
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("path,n", [(GEMV, 1), (GEMV, 8), (GEMM, 24)])
 def test_one_hot_activation(qtype, path, n):
     """x = e_j: every other product is an exact zero, so y equals the
@@ -135,7 +136,7 @@ def test_one_hot_activation(qtype, path, n):
     assert_bitwise(Y + np.float32(0.0), w + np.float32(0.0), "one-hot")
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("path,n", [(GEMV, 3), (GEMM, 40)])
 def test_zero_codes_scaling_permutation_padding_determinism(qtype, path, n):
     rows, k = 150, 1024
@@ -161,7 +162,9 @@ def test_zero_codes_scaling_permutation_padding_determinism(qtype, path, n):
     Wz = W.copy().reshape(rows, -1)
     bpb = O.BLOCK_BYTES[qtype]
     blk = Wz[:, :dense].reshape(rows, -1, bpb)
-    blk[:, :, 2:] = 0x88 if qtype == Q4 else 0
+    blk[:, :, 2:] = 0x88 if qtype == Q4 else 0  # codes equal to the zero point (and m = 0)
+    if qtype == Q50:
+        blk[:, :, 2:6] = 0xFF  # fifth bits set: codes 16
     Wz[:, :dense] = blk.reshape(rows, dense)
     yz = run_matmul(Wz, qtype, k, X, path)
     assert np.all(yz == 0.0)

@@ -13,6 +13,7 @@ from gpu_util import dev, say
 
 pytestmark = pytest.mark.gpu
 Q4, Q41, Q8 = O.TYPE_Q4_0, O.TYPE_Q4_1, O.TYPE_Q8_0
+Q50, Q51 = O.TYPE_Q5_0, O.TYPE_Q5_1
 
 
 def _stack(qtype, n_experts, rows, k, nb1, nb2, rng):
@@ -42,7 +43,7 @@ def _check(Y, y_ref, s, what):
     assert ok.all(), f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance"
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("layout", ["stream", "general"])
 @pytest.mark.parametrize("shared_x", [False, True])
 @pytest.mark.parametrize("n_tokens", [1, 3, 9])
@@ -126,7 +127,7 @@ def _skewed_ids(rng, n_tokens, n_ids, n_experts):
     return ids
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q41, Q8])
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("layout", ["aligned", "padded"])
 @pytest.mark.parametrize("shared_x", [False, True])
 @pytest.mark.parametrize("n_tokens,n_experts", [(9, 4), (300, 8)])
