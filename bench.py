@@ -90,7 +90,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-get-rows", action="store_true", help="skip the GET_ROWS (token-embedding gather) line")
     ap.add_argument("--no-matmul-id", action="store_true", help="skip the MUL_MAT_ID (routed expert FFN) lines")
-    ap.add_argument("--no-q4-1", action="store_true", help="skip the Q4_1 lines")
+    ap.add_argument("--no-other-types", action="store_true", help="skip the Q4_1 / Q5_0 / Q5_1 lines")
     ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
@@ -272,15 +272,16 @@ def time_get_rows(torch, qmm, synth, with_oracle=False):
     return res
 
 
-# ---------------------------------------------------------------- Q4_1
+# ---------------------------------------------------------------- other legacy types
 
-def time_q4_1(torch, qmm, synth, with_oracle=False):
-    """Q4_1 (the minimum-offset legacy type) on the 11008x4096 FFN projection:
-    decode (1 fp32 token) and prefill (2048 fp16 tokens), back-to-back launches
-    in a graph over >= 1.1 GiB of weight copies, so weights come from HBM."""
+def time_type(torch, qmm, synth, qt, with_oracle=False):
+    """Another legacy type (Q4_1, Q5_0, Q5_1) on the 11008x4096 FFN
+    projection: decode (1 fp32 token) and prefill (2048 fp16 tokens),
+    back-to-back launches in a graph over >= 1.1 GiB of weight copies, so
+    weights come from HBM."""
     import numpy as np
-    rows, k, qt = 11008, 4096, synth.TYPE_Q4_1
-    rng = np.random.Generator(np.random.PCG64(4141))
+    rows, k = 11008, 4096
+    rng = np.random.Generator(np.random.PCG64(4100 + qt))
     Wh = synth.make_weights(qt, rows, k, None, rng)
     W0 = torch.from_numpy(Wh).cuda()
     copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
@@ -298,7 +299,7 @@ def time_q4_1(torch, qmm, synth, with_oracle=False):
     us2 = _graph_time(torch, lambda: [qmm.qmm_matmul_x16(Ws[i % copies], qt, k, X2, Y=Y2) for i in range(copies)],
                       copies)
     tfl = 2 * T * rows * k / (us2 * 1e-6) / 1e12
-    res = {"workload": f"{rows}x{k} Q4_1",
+    res = {"workload": f"{rows}x{k} {synth.TYPE_NAMES[qt].upper()}",
            "decode": {"tokens": 1, "us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": byts,
                       "GB_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                       "kernel": "gemv_stream_kernel", "bound": "hbm"},
@@ -635,8 +636,9 @@ def main():
         out["get_rows"] = time_get_rows(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if not args.no_matmul_id:
         out["matmul_id"] = time_matmul_id(torch, qmm, synth, with_oracle=bool(cpu_layers))
-    if not args.no_q4_1:
-        out["q4_1"] = time_q4_1(torch, qmm, synth, with_oracle=bool(cpu_layers))
+    if not args.no_other_types:
+        for qt in (synth.TYPE_Q4_1, synth.TYPE_Q5_0, synth.TYPE_Q5_1):
+            out[synth.TYPE_NAMES[qt]] = time_type(torch, qmm, synth, qt, with_oracle=bool(cpu_layers))
     if cpu_layers:
         import oracle.qmm_oracle as O
         log("timing the CPU oracle on a sample")
