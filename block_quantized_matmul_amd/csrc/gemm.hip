@@ -13,10 +13,10 @@
 // v_mfma_f32_16x16x32_f16 with fp32 accumulation. A 256-thread workgroup owns
 // a 128-row x 128-token output tile; its four wavefronts each compute 64 x 64
 // as 4 x 4 MFMA tiles. k advances in stages of 64 (two blocks):
-//  * staging: each thread loads half of one row's two blocks (5 or 9
+//  * staging: each thread loads half of one row's two blocks (5, 6 or 9
 //    dwords inside the pair) and half of one token's 64 activations, two
-//    stages ahead of their use, decodes the blocks to fp16 d * (q - z) (exact
-//    integer code, one fp16 rounding of the product) and stores weights and
+//    stages ahead of their use, decodes the blocks to fp16 d * (q - z) or
+//    d * q + m (exact integer code, one fp16 rounding) and stores weights and
 //    activations into LDS;
 //  * LDS is double-buffered, so the stores of stage s + 1 (and their decode
 //    arithmetic) overlap the MFMAs of stage s, with one LDS-only barrier per
@@ -26,7 +26,8 @@
 //  * within a stage the MFMAs are interleaved with the decode, the LDS
 //    stores and the loads of the next stages (interleave_stage);
 //  * two workgroups fit a CU (64 KiB of LDS each), so one's loads and
-//    barriers overlap the other's matrix work.
+//    barriers overlap the other's matrix work; launches with few tiles use
+//    64-row tiles (three workgroups per CU).
 // Weights never exist in dequantised form outside LDS.
 #include "common.h"
 #include "launch.h"
@@ -133,10 +134,10 @@ __device__ __forceinline__ void store_block_f16(_Float16 *tile, int row, int c0,
 // (scale = high half of w[0], codes = w[1..]); all lie inside the pair. The
 // loaded dwords are not touched until the stage is stored, so the loads stay
 // in flight (any arithmetic on them right after the load would wait for it).
-// Q4_1 blocks (20 bytes) are dword-aligned in a pair: both halves are one
-// whole block, d|m in w[0] and the codes in w[1..4].
-// 5-bit types add the fifth-bit word: w[0] scale (and m), w[1] fifth bits
-// (Q5_0 half 0: shifted by 16 bits like everything else), w[2..5] codes.
+// Blocks whose size is a multiple of 4 (Q4_1, Q5_1) are dword-aligned in a
+// pair: both halves are one whole block, d|m in w[0] and the rest after it.
+// The 5-bit types add the fifth-bit word before the codes: w[1] (Q5_0 half
+// 0: shifted by 16 bits like everything else), codes in w[2..5].
 template <int QT> struct HalfRaw {
   static constexpr int nq = (QTraits<QT>::nibbles ? 4 : 8) + (QTraits<QT>::has_qh ? 1 : 0);
   uint32_t w[nq + 1];
