@@ -73,11 +73,20 @@ KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines, so that editing a
+    comment does not mark the recorded counters as stale."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash(kernel: str) -> str:
+    """Hash of the code (comments stripped) of the sources `kernel` is built from."""
     h = hashlib.sha256()
     for f in KERNELS[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
