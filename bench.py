@@ -187,7 +187,8 @@ def summarize_counters(dirs):
     for (k, _, cn), v in per.items():
         agg.setdefault((k, cn), []).append(v)
     for (k, cn), v in sorted(agg.items()):
-        print(f"{k[:58]:58s} {cn:11s} dispatches {len(v):5d} avg_KiB {statistics.mean(v):14.1f}")
+        unit = "avg_KiB" if cn in ("FETCH_SIZE", "WRITE_SIZE") else "avg"
+        print(f"{k[:58]:58s} {cn:11s} dispatches {len(v):5d} {unit} {statistics.mean(v):14.1f}")
     factor = {}
     for cn in ("FETCH_SIZE", "WRITE_SIZE"):
         cal = [v for (k, c), vs in agg.items() if c == cn and "copyBuffer" in k for v in vs
