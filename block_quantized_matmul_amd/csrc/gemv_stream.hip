@@ -59,13 +59,15 @@ template <int QT, int NT> struct RCfg {
   static constexpr int stage_vgprs = 4 * w_loads + NT * 4;
   static constexpr int depth = (64 / stage_vgprs) < 1 ? 1 : (64 / stage_vgprs > 6 ? 6 : 64 / stage_vgprs);
   // With 8 wavefronts per workgroup (launches larger than the GPU), the
-  // nibble types (Q5_1 aside, whose decode needs more registers) with one or
-  // two tokens take rounds of 2 stages (the whole share for k = 4096) so the
-  // kernel fits in ~60 VGPRs and 6-8 wavefronts per SIMD: more workgroups
-  // per CU overlap one another's loads and compute.
-  static constexpr bool lean = QTraits<QT>::nibbles && !(QTraits<QT>::has_qh && QTraits<QT>::has_min) && NT <= 2;
-  static constexpr int depth_large = lean ? 2 : depth;
-  static constexpr int waves_per_simd_large = !lean ? 4 : (NT == 1 ? 8 : 6);
+  // nibble types with one or two tokens take rounds of 2 stages (the whole
+  // share for k = 4096) so the kernel fits in ~60 VGPRs and 6-8 wavefronts
+  // per SIMD: more workgroups per CU overlap one another's loads and
+  // compute. Q5_1, whose decode needs more registers, takes 6 wavefronts per
+  // SIMD (~85 VGPRs; 4.5 % faster than 4 on 11008 x 4096, and 8 spill).
+  static constexpr bool mid = QTraits<QT>::has_qh && QTraits<QT>::has_min && NT <= 2;
+  static constexpr bool lean = QTraits<QT>::nibbles && !mid && NT <= 2;
+  static constexpr int depth_large = (lean || mid) ? 2 : depth;
+  static constexpr int waves_per_simd_large = lean ? (NT == 1 ? 8 : 6) : mid ? 6 : 4;
   static constexpr int w_lds = 16 * row_stride;
   static constexpr int x_lds = 8 * 4 * NT * 16;                      // 8 blocks x 4 lane groups x NT slots x 8 halves
   static constexpr int lds_per_wave = w_lds + x_lds;
