@@ -362,3 +362,22 @@ def test_binding_rejects_short_buffers():
                           torch.zeros((3, 2), dtype=torch.int32, device="cuda"),
                           Y=torch.empty((3, 2, rows // 2 - 1), device="cuda"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts_sweep(seed):
+    """Seeded random cases across everything the dispatch looks at: weight
+    type, rows, k (odd block counts included), row padding, a 2-byte-offset
+    W, token count on both sides of the decode/GEMM switch, activation type.
+    Each case is compared element by element with the oracle."""
+    rng = np.random.Generator(np.random.PCG64([600, seed]))
+    for case in range(7):
+        qtype = int(rng.choice([Q4, Q41, Q50, Q51, Q8]))
+        rows = int(rng.integers(1, 700))
+        k = 32 * int(rng.integers(1, 80))
+        extra = 2 * int(rng.integers(0, 40))
+        offset = int(rng.choice([0, 2]))
+        n = int(rng.choice([1, 2, 3, 5, 8, 9, 17, 64, 130, 300]))
+        xdt = np.float16 if rng.random() < 0.5 else np.float32
+        W, X = _inputs(qtype, rows, k, n, extra, seed=1000 * seed + case, xdt=xdt)
+        _parity(W, qtype, k, X, AUTO, offset, f"sweep {seed}.{case}")

@@ -304,3 +304,35 @@ def test_matmul_id_graph_replay_with_new_routing():
         assert torch.equal(got_d, Yd), f"decode replay {rep} differs"
         assert torch.equal(got_p, Yp), f"grouped replay {rep} differs"
         _ = (Xp * 2).sum().item()  # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_matmul_id_random_sweep(seed):
+    """Seeded random MUL_MAT_ID cases: type, expert count, slots, tokens
+    (both routes), shared or per-slot activations, padded or streaming
+    layouts, and a few ids that name no expert."""
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([601, seed]))
+    for case in range(4):
+        qtype = int(rng.choice([Q4, Q41, Q50, Q51, Q8]))
+        n_experts = int(rng.integers(1, 20))
+        n_ids = int(rng.integers(1, 5))
+        n_tokens = int(rng.choice([1, 4, 8, 12, 40]))
+        rows = int(rng.integers(1, 300))
+        k = 256 * int(rng.integers(1, 4))
+        dense = synth.dense_row_bytes(qtype, k)
+        padded = rng.random() < 0.5
+        nb1 = dense + (2 if padded else 0)
+        nb2 = rows * nb1 + (6 if padded else 0)
+        offset = 2 if padded else 0
+        W = _stack(qtype, n_experts, rows, k, nb1, nb2, rng)
+        xs = 1 if rng.random() < 0.5 else n_ids
+        X = synth.make_activations(n_tokens * xs, k, rng).reshape(n_tokens, xs, k)
+        ids = rng.integers(0, n_experts, size=(n_tokens, n_ids)).astype(np.int32)
+        ids[rng.random((n_tokens, n_ids)) < 0.05] = n_experts
+        grouped = qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0
+        say(f"matmul_id sweep {seed}.{case} type={qtype} experts={n_experts} ids={n_ids} tokens={n_tokens} "
+            f"rows={rows} k={k} padded={padded} grouped={grouped}")
+        Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
+        y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
+        _check(Y, y_ref, s, f"matmul_id sweep {seed}.{case}")
