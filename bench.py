@@ -328,6 +328,7 @@ def time_type(torch, qmm, synth, qt, with_oracle=False):
 
 MOE_EXPERTS, MOE_ROWS, MOE_K, MOE_USED = 8, 14336, 4096, 2
 MOE_PREFILL_TOKENS = 512
+MOE_BATCH_TOKENS = 8
 
 
 def _graph_time(torch, run, reps):
@@ -353,8 +354,9 @@ def _graph_time(torch, run, reps):
 def time_matmul_id(torch, qmm, synth, with_oracle=False):
     """MUL_MAT_ID on a routed FFN projection: 8 experts of 14336x4096 Q4_0,
     2 selected per token (seeded random routing), activations shared by the
-    slots. Decode (1 token, per-pair decode kernel) and the probe's 512-token
-    batch (grouped: routing kernel + matrix-core tiles), each as back-to-back
+    slots. Decode (1 token, per-pair decode kernel), batched decode (8
+    tokens, routing kernel + decode tiles of 2 pairs) and the probe's
+    512-token batch (routing kernel + matrix-core tiles), each as back-to-back
     launches in a graph over >= 1.1 GiB of expert-stack copies, a different
     routing per launch, so the weights come from HBM."""
     import numpy as np
@@ -386,6 +388,27 @@ def time_matmul_id(torch, qmm, synth, with_oracle=False):
     res["decode"] = {"tokens": 1, "us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": byts,
                      "GB_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                      "kernel": "gemv_stream_kernel", "bound": "hbm"}
+    # batched decode: a few tokens, their pairs grouped into decode tiles so
+    # an expert selected by several tokens is read once
+    Tb = MOE_BATCH_TOKENS
+    ids_b = [torch.from_numpy(routing(Tb)).cuda() for _ in range(reps)]
+    Xb = torch.from_numpy(synth.make_activations(Tb, k, rng)).cuda().view(Tb, 1, k)
+    Yb = torch.empty((Tb, used, rows), dtype=torch.float32, device="cuda")
+    ws_b = torch.empty(max(1, qmm.qmm_matmul_id_workspace_bytes(E, used, Tb)), dtype=torch.uint8, device="cuda")
+
+    def run_b():
+        for i in range(reps):
+            qmm.qmm_matmul_id(Ws[i % copies], qt, k, Xb, ids_b[i], Y=Yb, workspace=ws_b)
+
+    us_b = _graph_time(torch, run_b, reps)
+    # the distinct experts of each launch's routing are the weights it must read
+    distinct = float(np.mean([len(np.unique(i.cpu().numpy())) for i in ids_b]))
+    byts_b = int(distinct * rows * nb1) + 4 * Tb * k + 4 * Tb * used + 4 * Tb * used * rows
+    gbs_b = byts_b / (us_b * 1e-6) / 1e9
+    res["batched_decode"] = {"tokens": Tb, "mean_distinct_experts": distinct, "us_per_launch": round(us_b, 3),
+                             "algorithmic_bytes_per_launch": byts_b, "GB_per_s": round(gbs_b, 2),
+                             "frac_of_hbm_peak": round(gbs_b / HBM_PEAK_GBS, 4),
+                             "kernel": "route_kernel + gemv_stream_kernel (tiles)", "bound": "hbm"}
     # prefill-sized batch
     T = MOE_PREFILL_TOKENS
     reps_p = copies

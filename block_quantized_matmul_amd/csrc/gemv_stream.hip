@@ -109,11 +109,17 @@ constexpr int kRTableOffset = 64;
 // p % n_ids); its matrix is expert ids[p] of the stack (expert stride nb2),
 // its activation row X[token][slot] (X[token][0] when x_slots == 1), its
 // output Y[p].
+// The tile form (decode-sized MUL_MAT_ID with pairs grouped by expert):
+// grid row y is tile pair0 + y of `tiles` = (expert, first entry, count) of
+// the pair list `ids`, and the workgroup runs the count (<= NT) pairs of the
+// tile as token slots; X is read through one buffer of x_bytes bytes.
 struct RRoute {
   const int32_t *ids;
   int64_t nb2;
   int n_experts, n_ids, x_slots, pair0;
-  int pad[8];
+  const int32_t *tiles;
+  uint32_t x_bytes;
+  int pad[5];
 };
 static_assert(sizeof(RRoute) == 64, "one table slot");
 // Fourth word of a buffer resource: 32-bit data format, no swizzle.
@@ -228,7 +234,7 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
 template <int NT, int WAVES>
 __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const float acc[4],
                                          __attribute__((address_space(1))) float *Y, int row0, int n_rows,
-                                         int n_tokens) {
+                                         int n_tokens, GPtr<int32_t> tok_rows = nullptr) {
   constexpr int kRedLanes = NT > 4 ? 32 : 16;
   if (lane < kRedLanes) {
 #pragma unroll
@@ -246,11 +252,15 @@ __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const f
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
     const int row = row0 + r;
-    if (t < n_tokens && row < n_rows) Y[static_cast<int64_t>(t) * n_rows + row] = sum;
+    if (t < n_tokens && row < n_rows) {
+      // token slot t's output row: t, or (tile form) its pair's row
+      const int64_t yr = tok_rows ? static_cast<int64_t>(tok_rows[t]) : t;
+      Y[yr * n_rows + row] = sum;
+    }
   }
 }
 
-template <int QT, int NT, bool XF16, int WAVES, bool IDS = false>
+template <int QT, int NT, bool XF16, int WAVES, bool IDS = false, bool TILES = false>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::waves_per_simd_large : 4)) void gemv_stream_kernel(
     const uint8_t *W0, const void *X0, float *Y0, int64_t nb1_0, int n_rows0, int nblk0, int n_tokens0, int k0,
     int64_t, int64_t, const RBatch batch) {
@@ -266,7 +276,31 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   uint64_t wp0, xp0, yp0;
   int64_t nb1;
   int n_rows, nblk, n_tokens, k;
-  if constexpr (IDS) {
+  uint32_t x_records = 0;       // bytes of X the buffer resource covers
+  GPtr<int32_t> tok = nullptr;  // tile form: the tile's pairs
+  int n_ids_t = 1, x_slots_t = 1;
+  if constexpr (TILES) {
+    static_assert(IDS && !XF16, "the tile form is expert-routed with fp32 activations");
+    typedef const __attribute__((address_space(4))) char *KBytes;
+    const u32x16_t rec = ((KRec)((KBytes)__builtin_amdgcn_kernarg_segment_ptr() + kRTableOffset))[1];
+    const GPtr<int32_t> list = (GPtr<int32_t>)((static_cast<uint64_t>(rec[1]) << 32) | rec[0]);
+    const int64_t nb2 = static_cast<int64_t>((static_cast<uint64_t>(rec[3]) << 32) | rec[2]);
+    const GPtr<int32_t> tiles = (GPtr<int32_t>)((static_cast<uint64_t>(rec[9]) << 32) | rec[8]);
+    const int ti = static_cast<int>(rec[7]) + static_cast<int>(blockIdx.y);
+    const int e = __builtin_amdgcn_readfirstlane(tiles[4 * ti]);
+    const int first = __builtin_amdgcn_readfirstlane(tiles[4 * ti + 1]);
+    const int cnt = __builtin_amdgcn_readfirstlane(tiles[4 * ti + 2]);
+    if (cnt == 0) return;  // whole workgroup: an unused tile
+    n_ids_t = static_cast<int>(rec[5]);
+    x_slots_t = static_cast<int>(rec[6]);
+    x_records = rec[10];
+    tok = list + first;
+    nb1 = nb1_0;
+    n_rows = n_rows0, nblk = nblk0, n_tokens = cnt, k = k0;
+    wp0 = reinterpret_cast<uint64_t>(W0) + static_cast<uint64_t>(e) * static_cast<uint64_t>(nb2);
+    xp0 = reinterpret_cast<uint64_t>(X0);
+    yp0 = reinterpret_cast<uint64_t>(Y0);
+  } else if constexpr (IDS) {
     // Expert-routed: matrix 0's fields describe expert 0 of the stack and
     // the shared X and Y; the routing record selects this pair's expert.
     typedef const __attribute__((address_space(4))) char *KBytes;
@@ -335,16 +369,25 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   // Token slots past n_tokens re-read the last token.
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<void *>(wp0), 0, static_cast<int>(static_cast<uint32_t>(n_rows * nb1)), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void *>(xp0), 0, static_cast<int>(static_cast<uint32_t>(n_tokens * k * (XF16 ? 2 : 4))),
-      kRsrcWord3);
+  if constexpr (!TILES) x_records = static_cast<uint32_t>(n_tokens * k * (XF16 ? 2 : 4));
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(xp0), 0, static_cast<int>(x_records), kRsrcWord3);
   uint32_t wv[C::w_loads];
 #pragma unroll
   for (int j = 0; j < C::w_loads; ++j)
     wv[j] = static_cast<uint32_t>(row0) * static_cast<uint32_t>(nb1) + L.wv[j];
   uint32_t xv[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) xv[t] = (static_cast<uint32_t>(min(t, n_tokens - 1) * k) + 4 * lane) * (XF16 ? 2 : 4);
+  for (int t = 0; t < NT; ++t) {
+    uint32_t xrow = static_cast<uint32_t>(min(t, n_tokens - 1));
+    if constexpr (TILES) {
+      // the pair's activation row: X[token][slot], or X[token][0] when shared
+      const int p = tok[min(t, n_tokens - 1)];
+      const int tt = p / n_ids_t;
+      xrow = static_cast<uint32_t>(tt * x_slots_t + (x_slots_t > 1 ? p - tt * n_ids_t : 0));
+    }
+    xv[t] = (xrow * static_cast<uint32_t>(k) + 4 * lane) * (XF16 ? 2 : 4);
+  }
 
   auto issue = [&](RRegs<QT, NT, XF16> &r, int q) {
     const int wq = q * (QC * 16), xq = q * 256 * (XF16 ? 2 : 4);
@@ -374,7 +417,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
     for (int i = 0; i < D; ++i)
       if (q + i < q_hi) r_consume<QT, NT, XF16>(st[i], L, wl, xs, lane, acc);
   }
-  r_reduce<NT, WAVES>(red, wave, lane, acc, Y, row0, n_rows, n_tokens);
+  r_reduce<NT, WAVES>(red, wave, lane, acc, Y, row0, n_rows, n_tokens, tok);
 }
 
 // ------------------------------------------------------------------ host side
@@ -463,6 +506,51 @@ hipError_t launch_gemv_id_stream(const void *W, int qtype, int64_t n_experts, in
       constexpr int QT = decltype(qt)::value;
       return waves == kKSplitSmall ? id_go_w<QT, kKSplitSmall>(B, count, rg, stream)
                                    : id_go_w<QT, kKSplitLarge>(B, count, rg, stream);
+    });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int QT, int NT, int WAVES>
+static hipError_t idt_go_w(const RBatch &B, int count, int rg, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(WAVES) * RCfg<QT, NT>::lds_per_wave + WAVES * 32 * 4 * sizeof(float);
+  const RMat &m0 = B.m[0];
+  return launch(gemv_stream_kernel<QT, NT, false, WAVES, true, true>, dim3(rg, count), dim3(64 * WAVES), lds, s, m0.W,
+                m0.X, m0.Y, m0.nb1, m0.n_rows, m0.nblk, m0.n_tokens, m0.k, int64_t{0}, int64_t{0}, B);
+}
+
+hipError_t launch_gemv_id_tiles(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
+                                int64_t nb2, const float *X, int64_t x_slots, int64_t n_ids, int64_t n_tokens,
+                                const int32_t *list, const int32_t *tiles, int64_t max_tiles, int nt, float *Y,
+                                hipStream_t stream) {
+  RBatch B{};
+  B.m[0] = record(MatmulDesc{W, qtype, n_rows, k, nb1, X, false, 1, Y});
+  RRoute route{};
+  route.ids = list;
+  route.nb2 = nb2;
+  route.n_experts = static_cast<int>(n_experts);
+  route.n_ids = static_cast<int>(n_ids);
+  route.x_slots = static_cast<int>(x_slots);
+  route.tiles = tiles;
+  route.x_bytes = static_cast<uint32_t>(n_tokens * x_slots * k * 4);
+  const int rg = static_cast<int>((n_rows + 15) / 16);
+  const int waves = k_split_for(max_tiles * rg, device_cus());
+  constexpr int64_t kMaxY = 65535;  // grid rows per launch
+  for (int64_t t0 = 0; t0 < max_tiles; t0 += kMaxY) {
+    route.pair0 = static_cast<int>(t0);
+    __builtin_memcpy(&B.m[1], &route, sizeof(RRoute));
+    const int count = static_cast<int>(max_tiles - t0 < kMaxY ? max_tiles - t0 : kMaxY);
+    const hipError_t e = by_qtype(qtype, [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
+      auto go = [&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        return waves == kKSplitSmall ? idt_go_w<QT, NT, kKSplitSmall>(B, count, rg, stream)
+                                     : idt_go_w<QT, NT, kKSplitLarge>(B, count, rg, stream);
+      };
+      if (nt <= 2) return go(std::integral_constant<int, 2>{});
+      if (nt <= 4) return go(std::integral_constant<int, 4>{});
+      return go(std::integral_constant<int, 8>{});
     });
     if (e != hipSuccess) return e;
   }

@@ -78,11 +78,18 @@ hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, i
 // are counted in LDS, so n_experts <= kRouteMaxExperts.
 constexpr int kTileTokens = 128;
 constexpr int kRouteMaxExperts = 4096;
-int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs);
-int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs);
+// Tiles hold up to `tile` pairs of one expert: kTileTokens for the
+// matrix-core kernel, 2, 4 or 8 for the decode kernel's tile form.
+int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs, int tile);
+int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs, int tile);
 hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k,
                                     int64_t nb1, int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids,
-                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace, hipStream_t stream);
+                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace, int tile,
+                                    hipStream_t stream);
+hipError_t launch_gemv_id_tiles(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
+                                int64_t nb2, const float *X, int64_t x_slots, int64_t n_ids, int64_t n_tokens,
+                                const int32_t *list, const int32_t *tiles, int64_t max_tiles, int nt, float *Y,
+                                hipStream_t stream);
 hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
                               const float *X, int64_t x_slots, int64_t n_ids, const int32_t *list,
                               const int32_t *tiles, int64_t max_tiles, float *Y, hipStream_t stream);

@@ -201,23 +201,38 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
                                         static_cast<hipStream_t>(stream)));
 }
 
-// The grouped (bucket-by-expert) path serves calls with more tokens than the
-// decode kernels take and enough pairs per expert to amortise a matrix-core
-// tile: a selected expert costs about as much as 3 to 4 single-token passes
-// over its weights whatever its pair count (up to 128), so below an average
-// of 4 pairs per expert the per-pair decode route is faster. It needs the
-// workspace and counts experts in LDS.
-static bool id_grouped(int64_t n_experts, int64_t n_ids, int64_t n_tokens) {
+// MUL_MAT_ID routes, chosen from the sizes alone (ids are device data):
+//  * per pair: every (token, slot) pair is a single-token product on the
+//    decode kernels (one token, or about one pair per selected expert);
+//  * tiles: pairs bucketed by expert, the streaming decode kernel runs
+//    tiles of 2, 4 or 8 pairs of one expert as token slots (the tile size
+//    is the average pairs per expert, rounded up to a slot count);
+//  * gemm: more tokens than the decode kernels take and at least 4 pairs
+//    per expert on average: 128-pair tiles on the matrix cores (a selected
+//    expert costs about as much as 3 to 4 single-token passes over its
+//    weights whatever its pair count up to 128).
+// The grouped routes need the workspace and count experts in LDS.
+struct IdPlan {
+  enum Route { kPerPair, kTiles, kGemm } route;
+  int tile;
+};
+static IdPlan id_plan(int64_t n_experts, int64_t n_ids, int64_t n_tokens) {
   const int64_t pairs = n_ids * n_tokens;
   const int64_t used = n_experts < pairs ? n_experts : pairs;
-  return n_tokens > QMM_GEMV_MAX_TOKENS && n_experts <= qmm::kRouteMaxExperts && pairs >= 4 * used;
+  if (n_experts > qmm::kRouteMaxExperts || n_tokens < 2 || used == 0) return {IdPlan::kPerPair, 0};
+  if (n_tokens > QMM_GEMV_MAX_TOKENS && pairs >= 4 * used) return {IdPlan::kGemm, qmm::kTileTokens};
+  const int64_t avg = (pairs + used - 1) / used;
+  if (avg < 2) return {IdPlan::kPerPair, 0};
+  return {IdPlan::kTiles, avg <= 2 ? 2 : avg <= 4 ? 4 : 8};
 }
 
 int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t n_tokens) {
   if (n_experts < 0 || n_experts > kMaxDim || n_ids < 0 || n_tokens < 0) return QMM_ERR_SHAPE;
   if (n_ids > 0 && n_tokens > kMaxDim / n_ids) return QMM_ERR_SHAPE;
-  if (n_ids == 0 || !id_grouped(n_experts, n_ids, n_tokens)) return 0;
-  return qmm::route_workspace_bytes(n_experts, n_ids * n_tokens);
+  if (n_ids == 0) return 0;
+  const IdPlan plan = id_plan(n_experts, n_ids, n_tokens);
+  if (plan.route == IdPlan::kPerPair) return 0;
+  return qmm::route_workspace_bytes(n_experts, n_ids * n_tokens, plan.tile);
 }
 
 int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
@@ -233,25 +248,31 @@ int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_row
   if (expert_stride_bytes % 2 != 0 || expert_stride_bytes < n_rows * row_stride_bytes) return QMM_ERR_STRIDE;
   if (!aligned(X, 4) || !aligned(ids, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
   if (n_rows == 0 || n_ids == 0 || n_tokens == 0) return QMM_OK;
-  const bool grouped = id_grouped(n_experts, n_ids, n_tokens);
+  IdPlan plan = id_plan(n_experts, n_ids, n_tokens);
+  const bool streamable = qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
+  // the tile form reads X through one 32-bit buffer and needs the streaming layout
+  if (plan.route == IdPlan::kTiles && (!streamable || n_tokens * x_slots > ((int64_t{1} << 32) - 1) / (4 * k)))
+    plan = {IdPlan::kPerPair, 0};
+  const bool grouped = plan.route != IdPlan::kPerPair;
   if (grouped) {
     if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_WORKSPACE;
     if (!aligned(workspace, 4)) return QMM_ERR_ALIGN;
-    const int64_t row_tiles = (n_rows + 127) / 128;
-    if (row_tiles * qmm::route_max_tiles(n_experts, n_ids * n_tokens) > kMaxDim) return QMM_ERR_SHAPE;
+    const int64_t row_tiles = plan.route == IdPlan::kGemm ? (n_rows + 127) / 128 : 1;
+    if (row_tiles * qmm::route_max_tiles(n_experts, n_ids * n_tokens, plan.tile) > kMaxDim) return QMM_ERR_SHAPE;
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool streaming = !grouped && qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
+  const bool streaming = !grouped && streamable;
   if (trace_on())
     fprintf(stderr, "qmm: matmul_id %s %s experts=%lld rows=%lld k=%lld nb1=%lld nb2=%lld ids=%lld tokens=%lld\n",
-            grouped ? "grouped" : streaming ? "stream" : "general", type_name(ggml_type), (long long)n_experts,
+            plan.route == IdPlan::kGemm ? "grouped-gemm" : plan.route == IdPlan::kTiles ? "grouped-decode"
+            : streaming ? "stream" : "general", type_name(ggml_type), (long long)n_experts,
             (long long)n_rows, (long long)k, (long long)row_stride_bytes, (long long)expert_stride_bytes,
             (long long)n_ids, (long long)n_tokens);
   if (grouped)
     return status_of(qmm::launch_matmul_id_grouped(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
                                                    expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y,
-                                                   workspace, s));
+                                                   workspace, plan.tile, s));
   if (streaming)
     return status_of(qmm::launch_gemv_id_stream(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
                                                 expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));

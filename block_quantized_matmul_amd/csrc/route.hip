@@ -1,7 +1,8 @@
-// Grouped MUL_MAT_ID for many tokens: the (token, slot) pairs are bucketed by
-// expert on the GPU, then the matrix-core kernel runs one tile per (weight
-// row tile, 128 pairs of one expert), so each selected expert's weights are
-// read once per token tile instead of once per pair.
+// Grouped MUL_MAT_ID: the (token, slot) pairs are bucketed by expert on the
+// GPU, then either the matrix-core kernel runs one tile per (weight row tile,
+// 128 pairs of one expert) or, for decode-sized calls, the streaming decode
+// kernel runs tiles of 2, 4 or 8 pairs of one expert as token slots; each
+// selected expert's weights are read once per tile instead of once per pair.
 //
 // What is computed: the expert-routed MUL_MAT of [Load] "llama.cpp 源码完全拆解
 // (三)：GGUF 装载、mmap 与张量放置", section "第六步：能力校验" (the probe's
@@ -10,7 +11,7 @@
 //
 // Routing (one 1024-thread workgroup, ids are device data): count the pairs
 // per expert in LDS, scan the counts into list offsets and token-tile
-// offsets, write the tile table (expert, first list entry, count) padded
+// offsets, write the tile table (expert, first list entry, count <= tile) padded
 // with empty tiles up to the host's bound, then place every pair in its
 // expert's bucket. Pairs whose id names no expert go after the valid ones
 // and get rows of NaN. Within a bucket the order depends on LDS atomics; a
@@ -28,7 +29,7 @@ constexpr int kPerThread = kRouteMaxExperts / kRouteThreads;
 static_assert(kRouteMaxExperts % kRouteThreads == 0, "experts split evenly over the threads");
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__restrict__ ids, int n_pairs,
-                                                              int n_experts, int max_tiles,
+                                                              int n_experts, int max_tiles, int tile,
                                                               int32_t *__restrict__ list, int32_t *__restrict__ tiles,
                                                               float *__restrict__ Y, int n_rows) {
   __shared__ int cnt[kRouteMaxExperts];
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
   for (int i = 0; i < kPerThread; ++i) {
     const int c = cnt[kPerThread * tid + i];
     c_own += c;
-    t_own += (c + kTileTokens - 1) / kTileTokens;
+    t_own += (c + tile - 1) / tile;
   }
   scan_c[0][tid] = c_own;
   scan_t[0][tid] = t_own;
@@ -71,11 +72,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
   for (int i = 0; i < kPerThread; ++i) {
     const int e = kPerThread * tid + i, c = cnt[e];
     cur[e] = off;
-    for (int j = 0; j * kTileTokens < c; ++j, ++toff) {
+    for (int j = 0; j * tile < c; ++j, ++toff) {
       int32_t *t = tiles + 4 * static_cast<int64_t>(toff);
       t[0] = e;
-      t[1] = off + j * kTileTokens;
-      t[2] = min(kTileTokens, c - j * kTileTokens);
+      t[1] = off + j * tile;
+      t[2] = min(tile, c - j * tile);
       t[3] = 0;
     }
     off += c;
@@ -101,28 +102,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
 
 }  // namespace
 
-int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs) {
+int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs, int tile) {
   // sum over experts of ceil(count / tile) <= n_pairs / tile + (experts used)
-  return (n_pairs + kTileTokens - 1) / kTileTokens + (n_experts < n_pairs ? n_experts : n_pairs);
+  return (n_pairs + tile - 1) / tile + (n_experts < n_pairs ? n_experts : n_pairs);
 }
 
-int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs) {
-  return (n_pairs * 4 + 15) / 16 * 16 + 16 * route_max_tiles(n_experts, n_pairs);
+int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs, int tile) {
+  return (n_pairs * 4 + 15) / 16 * 16 + 16 * route_max_tiles(n_experts, n_pairs, tile);
 }
 
 hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k,
                                     int64_t nb1, int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids,
-                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace, int tile,
                                     hipStream_t stream) {
   const int64_t n_pairs = n_tokens * n_ids;
-  const int64_t max_tiles = route_max_tiles(n_experts, n_pairs);
+  const int64_t max_tiles = route_max_tiles(n_experts, n_pairs, tile);
   int32_t *list = static_cast<int32_t *>(workspace);
   int32_t *tiles = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + (n_pairs * 4 + 15) / 16 * 16);
   hipError_t e = launch(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, static_cast<int>(n_pairs),
-                        static_cast<int>(n_experts), static_cast<int>(max_tiles), list, tiles, Y,
+                        static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
                         static_cast<int>(n_rows));
   if (e != hipSuccess) return e;
-  return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, x_slots, n_ids, list, tiles, max_tiles, Y, stream);
+  if (tile == kTileTokens)
+    return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, x_slots, n_ids, list, tiles, max_tiles, Y, stream);
+  return launch_gemv_id_tiles(W, qtype, n_experts, n_rows, k, nb1, nb2, X, x_slots, n_ids, n_tokens, list, tiles,
+                              max_tiles, tile, Y, stream);
 }
 
 }  // namespace qmm

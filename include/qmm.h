@@ -230,11 +230,15 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
  *                        that size is 0. Its contents are overwritten; two
  *                        calls in flight must not share one.
  *   stream               hipStream_t or NULL
- * Up to QMM_GEMV_MAX_TOKENS tokens (decode), and whenever the pairs average
- * fewer than 4 per expert, every pair is a single-token product on the
- * decode kernels. Otherwise (with at most 4096 experts) a routing kernel
- * buckets the pairs by expert in the workspace and the matrix-core kernel
- * runs 128 pairs of one expert per tile. An id outside
+ * The route follows from the sizes alone (at most 4096 experts for the
+ * grouped ones, which first bucket the pairs by expert in the workspace):
+ * one token, or about one pair per selected expert: every pair is a
+ * single-token product on the decode kernels; more than QMM_GEMV_MAX_TOKENS
+ * tokens and at least 4 pairs per expert on average: the matrix-core kernel
+ * runs tiles of 128 pairs of one expert; otherwise the streaming decode
+ * kernel runs tiles of 2, 4 or 8 pairs of one expert (the per-pair route
+ * when the weights do not have the streaming layout: 16-byte aligned W,
+ * row and expert strides, k a multiple of 256). Results do not depend on the route's tile order. An id outside
  * [0, n_experts) cannot be checked on the host: that pair's output row is
  * filled with quiet NaNs and nothing is read for it.
  * Returns QMM_OK, or the status of the first failed check (QMM_ERR_NULL,
@@ -248,7 +252,7 @@ int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_row
 
 /*
  * qmm_matmul_id_workspace_bytes - the workspace qmm_matmul_id needs for these
- * sizes (0 when the call takes the decode kernels), or QMM_ERR_SHAPE for
+ * sizes (0 when the call takes the per-pair route), or QMM_ERR_SHAPE for
  * negative or too large sizes.
  */
 int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t n_tokens);

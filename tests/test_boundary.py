@@ -183,11 +183,15 @@ def test_matmul_id_validation(L):
 
 def test_matmul_id_workspace_sizes(L):
     W = L.qmm_matmul_id_workspace_bytes
-    assert W(8, 2, 1) == 0 and W(8, 2, 8) == 0           # decode: per-pair kernels
+    assert W(8, 2, 1) == 0                               # one token: per-pair decode
+    assert W(8, 2, 4) == 0                               # about one pair per expert: per-pair
+    assert W(8, 2, 8) == 64 + 16 * (8 + 8)               # 2 pairs per expert: decode tiles of 2
     assert W(8, 0, 512) == 0
     assert W(5000, 2, 512) == 0                          # too many experts to bucket in LDS
-    assert W(8, 2, 15) == 0 and W(8, 2, 16) > 0          # under / at 4 pairs per expert
-    assert W(64, 8, 9) == 0 and W(64, 8, 32) > 0
+    assert W(8, 2, 15) == 128 + 16 * (8 + 8)             # 30 pairs: decode tiles of 4
+    assert W(8, 2, 16) == 128 + 16 * (1 + 8)             # 4 pairs per expert: 128-pair GEMM tiles
+    assert W(64, 8, 9) == 288 + 16 * (36 + 64)           # 72 pairs over 64 experts: tiles of 2
+    assert W(64, 8, 32) > 0
     # 1024 pairs in up to 8 + 8 tiles of 128, plus the pair list
     assert W(8, 2, 512) == 1024 * 4 + 16 * (8 + 8)
     assert W(2, 1, 9) == 48 + 16 * (1 + 2)

@@ -63,13 +63,40 @@ def test_matmul_id_small(qtype, layout, shared_x, n_tokens):
     if n_tokens > 1:
         ids[1] = [-1, 0]                           # no expert, the first expert
         ids[2, 1] = n_experts                      # one past the last
-    if n_tokens == 9:  # more tokens than decode-sized, too few pairs per expert to group
+    if n_tokens == 9:  # 18 pairs over 8 experts: bucketed into decode tiles of 4 pairs
         import block_quantized_matmul_amd as qmm
-        assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) == 0
+        assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0
     say(f"matmul_id {layout} type={qtype} tokens={n_tokens} x_slots={X.shape[1]} ids={ids.tolist()}")
     Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
     y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
     _check(Y, y_ref, s, f"matmul_id {layout}")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
+@pytest.mark.parametrize("n_tokens,n_experts", [(2, 2), (5, 4), (8, 4), (12, 8), (8, 1)])
+@pytest.mark.parametrize("shared_x", [False, True])
+def test_matmul_id_decode_tiles(qtype, n_tokens, n_experts, shared_x):
+    """Decode-sized calls with several pairs per expert: the pairs are
+    bucketed by expert and the streaming decode kernel runs tiles of 2, 4 or
+    8 pairs of one expert, with repeated experts and one id that names none.
+    The same call on a padded layout takes the per-pair route. Both against
+    the oracle."""
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([509, qtype, n_tokens, n_experts, int(shared_x)]))
+    n_ids, rows, k = 2, 136, 512
+    assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0, "not a grouped route"
+    dense = synth.dense_row_bytes(qtype, k)
+    xs = 1 if shared_x else n_ids
+    X = synth.make_activations(n_tokens * xs, k, rng, np.float32).reshape(n_tokens, xs, k)
+    ids = rng.integers(0, n_experts, size=(n_tokens, n_ids)).astype(np.int32)
+    ids[0, 1] = -3
+    for nb1, nb2, offset, what in ((dense, rows * dense, 0, "tiles"),
+                                   (dense + 2, rows * (dense + 2), 2, "per-pair")):
+        W = _stack(qtype, n_experts, rows, k, nb1, nb2, rng)
+        say(f"matmul_id decode {what} type={qtype} tokens={n_tokens} experts={n_experts} x_slots={xs}")
+        Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
+        y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
+        _check(Y, y_ref, s, f"matmul_id decode {what}")
 
 
 @pytest.mark.parametrize("qtype", [Q4, Q8])
