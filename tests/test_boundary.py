@@ -168,7 +168,7 @@ def test_matmul_id_validation(L):
     assert _mid(L, X=ctypes.c_void_p(0x20002)) == qmm.QMM_ERR_ALIGN
     assert _mid(L, ids=ctypes.c_void_p(0x40002)) == qmm.QMM_ERR_ALIGN
     assert _mid(L, Y=ctypes.c_void_p(0x30002)) == qmm.QMM_ERR_ALIGN
-    # more tokens than the decode kernels take: the grouped path needs a workspace
+    # more tokens than the decode kernels take: the grouped GEMM route needs a workspace
     need = L.qmm_matmul_id_workspace_bytes(8, 2, 64)
     assert need >= 64 * 2 * 4 + 16 * 8
     assert _mid(L, n=64, ws=NULL, ws_bytes=need) == qmm.QMM_ERR_WORKSPACE

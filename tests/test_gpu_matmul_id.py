@@ -336,7 +336,7 @@ def test_matmul_id_graph_replay_with_new_routing():
 @pytest.mark.parametrize("seed", range(4))
 def test_matmul_id_random_sweep(seed):
     """Seeded random MUL_MAT_ID cases: type, expert count, slots, tokens
-    (both routes), shared or per-slot activations, padded or streaming
+    (every route), shared or per-slot activations, padded or streaming
     layouts, and a few ids that name no expert."""
     import block_quantized_matmul_amd as qmm
     rng = np.random.Generator(np.random.PCG64([601, seed]))
