@@ -235,6 +235,35 @@ def test_matmul_id_mixtral_prefill_sampled(qtype):
             assert ok.all(), f"token {t} expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
 
 
+@pytest.mark.parametrize("qtype", [Q4, Q8])
+def test_matmul_id_mixtral_batched_decode_sampled(qtype):
+    """8 tokens through 8 experts of 14336 x 4096, 2 selected per token (the
+    bench's batched-decode case, grouped decode tiles of 2 pairs); every
+    (token, slot) pair's sampled rows against the oracle."""
+    import torch
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([510, qtype]))
+    n_experts, rows, k, n_ids, n_tokens = 8, 14336, 4096, 2, 8
+    assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0, "not a grouped route"
+    nb1 = synth.dense_row_bytes(qtype, k)
+    Wn = synth.make_weights(qtype, n_experts * rows, k, nb1, rng)
+    X = synth.make_activations(n_tokens, k, rng, np.float32).reshape(n_tokens, 1, k)
+    ids = np.stack([rng.permutation(n_experts)[:n_ids] for _ in range(n_tokens)]).astype(np.int32)
+    say(f"matmul_id batched decode experts={n_experts} rows={rows} k={k} tokens={n_tokens} type={qtype}")
+    W = dev(Wn.reshape(n_experts, rows, nb1))
+    Y = qmm.qmm_matmul_id(W, qtype, k, dev(X), dev(ids))
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    for t in range(n_tokens):
+        rsamp = np.unique(np.concatenate([[0, 15, 16, rows - 1], rng.integers(0, rows, 24)]))
+        for i in range(n_ids):
+            e = ids[t, i]
+            We = Wn[e * rows:(e + 1) * rows]
+            y_ref, s = O.matmul_sampled(We, qtype, rows, k, nb1, X[t], np.zeros_like(rsamp), rsamp)
+            ok = O.within_tolerance(Y[t, i, rsamp], y_ref, s)
+            assert ok.all(), f"token {t} expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
+
+
 @pytest.mark.parametrize("n_experts,n_ids,n_tokens", [(256, 8, 128), (4096, 8, 2048), (4097, 2, 16)])
 def test_matmul_id_many_experts(n_experts, n_ids, n_tokens):
     """Many small experts: 256 and 4096 (the most the grouped route counts in
