@@ -9,7 +9,8 @@
 // GGML_OP_MUL_MAT_ID case: activations F32 [k, n_ids, 512], ids I32
 // [n_ids, 512]); the 512-token batch is what makes grouping pay.
 //
-// Routing (one 1024-thread workgroup, ids are device data): count the pairs
+// Routing (one 1024-thread workgroup, or one wavefront for up to 64 experts
+// and 512 pairs; ids are device data): count the pairs
 // per expert in LDS, scan the counts into list offsets and token-tile
 // offsets, write the tile table (expert, first list entry, count <= tile) padded
 // with empty tiles up to the host's bound, then place every pair in its
@@ -100,6 +101,75 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
   }
 }
 
+// The same routing for calls with few experts and pairs (a decode step of a
+// small-expert MoE): one wavefront, every id held in registers, the scan done
+// with cross-lane shuffles, so the kernel runs no workgroup-wide scans and
+// only three barriers. Expert e is lane e's.
+constexpr int kSmallExperts = 64;
+constexpr int kSmallPairsPerLane = 8;
+constexpr int kSmallPairs = 64 * kSmallPairsPerLane;
+
+__global__ __launch_bounds__(64) void route_small_kernel(const int32_t *__restrict__ ids, int n_pairs, int n_experts,
+                                                         int max_tiles, int tile, int32_t *__restrict__ list,
+                                                         int32_t *__restrict__ tiles, float *__restrict__ Y,
+                                                         int n_rows) {
+  __shared__ int cnt[kSmallExperts];
+  __shared__ int cur[kSmallExperts];
+  __shared__ int bad_cur;
+  const int lane = threadIdx.x;
+  int e[kSmallPairsPerLane];
+#pragma unroll
+  for (int i = 0; i < kSmallPairsPerLane; ++i) {
+    const int p = lane + 64 * i;
+    e[i] = p < n_pairs ? ids[p] : -1;
+  }
+  cnt[lane] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSmallPairsPerLane; ++i)
+    if (e[i] >= 0 && e[i] < n_experts) atomicAdd(&cnt[e[i]], 1);
+  __syncthreads();
+
+  const int c = lane < n_experts ? cnt[lane] : 0;
+  const int t = (c + tile - 1) / tile;
+  int ci = c, ti = t;  // inclusive scans over the lanes
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int cu = __shfl_up(ci, d), tu = __shfl_up(ti, d);
+    if (lane >= d) ci += cu, ti += tu;
+  }
+  const int off = ci - c, toff = ti - t;
+  const int n_valid = __shfl(ci, 63), n_tiles = __shfl(ti, 63);
+  cur[lane] = off;
+  for (int j = 0; j < t; ++j) {
+    int32_t *q = tiles + 4 * static_cast<int64_t>(toff + j);
+    q[0] = lane;
+    q[1] = off + j * tile;
+    q[2] = min(tile, c - j * tile);
+    q[3] = 0;
+  }
+  for (int i = n_tiles + lane; i < max_tiles; i += 64) {
+    int32_t *q = tiles + 4 * static_cast<int64_t>(i);
+    q[0] = 0, q[1] = 0, q[2] = 0, q[3] = 0;  // empty: its workgroups exit at once
+  }
+  if (lane == 0) bad_cur = n_valid;
+  __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < kSmallPairsPerLane; ++i) {
+    const int p = lane + 64 * i;
+    if (p < n_pairs) {
+      const bool ok = e[i] >= 0 && e[i] < n_experts;
+      list[ok ? atomicAdd(&cur[e[i]], 1) : atomicAdd(&bad_cur, 1)] = p;
+    }
+  }
+  __syncthreads();  // the bucket writes above are visible to the whole wavefront
+  for (int i = n_valid; i < n_pairs; ++i) {
+    float *y = Y + static_cast<int64_t>(list[i]) * n_rows;
+    for (int r = lane; r < n_rows; r += 64) y[r] = __builtin_bit_cast(float, 0x7FC00000u);
+  }
+}
+
 }  // namespace
 
 int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs, int tile) {
@@ -119,9 +189,13 @@ hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts,
   const int64_t max_tiles = route_max_tiles(n_experts, n_pairs, tile);
   int32_t *list = static_cast<int32_t *>(workspace);
   int32_t *tiles = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + (n_pairs * 4 + 15) / 16 * 16);
-  hipError_t e = launch(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, static_cast<int>(n_pairs),
-                        static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
-                        static_cast<int>(n_rows));
+  const bool small = n_experts <= kSmallExperts && n_pairs <= kSmallPairs;
+  hipError_t e = small ? launch(route_small_kernel, dim3(1), dim3(64), 0, stream, ids, static_cast<int>(n_pairs),
+                                static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
+                                static_cast<int>(n_rows))
+                       : launch(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, static_cast<int>(n_pairs),
+                                static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
+                                static_cast<int>(n_rows));
   if (e != hipSuccess) return e;
   if (tile == kTileTokens)
     return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, x_slots, n_ids, list, tiles, max_tiles, Y, stream);

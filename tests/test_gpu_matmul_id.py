@@ -264,6 +264,29 @@ def test_matmul_id_mixtral_batched_decode_sampled(qtype):
             assert ok.all(), f"token {t} expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
 
 
+@pytest.mark.parametrize("n_experts,n_tokens", [(64, 256), (64, 257), (65, 256), (64, 100), (65, 100)])
+def test_matmul_id_routing_kernel_sizes(n_experts, n_tokens):
+    """Both routing kernels: up to 64 experts and 512 pairs take the
+    one-wavefront kernel, more of either the workgroup kernel; the grouped
+    GEMM (256 / 257 tokens: 4 pairs per expert) and decode tiles (100 tokens:
+    about 3) on each side of the boundary, with ids that name no expert,
+    against the oracle."""
+    import block_quantized_matmul_amd as qmm
+    rng = np.random.Generator(np.random.PCG64([511, n_experts, n_tokens]))
+    qtype, n_ids, rows, k = Q4, 2, 40, 256
+    ids = rng.integers(0, n_experts, size=(n_tokens, n_ids)).astype(np.int32)
+    ids[0, 0] = -1
+    ids[n_tokens - 1, 1] = n_experts
+    assert qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens) > 0, "not a grouped route"
+    dense = synth.dense_row_bytes(qtype, k)
+    W = _stack(qtype, n_experts, rows, k, dense, rows * dense, rng)
+    X = synth.make_activations(n_tokens, k, rng, np.float32).reshape(n_tokens, 1, k)
+    say(f"matmul_id routing experts={n_experts} tokens={n_tokens}")
+    Y = _run(W, qtype, n_experts, rows, k, dense, rows * dense, X, ids)
+    y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, dense, rows * dense, X, ids)
+    _check(Y, y_ref, s, f"routing experts={n_experts} tokens={n_tokens}")
+
+
 @pytest.mark.parametrize("n_experts,n_ids,n_tokens", [(256, 8, 128), (4096, 8, 2048), (4097, 2, 16)])
 def test_matmul_id_many_experts(n_experts, n_ids, n_tokens):
     """Many small experts: 256 and 4096 (the most the grouped route counts in
