@@ -493,8 +493,8 @@ def main():
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures one GPU's "
-              "share of the work; how the path would shard over several GPUs is described, not built",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library and this benchmark use one GPU: "
+              "each GPU would take its own share of the rows or experts, with no communication in the product",
               file=sys.stderr)
         sys.exit(2)
 
