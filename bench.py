@@ -493,8 +493,8 @@ def main():
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library and this benchmark use one GPU: "
-              "each GPU would take its own share of the rows or experts, with no communication in the product",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): a MUL_MAT shards by weight rows "
+              "(or experts) across GPUs without communication, so one GPU's throughput is what is measured",
               file=sys.stderr)
         sys.exit(2)
 
