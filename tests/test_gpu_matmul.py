@@ -254,6 +254,33 @@ def test_config5_stack_layers_sampled(n_tokens):
         assert O.within_tolerance(Y[toks, rows], y_ref, s).all(), case.name
 
 
+def test_config5_decode_batched_as_benchmarked():
+    """Layers 0 and 31 of the stack at one token through qmm_matmul_batch in
+    exactly the benchmark's launch groups (q+k+v, o, gate+up, down, whose
+    batched launches split k by their own size), checked on sampled outputs
+    of every tensor."""
+    import torch
+    import bench
+    from gpu_util import dev
+    cases = {(c.layer, c.tensor): c for c in synth.stack_cases(1) if c.layer in (0, 31)}
+    for layer in (0, 31):
+        for grp in bench.LAYER_GROUPS:
+            items, host = [], []
+            for t in grp:
+                c = cases[(layer, t)]
+                W, X = c.weights(), c.activations()
+                items.append((dev(W), c.qtype, c.k, dev(X), torch.empty((1, c.rows), dtype=torch.float32, device="cuda")))
+                host.append((c, W, X))
+            say(f"decode batch layer {layer} tensors {grp}")
+            qmm.qmm_matmul_batch(items)
+            torch.cuda.synchronize()
+            for (c, W, X), it in zip(host, items):
+                rng = np.random.default_rng(1000 * layer + c.tensor)
+                rows = np.unique(np.concatenate([[0, 15, 16, c.rows - 1], rng.integers(0, c.rows, 1500)]))
+                y_ref, s = O.matmul_sampled(W, c.qtype, c.rows, c.k, c.nb1, X, np.zeros_like(rows), rows)
+                assert O.within_tolerance(it[4].cpu().numpy()[0, rows], y_ref, s).all(), c.name
+
+
 # ------------------------------------------------------------ batched calls and graph replay
 def _batch_specs():
     # (type, rows, k, n_tokens, x dtype): streaming-eligible, general-kernel and matrix-core entries,
