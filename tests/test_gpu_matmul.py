@@ -56,13 +56,16 @@ def test_gemm_ragged(qtype, xdt, n):
 
 
 @pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
-def test_gemm_full_size_tiles(qtype):
+@pytest.mark.parametrize("xdt", [np.float16, np.float32])
+def test_gemm_full_size_tiles(qtype, xdt):
     """More 128-row tiles than CUs: the 128-row tile variant (the ragged
     tests above are small enough to take the 64-row one), with ragged rows
-    and tokens and an odd block count, every element against the oracle."""
+    and tokens and an odd block count (rows only 2-byte aligned for the
+    18-, 22- and 34-byte blocks), every element against the oracle."""
     rows, k, n = 4230, 288, 1030
     assert ((rows + 127) // 128) * ((n + 127) // 128) > 256
-    W, X = _inputs(qtype, rows, k, n, xdt=np.float16)
+    W, X = _inputs(qtype, rows, k, n, xdt=xdt)
+    say(f"gemm 128-row tiles type={qtype} x={np.dtype(xdt).name}")
     _parity(W, qtype, k, X, GEMM, 0, "gemm 128-row tiles")
 
 
