@@ -28,7 +28,7 @@ since they were taken. The CPU oracle is timed on a bounded sample of the
 same decode workload.
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--layers 32]
-                  [--cpu-layers 12] [--no-cpu-baseline] [--per-call] [--copy-calibration]
+                  [--cpu-layers 4] [--no-cpu-baseline] [--per-call] [--copy-calibration]
   python bench.py --summarize-trace DIR      (rocprofv3 -f csv kernel trace)
   python bench.py --only PASS [--steps K] [--layers L] [--copy-calibration]
   python bench.py --summarize-counters DIR... (rocprofv3 -f csv --pmc runs)
@@ -100,7 +100,7 @@ def parse():
     ap.add_argument("--no-get-rows", action="store_true", help="skip the GET_ROWS (token-embedding gather) line")
     ap.add_argument("--no-matmul-id", action="store_true", help="skip the MUL_MAT_ID (routed expert FFN) lines")
     ap.add_argument("--no-other-types", action="store_true", help="skip the Q8_0 / Q4_1 / Q5_0 / Q5_1 lines")
-    ap.add_argument("--cpu-layers", type=int, default=12, help="layers of the decode pass the oracle times")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -465,25 +465,65 @@ def upload_stack(torch, synth, layers, keep_host_layers):
     return dec, pre, W, X1, X2, host
 
 
-def cpu_baseline(O, host):
-    """Time the oracle (as it stands) on the decode MUL_MATs of the first
-    layers of the same stack; report GB/s of algorithmic bytes."""
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = 1
-    nbytes = 0
-    t0 = time.perf_counter()
-    for c, w, x in host:
-        O.matmul(w, c.qtype, c.rows, c.k, c.nb1, x)
-        nbytes += c.w_bytes() + x.nbytes + c.rows * c.n_tokens * 4
-    dt = time.perf_counter() - t0
+        return 1
+
+
+def _oracle_legs(O, items, one_thread):
+    """Time oracle.matmul over (case, W rows, X) items as it stands; with
+    one_thread its BLAS is held to one thread (numpy's dequantisation runs
+    on one thread either way). Returns (seconds, algorithmic bytes, flops)."""
+    import contextlib
+    lim = contextlib.nullcontext()
+    if one_thread:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(1)
+    nbytes = flops = 0
+    with lim:
+        t0 = time.perf_counter()
+        for c, w, x in items:
+            rows = w.shape[0]
+            O.matmul(w, c.qtype, rows, c.k, c.nb1, x)
+            nbytes += rows * (c.w_bytes() // c.rows) + x.nbytes + rows * x.shape[0] * 4
+            flops += 2 * rows * c.k * x.shape[0]
+        return time.perf_counter() - t0, nbytes, flops
+
+
+def cpu_baseline(O, host, pre_layer0):
+    """The oracle as it stands, timed on the host beside the GPU run.
+
+    value: the decode MUL_MATs of the first stack layers (n_tokens = 1) with
+    numpy's BLAS on all its threads, GB/s of algorithmic bytes. Beside it:
+    the same on one thread (layer 0 only), and one layer's prefill MUL_MATs
+    at n_tokens = 2048 on a stated fraction of each tensor's rows, reported
+    as the whole layer's time extrapolated by that fraction (all threads and
+    one thread)."""
+    threads = _blas_threads()
+    dt, nbytes, _ = _oracle_legs(O, host, False)
     layers = len(host) // 7
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"decode MUL_MATs of layers 0..{layers - 1} of the same stack ({len(host)} matmuls, "
-                      f"n_tokens=1, {nbytes / 1e6:.1f} MB algorithmic) in {dt:.1f} s; dequantisation in numpy "
-                      f"on one thread, fp64 products on {threads} BLAS threads"}
+    dt1, nb1_, _ = _oracle_legs(O, host[:7], True)
+    res = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"decode MUL_MATs of layers 0..{layers - 1} of the same stack ({len(host)} matmuls, "
+                     f"n_tokens=1, {nbytes / 1e6:.1f} MB algorithmic) in {dt:.2f} s; dequantisation in numpy "
+                     f"on one thread, fp64 products on {threads} BLAS threads",
+           "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+           "decode_one_thread": {"value": round(nb1_ / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                 "sample": f"decode MUL_MATs of layer 0 (7 matmuls) in {dt1:.2f} s"}}
+    if pre_layer0:
+        for key, frac, one in (("prefill", 8, False), ("prefill_one_thread", 32, True)):
+            items = [(c, w[: c.rows // frac], x) for c, w, x in pre_layer0]
+            dtp, _, fl = _oracle_legs(O, items, one)
+            full = dtp * frac
+            res[key] = {"value": round(fl * frac / full / 1e9, 3), "unit": "GFLOP/s", "cores": 1 if one else threads,
+                        "layer_seconds_extrapolated": round(full, 2),
+                        "sample": f"prefill MUL_MATs of layer 0 (7 matmuls, n_tokens={PREFILL_TOKENS}) on the "
+                                  f"first 1/{frac} of each tensor's rows in {dtp:.2f} s; whole-layer time "
+                                  f"extrapolated by {frac}x"}
+    return res
 
 
 def main():
@@ -675,7 +715,8 @@ def main():
     if cpu_layers:
         import oracle.qmm_oracle as O
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(O, host)
+        pre0 = [(c, c.weights(), c.activations()) for c in pre[:7]]
+        out["cpu_baseline"] = cpu_baseline(O, host, pre0)
     print(json.dumps(out), flush=True)
 
 

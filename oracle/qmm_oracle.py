@@ -289,17 +289,23 @@ def matmul_sampled(W, qtype: int, n_rows: int, k: int, nb1: int, X, tokens, rows
 
 
 def within_tolerance(y, y_ref, s, rel: float = 1e-3, abs_: float = 1e-5) -> np.ndarray:
-    """Element-wise acceptance: |y - y_ref| <= rel * s + abs_, and a result
-    is non-finite exactly where the oracle's is."""
+    """Element-wise acceptance of a result y against the oracle's (y_ref, s).
+
+      y_ref NaN        -> y must be NaN;
+      y_ref +/-inf     -> y must be the infinity of the same sign;
+      y_ref finite     -> y must be finite and |y - y_ref| <= rel * s + abs_
+                          (the bound is inclusive).
+
+    The bound is the per-element tolerance the method is held to, with
+    s = sum_i |w_i x_i|; NaN positions (and infinities) must match exactly.
+    """
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     s = np.asarray(s, dtype=np.float64)
-    fin_ref = np.isfinite(y_ref) & np.isfinite(s)
-    fin = np.isfinite(y)
-    ok = fin == fin_ref
-    with np.errstate(invalid="ignore"):
-        close = np.abs(y - y_ref) <= rel * s + abs_
-    return ok & (close | ~fin_ref)
+    with np.errstate(invalid="ignore", over="ignore"):
+        close = np.isfinite(y) & (np.abs(y - y_ref) <= rel * s + abs_)
+        same_inf = y == y_ref  # true only for an infinity of the same sign here
+    return np.where(np.isnan(y_ref), np.isnan(y), np.where(np.isinf(y_ref), same_inf, close))
 
 
 # --------------------------------------------------------------------------
