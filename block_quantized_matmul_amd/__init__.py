@@ -32,6 +32,8 @@ QMM_ERR_ALIGN = -5
 QMM_ERR_HIP = -6
 QMM_ERR_PATH = -7
 QMM_ERR_WORKSPACE = -8
+QMM_ERR_SCRATCH = -9
+QMM_NOALLOC_SCRATCH_BYTES = 1048576
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 
@@ -67,10 +69,11 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_batch.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp]
         L.qmm_get_rows.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
         L.qmm_matmul_id.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp, i64, vp]
+        L.qmm_matmul_id_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
         L.qmm_matmul_id_workspace_bytes.argtypes = [i64, i64, i64]
         L.qmm_matmul_id_workspace_bytes.restype = i64
         for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch",
-                  "qmm_get_rows", "qmm_matmul_id"):
+                  "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc"):
             getattr(L, f).restype = i32
         L.qmm_row_bytes.argtypes = [i32, i64]
         L.qmm_row_bytes.restype = i64
@@ -226,15 +229,8 @@ def qmm_matmul_id_workspace_bytes(n_experts: int, n_ids: int, n_tokens: int) -> 
     return int(lib().qmm_matmul_id_workspace_bytes(int(n_experts), int(n_ids), int(n_tokens)))
 
 
-def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stride_bytes=None,
-                  expert_stride_bytes=None, Y=None, workspace=None, stream=None):
-    """MUL_MAT_ID (C: qmm_matmul_id): Y[t][i] = MUL_MAT(expert ids[t][i], X[t][i or 0]).
-
-    W is a contiguous uint8 [n_experts][n_rows][nb1] GPU tensor, or any uint8
-    GPU tensor with the four geometry arguments given. X is a contiguous fp32
-    [n_tokens][x_slots][k] tensor (x_slots 1 or n_ids), ids a contiguous int32
-    [n_tokens][n_ids] tensor; Y (fp32 [n_tokens][n_ids][n_rows]) is allocated
-    if None. An id outside [0, n_experts) gives a row of NaNs."""
+def _matmul_id_args(W, ggml_type, k, X, ids, n_experts, n_rows, row_stride_bytes, expert_stride_bytes, Y):
+    """Geometry and checked buffers of a MUL_MAT_ID call (shared by both entry points)."""
     import torch
     if W.dtype != torch.uint8:
         raise TypeError("W must be a uint8 tensor of raw blocks")
@@ -255,19 +251,50 @@ def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stri
     _check_span(W, torch.uint8, _weights_span(ggml_type, k, int(n_rows), int(row_stride_bytes), int(n_experts),
                                               int(expert_stride_bytes)), "W")
     _check_span(Y, torch.float32, n_tokens * n_ids * int(n_rows), "Y")
-    need = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens)
+    geo = (int(n_experts), int(n_rows), int(k), int(row_stride_bytes), int(expert_stride_bytes))
+    return geo, n_ids, n_tokens, Y
+
+
+def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stride_bytes=None,
+                  expert_stride_bytes=None, Y=None, workspace=None, stream=None):
+    """MUL_MAT_ID (C: qmm_matmul_id): Y[t][i] = MUL_MAT(expert ids[t][i], X[t][i or 0]).
+
+    W is a contiguous uint8 [n_experts][n_rows][nb1] GPU tensor, or any uint8
+    GPU tensor with the four geometry arguments given. X is a contiguous fp32
+    [n_tokens][x_slots][k] tensor (x_slots 1 or n_ids), ids a contiguous int32
+    [n_tokens][n_ids] tensor; Y (fp32 [n_tokens][n_ids][n_rows]) is allocated
+    if None. An id outside [0, n_experts) gives a row of NaNs."""
+    import torch
+    geo, n_ids, n_tokens, Y = _matmul_id_args(W, ggml_type, k, X, ids, n_experts, n_rows, row_stride_bytes,
+                                              expert_stride_bytes, Y)
+    need = qmm_matmul_id_workspace_bytes(geo[0], n_ids, n_tokens)
     if need < 0:
         raise QmmError(need, "qmm_matmul_id_workspace_bytes")
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     ws = _gpu_ptr(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().qmm_matmul_id(_gpu_ptr(W, "W"), int(ggml_type), int(n_experts), int(n_rows), int(k),
-                             int(row_stride_bytes), int(expert_stride_bytes), _gpu_ptr(X, "X"), int(X.shape[1]),
-                             _gpu_ptr(ids, "ids"), n_ids, n_tokens, _gpu_ptr(Y, "Y"), ws, ws_bytes,
-                             _stream(stream))
+    e, r, kk, nb1, nb2 = geo
+    st = lib().qmm_matmul_id(_gpu_ptr(W, "W"), int(ggml_type), e, r, kk, nb1, nb2, _gpu_ptr(X, "X"), int(X.shape[1]),
+                             _gpu_ptr(ids, "ids"), n_ids, n_tokens, _gpu_ptr(Y, "Y"), ws, ws_bytes, _stream(stream))
     if st != QMM_OK:
         raise QmmError(st, "qmm_matmul_id")
+    return Y
+
+
+def qmm_matmul_id_noalloc(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stride_bytes=None,
+                          expert_stride_bytes=None, Y=None, stream=None):
+    """MUL_MAT_ID on the library's own per-GPU scratch (C: qmm_matmul_id_noalloc):
+    the same arguments and result as qmm_matmul_id, no workspace. Pass a
+    preallocated Y to keep the call free of allocations."""
+    geo, n_ids, n_tokens, Y = _matmul_id_args(W, ggml_type, k, X, ids, n_experts, n_rows, row_stride_bytes,
+                                              expert_stride_bytes, Y)
+    e, r, kk, nb1, nb2 = geo
+    st = lib().qmm_matmul_id_noalloc(_gpu_ptr(W, "W"), int(ggml_type), e, r, kk, nb1, nb2, _gpu_ptr(X, "X"),
+                                     int(X.shape[1]), _gpu_ptr(ids, "ids"), n_ids, n_tokens, _gpu_ptr(Y, "Y"),
+                                     _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_matmul_id_noalloc")
     return Y
 
 

@@ -15,10 +15,20 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
 #include "launch.h"
+
+// Scratch of qmm_matmul_id_noalloc: the routing table of the grouped
+// MUL_MAT_ID routes, held in a file-scope device array so that the entry
+// point allocates nothing. Each GPU the library runs on keeps its own copy
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: kernels are given the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[QMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -68,6 +78,26 @@ const char *type_name(int t) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (nullptr if HIP cannot
+// give it).
+void *device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,6 +126,9 @@ const char *qmm_status_string(int status) {
     case QMM_ERR_HIP: return "QMM_ERR_HIP: the HIP runtime rejected the kernel launch";
     case QMM_ERR_PATH: return "QMM_ERR_PATH: unknown path, or GEMV forced with more than 8 tokens";
     case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or smaller than qmm_matmul_id_workspace_bytes";
+    case QMM_ERR_SCRATCH:
+      return "QMM_ERR_SCRATCH: the call needs more than the QMM_NOALLOC_SCRATCH_BYTES of scratch the no-allocation "
+             "entry point holds";
     default: return "unknown qmm status";
   }
 }
@@ -235,34 +268,40 @@ int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t 
   return qmm::route_workspace_bytes(n_experts, n_ids * n_tokens, plan.tile);
 }
 
-int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
-                  int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
-                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
-                  int64_t workspace_bytes, void *stream) {
+// Checks of a MUL_MAT_ID call, all on the host, except those of the
+// workspace; fills in the route and the workspace the sizes call for.
+static int check_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                           int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                           const int32_t *ids, int64_t n_ids, int64_t n_tokens, const float *Y, IdPlan *plan,
+                           int64_t *need) {
   if (X == nullptr || ids == nullptr || Y == nullptr) return QMM_ERR_NULL;
   int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
   if (st != QMM_OK) return st;
-  const int64_t need = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens);
-  if (need < 0) return static_cast<int>(need);
+  *need = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens);
+  if (*need < 0) return static_cast<int>(*need);
   if (x_slots != 1 && x_slots != n_ids) return QMM_ERR_SHAPE;
   if (expert_stride_bytes % 2 != 0 || expert_stride_bytes < n_rows * row_stride_bytes) return QMM_ERR_STRIDE;
   if (!aligned(X, 4) || !aligned(ids, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
-  if (n_rows == 0 || n_ids == 0 || n_tokens == 0) return QMM_OK;
-  IdPlan plan = id_plan(n_experts, n_ids, n_tokens);
+  *plan = id_plan(n_experts, n_ids, n_tokens);
   const bool streamable = qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
   // the tile form reads X through one 32-bit buffer and needs the streaming layout
-  if (plan.route == IdPlan::kTiles && (!streamable || n_tokens * x_slots > ((int64_t{1} << 32) - 1) / (4 * k)))
-    plan = {IdPlan::kPerPair, 0};
-  const bool grouped = plan.route != IdPlan::kPerPair;
-  if (grouped) {
-    if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_WORKSPACE;
-    if (!aligned(workspace, 4)) return QMM_ERR_ALIGN;
-    const int64_t row_tiles = plan.route == IdPlan::kGemm ? (n_rows + 127) / 128 : 1;
-    if (row_tiles * qmm::route_max_tiles(n_experts, n_ids * n_tokens, plan.tile) > kMaxDim) return QMM_ERR_SHAPE;
+  if (plan->route == IdPlan::kTiles && (!streamable || n_tokens * x_slots > ((int64_t{1} << 32) - 1) / (4 * k)))
+    *plan = {IdPlan::kPerPair, 0};
+  if (plan->route != IdPlan::kPerPair) {
+    const int64_t row_tiles = plan->route == IdPlan::kGemm ? (n_rows + 127) / 128 : 1;
+    if (row_tiles * qmm::route_max_tiles(n_experts, n_ids * n_tokens, plan->tile) > kMaxDim) return QMM_ERR_SHAPE;
   }
+  return QMM_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool streaming = !grouped && streamable;
+// Enqueue a checked MUL_MAT_ID call; `workspace` holds at least the bytes
+// check_matmul_id reported when the route is a grouped one.
+static int run_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                         int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                         const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                         const IdPlan &plan, hipStream_t s) {
+  const bool grouped = plan.route != IdPlan::kPerPair;
+  const bool streaming = !grouped && qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
   if (trace_on())
     fprintf(stderr, "qmm: matmul_id %s %s experts=%lld rows=%lld k=%lld nb1=%lld nb2=%lld ids=%lld tokens=%lld\n",
             plan.route == IdPlan::kGemm ? "grouped-gemm" : plan.route == IdPlan::kTiles ? "grouped-decode"
@@ -278,6 +317,43 @@ int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_row
                                                 expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));
   return status_of(qmm::launch_gemv_id_general(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
                                               expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));
+}
+
+int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                  int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                  const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                  int64_t workspace_bytes, void *stream) {
+  IdPlan plan{IdPlan::kPerPair, 0};
+  int64_t need = 0;
+  const int st = check_matmul_id(W, ggml_type, n_experts, n_rows, k, row_stride_bytes, expert_stride_bytes, X,
+                                 x_slots, ids, n_ids, n_tokens, Y, &plan, &need);
+  if (st != QMM_OK) return st;
+  if (n_rows == 0 || n_ids == 0 || n_tokens == 0) return QMM_OK;
+  if (plan.route != IdPlan::kPerPair) {
+    if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return QMM_ERR_ALIGN;
+  }
+  return run_matmul_id(W, ggml_type, n_experts, n_rows, k, row_stride_bytes, expert_stride_bytes, X, x_slots, ids,
+                       n_ids, n_tokens, Y, workspace, plan, static_cast<hipStream_t>(stream));
+}
+
+int qmm_matmul_id_noalloc(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                          int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                          const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *stream) {
+  IdPlan plan{IdPlan::kPerPair, 0};
+  int64_t need = 0;
+  const int st = check_matmul_id(W, ggml_type, n_experts, n_rows, k, row_stride_bytes, expert_stride_bytes, X,
+                                 x_slots, ids, n_ids, n_tokens, Y, &plan, &need);
+  if (st != QMM_OK) return st;
+  if (need > QMM_NOALLOC_SCRATCH_BYTES) return QMM_ERR_SCRATCH;
+  if (n_rows == 0 || n_ids == 0 || n_tokens == 0) return QMM_OK;
+  void *ws = nullptr;
+  if (plan.route != IdPlan::kPerPair) {
+    ws = device_scratch();
+    if (ws == nullptr) return QMM_ERR_HIP;
+  }
+  return run_matmul_id(W, ggml_type, n_experts, n_rows, k, row_stride_bytes, expert_stride_bytes, X, x_slots, ids,
+                       n_ids, n_tokens, Y, ws, plan, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -110,6 +110,10 @@ extern "C" {
 #define QMM_ERR_HIP (-6)    /* HIP reported an error for the launch */
 #define QMM_ERR_PATH (-7)   /* unknown path, or GEMV forced with too many tokens */
 #define QMM_ERR_WORKSPACE (-8) /* workspace NULL or smaller than the call needs */
+#define QMM_ERR_SCRATCH (-9)   /* the call needs more scratch than qmm_matmul_id_noalloc holds */
+
+/* Bytes of device scratch qmm_matmul_id_noalloc holds per GPU (1 MiB). */
+#define QMM_NOALLOC_SCRATCH_BYTES 1048576
 
 /*
  * qmm_matmul - Y = MUL_MAT(W, X) with fp32 activations ([Bind] section 2.3,
@@ -249,6 +253,30 @@ int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_row
                   int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
                   const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
                   int64_t workspace_bytes, void *stream);
+
+/*
+ * qmm_matmul_id_noalloc - qmm_matmul_id for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same routes, kernels and results,
+ * but the routing table of the grouped routes lives in a device array of
+ * QMM_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, so the call takes no workspace and calls no
+ * allocator. Its address is looked up (hipGetSymbolAddress) on the first
+ * call on each device, with that device current.
+ *   Arguments: as qmm_matmul_id, without workspace and workspace_bytes.
+ *   Scratch: the array is shared by every call on the same GPU and keeps the
+ *   last call's contents (each call rewrites every entry it reads, so
+ *   nothing has to start at zero); calls that overlap on one GPU (on
+ *   different streams, or from different threads) race on it and must not
+ *   be issued.
+ * Returns QMM_OK, or the status of the first failed check (as qmm_matmul_id;
+ * QMM_ERR_SCRATCH when qmm_matmul_id_workspace_bytes(n_experts, n_ids,
+ * n_tokens) exceeds QMM_NOALLOC_SCRATCH_BYTES) without launching, or
+ * QMM_ERR_HIP (also when the scratch address cannot be obtained).
+ */
+int qmm_matmul_id_noalloc(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
+                          int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
+                          const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *stream);
 
 /*
  * qmm_matmul_id_workspace_bytes - the workspace qmm_matmul_id needs for these

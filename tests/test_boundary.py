@@ -36,8 +36,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
-                            "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_workspace_bytes", "qmm_row_bytes", "qmm_supports",
-                            "qmm_status_string"])
+                            "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc",
+                            "qmm_matmul_id_workspace_bytes", "qmm_row_bytes", "qmm_supports", "qmm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -74,7 +74,7 @@ def test_row_bytes_and_supports(L):
 
 
 def test_status_strings(L):
-    for code in range(-7, 1):
+    for code in range(-9, 1):
         s = qmm.qmm_status_string(code)
         assert s.startswith("QMM_OK" if code == 0 else "QMM_ERR_")
     assert qmm.qmm_status_string(-99) == "unknown qmm status"
@@ -197,6 +197,30 @@ def test_matmul_id_workspace_sizes(L):
     assert W(2, 1, 9) == 48 + 16 * (1 + 2)
     assert W(-1, 2, 512) == qmm.QMM_ERR_SHAPE
     assert W(8, 1 << 16, 1 << 16) == qmm.QMM_ERR_SHAPE
+
+
+def _mid_na(L, W=P, t=Q4, ne=8, rows=16, k=64, nb1=36, nb2=576, X=P2, xs=2, ids=ctypes.c_void_p(0x40000), n_ids=2,
+            n=3, Y=P3):
+    return L.qmm_matmul_id_noalloc(W, t, ne, rows, k, nb1, nb2, X, xs, ids, n_ids, n, Y, NULL)
+
+
+def test_matmul_id_noalloc_validation(L):
+    # the same host checks as qmm_matmul_id, none of which touches the GPU
+    assert _mid_na(L, W=NULL) == qmm.QMM_ERR_NULL
+    assert _mid_na(L, ids=NULL) == qmm.QMM_ERR_NULL
+    assert _mid_na(L, t=5) == qmm.QMM_ERR_TYPE
+    assert _mid_na(L, k=48) == qmm.QMM_ERR_SHAPE
+    assert _mid_na(L, xs=3) == qmm.QMM_ERR_SHAPE
+    assert _mid_na(L, nb2=575) == qmm.QMM_ERR_STRIDE
+    assert _mid_na(L, Y=ctypes.c_void_p(0x30002)) == qmm.QMM_ERR_ALIGN
+    # a call whose routing table would exceed the held scratch is refused before any HIP call
+    n = 200000
+    assert L.qmm_matmul_id_workspace_bytes(8, 2, n) > qmm.QMM_NOALLOC_SCRATCH_BYTES
+    assert _mid_na(L, n=n, xs=1) == qmm.QMM_ERR_SCRATCH
+    assert "QMM_NOALLOC_SCRATCH_BYTES" in qmm.qmm_status_string(qmm.QMM_ERR_SCRATCH)
+    # empty calls succeed without touching the device
+    assert _mid_na(L, n=0) == qmm.QMM_OK
+    assert _mid_na(L, rows=0, nb2=0) == qmm.QMM_OK
 
 
 def test_binding_refuses_cpu_tensors():
