@@ -43,7 +43,7 @@ namespace qmm {
 
 constexpr int kRMaxMats = 16;
 
-template <int QT, int NT> struct RCfg {
+template <int QT, int NT, int G = 1> struct RCfg {
   // 16-byte chunks per row per quad of 8 blocks (144, 160 or 272 bytes)
   static constexpr int quad_chunks = Block<QT>::bytes / 2;
   // LDS bytes per row of the stage copy. Unpadded (chunk c at 16 c, one
@@ -53,7 +53,7 @@ template <int QT, int NT> struct RCfg {
   // wavefront then fall in distinct banks (at 36 or 68 they conflict 2-way on
   // gfx950), at the price of two 8-byte stores per chunk.
   static constexpr int row_stride = quad_chunks * 16 + (NT >= 4 ? 8 : 0);
-  static constexpr int w_loads = (16 * quad_chunks + 63) / 64;       // loads per lane for the 16 rows
+  static constexpr int w_loads = (16 * G * quad_chunks + 63) / 64;   // loads per lane for the 16 G rows
   // stages per round, sized so a round's registers stay near 64 VGPRs (the
   // kernel then fits 4 wavefronts per SIMD, i.e. 2 workgroups per CU)
   static constexpr int stage_vgprs = 4 * w_loads + NT * 4;
@@ -67,10 +67,16 @@ template <int QT, int NT> struct RCfg {
   static constexpr bool mid = QTraits<QT>::has_qh && QTraits<QT>::has_min && NT <= 2;
   static constexpr bool lean = QTraits<QT>::nibbles && !mid && NT <= 2;
   static constexpr int depth_large = (lean || mid) ? 2 : depth;
-  static constexpr int waves_per_simd_large = lean ? (NT == 1 ? 8 : 6) : mid ? 6 : 4;
-  static constexpr int w_lds = 16 * row_stride;
+  static constexpr int w_lds = 16 * G * row_stride;
   static constexpr int x_lds = 8 * 4 * NT * 16;                      // 8 blocks x 4 lane groups x NT slots x 8 halves
   static constexpr int lds_per_wave = w_lds + x_lds;
+  // With several row groups per workgroup the stage copies make LDS the
+  // occupancy limit (one or two workgroups of 8 wavefronts per CU), so the
+  // register budget follows from it instead of the single-group tuning.
+  static constexpr int lds_wg_large = kKSplitLarge * (lds_per_wave + G * 32 * 4 * 4);
+  static constexpr int wgs_per_cu_large = (160 * 1024) / lds_wg_large;
+  static constexpr int waves_per_simd_large =
+      G > 1 ? (2 * wgs_per_cu_large < 4 ? 2 * wgs_per_cu_large : 4) : lean ? (NT == 1 ? 8 : 6) : mid ? 6 : 4;
 };
 
 // One matrix of a launch: 64 bytes, so a workgroup fetches all of it with a
@@ -125,8 +131,8 @@ static_assert(sizeof(RRoute) == 64, "one table slot");
 // Fourth word of a buffer resource: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
 
-template <int QT, int NT, bool XF16> struct RRegs {
-  u32x4_t w[RCfg<QT, NT>::w_loads];
+template <int QT, int NT, bool XF16, int G = 1> struct RRegs {
+  u32x4_t w[RCfg<QT, NT, G>::w_loads];
   typename std::conditional<XF16, half4_t, float4_t>::type x[NT];
 };
 
@@ -136,19 +142,19 @@ template <int QT, int NT, bool XF16> struct RRegs {
 // wavefront's LDS copy; chunks past 16 * QC re-read chunk 0 and are not stored
 // (woff < 0). The activation piece of a lane is block lane / 8 of the quad,
 // elements 4 (lane % 8) .. +3, staged at LDS byte xw (token slot 0).
-template <int QT, int NT> struct RLane {
-  int woff[RCfg<QT, NT>::w_loads];
-  uint32_t wv[RCfg<QT, NT>::w_loads];
+template <int QT, int NT, int G = 1> struct RLane {
+  int woff[RCfg<QT, NT, G>::w_loads];
+  uint32_t wv[RCfg<QT, NT, G>::w_loads];
   int xw;
 
   __device__ __forceinline__ RLane(int lane, uint32_t nb1) {
-    constexpr int QC = RCfg<QT, NT>::quad_chunks;
+    constexpr int QC = RCfg<QT, NT, G>::quad_chunks;
 #pragma unroll
-    for (int j = 0; j < RCfg<QT, NT>::w_loads; ++j) {
+    for (int j = 0; j < RCfg<QT, NT, G>::w_loads; ++j) {
       const int c = 64 * j + lane;
-      const bool ok = c < 16 * QC;
+      const bool ok = c < 16 * G * QC;
       const uint32_t r = static_cast<uint32_t>(c) / QC;
-      woff[j] = ok ? static_cast<int>(r) * RCfg<QT, NT>::row_stride + 16 * (c - QC * static_cast<int>(r)) : -1;
+      woff[j] = ok ? static_cast<int>(r) * RCfg<QT, NT, G>::row_stride + 16 * (c - QC * static_cast<int>(r)) : -1;
       // r nb1 + 16 (c - QC r) with one 24-bit multiply-add (nb1 < 2^24)
       wv[j] = ok ? __umul24(r, nb1 - 16 * QC) + 16 * c : 0;
     }
@@ -162,10 +168,10 @@ template <int QT, int NT> struct RLane {
 // Consume one stage: copy the weights into the wavefront's LDS area (wl) and
 // the activations, as fp16 in MFMA operand order, into xs; then run the 8
 // blocks (4 pairs) through the matrix cores into acc.
-template <int QT, int NT, bool XF16>
-__device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RLane<QT, NT> &L, unsigned char *wl,
-                                          half8_t *xs, int lane, float acc[4]) {
-  using C = RCfg<QT, NT>;
+template <int QT, int NT, bool XF16, int G>
+__device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16, G> &r, const RLane<QT, NT, G> &L, unsigned char *wl,
+                                          half8_t *xs, int lane, float (&acc)[G][4]) {
+  using C = RCfg<QT, NT, G>;
 #pragma unroll
   for (int j = 0; j < C::w_loads; ++j)
     if (L.woff[j] >= 0) {
@@ -188,70 +194,77 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16> &r, const RL
     *reinterpret_cast<half4_t *>(reinterpret_cast<unsigned char *>(xs) + L.xw + 16 * t) = h;
   }
   const int r16 = lane & 15, g = lane >> 4;
-  const unsigned char *rb0 = wl + r16 * C::row_stride;
   const int slot = min(r16, NT - 1);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {  // pairs of blocks in the quad
-    const unsigned char *rb = rb0 + u * (2 * Block<QT>::bytes);
     // A-operand rows past the NT token slots repeat the last slot (no
     // divergent reads; their results are never stored)
     const half8_t xe = xs[(4 * (2 * u) + g) * NT + slot];
     const half8_t xo = xs[(4 * (2 * u + 1) + g) * NT + slot];
-    auto ld = [&](int off) { return *reinterpret_cast<const uint32_t *>(rb + off); };
-    if constexpr (QT == QMM_TYPE_Q4_0) {
-      const uint32_t a0 = ld(4 * g), a1 = ld(4 * g + 4), b = ld(20 + 4 * g), d0 = ld(0), d1 = ld(16);
-      gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), 0), d0 & 0xFFFFu);
-      gemv_block<NT>(acc, xo, gemv_codes<QT>(b, 0), d1 >> 16);
-    } else if constexpr (QT == QMM_TYPE_Q4_1) {
-      // blocks at bytes 0 and 20 of the pair: d|m dword, then 4 code dwords
-      const uint32_t a = ld(4 + 4 * g), b = ld(24 + 4 * g), dm0 = ld(0), dm1 = ld(20);
-      gemv_block_min<NT>(acc, xe, gemv_codes<QT>(a, 0), dm0);
-      gemv_block_min<NT>(acc, xo, gemv_codes<QT>(b, 0), dm1);
-    } else if constexpr (QT == QMM_TYPE_Q5_0) {
-      // blocks at bytes 0 and 22: d, fifth-bit word, codes (block 0's start
-      // 2 bytes into a dword, block 1's are dword-aligned)
-      const uint32_t w0 = ld(0), w1 = ld(4), a0 = ld(4 + 4 * g), a1 = ld(8 + 4 * g);
-      const uint32_t w5 = ld(20), h1 = ld(24), b = ld(28 + 4 * g);
-      gemv_block<NT>(acc, xe, gemv_codes5<QT>(shift16(a0, a1), shift16(w0, w1), 4 * g), w0 & 0xFFFFu);
-      gemv_block<NT>(acc, xo, gemv_codes5<QT>(b, h1, 4 * g), w5 >> 16);
-    } else if constexpr (QT == QMM_TYPE_Q5_1) {
-      // blocks at bytes 0 and 24: d|m, fifth-bit word, 4 code dwords
-      const uint32_t dm0 = ld(0), h0 = ld(4), a = ld(8 + 4 * g), dm1 = ld(24), h1 = ld(28), b = ld(32 + 4 * g);
-      gemv_block_min<NT>(acc, xe, gemv_codes5<QT>(a, h0, 4 * g), dm0);
-      gemv_block_min<NT>(acc, xo, gemv_codes5<QT>(b, h1, 4 * g), dm1);
-    } else {
-      const uint32_t a0 = ld(8 * g), a1 = ld(8 * g + 4), a2 = ld(8 * g + 8);
-      const uint32_t b0 = ld(36 + 8 * g), b1 = ld(40 + 8 * g), d0 = ld(0), d1 = ld(32);
-      gemv_block<NT>(acc, xe, gemv_codes<QT>(shift16(a0, a1), shift16(a1, a2)), d0 & 0xFFFFu);
-      gemv_block<NT>(acc, xo, gemv_codes<QT>(b0, b1), d1 >> 16);
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {  // 16-row groups sharing the activations
+      float *acc_g = acc[gi];
+      const unsigned char *rb = wl + (16 * gi + r16) * C::row_stride + u * (2 * Block<QT>::bytes);
+      auto ld = [&](int off) { return *reinterpret_cast<const uint32_t *>(rb + off); };
+      if constexpr (QT == QMM_TYPE_Q4_0) {
+        const uint32_t a0 = ld(4 * g), a1 = ld(4 * g + 4), b = ld(20 + 4 * g), d0 = ld(0), d1 = ld(16);
+        gemv_block<NT>(acc_g, xe, gemv_codes<QT>(shift16(a0, a1), 0), d0 & 0xFFFFu);
+        gemv_block<NT>(acc_g, xo, gemv_codes<QT>(b, 0), d1 >> 16);
+      } else if constexpr (QT == QMM_TYPE_Q4_1) {
+        // blocks at bytes 0 and 20 of the pair: d|m dword, then 4 code dwords
+        const uint32_t a = ld(4 + 4 * g), b = ld(24 + 4 * g), dm0 = ld(0), dm1 = ld(20);
+        gemv_block_min<NT>(acc_g, xe, gemv_codes<QT>(a, 0), dm0);
+        gemv_block_min<NT>(acc_g, xo, gemv_codes<QT>(b, 0), dm1);
+      } else if constexpr (QT == QMM_TYPE_Q5_0) {
+        // blocks at bytes 0 and 22: d, fifth-bit word, codes (block 0's start
+        // 2 bytes into a dword, block 1's are dword-aligned)
+        const uint32_t w0 = ld(0), w1 = ld(4), a0 = ld(4 + 4 * g), a1 = ld(8 + 4 * g);
+        const uint32_t w5 = ld(20), h1 = ld(24), b = ld(28 + 4 * g);
+        gemv_block<NT>(acc_g, xe, gemv_codes5<QT>(shift16(a0, a1), shift16(w0, w1), 4 * g), w0 & 0xFFFFu);
+        gemv_block<NT>(acc_g, xo, gemv_codes5<QT>(b, h1, 4 * g), w5 >> 16);
+      } else if constexpr (QT == QMM_TYPE_Q5_1) {
+        // blocks at bytes 0 and 24: d|m, fifth-bit word, 4 code dwords
+        const uint32_t dm0 = ld(0), h0 = ld(4), a = ld(8 + 4 * g), dm1 = ld(24), h1 = ld(28), b = ld(32 + 4 * g);
+        gemv_block_min<NT>(acc_g, xe, gemv_codes5<QT>(a, h0, 4 * g), dm0);
+        gemv_block_min<NT>(acc_g, xo, gemv_codes5<QT>(b, h1, 4 * g), dm1);
+      } else {
+        const uint32_t a0 = ld(8 * g), a1 = ld(8 * g + 4), a2 = ld(8 * g + 8);
+        const uint32_t b0 = ld(36 + 8 * g), b1 = ld(40 + 8 * g), d0 = ld(0), d1 = ld(32);
+        gemv_block<NT>(acc_g, xe, gemv_codes<QT>(shift16(a0, a1), shift16(a1, a2)), d0 & 0xFFFFu);
+        gemv_block<NT>(acc_g, xo, gemv_codes<QT>(b0, b1), d1 >> 16);
+      }
     }
   }
 }
 
 // Partial sums of the wavefronts, added in wavefront order. D element e of
-// lane l: token 4 (l / 16) + e, row l % 16. The barrier waits on LDS only, so
-// weight loads in flight need not land first.
-template <int NT, int WAVES>
-__device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const float acc[4],
+// lane l: token 4 (l / 16) + e, row l % 16 of row group gi. The barrier
+// waits on LDS only, so weight loads in flight need not land first.
+template <int NT, int WAVES, int G>
+__device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const float (&acc)[G][4],
                                          __attribute__((address_space(1))) float *Y, int row0, int n_rows,
                                          int n_tokens, GPtr<int32_t> tok_rows = nullptr) {
   constexpr int kRedLanes = NT > 4 ? 32 : 16;
+  static_assert(16 * G * NT <= 64 * WAVES, "one thread per output of the workgroup");
   if (lane < kRedLanes) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[(wave * 32 + lane) * 4 + e] = acc[e];
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[((wave * G + gi) * 32 + lane) * 4 + e] = acc[gi][e];
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (threadIdx.x < 16 * NT) {
-    const int r = threadIdx.x & 15;
-    const int t = threadIdx.x >> 4;
+  if (threadIdx.x < 16 * G * NT) {
+    const int gi = threadIdx.x / (16 * NT), rem = threadIdx.x - gi * (16 * NT);
+    const int r = rem & 15;
+    const int t = rem >> 4;
     const int src = r + 16 * (t >> 2);
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += red[(w * 32 + src) * 4 + (t & 3)];
-    const int row = row0 + r;
+    for (int w = 0; w < WAVES; ++w) sum += red[((w * G + gi) * 32 + src) * 4 + (t & 3)];
+    const int row = row0 + 16 * gi + r;
     if (t < n_tokens && row < n_rows) {
       // token slot t's output row: t, or (tile form) its pair's row
       const int64_t yr = tok_rows ? static_cast<int64_t>(tok_rows[t]) : t;
@@ -260,12 +273,13 @@ __device__ __forceinline__ void r_reduce(float *red, int wave, int lane, const f
   }
 }
 
-template <int QT, int NT, bool XF16, int WAVES, bool IDS = false, bool TILES = false>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::waves_per_simd_large : 4)) void gemv_stream_kernel(
+template <int QT, int NT, bool XF16, int WAVES, bool IDS = false, bool TILES = false, int G = 1>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT, G>::waves_per_simd_large : 4)) void gemv_stream_kernel(
     const uint8_t *W0, const void *X0, float *Y0, int64_t nb1_0, int n_rows0, int nblk0, int n_tokens0, int k0,
     int64_t, int64_t, const RBatch batch) {
   (void)batch;  // read through the kernel-argument pointer
-  using C = RCfg<QT, NT>;
+  static_assert(G == 1 || (!IDS && !TILES), "row groups of 16 G rows: plain MUL_MATs only");
+  using C = RCfg<QT, NT, G>;
   constexpr int QC = C::quad_chunks;
   constexpr int D = WAVES == kKSplitLarge ? C::depth_large : C::depth;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
     k = static_cast<int>(rec[11]);
   }
   const int rg = blockIdx.x;
-  if (rg * 16 >= n_rows) return;  // whole workgroup: past this matrix's rows
+  if (rg * 16 * G >= n_rows) return;  // whole workgroup: past this matrix's rows
   // The output pointer may be rebuilt from integers, so it is cast to the
   // global address space explicitly (a generic pointer would make the store a
   // flat access).
@@ -351,7 +365,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = rg * 16;
+  const int row0 = rg * 16 * G;
   // this wavefront's quads [q_lo, q_hi)
   const int qn = nblk >> 3;
   const int q_lo = (wave * qn) / WAVES, q_hi = ((wave + 1) * qn) / WAVES;
@@ -359,7 +373,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
   unsigned char *wl = smem + wave * C::lds_per_wave;
   half8_t *xs = reinterpret_cast<half8_t *>(wl + C::w_lds);
   float *red = reinterpret_cast<float *>(smem + WAVES * C::lds_per_wave);
-  const RLane<QT, NT> L(lane, static_cast<uint32_t>(nb1));
+  const RLane<QT, NT, G> L(lane, static_cast<uint32_t>(nb1));
 
   // Weights and activations are read through buffer resources: a uniform
   // base with 32-bit per-lane offsets (one multiply per load slot, once) and
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
     xv[t] = (xrow * static_cast<uint32_t>(k) + 4 * lane) * (XF16 ? 2 : 4);
   }
 
-  auto issue = [&](RRegs<QT, NT, XF16> &r, int q) {
+  auto issue = [&](RRegs<QT, NT, XF16, G> &r, int q) {
     const int wq = q * (QC * 16), xq = q * 256 * (XF16 ? 2 : 4);
 #pragma unroll
     for (int j = 0; j < C::w_loads; ++j)
@@ -403,37 +417,58 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT>::
     }
   };
 
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[G][4];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) acc[gi][0] = acc[gi][1] = acc[gi][2] = acc[gi][3] = 0.f;
   // Rounds of up to D stages: all loads of a round are issued at once (the
   // whole wavefront's share of k in one round for the common shapes), then
   // the stages are consumed in order. Other wavefronts on the CU overlap
   // their computation with this one's loads.
-  RRegs<QT, NT, XF16> st[D];
+  RRegs<QT, NT, XF16, G> st[D];
   for (int q = q_lo; q < q_hi; q += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i)
       if (q + i < q_hi) issue(st[i], q + i);
 #pragma unroll
     for (int i = 0; i < D; ++i)
-      if (q + i < q_hi) r_consume<QT, NT, XF16>(st[i], L, wl, xs, lane, acc);
+      if (q + i < q_hi) r_consume<QT, NT, XF16, G>(st[i], L, wl, xs, lane, acc);
   }
-  r_reduce<NT, WAVES>(red, wave, lane, acc, Y, row0, n_rows, n_tokens, tok);
+  r_reduce<NT, WAVES, G>(red, wave, lane, acc, Y, row0, n_rows, n_tokens, tok);
 }
 
 // ------------------------------------------------------------------ host side
 
-template <int QT, int NT, bool XF16, int WAVES>
+// Row groups per workgroup. A multi-token call reads its n_tokens x k
+// activations once per workgroup, so a workgroup that covers G 16-row groups
+// (one staged activation set feeding G MFMA row tiles) divides that traffic
+// by G, at the price of more stage registers and LDS per wavefront. Measured
+// on MI355X (32000 x 4096 and 11008 x 4096 Q4_0, weights from HBM): with 8
+// token slots G = 2 takes 34.4 -> 26.6 us and 14.9 -> 14.2 us, G = 4 29.5 and
+// 13.7 us; with 4 slots G = 2 helps the 32000-row matrix (-7 %) and slows the
+// 11008-row one (+12 %), G = 4 slows both; 2 slots and single-token calls
+// gain nothing. So only 8-slot calls on launches of more row groups than CUs
+// (8 wavefronts per workgroup) use G = 2, where the stage copies fit LDS.
+template <int QT, int NT, int G> constexpr bool groups_fit() {
+  return kKSplitLarge * RCfg<QT, NT, G>::lds_per_wave + kKSplitLarge * G * 32 * 4 * 4 <= 160 * 1024;
+}
+template <int QT, int NT> constexpr int row_groups_for() {
+  if constexpr (NT == 8 && groups_fit<QT, NT, 2>()) return 2;
+  else return 1;
+}
+
+template <int QT, int NT, bool XF16, int WAVES, int G>
 static hipError_t r_go_w(const RBatch &B, int count, int max_rg, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(WAVES) * RCfg<QT, NT>::lds_per_wave + WAVES * 32 * 4 * sizeof(float);
+  const size_t lds = static_cast<size_t>(WAVES) * RCfg<QT, NT, G>::lds_per_wave + WAVES * G * 32 * 4 * sizeof(float);
   const RMat &m0 = B.m[0];
-  return launch(gemv_stream_kernel<QT, NT, XF16, WAVES>, dim3(max_rg, count), dim3(64 * WAVES), lds, s, m0.W, m0.X,
-                m0.Y, m0.nb1, m0.n_rows, m0.nblk, m0.n_tokens, m0.k, int64_t{0}, int64_t{0}, B);
+  return launch(gemv_stream_kernel<QT, NT, XF16, WAVES, false, false, G>, dim3((max_rg + G - 1) / G, count),
+                dim3(64 * WAVES), lds, s, m0.W, m0.X, m0.Y, m0.nb1, m0.n_rows, m0.nblk, m0.n_tokens, m0.k, int64_t{0},
+                int64_t{0}, B);
 }
 
 template <int QT, int NT, bool XF16>
 static hipError_t r_go(const RBatch &B, int count, int max_rg, int waves, hipStream_t s) {
-  return waves == kKSplitSmall ? r_go_w<QT, NT, XF16, kKSplitSmall>(B, count, max_rg, s)
-                               : r_go_w<QT, NT, XF16, kKSplitLarge>(B, count, max_rg, s);
+  return waves == kKSplitSmall ? r_go_w<QT, NT, XF16, kKSplitSmall, 1>(B, count, max_rg, s)
+                               : r_go_w<QT, NT, XF16, kKSplitLarge, row_groups_for<QT, NT>()>(B, count, max_rg, s);
 }
 
 template <int QT, bool XF16>

@@ -47,6 +47,28 @@ def test_gemv_ragged(qtype, xdt, n):
 
 @pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])
+@pytest.mark.parametrize("n", [5, 8])
+def test_gemv_multi_row_group_workgroups(qtype, xdt, n):
+    """Decode calls with 5 to 8 tokens on launches of more 16-row groups than
+    CUs: each workgroup covers two row groups with one set of staged
+    activations; 4112 rows make the last workgroup's second group fall past
+    the matrix, and padded rows keep the streaming layout. Every element
+    against the oracle, and the same outputs bitwise from the matrix written
+    as a dense copy and from a run with the rows permuted."""
+    rows, k = 4112, 512
+    assert (rows + 15) // 16 > 256
+    W, X = _inputs(qtype, rows, k, n, 16 * 3, xdt=xdt)
+    y = run_matmul(W, qtype, k, X, GEMV)
+    say(f"gemv two row groups per workgroup type={qtype} n={n} x={np.dtype(xdt).name}")
+    assert_close_to_oracle(y, W, qtype, k, X, "gemv 2 row groups")
+    dense = synth.dense_row_bytes(qtype, k)
+    assert_bitwise(run_matmul(np.ascontiguousarray(W[:, :dense]), qtype, k, X, GEMV), y, "dense copy")
+    perm = np.random.default_rng(11).permutation(rows)
+    assert_bitwise(run_matmul(W[perm], qtype, k, X, GEMV), y[:, perm], "row permutation")
+
+
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
+@pytest.mark.parametrize("xdt", [np.float32, np.float16])
 @pytest.mark.parametrize("n", [1, 9, 16, 37, 128, 200])
 def test_gemm_ragged(qtype, xdt, n):
     for rows, k, extra, offset in ((1, 32, 0, 0), (37, 96, 2, 2), (130, 160, 0, 0), (300, 512, 4, 0),
