@@ -324,6 +324,64 @@ def time_type(torch, qmm, synth, qt, with_oracle=False):
     return res
 
 
+# ---------------------------------------------------------------- output projection and 512-token prefill
+
+def _roof(achieved, peak, unit, bound):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None}
+
+
+def time_output_projection(torch, qmm, synth):
+    """The output-projection workload: Q4_0 32000x4096 with rows padded to
+    nb1 = 2560 (256 random padding bytes per row), fp32 activations of 1, 2,
+    4 and 8 tokens, on the decode kernel. Back-to-back launches in a graph
+    over >= 1.1 GiB of weight copies, so the weights come from HBM.
+    Algorithmic bytes: the blocks (padding excluded), X and Y."""
+    import numpy as np
+    rows, k, nb1, qt = synth.N_VOCAB, synth.N_EMBD, 2560, synth.TYPE_Q4_0
+    rng = np.random.Generator(np.random.PCG64(4400))
+    W0 = torch.from_numpy(synth.make_weights(qt, rows, k, nb1, rng)).cuda()
+    copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    reps = 4 * copies
+    out = {"workload": f"{rows}x{k} Q4_0, nb1 = {nb1} (padded rows), fp32 activations"}
+    for n in (1, 2, 4, 8):
+        X = torch.from_numpy(synth.make_activations(n, k, rng)).cuda()
+        Y = torch.empty((n, rows), dtype=torch.float32, device="cuda")
+        us = _graph_time(torch, lambda: [qmm.qmm_matmul(Ws[i % copies], qt, k, X, Y=Y) for i in range(reps)], reps)
+        byts = rows * synth.dense_row_bytes(qt, k) + 4 * n * k + 4 * n * rows
+        gbs = byts / (us * 1e-6) / 1e9
+        out[f"n{n}"] = {"tokens": n, "us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": byts,
+                        "GB_per_s": round(gbs, 2), "kernel": "gemv_stream_kernel",
+                        "roofline": _roof(gbs, HBM_PEAK_GBS, "GB/s", "hbm")}
+    return out
+
+
+def time_prefill_512(torch, qmm, synth):
+    """The 512-token prefill workload: Q4_0 4096x4096 and 11008x4096 with
+    fp16 activations of 512 tokens (the batch of the capability probe), on
+    the matrix-core kernel; back-to-back launches in a graph over >= 1.1 GiB
+    of weight copies. Flops: 2 * rows * k * tokens."""
+    import numpy as np
+    qt, k, T = synth.TYPE_Q4_0, synth.N_EMBD, 512
+    rng = np.random.Generator(np.random.PCG64(4500))
+    out = {"workload": f"Q4_0 4096x4096 and 11008x4096, {T} fp16 tokens"}
+    for rows in (synth.N_EMBD, synth.N_FF):
+        W0 = torch.from_numpy(synth.make_weights(qt, rows, k, None, rng)).cuda()
+        copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
+        Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+        X = torch.from_numpy(synth.make_activations(T, k, rng, np.float16)).cuda()
+        Y = torch.empty((T, rows), dtype=torch.float32, device="cuda")
+        us = _graph_time(torch, lambda: [qmm.qmm_matmul_x16(Ws[i % copies], qt, k, X, Y=Y) for i in range(copies)],
+                         copies)
+        tfl = 2 * rows * k * T / (us * 1e-6) / 1e12
+        out[f"{rows}x{k}"] = {"tokens": T, "us_per_launch": round(us, 3), "flops_per_launch": 2 * rows * k * T,
+                              "TFLOP_per_s": round(tfl, 2), "kernel": "gemm_kernel",
+                              "roofline": _roof(tfl, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma")}
+        del Ws, W0
+    return out
+
+
 # ---------------------------------------------------------------- MUL_MAT_ID
 
 MOE_EXPERTS, MOE_ROWS, MOE_K, MOE_USED = 8, 14336, 4096, 2
@@ -705,6 +763,8 @@ def main():
         out["decode_per_call"] = {"ms_per_pass": round(ms["decode_per_call"], 4), "launches": n,
                                   "us_per_launch": round(us_launch["decode_per_call"], 3),
                                   "GB_per_s": round(gbs_pc, 2), "frac_of_hbm_peak": round(gbs_pc / HBM_PEAK_GBS, 4)}
+    out["output_projection"] = time_output_projection(torch, qmm, synth)
+    out["prefill_512"] = time_prefill_512(torch, qmm, synth)
     if not args.no_get_rows:
         out["get_rows"] = time_get_rows(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if not args.no_matmul_id:

@@ -335,16 +335,27 @@ struct GemmRoute {
 // BM = 128 rows per tile, or 64 for launches with few tiles: each
 // wavefront then computes 32 x 64, only the first 128 threads stage
 // weights, and (with fp16 activations) three workgroups fit a CU.
-template <int QT, bool XF16, bool ALIGN4, bool ROUTED = false, int BM = kBM>
-__global__ __launch_bounds__(kGemmThreads, (BM == kBM || !XF16) ? 2 : 3) void gemm_kernel(
+// KS = 2 (64-row tiles, a block count that is a multiple of 4): the
+// workgroup holds two groups of four wavefronts, each taking half of k with
+// LDS stages of its own; the second group's partial tile is added to the
+// first's through LDS in a fixed order before the store. A launch that
+// fills only one wavefront per SIMD then has two, with no memory beyond LDS.
+template <int QT, bool XF16, bool ALIGN4, bool ROUTED = false, int BM = kBM, int KS = 1>
+__global__ __launch_bounds__(kGemmThreads * KS, KS == 2 ? 1 : ((BM == kBM || !XF16) ? 2 : 3)) void gemm_kernel(
     const uint8_t *__restrict__ W, int n_rows, int nblk, int64_t nb1, const void *__restrict__ X, int n_tokens, int k,
     float *__restrict__ Y, bool y_vec4, int row_tiles, GemmRoute route) {
   static_assert(BM == kBM || (BM == kBM / 2 && !ROUTED), "128-row tiles, or 64 for the plain product");
+  static_assert(KS == 1 || (KS == 2 && BM == kBM / 2 && !ROUTED), "the k split is for plain 64-row tiles");
   constexpr int MI = BM / 32;  // 16-row MFMA tiles per wavefront
-  __shared__ __attribute__((aligned(16))) _Float16 Ws[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) _Float16 Xs[2][kBN * kBK];
+  constexpr int kTileHalves = 2 * (BM + kBN) * kBK;  // one group's two stages of weights and activations
+  __shared__ __attribute__((aligned(16))) _Float16 lds_static[KS == 1 ? kTileHalves : 8];
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
+  const int kg = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kGemmThreads);
+  _Float16 *lds_group = (KS == 1 ? lds_static : lds_dynamic) + kg * kTileHalves;
+  _Float16 *Ws[2] = {lds_group, lds_group + BM * kBK};
+  _Float16 *Xs[2] = {lds_group + 2 * BM * kBK, lds_group + 2 * BM * kBK + kBN * kBK};
 
-  const int tid = threadIdx.x;
+  const int tid = static_cast<int>(threadIdx.x) - kg * kGemmThreads;  // thread within the k group
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -403,18 +414,21 @@ __global__ __launch_bounds__(kGemmThreads, (BM == kBM || !XF16) ? 2 : 3) void ge
     XPieces<XF16> x;
   };
   // Stages with a whole pair of blocks; an odd block count leaves one more.
-  const int n_full = nblk / 2;
+  // With KS = 2 each group takes half of them (nblk % 4 == 0): group kg
+  // computes stages st0 .. st0 + n_full - 1.
+  const int n_full = nblk / (2 * KS);
+  const int st0 = kg * n_full;
   auto load = [&](Stage &r, int st) {
     if (wstage) {
       if constexpr (ALIGN4)
-        r.w = load_half_pair<QT>(rp, st, sh);
+        r.w = load_half_pair<QT>(rp, st0 + st, sh);
       else
-        r.w = load_half_u16<QT>(rp, 2 * st + sh, nblk);
+        r.w = load_half_u16<QT>(rp, 2 * (st0 + st) + sh, nblk);
     }
     if constexpr (ROUTED)
       r.x = load_x_rows<XF16>(xrow, k, kBK * st, tid, false);
     else
-      r.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * st, tid, false);
+      r.x = load_x_pieces<XF16>(X, tok0, n_tokens, k, kBK * (st0 + st), tid, false);
   };
   auto store = [&](int buf, const Stage &r) {
     if (wstage) store_half<QT>(Ws[buf], srow, 4 * sh, r.w, ALIGN4 && sh == 0);
@@ -471,7 +485,7 @@ __global__ __launch_bounds__(kGemmThreads, (BM == kBM || !XF16) ? 2 : 3) void ge
     }
     if (s < n_full) compute(0);  // odd count of whole stages: the last one
   }
-  if (nblk & 1) {
+  if (KS == 1 && (nblk & 1)) {
     // the last, single block: half 0 loads it, half 1 stores zeros
     const int buf = n_full & 1;
     Stage t;
@@ -486,6 +500,25 @@ __global__ __launch_bounds__(kGemmThreads, (BM == kBM || !XF16) ? 2 : 3) void ge
     compute(buf);
   }
 
+  if constexpr (KS == 2) {
+    // group 1's partial tile through LDS (its stage buffers are free once
+    // every wavefront has passed this barrier), added to group 0's in a
+    // fixed order; group 0 stores
+    lds_barrier();
+    float4_t *red = reinterpret_cast<float4_t *>(lds_dynamic) + (wave * 64 + lane) * (MI * 4);
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[i * 4 + j] = acc[i][j];
+    }
+    lds_barrier();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += red[i * 4 + j];
+  }
   // D element e of lane l in tile (i, j): row (BM / 2) wm + 16 i + 4 (l / 16) + e,
   // token 64 wn + 16 j + l % 16.
 #pragma unroll
@@ -508,15 +541,18 @@ __global__ __launch_bounds__(kGemmThreads, (BM == kBM || !XF16) ? 2 : 3) void ge
   }
 }
 
-template <int QT, bool XF16, int BM>
+template <int QT, bool XF16, int BM, int KS = 1>
 static hipError_t gemm_dispatch(bool align4, dim3 grid, hipStream_t s, const uint8_t *w, int n_rows, int nblk,
                                 int64_t nb1, const void *X, int n_tokens, int k, float *Y, bool y_vec4, int row_tiles) {
   const GemmRoute none{nullptr, nullptr, 0, 0, 0};
+  // KS = 2: each k group's two stages of weights and activations in dynamic LDS
+  const size_t lds = KS == 1 ? 0 : static_cast<size_t>(KS) * 2 * (BM + kBN) * kBK * sizeof(_Float16);
+  const dim3 block(kGemmThreads * KS);
   if (align4)
-    return launch(gemm_kernel<QT, XF16, true, false, BM>, grid, dim3(kGemmThreads), 0, s, w, n_rows, nblk, nb1, X,
-                  n_tokens, k, Y, y_vec4, row_tiles, none);
-  return launch(gemm_kernel<QT, XF16, false, false, BM>, grid, dim3(kGemmThreads), 0, s, w, n_rows, nblk, nb1, X,
-                n_tokens, k, Y, y_vec4, row_tiles, none);
+    return launch(gemm_kernel<QT, XF16, true, false, BM, KS>, grid, block, lds, s, w, n_rows, nblk, nb1, X, n_tokens,
+                  k, Y, y_vec4, row_tiles, none);
+  return launch(gemm_kernel<QT, XF16, false, false, BM, KS>, grid, block, lds, s, w, n_rows, nblk, nb1, X, n_tokens, k,
+                Y, y_vec4, row_tiles, none);
 }
 
 hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
@@ -559,8 +595,16 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
   const int rt = static_cast<int>(row_tiles);
   const int nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows), nt = static_cast<int>(n_tokens),
             kk = static_cast<int>(k);
+  // Small launches whose block count splits into two equal halves of whole
+  // stages also split k inside the workgroup (two wavefronts per SIMD).
+  const bool ksplit = small && nblk % 4 == 0;
   return by_qtype(qtype, [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
+    if (ksplit) {
+      if (x_f16)
+        return gemm_dispatch<QT, true, kBM / 2, 2>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
+      return gemm_dispatch<QT, false, kBM / 2, 2>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
+    }
     if (small) {
       if (x_f16) return gemm_dispatch<QT, true, kBM / 2>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
       return gemm_dispatch<QT, false, kBM / 2>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
