@@ -22,9 +22,13 @@ TYPE_Q4_1 = 3
 TYPE_Q5_0 = 6
 TYPE_Q5_1 = 7
 TYPE_Q8_0 = 8
+TYPE_Q4_K = 12
 QK = 32
-BLOCK_BYTES = {TYPE_Q4_0: 18, TYPE_Q4_1: 20, TYPE_Q5_0: 22, TYPE_Q5_1: 24, TYPE_Q8_0: 34}
-TYPE_NAMES = {TYPE_Q4_0: "q4_0", TYPE_Q4_1: "q4_1", TYPE_Q5_0: "q5_0", TYPE_Q5_1: "q5_1", TYPE_Q8_0: "q8_0"}
+QK_K = 256
+BLOCK_BYTES = {TYPE_Q4_0: 18, TYPE_Q4_1: 20, TYPE_Q5_0: 22, TYPE_Q5_1: 24, TYPE_Q8_0: 34, TYPE_Q4_K: 144}
+BLOCK_WEIGHTS = {TYPE_Q4_0: QK, TYPE_Q4_1: QK, TYPE_Q5_0: QK, TYPE_Q5_1: QK, TYPE_Q8_0: QK, TYPE_Q4_K: QK_K}
+TYPE_NAMES = {TYPE_Q4_0: "q4_0", TYPE_Q4_1: "q4_1", TYPE_Q5_0: "q5_0", TYPE_Q5_1: "q5_1", TYPE_Q8_0: "q8_0",
+              TYPE_Q4_K: "q4_k"}
 
 N_EMBD = 4096
 N_FF = 11008
@@ -52,7 +56,7 @@ def rng_for(config: int, layer: int, tensor: int, what: int) -> np.random.Genera
 
 
 def dense_row_bytes(qtype: int, k: int) -> int:
-    return (k // QK) * BLOCK_BYTES[qtype]
+    return (k // BLOCK_WEIGHTS[qtype]) * BLOCK_BYTES[qtype]
 
 
 def assemble_rows(d_bits: np.ndarray, code_bytes: np.ndarray, nb1: int,
@@ -84,7 +88,24 @@ def make_weights(qtype: int, rows: int, k: int, nb1: int | None, rng: np.random.
     about [-7.5 d, 7.5 d], as a min/max quantiser makes them); Q5_0 four
     random bytes of fifth bits then the code bytes; Q5_1 a minimum
     fp16(-U[12, 18] * |d draw|), then the same as Q5_0; Q8_0 codes uniform
-    integers in [-127, 127]; padding bytes uniform 0..255."""
+    integers in [-127, 127]; Q4_K (256-weight super-blocks) d and dmin =
+    fp16(U[d_lo, d_hi] / 25), then 12 uniform random scale bytes (so every
+    6-bit sub-block scale and minimum value occurs) and 128 uniform random
+    code bytes; padding bytes uniform 0..255."""
+    if qtype == TYPE_Q4_K:
+        if k % QK_K:
+            raise ValueError("k must be a multiple of 256")
+        nsb = k // QK_K
+        dense = dense_row_bytes(qtype, k)
+        nb1 = dense if nb1 is None else nb1
+        dd = rng.uniform(d_lo / 25, d_hi / 25, size=(rows, nsb, 2)).astype(np.float16).view(np.uint8)
+        W = np.empty((rows, nb1), dtype=np.uint8)
+        blk = W[:, :dense].reshape(rows, nsb, 144)
+        blk[:, :, 0:4] = dd.reshape(rows, nsb, 4)  # d then dmin, little-endian
+        blk[:, :, 4:] = rng.integers(0, 256, size=(rows, nsb, 140), dtype=np.uint8)
+        if nb1 > dense:
+            W[:, dense:] = rng.integers(0, 256, size=(rows, nb1 - dense), dtype=np.uint8)
+        return W
     if k % QK:
         raise ValueError("k must be a multiple of 32")
     nblk = k // QK

@@ -42,6 +42,19 @@ Readings taken where the pages are silent (also listed in the design notes):
     32-bit little-endian word whose bit j is the fifth bit of element j,
     then the 16 nibble bytes in Q4_0's order holding the low four bits.
     Codes 0..31; Q5_0 has z = 16 (w = d * (q - 16)), Q5_1 w = d * q + m.
+  * Q4_K (a k-quant; [Arch] says k-quants use 256-weight blocks with scales
+    and minimums stored in two levels, 6-bit upper and 4-bit lower, and
+    [Graph]/[Load] size a Q4_K tensor as ne[0] / 256 blocks; the bit layout
+    is not printed, so this is the GGUF layout taken as a reading): a
+    144-byte super-block of 256 weights = binary16 d, binary16 dmin, 12
+    bytes holding eight 6-bit sub-block scales sc_j and minimums m_j, then
+    128 code bytes. Scale bytes s[0..11]: for j < 4, sc_j = s[j] & 63 and
+    m_j = s[j + 4] & 63; for j >= 4, sc_j = (s[j + 4] & 15) | (s[j - 4] >> 6) << 4
+    and m_j = (s[j + 4] >> 4) | (s[j] >> 6) << 4. Code byte 32 c + l holds
+    element 64 c + l (sub-block 2 c) in its low nibble and element
+    64 c + 32 + l (sub-block 2 c + 1) in its high nibble. Weight of element i
+    of sub-block j: w = d * sc_j * q_i - dmin * m_j, rounded once to fp32
+    (both products are exact).
   * The scale d (and m) is stored little-endian as IEEE-754 binary16.
   * Activations X are [n_tokens][k] with k contiguous; Y is [n_tokens][n_rows]
     with rows contiguous, fully overwritten.
@@ -49,7 +62,8 @@ Readings taken where the pages are silent (also listed in the design notes):
     every finite binary16 d and every code); the dot products are
     accumulated in fp64 here.
 
-Parity pins live in tests/test_oracle_pins.py. No function here is unpinned.
+Parity pins live in tests/test_oracle_pins.py and tests/test_q4_k_pins.py. No function here
+is unpinned.
 """
 from __future__ import annotations
 
@@ -61,8 +75,10 @@ TYPE_Q4_1 = 3
 TYPE_Q5_0 = 6
 TYPE_Q5_1 = 7
 TYPE_Q8_0 = 8
+TYPE_Q4_K = 12
 
-QK = 32  # weights per block for both legacy types ([Arch] legacy-family paragraph)
+QK = 32  # weights per block of the legacy types ([Arch] legacy-family paragraph)
+QK_K = 256  # weights per k-quant super-block ([Arch] k-quants: block size raised to 256)
 
 BLOCK_BYTES = {
     TYPE_Q4_0: 2 + QK // 2,      # ggml_half d + uint8_t qs[16]  ([Bind] section 2.3)
@@ -70,7 +86,10 @@ BLOCK_BYTES = {
     TYPE_Q5_0: 2 + 4 + QK // 2,  # d, qh (fifth bits), qs[16]    (reading, see header)
     TYPE_Q5_1: 2 + 2 + 4 + QK // 2,  # d, m, qh, qs[16]          (reading, see header)
     TYPE_Q8_0: 2 + QK,           # ggml_half d + int8 qs[32]     (reading, see header)
+    TYPE_Q4_K: 2 + 2 + 12 + QK_K // 2,  # d, dmin, 6-bit scales/mins, 4-bit codes (per 256; reading)
 }
+# weights per block (the block that BLOCK_BYTES describes)
+BLOCK_WEIGHTS = {TYPE_Q4_0: QK, TYPE_Q4_1: QK, TYPE_Q5_0: QK, TYPE_Q5_1: QK, TYPE_Q8_0: QK, TYPE_Q4_K: QK_K}
 
 ZERO_POINT = {TYPE_Q4_0: 8, TYPE_Q4_1: 0, TYPE_Q5_0: 16, TYPE_Q5_1: 0, TYPE_Q8_0: 0}
 CODE_RANGE = {TYPE_Q4_0: (0, 15), TYPE_Q4_1: (0, 15), TYPE_Q5_0: (0, 31), TYPE_Q5_1: (0, 31),
@@ -107,13 +126,15 @@ def half_bits_to_double(bits) -> np.ndarray:
 
 
 def row_bytes(qtype: int, k: int) -> int:
-    """Dense row stride nb[1] without padding: (k / 32) blocks of nb[0] bytes
-    ([Graph] ggml_tensor stride comment; [Bind] section 2.3 on ggml_nbytes)."""
+    """Dense row stride nb[1] without padding: (k / block weights) blocks of
+    nb[0] bytes ([Graph] ggml_tensor stride comment; [Bind] section 2.3 on
+    ggml_nbytes; for Q4_K, ne[0] / 256 blocks as [Graph] and [Load] state)."""
     if qtype not in BLOCK_BYTES:
         raise ValueError(f"unsupported type {qtype}")
-    if k <= 0 or k % QK:
-        raise ValueError("k must be a positive multiple of 32")
-    return (k // QK) * BLOCK_BYTES[qtype]
+    bw = BLOCK_WEIGHTS[qtype]
+    if k <= 0 or k % bw:
+        raise ValueError(f"k must be a positive multiple of {bw}")
+    return (k // bw) * BLOCK_BYTES[qtype]
 
 
 def _check_layout(W: np.ndarray, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
@@ -182,6 +203,8 @@ def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
     rounding, so w = fp32(d q + m) exactly rounded. This is the bit-exact
     target.
     """
+    if qtype == TYPE_Q4_K:
+        return dequantize_q4_k(W, n_rows, k, nb1)
     d, q = block_scales_and_codes(W, qtype, n_rows, k, nb1)
     c = (q - ZERO_POINT[qtype]).astype(np.float32)
     d32 = np.repeat(d.astype(np.float32), QK, axis=1)
@@ -190,6 +213,91 @@ def dequantize(W, qtype: int, n_rows: int, k: int, nb1: int) -> np.ndarray:
         if HAS_MIN[qtype]:
             w = w + np.repeat(block_mins(W, qtype, n_rows, k, nb1).astype(np.float32), QK, axis=1)
         return w
+
+
+# --------------------------------------------------------------------------
+# Q4_K super-blocks (reading of [Arch]'s k-quant description; see header).
+# --------------------------------------------------------------------------
+def q4_k_unpack_scales(s) -> tuple:
+    """Eight 6-bit sub-block scales and minimums from the 12 scale bytes
+    (uint8 [..., 12]) -> (sc, m), each int64 [..., 8]."""
+    s = np.asarray(s, dtype=np.int64)
+    sc = np.empty(s.shape[:-1] + (8,), dtype=np.int64)
+    m = np.empty_like(sc)
+    for j in range(4):
+        sc[..., j] = s[..., j] & 63
+        m[..., j] = s[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (s[..., j + 4] & 15) | ((s[..., j - 4] >> 6) << 4)
+        m[..., j] = (s[..., j + 4] >> 4) | ((s[..., j] >> 6) << 4)
+    return sc, m
+
+
+def q4_k_fields(W, n_rows: int, k: int, nb1: int) -> tuple:
+    """Split every Q4_K super-block into (d, dmin) as float64 [n_rows, k/256],
+    (sc, m) as int64 [n_rows, k/256, 8] and the codes q as int64
+    [n_rows, k/256, 256] in element order."""
+    W = _check_layout(W, TYPE_Q4_K, n_rows, k, nb1)
+    nsb = k // QK_K
+    blocks = W[:, : nsb * 144].reshape(n_rows, nsb, 144)
+    d = half_bits_to_double(blocks[:, :, 0].astype(np.uint32) | (blocks[:, :, 1].astype(np.uint32) << 8))
+    dmin = half_bits_to_double(blocks[:, :, 2].astype(np.uint32) | (blocks[:, :, 3].astype(np.uint32) << 8))
+    sc, m = q4_k_unpack_scales(blocks[:, :, 4:16])
+    qs = blocks[:, :, 16:].reshape(n_rows, nsb, 4, 32).astype(np.int64)
+    # chunk c: elements 64 c .. 64 c + 31 in the low nibbles, 64 c + 32 .. in the high ones
+    q = np.concatenate([qs & 15, qs >> 4], axis=3).reshape(n_rows, nsb, 256)
+    return d, dmin, sc, m, q
+
+
+def dequantize_q4_k(W, n_rows: int, k: int, nb1: int) -> np.ndarray:
+    """Q4_K weights as fp32 [n_rows][k]: w = fp32(d * sc_j * q - dmin * m_j),
+    the exact value (products of binary16 numbers with small integers, exact
+    in fp64) rounded once."""
+    d, dmin, sc, m, q = q4_k_fields(W, n_rows, k, nb1)
+    j = np.arange(256) // 32                           # sub-block of each element
+    with np.errstate(invalid="ignore", over="ignore"):
+        w = d[:, :, None] * sc[:, :, j] * q - dmin[:, :, None] * m[:, :, j]
+        return w.reshape(n_rows, k).astype(np.float32)
+
+
+def q4_k_pack(d_bits, dmin_bits, sc, m, q) -> np.ndarray:
+    """Lay out Q4_K super-blocks from binary16 d and dmin (uint16 [rows, nsb]),
+    6-bit sc and m (int [rows, nsb, 8]) and 4-bit codes (int [rows, nsb, 256]
+    in element order): uint8 [rows, nsb * 144]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    dmin_bits = np.asarray(dmin_bits, dtype=np.uint16)
+    sc = np.asarray(sc, dtype=np.int64)
+    m = np.asarray(m, dtype=np.int64)
+    q = np.asarray(q, dtype=np.int64)
+    rows, nsb = d_bits.shape
+    out = np.zeros((rows, nsb, 144), dtype=np.uint8)
+    out[:, :, 0], out[:, :, 1] = d_bits & 0xFF, d_bits >> 8
+    out[:, :, 2], out[:, :, 3] = dmin_bits & 0xFF, dmin_bits >> 8
+    s = np.zeros((rows, nsb, 12), dtype=np.int64)
+    for j in range(4):
+        s[:, :, j] |= sc[:, :, j] & 63
+        s[:, :, j + 4] |= m[:, :, j] & 63
+    for j in range(4, 8):
+        s[:, :, j + 4] |= (sc[:, :, j] & 15) | ((m[:, :, j] & 15) << 4)
+        s[:, :, j - 4] |= (sc[:, :, j] >> 4) << 6
+        s[:, :, j] |= (m[:, :, j] >> 4) << 6
+    out[:, :, 4:16] = s.astype(np.uint8)
+    qc = q.reshape(rows, nsb, 4, 2, 32)
+    out[:, :, 16:] = ((qc[:, :, :, 0, :] & 15) | ((qc[:, :, :, 1, :] & 15) << 4)).reshape(rows, nsb, 128)
+    return out.reshape(rows, nsb * 144)
+
+
+def q4_k_quantize_codes(w, d, dmin, sc, m) -> np.ndarray:
+    """Test quantiser for given super-block fields: q = clip(round((w + dmin m_j)
+    / (d sc_j)), 0, 15) (round half away from zero; q = 0 where d sc_j = 0).
+    w is float [rows, nsb, 256]; returns int64 codes of the same shape."""
+    w = np.asarray(w, dtype=np.float64)
+    j = np.arange(256) // 32
+    step = np.asarray(d, np.float64)[:, :, None] * np.asarray(sc, np.float64)[:, :, j]
+    off = np.asarray(dmin, np.float64)[:, :, None] * np.asarray(m, np.float64)[:, :, j]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(step != 0.0, _round_half_away((w + off) / np.where(step != 0.0, step, 1.0)), 0.0)
+    return np.clip(r, 0, 15).astype(np.int64)
 
 
 def get_rows(W, qtype: int, n_rows: int, k: int, nb1: int, ids) -> np.ndarray:
