@@ -99,7 +99,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-get-rows", action="store_true", help="skip the GET_ROWS (token-embedding gather) line")
     ap.add_argument("--no-matmul-id", action="store_true", help="skip the MUL_MAT_ID (routed expert FFN) lines")
-    ap.add_argument("--no-other-types", action="store_true", help="skip the Q8_0 / Q4_1 / Q5_0 / Q5_1 lines")
+    ap.add_argument("--no-other-types", action="store_true", help="skip the Q8_0 / Q4_1 / Q5_0 / Q5_1 / Q4_K lines")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
@@ -285,7 +285,7 @@ def time_get_rows(torch, qmm, synth, with_oracle=False):
 # ---------------------------------------------------------------- other legacy types
 
 def time_type(torch, qmm, synth, qt, with_oracle=False):
-    """Another weight type (Q8_0, Q4_1, Q5_0, Q5_1) on the 11008x4096 FFN
+    """Another weight type (Q8_0, Q4_1, Q5_0, Q5_1, Q4_K) on the 11008x4096 FFN
     projection: decode (1 fp32 token) and prefill (2048 fp16 tokens),
     back-to-back launches in a graph over >= 1.1 GiB of weight copies, so
     weights come from HBM."""
@@ -770,7 +770,7 @@ def main():
     if not args.no_matmul_id:
         out["matmul_id"] = time_matmul_id(torch, qmm, synth, with_oracle=bool(cpu_layers))
     if not args.no_other_types:
-        for qt in (synth.TYPE_Q8_0, synth.TYPE_Q4_1, synth.TYPE_Q5_0, synth.TYPE_Q5_1):
+        for qt in (synth.TYPE_Q8_0, synth.TYPE_Q4_1, synth.TYPE_Q5_0, synth.TYPE_Q5_1, synth.TYPE_Q4_K):
             out[synth.TYPE_NAMES[qt]] = time_type(torch, qmm, synth, qt, with_oracle=bool(cpu_layers))
     if cpu_layers:
         import oracle.qmm_oracle as O

@@ -16,6 +16,7 @@ QMM_TYPE_Q4_1 = 3
 QMM_TYPE_Q5_0 = 6
 QMM_TYPE_Q5_1 = 7
 QMM_TYPE_Q8_0 = 8
+QMM_TYPE_Q4_K = 12
 QMM_X_F32 = 0
 QMM_X_F16 = 1
 QMM_PATH_AUTO = 0

@@ -13,6 +13,12 @@
 // reading): d (and m for Q5_1), a 32-bit word whose bit j is the fifth bit
 // of element j, then 16 nibble bytes with the low four bits; codes 0..31,
 // w = d * (q - 16) for Q5_0 and d * q + m for Q5_1.
+// Q4_K (a k-quant; the same page says k-quants use 256-weight blocks whose
+// scales and minimums are stored in two levels; the bit layout is this
+// library's reading, the GGUF one): a 144-byte super-block of 256 weights =
+// binary16 d, binary16 dmin, 12 bytes of eight 6-bit sub-block scales sc_j
+// and minimums m_j, 128 code bytes (byte 32 c + l: element 64 c + l in the
+// low nibble, element 64 c + 32 + l in the high one); w = d sc_j q - dmin m_j.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,6 +51,9 @@ template <> struct Block<QMM_TYPE_Q4_1> { static constexpr int bytes = 20; };
 template <> struct Block<QMM_TYPE_Q5_0> { static constexpr int bytes = 22; };
 template <> struct Block<QMM_TYPE_Q5_1> { static constexpr int bytes = 24; };
 template <> struct Block<QMM_TYPE_Q8_0> { static constexpr int bytes = 34; };
+// Q4_K: bytes per 32 weights (a 256-weight super-block is 144 bytes), so that
+// the decode kernel's 8-block quads are exactly one super-block
+template <> struct Block<QMM_TYPE_Q4_K> { static constexpr int bytes = 18; };
 
 // nibbles: (low) 4-bit codes in Q4_0's byte order; has_min: a binary16 m
 // follows d; has_qh: a 32-bit word of fifth bits follows (at byte qh);
@@ -56,16 +65,24 @@ template <int QT> struct QTraits {
   static constexpr int qh = has_min ? 4 : 2;
   static constexpr int codes = 2 + (has_min ? 2 : 0) + (has_qh ? 4 : 0);
   static constexpr int zero = QT == QMM_TYPE_Q4_0 ? 8 : QT == QMM_TYPE_Q5_0 ? 16 : 0;
+  // 256-weight super-blocks with 6-bit sub-block scales and minimums
+  static constexpr bool kquant = QT == QMM_TYPE_Q4_K;
 };
 
 // Calls f(std::integral_constant<int, QT>) for the run-time type id (one of
 // the three the library accepts; the entry points validate it first).
+// by_qtype covers the 32-weight block types; by_qtype_k also Q4_K (for the
+// kernels that take it: the decoder, the streaming decode kernel, the GEMM).
 template <class F> __host__ inline auto by_qtype(int qtype, F f) {
   if (qtype == QMM_TYPE_Q4_0) return f(std::integral_constant<int, QMM_TYPE_Q4_0>{});
   if (qtype == QMM_TYPE_Q4_1) return f(std::integral_constant<int, QMM_TYPE_Q4_1>{});
   if (qtype == QMM_TYPE_Q5_0) return f(std::integral_constant<int, QMM_TYPE_Q5_0>{});
   if (qtype == QMM_TYPE_Q5_1) return f(std::integral_constant<int, QMM_TYPE_Q5_1>{});
   return f(std::integral_constant<int, QMM_TYPE_Q8_0>{});
+}
+template <class F> __host__ inline auto by_qtype_k(int qtype, F f) {
+  if (qtype == QMM_TYPE_Q4_K) return f(std::integral_constant<int, QMM_TYPE_Q4_K>{});
+  return by_qtype(qtype, f);
 }
 
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
@@ -148,6 +165,24 @@ __device__ __forceinline__ void q8_unpack(uint32_t qs, half2_t out[2]) {
 
 __device__ __forceinline__ half8_t make_half8(half2_t a, half2_t b, half2_t c, half2_t d) {
   return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Q4_K: sub-block j's 6-bit scale and minimum from the 12 scale bytes held
+// as three little-endian dwords (s0 = bytes 0-3, s1 = 4-7, s2 = 8-11). For
+// j < 4 they are the low 6 bits of bytes j and j + 4; for j >= 4 the low 4
+// bits come from the nibbles of byte j + 4 and the high 2 from the top bits
+// of bytes j - 4 (scale) and j (minimum).
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j, uint32_t &sc,
+                                              uint32_t &m) {
+  if (j < 4) {
+    sc = (s0 >> (8 * j)) & 63u;
+    m = (s1 >> (8 * j)) & 63u;
+  } else {
+    const int i = 8 * (j - 4);
+    const uint32_t b = s2 >> i;
+    sc = (b & 15u) | (((s0 >> (i + 6)) & 3u) << 4);
+    m = ((b >> 4) & 15u) | (((s1 >> (i + 6)) & 3u) << 4);
+  }
 }
 
 // fp32 -> fp16, round to nearest even (v_cvt_pk_f16_f32).

@@ -1,6 +1,7 @@
 // Block decoder: out[r][i] = fp32(d) * fp32(q - z) (Q4_1, Q5_1: fp32(d) * q
-// + m, one rounding), bit-exact, for every row of W or for the rows an index
-// vector selects (GET_ROWS).
+// + m, one rounding; Q4_K: fp32(d sc_j) q - fp32(dmin m_j), one rounding),
+// bit-exact, for every row of W or for the rows an index vector selects
+// (GET_ROWS).
 //
 // [Bind] "llama.cpp 源码分析：GGUF 权重与计算图的绑定", section 2.3 (block
 // layout); [Arch] "llama.cpp 源码完全拆解(一)：整体架构与模块全景", section
@@ -46,9 +47,27 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         __builtin_nontemporal_store(float4_a4{nan, nan, nan, nan}, o);
         continue;
       }
+      float v[4];
+      if constexpr (QTraits<QT>::kquant) {
+        // 32-weight sub-block j of super-block b / 8 (16-byte-aligned rows):
+        // elements e0..e0+3 are the low (j even) or high nibbles of code
+        // bytes 16 + 32 (j / 2) + e0 .. +3; w = fp32(d sc) q - fp32(dmin m),
+        // both products exact, rounded once by the fma
+        const int j = b & 7;
+        const uint8_t *sb = W + row * nb1 + static_cast<int64_t>(b >> 3) * 144;
+        const u32x4_t hdr = *reinterpret_cast<const u32x4_t *>(sb);
+        const uint32_t four = ld_u32(sb + 16 + 32 * (j >> 1) + e0) >> (4 * (j & 1));
+        uint32_t sc, mn;
+        q4k_scale_min(hdr.y, hdr.z, hdr.w, j, sc, mn);
+        const float dsc = half_bits_to_float(hdr.x & 0xFFFFu) * static_cast<float>(sc);
+        const float dmm = half_bits_to_float(hdr.x >> 16) * static_cast<float>(mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(static_cast<float>((four >> (8 * i)) & 0xF), dsc, -dmm);
+        __builtin_nontemporal_store(float4_a4{v[0], v[1], v[2], v[3]}, o);
+        continue;
+      }
       const uint8_t *p = W + row * nb1 + static_cast<int64_t>(b) * Block<QT>::bytes;
       const float d = half_bits_to_float(ld_u16(p));
-      float v[4];
       if constexpr (QTraits<QT>::nibbles) {
         // elements e0..e0+3: the low (e0 < 16) or high nibbles of code bytes
         // e0 % 16 .. +3, with their fifth bits (5-bit types) from bits e0..e0+3
@@ -90,7 +109,7 @@ static hipError_t decode_rows(const void *W, int qtype, int64_t n_rows, int64_t 
   const int64_t want = (blocks + 63) / 64;  // 4 wavefronts of 16 blocks per workgroup
   const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
   const uint8_t *w = static_cast<const uint8_t *>(W);
-  return by_qtype(qtype, [&](auto qt) {
+  return by_qtype_k(qtype, [&](auto qt) {
     return launch(dequant_kernel<decltype(qt)::value>, dim3(grid), dim3(256), 0, stream, w, blocks, nblk, nb1, ids,
                   n_rows, out);
   });

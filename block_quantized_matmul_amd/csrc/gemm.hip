@@ -144,7 +144,39 @@ template <int QT> struct HalfRaw {
 };
 
 template <int QT>
+__device__ __forceinline__ HalfRaw<QT> load_half_pair_blocks(const uint8_t *rp, int st, int h);
+
+// Q4_K: a stage (64 weights) is code chunk st % 4 of super-block st / 4,
+// whose low nibbles are sub-block 2 (st % 4) and high nibbles sub-block
+// 2 (st % 4) + 1; half h keeps the 16-byte header (d | dmin, scale bytes)
+// and the chunk's 32 code bytes, and j = its sub-block. Rows are 16-byte
+// aligned (the entry points require it for this type).
+template <> struct HalfRaw<QMM_TYPE_Q4_K> {
+  static constexpr int nq = 11;
+  uint32_t w[12];
+  int j;
+};
+
+template <int QT>
 __device__ __forceinline__ HalfRaw<QT> load_half_pair(const uint8_t *rp, int st, int h) {
+  if constexpr (QTraits<QT>::kquant) {
+    const uint8_t *sb = rp + static_cast<int64_t>(st >> 2) * 144;
+    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(sb);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t *>(sb + 16 + 32 * (st & 3));
+    const u32x4_t c = *reinterpret_cast<const u32x4_t *>(sb + 32 + 32 * (st & 3));
+    HalfRaw<QT> r;
+    r.w[0] = a.x, r.w[1] = a.y, r.w[2] = a.z, r.w[3] = a.w;
+    r.w[4] = b.x, r.w[5] = b.y, r.w[6] = b.z, r.w[7] = b.w;
+    r.w[8] = c.x, r.w[9] = c.y, r.w[10] = c.z, r.w[11] = c.w;
+    r.j = 2 * (st & 3) + h;
+    return r;
+  } else {
+    return load_half_pair_blocks<QT>(rp, st, h);
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ HalfRaw<QT> load_half_pair_blocks(const uint8_t *rp, int st, int h) {
   constexpr int nq = HalfRaw<QT>::nq;
   constexpr int BB = Block<QT>::bytes;
   constexpr int h1 = BB % 4 == 0 ? BB : BB - 2;  // half 1 starts here, 4-byte aligned
@@ -171,6 +203,10 @@ __device__ __forceinline__ HalfRaw<QT> load_half_pair(const uint8_t *rp, int st,
 template <int QT>
 __device__ __forceinline__ HalfRaw<QT> load_half_u16(const uint8_t *rp, int blk, int nblk) {
   constexpr int nq = HalfRaw<QT>::nq;
+  if constexpr (QTraits<QT>::kquant) {
+    // Q4_K rows are always 16-byte aligned and hold whole stages
+    return load_half_pair<QT>(rp, blk >> 1, blk & 1);
+  }
   HalfRaw<QT> r;
   if (blk < nblk) {
     uint32_t d;
@@ -189,6 +225,31 @@ __device__ __forceinline__ HalfRaw<QT> load_half_u16(const uint8_t *rp, int blk,
 template <int QT>
 __device__ __forceinline__ void store_half(_Float16 *tile, int row, int c0, const HalfRaw<QT> &r, bool first_layout) {
   constexpr int nq = HalfRaw<QT>::nq;
+  if constexpr (QTraits<QT>::kquant) {
+    // sub-block j: fp32 fma(q, d sc_j, -dmin m_j) (both products exact, one
+    // rounding), then fp16; element 4 i + b is byte b of code dword i
+    uint32_t sc, mn;
+    q4k_scale_min(r.w[1], r.w[2], r.w[3], r.j, sc, mn);
+    const float dsc = half_bits_to_float(r.w[0] & 0xFFFFu) * static_cast<float>(sc);
+    const float dmm = half_bits_to_float(r.w[0] >> 16) * static_cast<float>(mn);
+    const int shift = 4 * (r.j & 1);
+    uint32_t h[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = (r.w[4 + i] >> shift) & 0x0F0F0F0Fu;
+      const float f0 = __builtin_fmaf(static_cast<float>(v & 0xFFu), dsc, -dmm);
+      const float f1 = __builtin_fmaf(static_cast<float>((v >> 8) & 0xFFu), dsc, -dmm);
+      const float f2 = __builtin_fmaf(static_cast<float>((v >> 16) & 0xFFu), dsc, -dmm);
+      const float f3 = __builtin_fmaf(static_cast<float>(v >> 24), dsc, -dmm);
+      h[2 * i] = as_u32(cvt_half2(f0, f1));
+      h[2 * i + 1] = as_u32(cvt_half2(f2, f3));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t *>(tile + lds_at(row, c0 + i)) = u32x4_t{h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]};
+    (void)first_layout;
+    return;
+  }
   uint32_t q[nq];
   if constexpr (QTraits<QT>::has_min) {  // one layout for both halves
 #pragma unroll
@@ -568,7 +629,7 @@ hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t 
   const int rt = static_cast<int>(row_tiles), nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows),
             kk = static_cast<int>(k);
   const dim3 block(kGemmThreads);
-  return by_qtype(qtype, [&](auto qt) {
+  return by_qtype_k(qtype, [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
     return align4 ? launch(gemm_kernel<QT, false, true, true>, grid, block, 0, stream, w, nr, nblk, nb1,
                            static_cast<const void *>(X), 0, kk, Y, y_vec4, rt, route)
@@ -598,7 +659,7 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
   // Small launches whose block count splits into two equal halves of whole
   // stages also split k inside the workgroup (two wavefronts per SIMD).
   const bool ksplit = small && nblk % 4 == 0;
-  return by_qtype(qtype, [&](auto qt) {
+  return by_qtype_k(qtype, [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
     if (ksplit) {
       if (x_f16)

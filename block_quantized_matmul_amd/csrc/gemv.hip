@@ -332,6 +332,9 @@ static hipError_t gemv_nt(int nt, bool align4, GemvLaunch a) {
 hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
                                   int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids, int64_t n_ids,
                                   int64_t n_tokens, float *Y, hipStream_t stream) {
+  // Q4_K has no general-layout path: the entry points admit only layouts the
+  // streaming kernel takes (16-byte-aligned rows)
+  if (qtype == QMM_TYPE_Q4_K) return hipErrorInvalidValue;
   const int64_t pairs = n_tokens * n_ids;
   constexpr int64_t kMaxY = 65535;  // grid rows per launch
   const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0) && (nb2 % 4 == 0);
@@ -360,6 +363,9 @@ hipError_t launch_gemv_id_general(const void *W, int qtype, int64_t n_experts, i
 
 hipError_t launch_gemv_general(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X,
                                bool x_f16, int64_t n_tokens, float *Y, hipStream_t stream) {
+  // Q4_K has no general-layout path: the entry points admit only layouts the
+  // streaming kernel takes (16-byte-aligned rows)
+  if (qtype == QMM_TYPE_Q4_K) return hipErrorInvalidValue;
   GemvLaunch a;
   a.grid = dim3(static_cast<unsigned>((n_rows + 15) / 16));
   a.lds = 0;

@@ -102,6 +102,21 @@ __device__ __forceinline__ void gemv_block_min(float acc[4], half8_t xop, half8_
   for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(m, sx[e], __builtin_fmaf(d, part[e], acc[e]));
 }
 
+// A Q4_K sub-block: sum_i (dsc q_i - dmm) x_i = dsc * sum_i q_i x_i - dmm *
+// sum_i x_i, with dsc = d sc_j and dmm = dmin m_j exact in fp32; the second
+// sum comes from an MFMA with an all-ones B operand, as for Q4_1.
+template <int NT>
+__device__ __forceinline__ void gemv_block_k(float acc[4], half8_t xop, half8_t wop, float dsc, float dmm) {
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const _Float16 one = static_cast<_Float16>(1.0f);
+  const half8_t ones = {one, one, one, one, one, one, one, one};
+  const float4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, wop, zero, 0, 0, 0);
+  const float4_t sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, ones, zero, 0, 0, 0);
+  constexpr int E = NT < 4 ? NT : 4;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(dsc, part[e], __builtin_fmaf(-dmm, sx[e], acc[e]));
+}
+
 // One block's contribution for any type: dm_bits = d (low half) and, for a
 // type with a minimum, m (high half).
 template <int QT, int NT>

@@ -65,7 +65,7 @@ template <int QT, int NT, int G = 1> struct RCfg {
   // compute. Q5_1, whose decode needs more registers, takes 6 wavefronts per
   // SIMD (~85 VGPRs; 4.5 % faster than 4 on 11008 x 4096, and 8 spill).
   static constexpr bool mid = QTraits<QT>::has_qh && QTraits<QT>::has_min && NT <= 2;
-  static constexpr bool lean = QTraits<QT>::nibbles && !mid && NT <= 2;
+  static constexpr bool lean = QTraits<QT>::nibbles && !QTraits<QT>::kquant && !mid && NT <= 2;
   static constexpr int depth_large = (lean || mid) ? 2 : depth;
   static constexpr int w_lds = 16 * G * row_stride;
   static constexpr int x_lds = 8 * 4 * NT * 16;                      // 8 blocks x 4 lane groups x NT slots x 8 halves
@@ -159,8 +159,11 @@ template <int QT, int NT, int G = 1> struct RLane {
       wv[j] = ok ? __umul24(r, nb1 - 16 * QC) + 16 * c : 0;
     }
     const int xb = lane >> 3, xj = lane & 7;
-    const int xg = QTraits<QT>::nibbles ? (xj & 3) : (xj >> 1);
-    const int xh = QTraits<QT>::nibbles ? 4 * (xj >> 2) : 4 * (xj & 1);
+    // element order of a lane group: Q4_0's nibble order for the 32-weight
+    // nibble types, contiguous (8 g .. 8 g + 7) for Q8_0 and Q4_K
+    constexpr bool nib = QTraits<QT>::nibbles && !QTraits<QT>::kquant;
+    const int xg = nib ? (xj & 3) : (xj >> 1);
+    const int xh = nib ? 4 * (xj >> 2) : 4 * (xj & 1);
     xw = (4 * xb + xg) * NT * 16 + 2 * xh;
   }
 };
@@ -195,6 +198,38 @@ __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16, G> &r, const
   }
   const int r16 = lane & 15, g = lane >> 4;
   const int slot = min(r16, NT - 1);
+  if constexpr (QTraits<QT>::kquant) {
+    // The quad is one Q4_K super-block: bytes 0..15 hold d | dmin and the
+    // 12 scale bytes, then code chunk u (32 bytes at 16 + 32 u) carries
+    // sub-block 2 u in its low nibbles and 2 u + 1 in its high ones; this
+    // lane's 8 codes of a sub-block are bytes 8 g .. 8 g + 7 of the chunk.
+    const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    auto codes = [&](uint32_t a0, uint32_t a1) {
+      return make_half8(bytes01_plus_1024(a0) + m1024, bytes23_plus_1024(a0) + m1024,
+                        bytes01_plus_1024(a1) + m1024, bytes23_plus_1024(a1) + m1024);
+    };
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const unsigned char *rb = wl + (16 * gi + r16) * C::row_stride;
+      auto ld = [&](int off) { return *reinterpret_cast<const uint32_t *>(rb + off); };
+      const uint32_t h0 = ld(0), s0 = ld(4), s1 = ld(8), s2 = ld(12);
+      const float d = half_bits_to_float(h0 & 0xFFFFu), dmin = half_bits_to_float(h0 >> 16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const half8_t xe = xs[(4 * (2 * u) + g) * NT + slot];
+        const half8_t xo = xs[(4 * (2 * u + 1) + g) * NT + slot];
+        const uint32_t a0 = ld(16 + 32 * u + 8 * g), a1 = ld(20 + 32 * u + 8 * g);
+        uint32_t sc0, mn0, sc1, mn1;
+        q4k_scale_min(s0, s1, s2, 2 * u, sc0, mn0);
+        q4k_scale_min(s0, s1, s2, 2 * u + 1, sc1, mn1);
+        gemv_block_k<NT>(acc[gi], xe, codes(a0 & 0x0F0F0F0Fu, a1 & 0x0F0F0F0Fu), d * static_cast<float>(sc0),
+                         dmin * static_cast<float>(mn0));
+        gemv_block_k<NT>(acc[gi], xo, codes((a0 >> 4) & 0x0F0F0F0Fu, (a1 >> 4) & 0x0F0F0F0Fu),
+                         d * static_cast<float>(sc1), dmin * static_cast<float>(mn1));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {  // pairs of blocks in the quad
     // A-operand rows past the NT token slots repeat the last slot (no
@@ -537,7 +572,7 @@ hipError_t launch_gemv_id_stream(const void *W, int qtype, int64_t n_experts, in
     __builtin_memcpy(&B.m[1], &route, sizeof(RRoute));
     const int count = static_cast<int>(pairs - p0 < kMaxY ? pairs - p0 : kMaxY);
     hipError_t e;
-    e = by_qtype(qtype, [&](auto qt) {
+    e = by_qtype_k(qtype, [&](auto qt) {
       constexpr int QT = decltype(qt)::value;
       return waves == kKSplitSmall ? id_go_w<QT, kKSplitSmall>(B, count, rg, stream)
                                    : id_go_w<QT, kKSplitLarge>(B, count, rg, stream);
@@ -576,7 +611,7 @@ hipError_t launch_gemv_id_tiles(const void *W, int qtype, int64_t n_experts, int
     route.pair0 = static_cast<int>(t0);
     __builtin_memcpy(&B.m[1], &route, sizeof(RRoute));
     const int count = static_cast<int>(max_tiles - t0 < kMaxY ? max_tiles - t0 : kMaxY);
-    const hipError_t e = by_qtype(qtype, [&](auto qt) {
+    const hipError_t e = by_qtype_k(qtype, [&](auto qt) {
       constexpr int QT = decltype(qt)::value;
       auto go = [&](auto ntc) {
         constexpr int NT = decltype(ntc)::value;
@@ -626,7 +661,7 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t str
       ++j;
     }
     const int waves = k_split_for(total_rg, device_cus());
-    const hipError_t e = by_qtype(qt, [&](auto q) {
+    const hipError_t e = by_qtype_k(qt, [&](auto q) {
       constexpr int QT = decltype(q)::value;
       return xf ? r_nt<QT, true>(nt, B, count, max_rg, waves, stream)
                 : r_nt<QT, false>(nt, B, count, max_rg, waves, stream);

@@ -34,6 +34,11 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 
+// Bytes and weights of one block of the type (0 for an unknown type). The
+// 32-weight types follow [Bind] section 2.3 and the library's readings; Q4_K
+// is a 256-weight super-block, a Q4_K tensor being ne[0] / 256 blocks
+// ([Graph] "llama.cpp 源码完全拆解(二)：ggml 计算图与内存分配器", the figure
+// notes on quantised matmul).
 int block_bytes(int type) {
   switch (type) {
     case QMM_TYPE_Q4_0: return 18;
@@ -41,9 +46,11 @@ int block_bytes(int type) {
     case QMM_TYPE_Q5_0: return 22;
     case QMM_TYPE_Q5_1: return 24;
     case QMM_TYPE_Q8_0: return 34;
+    case QMM_TYPE_Q4_K: return 144;
     default: return 0;
   }
 }
+int block_weights(int type) { return type == QMM_TYPE_Q4_K ? 256 : 32; }
 
 bool trace_on() {
   static const bool on = [] {
@@ -56,13 +63,18 @@ bool trace_on() {
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 // Checks shared by every entry point that takes a weight matrix.
+// Q4_K weights are read only as whole 16-byte pieces (GGUF aligns tensor
+// data to at least 32 bytes), so their rows must start 16-byte aligned.
 int check_weights(const void *W, int type, int64_t n_rows, int64_t k, int64_t nb1) {
   if (W == nullptr) return QMM_ERR_NULL;
-  const int bb = block_bytes(type);
+  const int bb = block_bytes(type), bw = block_weights(type);
   if (bb == 0) return QMM_ERR_TYPE;
-  if (k <= 0 || k % 32 != 0 || k > kMaxDim || n_rows < 0 || n_rows > kMaxDim) return QMM_ERR_SHAPE;
-  if (nb1 % 2 != 0 || nb1 < (k / 32) * bb) return QMM_ERR_STRIDE;
-  if (!aligned(W, 2)) return QMM_ERR_ALIGN;
+  if (k <= 0 || k % bw != 0 || k > kMaxDim || n_rows < 0 || n_rows > kMaxDim) return QMM_ERR_SHAPE;
+  if (nb1 % 2 != 0 || nb1 < (k / bw) * bb) return QMM_ERR_STRIDE;
+  if (type == QMM_TYPE_Q4_K && nb1 % 16 != 0) return QMM_ERR_STRIDE;
+  // the decode kernel addresses a Q4_K matrix with 32-bit offsets
+  if (type == QMM_TYPE_Q4_K && (n_rows * nb1 >= (int64_t{1} << 32) || nb1 >= (int64_t{1} << 24))) return QMM_ERR_SHAPE;
+  if (!aligned(W, type == QMM_TYPE_Q4_K ? 16 : 2)) return QMM_ERR_ALIGN;
   return QMM_OK;
 }
 
@@ -72,6 +84,7 @@ const char *type_name(int t) {
     case QMM_TYPE_Q4_1: return "q4_1";
     case QMM_TYPE_Q5_0: return "q5_0";
     case QMM_TYPE_Q5_1: return "q5_1";
+    case QMM_TYPE_Q4_K: return "q4_k";
     default: return "q8_0";
   }
 }
@@ -103,16 +116,17 @@ void *device_scratch() {
 extern "C" {
 
 int64_t qmm_row_bytes(int ggml_type, int64_t k) {
-  const int bb = block_bytes(ggml_type);
+  const int bb = block_bytes(ggml_type), bw = block_weights(ggml_type);
   if (bb == 0) return QMM_ERR_TYPE;
-  if (k <= 0 || k % 32 != 0 || k > kMaxDim) return QMM_ERR_SHAPE;
-  return (k / 32) * bb;
+  if (k <= 0 || k % bw != 0 || k > kMaxDim) return QMM_ERR_SHAPE;
+  return (k / bw) * bb;
 }
 
 int qmm_supports(int ggml_type, int64_t k, int64_t row_stride_bytes) {
-  const int bb = block_bytes(ggml_type);
-  if (bb == 0 || k <= 0 || k % 32 != 0 || k > kMaxDim) return 0;
-  return (row_stride_bytes % 2 == 0 && row_stride_bytes >= (k / 32) * bb) ? 1 : 0;
+  const int bb = block_bytes(ggml_type), bw = block_weights(ggml_type);
+  if (bb == 0 || k <= 0 || k % bw != 0 || k > kMaxDim) return 0;
+  if (ggml_type == QMM_TYPE_Q4_K && row_stride_bytes % 16 != 0) return 0;
+  return (row_stride_bytes % 2 == 0 && row_stride_bytes >= (k / bw) * bb) ? 1 : 0;
 }
 
 const char *qmm_status_string(int status) {
@@ -120,9 +134,11 @@ const char *qmm_status_string(int status) {
     case QMM_OK: return "QMM_OK";
     case QMM_ERR_NULL: return "QMM_ERR_NULL: a required pointer is NULL";
     case QMM_ERR_TYPE: return "QMM_ERR_TYPE: unsupported weight or activation type";
-    case QMM_ERR_SHAPE: return "QMM_ERR_SHAPE: k must be a positive multiple of 32; sizes must be in [0, 2^31)";
-    case QMM_ERR_STRIDE: return "QMM_ERR_STRIDE: row stride must be even and cover the row's blocks";
-    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte, X, Y and out 4-byte alignment";
+    case QMM_ERR_SHAPE:
+      return "QMM_ERR_SHAPE: k must be a positive multiple of 32 (of 256 for Q4_K); sizes must be in [0, 2^31)";
+    case QMM_ERR_STRIDE:
+      return "QMM_ERR_STRIDE: row stride must be even (a multiple of 16 for Q4_K) and cover the row's blocks";
+    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte (Q4_K: 16-byte), X, Y and out 4-byte alignment";
     case QMM_ERR_HIP: return "QMM_ERR_HIP: the HIP runtime rejected the kernel launch";
     case QMM_ERR_PATH: return "QMM_ERR_PATH: unknown path, or GEMV forced with more than 8 tokens";
     case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or smaller than qmm_matmul_id_workspace_bytes";
@@ -281,6 +297,7 @@ static int check_matmul_id(const void *W, int ggml_type, int64_t n_experts, int6
   if (*need < 0) return static_cast<int>(*need);
   if (x_slots != 1 && x_slots != n_ids) return QMM_ERR_SHAPE;
   if (expert_stride_bytes % 2 != 0 || expert_stride_bytes < n_rows * row_stride_bytes) return QMM_ERR_STRIDE;
+  if (ggml_type == QMM_TYPE_Q4_K && expert_stride_bytes % 16 != 0) return QMM_ERR_STRIDE;
   if (!aligned(X, 4) || !aligned(ids, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
   *plan = id_plan(n_experts, n_ids, n_tokens);
   const bool streamable = qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);

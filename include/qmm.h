@@ -42,7 +42,18 @@
  *      Q4_0's nibble order; weight = d * (q - 16), codes 0..31. Q5_1 block =
  *      24 bytes: d, m, the fifth-bit word, qs; weight = d * q + m (the
  *      packing of both is this library's reading: the pages give none). Q8_0 block = 34
- *      bytes: binary16 d, then 32 int8 codes; weight = d * q. Bytes between
+ *      bytes: binary16 d, then 32 int8 codes; weight = d * q. Q4_K (a k-quant:
+ *      256-weight super-blocks with scales and minimums in two levels, [Arch]
+ *      paragraph on the three quantisation families; a Q4_K row is k / 256
+ *      blocks, [Graph]; the bit layout is this library's reading, the GGUF
+ *      one) super-block = 144 bytes: binary16 d, binary16 dmin, 12 bytes of
+ *      eight 6-bit sub-block scales sc_j and minimums m_j (j < 4: sc_j =
+ *      s[j] & 63, m_j = s[j+4] & 63; j >= 4: sc_j = (s[j+4] & 15) |
+ *      (s[j-4] >> 6) << 4, m_j = (s[j+4] >> 4) | (s[j] >> 6) << 4), then 128
+ *      code bytes (byte 32c + l: element 64c + l in the low nibble, element
+ *      64c + 32 + l in the high one); weight = d * sc_j * q - dmin * m_j.
+ *      Q4_K needs k a multiple of 256, W 16-byte aligned, a row stride that
+ *      is a multiple of 16 and a matrix under 4 GiB. Bytes between
  *      the last block of a row and the next row (padding) are never read.
  *   X  activations [n_tokens][k], k contiguous (fp32, or fp16 for *_x16).
  *   Y  output [n_tokens][n_rows] fp32, n_rows contiguous; fully overwritten.
@@ -61,7 +72,8 @@
  *
  * Numerics: dequantised weights are exact (fp32 d * (q - z) is exact for every
  * finite binary16 d; the d * q + m of Q4_1 / Q5_1 is that exact product plus
- * m, rounded once to fp32). The matmul accumulates in fp32. Decode-sized calls
+ * m, rounded once to fp32; Q4_K's d sc q - dmin m is two exact products,
+ * rounded once). The matmul accumulates in fp32. Decode-sized calls
  * (n_tokens <= QMM_GEMV_MAX_TOKENS) round activations to fp16 and multiply
  * them by the exact integer codes, applying d in fp32 once per block (Q4_1,
  * Q5_1: plus m times the block's sum of the fp16 activations); larger
@@ -88,6 +100,7 @@ extern "C" {
 #define QMM_TYPE_Q5_0 6
 #define QMM_TYPE_Q5_1 7
 #define QMM_TYPE_Q8_0 8
+#define QMM_TYPE_Q4_K 12
 
 /* Activation element types for qmm_matmul_path. */
 #define QMM_X_F32 0
@@ -120,7 +133,7 @@ extern "C" {
  * [Load] section 第六步, [Arch] section 权重装载).
  *   W                device pointer, 2-byte aligned, n_rows rows of
  *                    row_stride_bytes bytes (see layout above)
- *   ggml_type        QMM_TYPE_Q4_0, _Q4_1, _Q5_0, _Q5_1 or _Q8_0
+ *   ggml_type        QMM_TYPE_Q4_0, _Q4_1, _Q5_0, _Q5_1, _Q8_0 or _Q4_K
  *   n_rows           ne1 of W (>= 0)
  *   k                ne0 of W and of X; positive multiple of 32
  *   row_stride_bytes nb1 of W; even and >= qmm_row_bytes(ggml_type, k)

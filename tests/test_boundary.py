@@ -60,7 +60,7 @@ def test_row_bytes_and_supports(L):
     assert L.qmm_row_bytes(qmm.QMM_TYPE_Q4_1, 4096) == 2560
     assert L.qmm_supports(qmm.QMM_TYPE_Q4_1, 64, 40) == 1 and L.qmm_supports(qmm.QMM_TYPE_Q4_1, 64, 38) == 0
     assert L.qmm_row_bytes(qmm.QMM_TYPE_Q5_0, 4096) == 2816 and L.qmm_row_bytes(qmm.QMM_TYPE_Q5_1, 4096) == 3072
-    for bad_type in (0, 1, 4, 5, 9, 12):
+    for bad_type in (0, 1, 4, 5, 9, 11, 13):
         assert L.qmm_row_bytes(bad_type, 4096) == qmm.QMM_ERR_TYPE
     for bad_k in (0, -32, 48, 1 << 31):
         assert L.qmm_row_bytes(Q4, bad_k) == qmm.QMM_ERR_SHAPE
@@ -71,6 +71,26 @@ def test_row_bytes_and_supports(L):
     assert L.qmm_supports(Q4, 4096, 2302) == 0
     assert L.qmm_supports(Q8, 48, 100) == 0
     assert L.qmm_supports(5, 4096, 4096) == 0
+
+
+def test_q4_k_layout_rules(L):
+    QK = qmm.QMM_TYPE_Q4_K
+    assert L.qmm_row_bytes(QK, 4096) == 2304 and L.qmm_row_bytes(QK, 256) == 144
+    assert L.qmm_row_bytes(QK, 11008) == 43 * 144
+    for bad_k in (32, 128, 4000, 0):
+        assert L.qmm_row_bytes(QK, bad_k) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_supports(QK, 256, 144) == 1 and L.qmm_supports(QK, 256, 160) == 1
+    assert L.qmm_supports(QK, 256, 146) == 0   # rows must stay 16-byte aligned
+    assert L.qmm_supports(QK, 256, 128) == 0   # smaller than the row's block
+    assert L.qmm_supports(QK, 32, 144) == 0
+    # host checks, nothing launched
+    assert _mm(L, t=QK, k=96, nb1=144) == qmm.QMM_ERR_SHAPE
+    assert _mm(L, t=QK, k=256, nb1=152) == qmm.QMM_ERR_STRIDE
+    assert _mm(L, t=QK, k=256, nb1=144, W=ctypes.c_void_p(0x10008)) == qmm.QMM_ERR_ALIGN
+    assert _mm(L, t=QK, k=256, nb1=144, n=0) == qmm.QMM_OK   # empty: no launch
+    assert _mm(L, t=QK, k=256, nb1=1 << 24, rows=2) == qmm.QMM_ERR_SHAPE  # beyond 32-bit offsets
+    assert _mid(L, t=QK, k=256, nb1=144, rows=4, nb2=584) == qmm.QMM_ERR_STRIDE  # expert stride not 16-aligned
+    assert _mid(L, t=QK, k=256, nb1=144, rows=4, nb2=576, n=0) == qmm.QMM_OK
 
 
 def test_status_strings(L):
