@@ -80,10 +80,19 @@
  * calls round both the dequantised weights and the activations to fp16 for
  * the matrix cores. Every element satisfies
  *   |y - y_exact| <= 1e-3 * sum_i |w_i x_i| + 1e-5
- * for activations of magnitude at most 65504 (fp16 range) and, on the
- * matrix-core path, |d * (q - z)| <= 65504. Scales d must be finite (the
- * loader rejects NaN/Inf scales); a non-finite d or x yields a non-finite
- * result in every output it touches.
+ * when every activation is 0 or of magnitude in [2^-14, 65504] (the fp16
+ * normal range) and, on the matrix-core path, every dequantised weight is 0
+ * or in that range too (always so for Q4_0, Q5_0 and Q8_0 whose fp16 scale
+ * is finite: their weights are exact in fp16 or rounded relatively). Below
+ * 2^-14 fp16 rounding is absolute: activations add at most 2^-25 sum_i |w_i|
+ * to the bound, and on the matrix-core path weights of Q4_1, Q5_1 and Q4_K
+ * whose minimum nearly cancels d q add at most 2^-25 sum_i |x_i|. The
+ * decode kernels' d sum(q x) + m sum(x) split of Q4_1, Q5_1 and Q4_K can
+ * lose the bound's relative part in fp32 when both terms nearly cancel over
+ * a whole block. Activations beyond 65504 overflow fp16: every output they
+ * touch is non-finite. Scales d must be finite (the loader rejects NaN/Inf
+ * scales); a non-finite d or x yields a non-finite result in every output it
+ * touches.
  */
 #ifndef QMM_H
 #define QMM_H
