@@ -257,26 +257,39 @@ def test_config4_prefill_gemm():
         toks = rng.integers(0, case.n_tokens, 4096)
         y_ref, s = O.matmul_sampled(W, case.qtype, case.rows, case.k, case.nb1, X, toks, rows)
         assert O.within_tolerance(Y16[toks, rows], y_ref, s).all(), case.name
-    c = synth.config_cases()[4][0]
-    _run_case(c)  # the 4096 x 4096 case element by element
+    for c in synth.config_cases()[4]:
+        _run_case(c)  # 4096 x 4096 and 11008 x 4096 element by element
 
 
-@pytest.mark.parametrize("n_tokens", [1, 2048])
-def test_config5_stack_layers_sampled(n_tokens):
-    """Full-size layer tensors of the 32-layer stack (layers 0 and 31), in the
-    launch configuration the benchmark times, checked on sampled outputs."""
-    for case in synth.stack_cases(n_tokens):
-        if case.layer not in (0, 31):
-            continue
+def _stack_layer_sampled(n_tokens, layer, m=4096):
+    for case in synth.stack_cases(n_tokens, layers=layer + 1)[7 * layer:]:
         W, X = case.weights(), case.activations()
         say(case.name)
         Y = run_matmul(W, case.qtype, case.k, X)
         rng = np.random.default_rng(case.layer * 10 + case.tensor)
-        m = 4096
         rows = rng.integers(0, case.rows, m)
         toks = rng.integers(0, case.n_tokens, m)
         y_ref, s = O.matmul_sampled(W, case.qtype, case.rows, case.k, case.nb1, X, toks, rows)
         assert O.within_tolerance(Y[toks, rows], y_ref, s).all(), case.name
+
+
+@pytest.mark.parametrize("layer", range(synth.N_LAYER))
+def test_config5_stack_decode_every_layer_sampled(layer):
+    """Every layer's seven full-size tensors of the 32-layer stack at one
+    token, in the launch configuration the benchmark times, checked on
+    sampled outputs."""
+    _stack_layer_sampled(1, layer)
+
+
+def test_config5_stack_prefill_last_layer_sampled():
+    _stack_layer_sampled(2048, synth.N_LAYER - 1)
+
+
+def test_config5_stack_prefill_layer0_full():
+    """Layer 0 of the stack at 2048 fp16 tokens, all seven tensors element by
+    element (2048 x 4096 and 2048 x 11008 outputs)."""
+    for case in synth.stack_cases(2048, layers=1):
+        _run_case(case)
 
 
 def test_config5_decode_batched_as_benchmarked():
