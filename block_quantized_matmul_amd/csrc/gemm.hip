@@ -602,6 +602,224 @@ __global__ __launch_bounds__(kGemmThreads * KS, KS == 2 ? 1 : ((BM == kBM || !XF
   }
 }
 
+// Large launches with fp16 activations (at least one 128 x 256 tile per CU,
+// an even block count): one workgroup of eight wavefronts per CU owns a
+// 128-row x 256-token tile and runs as two groups of four that take turns
+// ("ping-pong"). While one group issues the MFMAs of a stage from LDS, the
+// other stages its share of the next stage (weight rows 64 g .. 64 g + 63
+// decoded to fp16) and starts the copies of later stages; an LDS-only
+// barrier ends each phase and the groups swap. Every SIMD then holds one
+// wavefront of each group, so its matrix core is fed by one of them while
+// the other's decode, loads and stores run beside it, instead of two
+// wavefronts that reach their MFMAs and their decode at the same time. Each
+// wavefront computes 64 x 64 (rows 64 (w % 2), tokens 128 g + 64 (w / 2)),
+// a stage's weights are decoded once for 256 tokens, and the two groups
+// progress in lockstep, so neither finishes long after the other.
+// Activations go from global memory straight into LDS (global_load_lds:
+// lane l's 16 bytes land at M0 + 16 l), so they take no registers, VALU or
+// LDS store instructions; three activation buffers let the copy of stage
+// s + 2 start while stages s and s + 1 are in use.
+constexpr int kPPThreads = 512;
+constexpr int kPPBN = 256;                       // tokens per tile
+constexpr int kPPWHalves = kBM * kBK;            // one weight stage (16 KiB)
+constexpr int kPPXHalves = kPPBN * kBK;          // one activation stage (32 KiB)
+constexpr int kPPXOps = kPPXHalves * 2 / 2 / (kGemmThreads * 16);  // copies per lane per stage (4)
+constexpr size_t kPPLds = (2 * kPPWHalves + 3 * kPPXHalves) * sizeof(_Float16);  // 128 KiB
+
+__device__ __forceinline__ uint32_t lds_byte_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+// 16 bytes per lane from base + voff into LDS at m0 + 16 lane. M0 is written
+// by a scalar move, and an LDS-DMA load must not follow it directly.
+__device__ __forceinline__ void dma16(uint32_t voff, const void *base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int QT, bool ALIGN4>
+__global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
+                                                                int64_t nb1, const _Float16 *__restrict__ X,
+                                                                int n_tokens, int k, float *__restrict__ Y,
+                                                                bool y_vec4, int row_tiles) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
+  _Float16 *const Wbuf = lds_dynamic;                   // 2 weight stages
+  _Float16 *const Xbuf = lds_dynamic + 2 * kPPWHalves;  // 3 activation stages
+  const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kGemmThreads);
+  const int tid = static_cast<int>(threadIdx.x) - g * kGemmThreads;  // thread within the group
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // tile order: as gemm_kernel (XCD-contiguous ranges, groups of row tiles)
+  const int n_tiles = static_cast<int>(gridDim.x);
+  const int bid = static_cast<int>(blockIdx.x);
+  const int per_xcd = n_tiles / kXcds;
+  const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
+  const int tok_tiles = n_tiles / row_tiles;
+  const int in_group = kGroupRows * tok_tiles;
+  const int first_row = (lin / in_group) * kGroupRows;
+  const int group_rows = min(row_tiles - first_row, kGroupRows);
+  const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
+  const int tok0 = ((lin % in_group) / group_rows) * kPPBN;
+
+  // Weight staging share of group g: rows 64 g + tid / 2, block tid % 2 of
+  // the stage's pair, by threads tid < 128.
+  const bool wstage = tid < kBM;  // uniform per wavefront
+  const int srow = (kBM / 2) * g + ((tid >> 1) & (kBM / 2 - 1)), sh = tid & 1;
+  const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
+  // Activation copies of group g: tokens 128 g .. 128 g + 127 of the tile,
+  // copy i of wavefront w filling LDS rows 128 g + 8 (4 w + i) .. + 7. Lane
+  // p of a copy writes position p % 8 of row p / 8, which holds chunk
+  // (p % 8) ^ (row % 8) (the lds_at permutation); token rows past the end
+  // re-read the last token.
+  uint32_t xoff[kPPXOps];
+#pragma unroll
+  for (int i = 0; i < kPPXOps; ++i) {
+    const int row = (kPPBN / 2) * g + 8 * (kPPXOps * wave + i) + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7);
+    const int tok = min(tok0 + row, n_tokens - 1);
+    xoff[i] = static_cast<uint32_t>((tok * k + 8 * c) * 2);
+  }
+  const uint32_t xlds0 = lds_byte_addr(Xbuf) + ((kPPBN / 2) * g + 8 * kPPXOps * wave) * (kBK * 2);
+
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int n_st = nblk / 2;
+  const int last = n_st - 1;
+  auto load_w = [&](HalfRaw<QT> &r, int st) {
+    if (wstage) {
+      if constexpr (ALIGN4)
+        r = load_half_pair<QT>(rp, st, sh);
+      else
+        r = load_half_u16<QT>(rp, 2 * st + sh, nblk);
+    }
+  };
+  auto store_w = [&](int buf, const HalfRaw<QT> &r) {
+    if (wstage) store_half<QT>(Wbuf + buf * kPPWHalves, srow, 4 * sh, r, ALIGN4 && sh == 0);
+  };
+  auto copy_x = [&](int st) {
+    const _Float16 *base = X + static_cast<int64_t>(kBK) * st;
+    const uint32_t lds = xlds0 + static_cast<uint32_t>((st % 3) * kPPXHalves * 2);
+#pragma unroll
+    for (int i = 0; i < kPPXOps; ++i) dma16(xoff[i], base, lds + i * 1024);
+  };
+  int aofs[2], bofs[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    aofs[h] = lds_at(64 * wm + (lane & 15), (lane >> 4) + 4 * h);
+    bofs[h] = lds_at((kPPBN / 2) * g + 64 * wn + (lane & 15), (lane >> 4) + 4 * h);
+  }
+  // All 16 operand reads of a stage go out before its first MFMA, so the
+  // LDS latency is paid once per phase rather than between MFMA groups.
+  auto compute = [&](int st) {
+    const _Float16 *ws = Wbuf + (st & 1) * kPPWHalves;
+    const _Float16 *xs = Xbuf + (st % 3) * kPPXHalves;
+    half8_t a[2][4], b[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
+#pragma unroll
+    for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+  };
+  auto phase_end = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // memory(s): this group's weights of stage s + 1 into buffer (s + 1) % 2
+  // from registers loaded two stages earlier, the copy of stage s + 2's
+  // activations, a wait that leaves only that copy in flight (so stage
+  // s + 1's copy, issued one memory phase earlier, has landed), then the
+  // weight loads of stage s + 3 into the registers just freed.
+  auto memory = [&](int s, HalfRaw<QT> &r, int buf) {
+    store_w(buf, r);
+    copy_x(min(s + 2, last));
+    wait_vmcnt<kPPXOps>();
+    load_w(r, min(s + 3, last));
+  };
+
+  HalfRaw<QT> r0, r1;
+  copy_x(0);
+  load_w(r0, 0);
+  load_w(r1, min(1, last));
+  copy_x(min(1, last));
+  store_w(0, r0);
+  wait_vmcnt<0>();
+  load_w(r0, min(2, last));
+  phase_end();  // stage 0 is in LDS
+  // Group 0 runs compute(s), memory(s); group 1 memory(s), compute(s): both
+  // pass the same barriers, and each phase pairs one group's MFMAs with the
+  // other's staging.
+  if (g == 0) {
+    for (int s = 0; s < n_st; s += 2) {
+      compute(s);
+      phase_end();
+      memory(s, r1, 1);
+      phase_end();
+      if (s + 1 < n_st) {
+        compute(s + 1);
+        phase_end();
+        memory(s + 1, r0, 0);
+        phase_end();
+      }
+    }
+  } else {
+    for (int s = 0; s < n_st; s += 2) {
+      memory(s, r1, 1);
+      phase_end();
+      compute(s);
+      phase_end();
+      if (s + 1 < n_st) {
+        memory(s + 1, r0, 0);
+        phase_end();
+        compute(s + 1);
+        phase_end();
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no copy outlives the workgroup
+
+  // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
+  // token 128 g + 64 wn + 16 j + l % 16.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tok = tok0 + (kPPBN / 2) * g + 64 * wn + 16 * j + (lane & 15);
+    if (tok >= n_tokens) continue;
+    float *yrow = Y + static_cast<int64_t>(tok) * n_rows;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + 64 * wm + 16 * i + 4 * (lane >> 4);
+      if (y_vec4 && r + 3 < n_rows) {
+        *reinterpret_cast<float4_t *>(yrow + r) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r + e < n_rows) yrow[r + e] = acc[i][j][e];
+      }
+    }
+  }
+}
+
 template <int QT, bool XF16, int BM, int KS = 1>
 static hipError_t gemm_dispatch(bool align4, dim3 grid, hipStream_t s, const uint8_t *w, int n_rows, int nblk,
                                 int64_t nb1, const void *X, int n_tokens, int k, float *Y, bool y_vec4, int row_tiles) {
@@ -659,6 +877,27 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
   // Small launches whose block count splits into two equal halves of whole
   // stages also split k inside the workgroup (two wavefronts per SIMD).
   const bool ksplit = small && nblk % 4 == 0;
+  // fp16 activations, at least one 128 x 256 tile per CU in rounds that
+  // keep at least 3/4 of the CUs busy, whole stages, and activations whose
+  // byte offsets fit 32 bits: the ping-pong kernel. (Q4_K, whose fp32
+  // decode is the longest, measured slower there: 98.5 against 91.8 us on
+  // 4096 x 4096 at 2048 tokens.)
+  const int64_t pp_tiles = ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
+  const int64_t pp_rounds = cus > 0 ? (pp_tiles + cus - 1) / cus : 0;
+  const bool pp = x_f16 && qtype != QMM_TYPE_Q4_K && cus > 0 && pp_tiles >= cus && 4 * pp_tiles >= 3 * pp_rounds * cus && nblk % 2 == 0 &&
+                  pp_tiles <= 0x7FFFFFFF && n_tokens * k * 2 < (int64_t{1} << 32);
+  if (pp) {
+    const dim3 ppgrid(static_cast<unsigned>(pp_tiles));
+    const int prt = static_cast<int>((n_rows + kBM - 1) / kBM);
+    const _Float16 *xh = static_cast<const _Float16 *>(X);
+    return by_qtype_k(qtype, [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
+      auto go = [&](auto kern) {
+        return launch(kern, ppgrid, dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, xh, nt, kk, Y, y_vec4, prt);
+      };
+      return align4 ? go(gemm_pp_kernel<QT, true>) : go(gemm_pp_kernel<QT, false>);
+    });
+  }
   return by_qtype_k(qtype, [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
     if (ksplit) {
