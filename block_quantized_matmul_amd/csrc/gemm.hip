@@ -606,25 +606,27 @@ __global__ __launch_bounds__(kGemmThreads * KS, KS == 2 ? 1 : ((BM == kBM || !XF
 // an even block count): one workgroup of eight wavefronts per CU owns a
 // 128-row x 256-token tile and runs as two groups of four that take turns
 // ("ping-pong"). While one group issues the MFMAs of a stage from LDS, the
-// other stages its share of the next stage (weight rows 64 g .. 64 g + 63
-// decoded to fp16) and starts the copies of later stages; an LDS-only
-// barrier ends each phase and the groups swap. Every SIMD then holds one
-// wavefront of each group, so its matrix core is fed by one of them while
-// the other's decode, loads and stores run beside it, instead of two
-// wavefronts that reach their MFMAs and their decode at the same time. Each
-// wavefront computes 64 x 64 (rows 64 (w % 2), tokens 128 g + 64 (w / 2)),
-// a stage's weights are decoded once for 256 tokens, and the two groups
-// progress in lockstep, so neither finishes long after the other.
-// Activations go from global memory straight into LDS (global_load_lds:
-// lane l's 16 bytes land at M0 + 16 l), so they take no registers, VALU or
-// LDS store instructions; three activation buffers let the copy of stage
-// s + 2 start while stages s and s + 1 are in use.
+// other stages data for later stages; an LDS-only barrier ends each phase
+// and the groups swap. Every SIMD holds one wavefront of each group, so its
+// matrix core is fed by one of them while the other's staging runs beside
+// it, instead of two wavefronts that reach their MFMAs and their decode at
+// the same time. Each wavefront computes 64 x 64 (rows 64 (w % 2), tokens
+// 128 g + 64 (w / 2)); a stage's weights are decoded once for 256 tokens,
+// and the groups progress in lockstep, so neither finishes long after the
+// other. The staging is split by kind so that every wavefront of a group
+// has the same work: group 0 decodes the weights (one block of one row per
+// thread, loaded from global memory two stages ahead into registers), group
+// 1 copies the activations from global memory straight into LDS
+// (global_load_lds: lane l's 16 bytes land at M0 + 16 l; no registers, VALU
+// or LDS store instructions) three stages ahead, into four buffers (an L2
+// hit under this load takes more than one stage to land).
 constexpr int kPPThreads = 512;
 constexpr int kPPBN = 256;                       // tokens per tile
 constexpr int kPPWHalves = kBM * kBK;            // one weight stage (16 KiB)
 constexpr int kPPXHalves = kPPBN * kBK;          // one activation stage (32 KiB)
-constexpr int kPPXOps = kPPXHalves * 2 / 2 / (kGemmThreads * 16);  // copies per lane per stage (4)
-constexpr size_t kPPLds = (2 * kPPWHalves + 3 * kPPXHalves) * sizeof(_Float16);  // 128 KiB
+constexpr int kPPXOps = kPPXHalves * 2 / (kGemmThreads * 16);  // copies per lane per stage (8)
+constexpr int kPPXBufs = 4;
+constexpr size_t kPPLds = (2 * kPPWHalves + kPPXBufs * kPPXHalves) * sizeof(_Float16);  // 160 KiB
 
 __device__ __forceinline__ uint32_t lds_byte_addr(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
@@ -647,7 +649,7 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
                                                                 bool y_vec4, int row_tiles) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
   _Float16 *const Wbuf = lds_dynamic;                   // 2 weight stages
-  _Float16 *const Xbuf = lds_dynamic + 2 * kPPWHalves;  // 3 activation stages
+  _Float16 *const Xbuf = lds_dynamic + 2 * kPPWHalves;  // kPPXBufs activation stages
   const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kGemmThreads);
   const int tid = static_cast<int>(threadIdx.x) - g * kGemmThreads;  // thread within the group
   const int lane = tid & 63;
@@ -666,25 +668,22 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
   const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
   const int tok0 = ((lin % in_group) / group_rows) * kPPBN;
 
-  // Weight staging share of group g: rows 64 g + tid / 2, block tid % 2 of
-  // the stage's pair, by threads tid < 128.
-  const bool wstage = tid < kBM;  // uniform per wavefront
-  const int srow = (kBM / 2) * g + ((tid >> 1) & (kBM / 2 - 1)), sh = tid & 1;
+  // group 0: row tid / 2, block tid % 2 of the stage's pair
+  const int srow = tid >> 1, sh = tid & 1;
   const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
-  // Activation copies of group g: tokens 128 g .. 128 g + 127 of the tile,
-  // copy i of wavefront w filling LDS rows 128 g + 8 (4 w + i) .. + 7. Lane
-  // p of a copy writes position p % 8 of row p / 8, which holds chunk
-  // (p % 8) ^ (row % 8) (the lds_at permutation); token rows past the end
-  // re-read the last token.
+  // group 1: copy i of wavefront w fills LDS rows 8 (8 w + i) .. + 7 of the
+  // activation tile; lane p writes position p % 8 of row p / 8, which holds
+  // chunk (p % 8) ^ (row % 8) (the lds_at permutation). Token rows past the
+  // end re-read the last token.
   uint32_t xoff[kPPXOps];
 #pragma unroll
   for (int i = 0; i < kPPXOps; ++i) {
-    const int row = (kPPBN / 2) * g + 8 * (kPPXOps * wave + i) + (lane >> 3);
+    const int row = 8 * (kPPXOps * wave + i) + (lane >> 3);
     const int c = (lane & 7) ^ (row & 7);
     const int tok = min(tok0 + row, n_tokens - 1);
     xoff[i] = static_cast<uint32_t>((tok * k + 8 * c) * 2);
   }
-  const uint32_t xlds0 = lds_byte_addr(Xbuf) + ((kPPBN / 2) * g + 8 * kPPXOps * wave) * (kBK * 2);
+  const uint32_t xlds0 = lds_byte_addr(Xbuf) + 8 * kPPXOps * wave * (kBK * 2);
 
   float4_t acc[4][4];
 #pragma unroll
@@ -695,19 +694,17 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
   const int n_st = nblk / 2;
   const int last = n_st - 1;
   auto load_w = [&](HalfRaw<QT> &r, int st) {
-    if (wstage) {
-      if constexpr (ALIGN4)
-        r = load_half_pair<QT>(rp, st, sh);
-      else
-        r = load_half_u16<QT>(rp, 2 * st + sh, nblk);
-    }
+    if constexpr (ALIGN4)
+      r = load_half_pair<QT>(rp, st, sh);
+    else
+      r = load_half_u16<QT>(rp, 2 * st + sh, nblk);
   };
   auto store_w = [&](int buf, const HalfRaw<QT> &r) {
-    if (wstage) store_half<QT>(Wbuf + buf * kPPWHalves, srow, 4 * sh, r, ALIGN4 && sh == 0);
+    store_half<QT>(Wbuf + buf * kPPWHalves, srow, 4 * sh, r, ALIGN4 && sh == 0);
   };
   auto copy_x = [&](int st) {
     const _Float16 *base = X + static_cast<int64_t>(kBK) * st;
-    const uint32_t lds = xlds0 + static_cast<uint32_t>((st % 3) * kPPXHalves * 2);
+    const uint32_t lds = xlds0 + static_cast<uint32_t>((st % kPPXBufs) * kPPXHalves * 2);
 #pragma unroll
     for (int i = 0; i < kPPXOps; ++i) dma16(xoff[i], base, lds + i * 1024);
   };
@@ -717,87 +714,140 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
     aofs[h] = lds_at(64 * wm + (lane & 15), (lane >> 4) + 4 * h);
     bofs[h] = lds_at((kPPBN / 2) * g + 64 * wn + (lane & 15), (lane >> 4) + 4 * h);
   }
-  // All 16 operand reads of a stage go out before its first MFMA, so the
-  // LDS latency is paid once per phase rather than between MFMA groups.
-  auto compute = [&](int st) {
+  // Operands of a stage in registers. A stage's activations are complete in
+  // LDS one phase before its weights, and both are complete for group 1 one
+  // phase before it computes the stage, so the reads are issued ahead:
+  // group 1 reads all operands of stage s during its memory phase, group 0
+  // the activations of stage s + 1 during its memory phase and the weights
+  // at the start of its compute phase. The MFMAs then wait on LDS latency
+  // once per stage at most.
+  half8_t pa[2][4], pb[2][4];
+  auto read_a = [&](int st) {
     const _Float16 *ws = Wbuf + (st & 1) * kPPWHalves;
-    const _Float16 *xs = Xbuf + (st % 3) * kPPXHalves;
-    half8_t a[2][4], b[2][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
+      for (int i = 0; i < 4; ++i) pa[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
+  };
+  auto read_b = [&](int st) {
+    const _Float16 *xs = Xbuf + (st % kPPXBufs) * kPPXHalves;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pb[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
+  };
+  auto mfmas = [&] {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
-#pragma unroll
-    for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[h][i], pb[h][j], acc[i][j], 0, 0, 0);
   };
   auto phase_end = [] {
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // memory(s): this group's weights of stage s + 1 into buffer (s + 1) % 2
-  // from registers loaded two stages earlier, the copy of stage s + 2's
-  // activations, a wait that leaves only that copy in flight (so stage
-  // s + 1's copy, issued one memory phase earlier, has landed), then the
-  // weight loads of stage s + 3 into the registers just freed.
+  // memory(s), group 0: the weights of stage s + 1 into buffer (s + 1) % 2
+  // from registers loaded two stages earlier, the loads of stage s + 3 into
+  // those registers (past the last stage they re-read it; what they bring
+  // is stored into the idle buffer and never read), and the activation
+  // operands of stage s + 1. Group 1: the copy of stage s + 3's activations
+  // and a wait that leaves the copies of stages s + 2 and s + 3 in flight, so
+  // stage s + 1's (issued two memory phases earlier) has landed before the
+  // barrier; then the operands of stage s.
+  HalfRaw<QT> r0, r1;
   auto memory = [&](int s, HalfRaw<QT> &r, int buf) {
-    store_w(buf, r);
-    copy_x(min(s + 2, last));
-    wait_vmcnt<kPPXOps>();
-    load_w(r, min(s + 3, last));
+    if (g == 0) {
+      store_w(buf, r);
+      load_w(r, min(s + 3, last));
+      if (s < last) read_b(s + 1);
+    } else {
+      if (s + 3 <= last) {
+        copy_x(s + 3);
+        wait_vmcnt<2 * kPPXOps>();
+      } else if (s + 2 <= last) {
+        wait_vmcnt<kPPXOps>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      read_a(s);
+      read_b(s);
+    }
+  };
+  auto compute = [&](int s) {
+    if (g == 0) {
+      read_a(s);
+      mfmas();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
+#pragma unroll
+      for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+    } else {
+      mfmas();
+    }
   };
 
-  HalfRaw<QT> r0, r1;
-  copy_x(0);
-  load_w(r0, 0);
-  load_w(r1, min(1, last));
-  copy_x(min(1, last));
-  store_w(0, r0);
-  wait_vmcnt<0>();
-  load_w(r0, min(2, last));
+  if (g == 0) {
+    load_w(r0, 0);
+    load_w(r1, min(1, last));
+    store_w(0, r0);
+    load_w(r0, min(2, last));
+  } else {
+    copy_x(0);
+    if (last >= 1) copy_x(1);
+    if (last >= 2) copy_x(2);
+    if (last >= 2)
+      wait_vmcnt<2 * kPPXOps>();
+    else
+      wait_vmcnt<0>();
+  }
   phase_end();  // stage 0 is in LDS
+  if (g == 0) read_b(0);
   // Group 0 runs compute(s), memory(s); group 1 memory(s), compute(s): both
   // pass the same barriers, and each phase pairs one group's MFMAs with the
   // other's staging.
+  // The loops run whole pairs of stages (straight-line bodies, so the wait
+  // for a register set's loads leaves the other set's loads in flight), then
+  // an odd last stage.
+  int s = 0;
   if (g == 0) {
-    for (int s = 0; s < n_st; s += 2) {
+    for (; s + 1 < n_st; s += 2) {
       compute(s);
       phase_end();
       memory(s, r1, 1);
       phase_end();
-      if (s + 1 < n_st) {
-        compute(s + 1);
-        phase_end();
-        memory(s + 1, r0, 0);
-        phase_end();
-      }
+      compute(s + 1);
+      phase_end();
+      memory(s + 1, r0, 0);
+      phase_end();
+    }
+    if (s < n_st) {
+      compute(s);
+      phase_end();
+      memory(s, r1, 1);
+      phase_end();
     }
   } else {
-    for (int s = 0; s < n_st; s += 2) {
+    for (; s + 1 < n_st; s += 2) {
       memory(s, r1, 1);
       phase_end();
       compute(s);
       phase_end();
-      if (s + 1 < n_st) {
-        memory(s + 1, r0, 0);
-        phase_end();
-        compute(s + 1);
-        phase_end();
-      }
+      memory(s + 1, r0, 0);
+      phase_end();
+      compute(s + 1);
+      phase_end();
+    }
+    if (s < n_st) {
+      memory(s, r1, 1);
+      phase_end();
+      compute(s);
+      phase_end();
     }
   }
-  wait_vmcnt<0>();  // no copy outlives the workgroup
+  wait_vmcnt<0>();  // no load outlives the workgroup
 
   // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
   // token 128 g + 64 wn + 16 j + l % 16.
