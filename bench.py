@@ -66,10 +66,11 @@ KERNELS = {
     # name fragment in the kernel symbol -> sources the kernel is built from
     "gemv_stream_kernel": ("gemv_stream.hip", "gemv_common.h", "common.h", "launch.h"),
     "gemm_kernel": ("gemm.hip", "common.h", "launch.h"),
+    "gemm_pp_kernel": ("gemm.hip", "common.h", "launch.h"),
 }
 # Template arguments of the plain (MUL_MAT) instantiations; the expert-routed
 # (MUL_MAT_ID) ones carry one more, which the demangled name shows.
-KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3}
+KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3, "gemm_pp_kernel": 2}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -105,7 +106,7 @@ def parse():
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run one plain {COPY_CAL_BYTES >> 20} MiB device copy (for counter calibration)")
-    ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill"),
+    ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill", "output_projection", "prefill_512"),
                     help="run just this pass (eagerly once, then --steps graph replays) and print no JSON; "
                          "for hardware-counter runs, whose per-dispatch averages must cover one pass only")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -127,8 +128,24 @@ def _find(d, suffix):
         return list(csv.DictReader(fh))
 
 
+def _demangle_simple(name):
+    """qmm::kernel<...> for an Itanium-mangled kernel symbol whose template
+    arguments are integers and booleans (the form rocprofv3 sometimes
+    reports), else the name unchanged."""
+    m = re.match(r"_ZN((?:\d+[A-Za-z_]\w*?)+)I((?:L[ib]\d+E)+)EE", name)
+    if not m:
+        return name
+    parts, rest = [], m.group(1)
+    while rest:
+        n = re.match(r"\d+", rest).group(0)
+        parts.append(rest[len(n):len(n) + int(n)])
+        rest = rest[len(n) + int(n):]
+    args = [("true" if v == "1" else "false") if t == "b" else v for t, v in re.findall(r"L([ib])(\d+)E", m.group(2))]
+    return "::".join(parts) + "<" + ", ".join(args) + ">"
+
+
 def _short(name):
-    name = name.replace("(anonymous namespace)::", "")
+    name = _demangle_simple(name).replace("(anonymous namespace)::", "")
     return re.sub(r"\(.*", "", name).replace("void ", "")
 
 
@@ -314,8 +331,8 @@ def time_type(torch, qmm, synth, qt, with_oracle=False):
                       "GB_per_s": round(gbs, 2), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                       "kernel": "gemv_stream_kernel", "bound": "hbm"},
            "prefill": {"tokens": T, "us_per_launch": round(us2, 3), "TFLOP_per_s": round(tfl, 2),
-                       "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4), "kernel": "gemm_kernel",
-                       "bound": "mfma"}}
+                       "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
+                       "kernel": "gemm_kernel" if qt == synth.TYPE_Q4_K else "gemm_pp_kernel", "bound": "mfma"}}
     if with_oracle:
         import oracle.qmm_oracle as O
         t0 = time.perf_counter()
@@ -608,6 +625,18 @@ def main():
     layers = args.layers
     cpu_layers = 0 if args.no_cpu_baseline else max(1, min(args.cpu_layers, layers))
 
+    if args.only in ("output_projection", "prefill_512"):
+        # one of the single-matrix workloads alone (for counter runs): its
+        # timed graphs, after a plain copy of known size when calibrating
+        if args.copy_calibration:
+            a = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+            torch.empty_like(a).copy_(a)
+            torch.cuda.synchronize()
+            del a
+        res = (time_output_projection if args.only == "output_projection" else time_prefill_512)(torch, qmm, synth)
+        log(json.dumps(res))
+        return
+
     log(f"generating and uploading the {layers}-layer stack")
     dec, pre, W, X1, X2, host = upload_stack(torch, synth, layers, cpu_layers)
     if args.copy_calibration:  # a plain device copy of known size, for counter calibration
@@ -722,7 +751,7 @@ def main():
     r_dec = roof("gemv_stream_kernel", "hbm", dec_bytes / launches["decode"], "GB/s", HBM_PEAK_GBS,
                  (dec_bytes / launches["decode"]) / (us_launch["decode"] * 1e-6) / 1e9)
     r_dec["avg_launch_us"] = round(us_launch["decode"], 3)
-    r_pre = roof("gemm_kernel", "mfma", pre_flops / launches["prefill"], "TFLOP/s", MFMA_F16_PEAK_TFLOPS,
+    r_pre = roof("gemm_pp_kernel", "mfma", pre_flops / launches["prefill"], "TFLOP/s", MFMA_F16_PEAK_TFLOPS,
                  (pre_flops / launches["prefill"]) / (us_launch["prefill"] * 1e-6) / 1e12)
     r_pre["avg_launch_us"] = round(us_launch["prefill"], 3)
 
