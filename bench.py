@@ -490,7 +490,7 @@ def time_matmul_id(torch, qmm, synth, with_oracle=False):
     ids_p = [torch.from_numpy(routing(T)).cuda() for _ in range(reps_p)]
     Xp = torch.from_numpy(synth.make_activations(T, k, rng)).cuda().view(T, 1, k)
     Yp = torch.empty((T, used, rows), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qmm.qmm_matmul_id_workspace_bytes(E, used, T), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qmm.qmm_matmul_id_workspace_bytes_x16(E, used, T, k, 1), dtype=torch.uint8, device="cuda")
 
     def run_p():
         for i in range(reps_p):

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_id_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
         L.qmm_matmul_id_workspace_bytes.argtypes = [i64, i64, i64]
         L.qmm_matmul_id_workspace_bytes.restype = i64
+        L.qmm_matmul_id_workspace_bytes_x16.argtypes = [i64, i64, i64, i64, i64]
+        L.qmm_matmul_id_workspace_bytes_x16.restype = i64
         for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch",
                   "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc"):
             getattr(L, f).restype = i32
@@ -230,6 +232,11 @@ def qmm_matmul_id_workspace_bytes(n_experts: int, n_ids: int, n_tokens: int) -> 
     return int(lib().qmm_matmul_id_workspace_bytes(int(n_experts), int(n_ids), int(n_tokens)))
 
 
+def qmm_matmul_id_workspace_bytes_x16(n_experts: int, n_ids: int, n_tokens: int, k: int, x_slots: int) -> int:
+    return int(lib().qmm_matmul_id_workspace_bytes_x16(int(n_experts), int(n_ids), int(n_tokens), int(k),
+                                                       int(x_slots)))
+
+
 def _matmul_id_args(W, ggml_type, k, X, ids, n_experts, n_rows, row_stride_bytes, expert_stride_bytes, Y):
     """Geometry and checked buffers of a MUL_MAT_ID call (shared by both entry points)."""
     import torch
@@ -264,11 +271,17 @@ def qmm_matmul_id(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, row_stri
     GPU tensor with the four geometry arguments given. X is a contiguous fp32
     [n_tokens][x_slots][k] tensor (x_slots 1 or n_ids), ids a contiguous int32
     [n_tokens][n_ids] tensor; Y (fp32 [n_tokens][n_ids][n_rows]) is allocated
-    if None. An id outside [0, n_experts) gives a row of NaNs."""
+    if None. An id outside [0, n_experts) gives a row of NaNs. Without a
+    workspace, one of qmm_matmul_id_workspace_bytes_x16 bytes is allocated
+    (the fastest route); a given workspace needs at least
+    qmm_matmul_id_workspace_bytes."""
     import torch
     geo, n_ids, n_tokens, Y = _matmul_id_args(W, ggml_type, k, X, ids, n_experts, n_rows, row_stride_bytes,
                                               expert_stride_bytes, Y)
-    need = qmm_matmul_id_workspace_bytes(geo[0], n_ids, n_tokens)
+    if workspace is None:
+        need = qmm_matmul_id_workspace_bytes_x16(geo[0], n_ids, n_tokens, int(k), int(X.shape[1]))
+    else:
+        need = qmm_matmul_id_workspace_bytes(geo[0], n_ids, n_tokens)
     if need < 0:
         raise QmmError(need, "qmm_matmul_id_workspace_bytes")
     if workspace is None and need > 0:

@@ -637,6 +637,10 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void *base, uint32_t 
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");
 }
+// The same with a per-lane 64-bit address (rows gathered through a list).
+__device__ __forceinline__ void dma16(const void *p, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds) : "memory", "m0");
+}
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -870,6 +874,255 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
   }
 }
 
+// Expert-routed MUL_MAT_ID with many pairs, on the two-group structure: a
+// workgroup takes two tiles of the routing table (tiles 2 p and 2 p + 1, up
+// to 128 pairs of one expert each) for one 128-row tile, one tile per
+// group. Each group has its own weight and activation stages in LDS (its
+// expert's rows, its pairs' activation rows) and does all of its own
+// staging in its memory phase: one block of one row per thread, decoded
+// from registers loaded two stages ahead, and its 128 activation rows
+// copied two stages ahead from an fp16 copy of X (made by the caller's
+// conversion kernel, the same rounding the one-group kernel applies)
+// straight into LDS, gathered through the pair list. The phases alternate
+// as in the dense kernel, so one group's MFMAs run beside the other's
+// staging. Each output element gets the same MFMAs in the same k order as
+// in the one-group routed kernel, so the two agree bit for bit. A group
+// whose tile is empty (past the routing table's last tile) runs on its
+// tile's valid placeholder entries and stores nothing; a workgroup whose
+// two tiles are empty returns at once.
+constexpr int kPPRXOps = (kPPBN / 2) * kBK * 2 / (kGemmThreads * 16);  // copies per lane per stage (4)
+constexpr size_t kPPRoutedLds = (2 * 2 * kPPWHalves + 3 * 2 * (kPPBN / 2) * kBK) * sizeof(_Float16);  // 160 KiB
+
+template <int QT, bool ALIGN4>
+__global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uint8_t *__restrict__ W, int n_rows,
+                                                                       int nblk, int64_t nb1,
+                                                                       const _Float16 *__restrict__ Xh, int k,
+                                                                       float *__restrict__ Y, bool y_vec4,
+                                                                       int row_tiles, GemmRoute route,
+                                                                       int n_tiles_all) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
+  constexpr int kXH = (kPPBN / 2) * kBK;  // one group's activation stage
+  const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kGemmThreads);
+  const int tid = static_cast<int>(threadIdx.x) - g * kGemmThreads;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  // LDS: [stage][group] weight tiles (2 stages), then [stage][group]
+  // activation tiles (3 stages)
+  auto wtile = [&](int buf) { return lds_dynamic + (2 * buf + g) * kPPWHalves; };
+  auto xtile = [&](int buf) { return lds_dynamic + 4 * kPPWHalves + (2 * buf + g) * kXH; };
+
+  // tile order: as the dense kernels, tile pairs in place of token tiles
+  const int n_wg = static_cast<int>(gridDim.x);
+  const int bid = static_cast<int>(blockIdx.x);
+  const int per_xcd = n_wg / kXcds;
+  const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
+  const int pair_tiles = n_wg / row_tiles;
+  const int in_group = kGroupRows * pair_tiles;
+  const int first_row = (lin / in_group) * kGroupRows;
+  const int group_rows = min(row_tiles - first_row, kGroupRows);
+  const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
+  const int tp = (lin % in_group) / group_rows;
+
+  // the two tiles; entries past the table read as empty
+  int e2[2], f2[2], c2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 2 * tp + h;
+    const bool in = t < n_tiles_all;
+    e2[h] = in ? __builtin_amdgcn_readfirstlane(route.tiles[4 * t]) : 0;
+    f2[h] = in ? __builtin_amdgcn_readfirstlane(route.tiles[4 * t + 1]) : 0;
+    c2[h] = in ? __builtin_amdgcn_readfirstlane(route.tiles[4 * t + 2]) : 0;
+  }
+  if (c2[0] == 0 && c2[1] == 0) return;  // whole workgroup: no pairs
+  const int e = g ? e2[1] : e2[0], first = g ? f2[1] : f2[0], cnt = g ? c2[1] : c2[0];
+
+  // weights of this group's expert: row tid / 2, block tid % 2 of the pair
+  const int srow = tid >> 1, sh = tid & 1;
+  const uint8_t *rp = W + static_cast<int64_t>(e) * route.nb2 + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
+  // activations: copy i of wavefront w fills LDS rows 8 (4 w + i) .. + 7 of
+  // the group's tile (token slots); lane p writes position p % 8 of row p / 8,
+  // which holds chunk (p % 8) ^ (row % 8) (the lds_at permutation); slots
+  // past the tile's count repeat its last pair
+  const _Float16 *xsrc[kPPRXOps];
+#pragma unroll
+  for (int i = 0; i < kPPRXOps; ++i) {
+    const int slot = 8 * (kPPRXOps * wave + i) + (lane >> 3);
+    const int c = (lane & 7) ^ (slot & 7);
+    const int p = route.list[first + min(slot, max(cnt, 1) - 1)];
+    const int t = p / route.n_ids;
+    const int64_t xr = static_cast<int64_t>(t) * route.x_slots + (route.x_slots > 1 ? p - t * route.n_ids : 0);
+    xsrc[i] = Xh + xr * k + 8 * c;
+  }
+  const uint32_t xdst0 = lds_byte_addr(lds_dynamic + 4 * kPPWHalves + g * kXH) + 8 * kPPRXOps * wave * (kBK * 2);
+
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int n_st = nblk / 2;
+  const int last = n_st - 1;
+  auto load_w = [&](HalfRaw<QT> &r, int st) {
+    if constexpr (ALIGN4)
+      r = load_half_pair<QT>(rp, st, sh);
+    else
+      r = load_half_u16<QT>(rp, 2 * st + sh, nblk);
+  };
+  auto store_w = [&](int buf, const HalfRaw<QT> &r) {
+    store_half<QT>(wtile(buf), srow, 4 * sh, r, ALIGN4 && sh == 0);
+  };
+  // the copy of stage st into activation buffer b % 3
+  auto copy_x = [&](int st, int b) {
+    const uint32_t dst = xdst0 + static_cast<uint32_t>((b % 3) * 2 * kXH * 2);
+#pragma unroll
+    for (int i = 0; i < kPPRXOps; ++i) dma16(xsrc[i] + kBK * st, dst + i * 1024);
+  };
+  int aofs[2], bofs[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    aofs[h] = lds_at(64 * wm + (lane & 15), (lane >> 4) + 4 * h);
+    bofs[h] = lds_at(64 * wn + (lane & 15), (lane >> 4) + 4 * h);
+  }
+  auto compute = [&](int s) {
+    const _Float16 *ws = wtile(s & 1), *xs = xtile(s % 3);
+    half8_t a[2][4], b[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
+#pragma unroll
+    for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+  };
+  auto phase_end = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // memory(s): the weights of stage s + 1 into buffer (s + 1) % 2 from
+  // registers loaded three memory phases earlier (three register sets: the
+  // weights come from HBM, each expert's rows being read by one or two
+  // workgroups), the copy of stage s + 2, then a wait that leaves only that
+  // copy and the weight loads issued after stage s + 1's copy in flight (so
+  // stage s + 1's copy, issued one memory phase earlier, has landed before
+  // the barrier; the weight loads are counted as two operations, at most
+  // their number, so the wait is at worst stricter), then the weight loads
+  // of stage s + 4. Past the last stage copies and loads re-read it into the
+  // free buffer and the registers, whose stores go to the idle buffer; none
+  // of it is read.
+  HalfRaw<QT> r0, r1, r2;
+  auto memory = [&](int s, HalfRaw<QT> &r) {
+    store_w((s + 1) & 1, r);
+    copy_x(min(s + 2, last), s + 2);
+    wait_vmcnt<kPPRXOps + 2>();
+    load_w(r, min(s + 4, last));
+  };
+
+  // prologue: copies of stages 0 and 1, weights of stages 0 to 3, stage 0
+  // stored (the wait for its weight registers covers its copy, issued before
+  // them)
+  copy_x(0, 0);
+  load_w(r0, 0);
+  copy_x(min(1, last), 1);
+  load_w(r1, min(1, last));
+  load_w(r2, min(2, last));
+  store_w(0, r0);
+  wait_vmcnt<kPPRXOps + 4>();  // stage 0's copy has landed (stage 1's copy and two weight sets may not)
+  load_w(r0, min(3, last));
+  phase_end();  // stage 0 is in LDS
+  // Whole triples of stages (straight-line bodies, so the wait for one
+  // register set leaves the others' loads in flight), then up to two.
+  int s = 0;
+  if (g == 0) {
+    for (; s + 2 < n_st; s += 3) {
+      compute(s);
+      phase_end();
+      memory(s, r1);
+      phase_end();
+      compute(s + 1);
+      phase_end();
+      memory(s + 1, r2);
+      phase_end();
+      compute(s + 2);
+      phase_end();
+      memory(s + 2, r0);
+      phase_end();
+    }
+    if (s < n_st) {
+      compute(s);
+      phase_end();
+      memory(s, r1);
+      phase_end();
+    }
+    if (s + 1 < n_st) {
+      compute(s + 1);
+      phase_end();
+      memory(s + 1, r2);
+      phase_end();
+    }
+  } else {
+    for (; s + 2 < n_st; s += 3) {
+      memory(s, r1);
+      phase_end();
+      compute(s);
+      phase_end();
+      memory(s + 1, r2);
+      phase_end();
+      compute(s + 1);
+      phase_end();
+      memory(s + 2, r0);
+      phase_end();
+      compute(s + 2);
+      phase_end();
+    }
+    if (s < n_st) {
+      memory(s, r1);
+      phase_end();
+      compute(s);
+      phase_end();
+    }
+    if (s + 1 < n_st) {
+      memory(s + 1, r2);
+      phase_end();
+      compute(s + 1);
+      phase_end();
+    }
+  }
+  wait_vmcnt<0>();  // no copy outlives the workgroup
+
+  // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
+  // token slot 64 wn + 16 j + l % 16 of this group's tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = 64 * wn + 16 * j + (lane & 15);
+    if (slot >= cnt) continue;
+    float *yrow = Y + static_cast<int64_t>(route.list[first + slot]) * n_rows;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + 64 * wm + 16 * i + 4 * (lane >> 4);
+      if (y_vec4 && r + 3 < n_rows) {
+        *reinterpret_cast<float4_t *>(yrow + r) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (r + q < n_rows) yrow[r + q] = acc[i][j][q];
+      }
+    }
+  }
+}
+
 template <int QT, bool XF16, int BM, int KS = 1>
 static hipError_t gemm_dispatch(bool align4, dim3 grid, hipStream_t s, const uint8_t *w, int n_rows, int nblk,
                                 int64_t nb1, const void *X, int n_tokens, int k, float *Y, bool y_vec4, int row_tiles) {
@@ -884,9 +1137,15 @@ static hipError_t gemm_dispatch(bool align4, dim3 grid, hipStream_t s, const uin
                 Y, y_vec4, row_tiles, none);
 }
 
+bool routed_two_group(int qtype, int64_t k, int64_t n_rows, int64_t max_tiles, int64_t cus) {
+  const int64_t row_tiles = (n_rows + kBM - 1) / kBM;
+  return qtype != QMM_TYPE_Q4_K && cus > 0 && row_tiles * ((max_tiles + 1) / 2) >= cus && (k / 32) % 2 == 0;
+}
+
 hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
-                              const float *X, int64_t x_slots, int64_t n_ids, const int32_t *list,
-                              const int32_t *tiles, int64_t max_tiles, float *Y, hipStream_t stream) {
+                              const float *X, const _Float16 *Xh, int64_t x_slots, int64_t n_ids,
+                              const int32_t *list, const int32_t *tiles, int64_t max_tiles, float *Y,
+                              hipStream_t stream) {
   const uint8_t *w = static_cast<const uint8_t *>(W);
   const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0) && (nb2 % 4 == 0);
   const bool y_vec4 = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && (n_rows % 4 == 0);
@@ -896,6 +1155,23 @@ hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t 
   const GemmRoute route{list, tiles, nb2, static_cast<int>(n_ids), static_cast<int>(x_slots)};
   const int rt = static_cast<int>(row_tiles), nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows),
             kk = static_cast<int>(k);
+  // With the fp16 copy of X (Xh), two tiles per workgroup on the two-group
+  // kernel when the tile pairs give at least one workgroup per CU and the
+  // block count is whole stages.
+  const int64_t pairs_of_tiles = (max_tiles + 1) / 2;
+  const int64_t cus = device_cus();
+  if (Xh != nullptr && routed_two_group(qtype, k, n_rows, max_tiles, cus)) {
+    const dim3 pgrid(static_cast<unsigned>(row_tiles * pairs_of_tiles));
+    const int nt_all = static_cast<int>(max_tiles);
+    return by_qtype(qtype, [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
+      auto go = [&](auto kern) {
+        return launch(kern, pgrid, dim3(kPPThreads), kPPRoutedLds, stream, w, nr, nblk, nb1, Xh, kk, Y, y_vec4, rt,
+                      route, nt_all);
+      };
+      return align4 ? go(gemm_pp_routed_kernel<QT, true>) : go(gemm_pp_routed_kernel<QT, false>);
+    });
+  }
   const dim3 block(kGemmThreads);
   return by_qtype_k(qtype, [&](auto qt) {
     constexpr int QT = decltype(qt)::value;

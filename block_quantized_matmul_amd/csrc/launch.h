@@ -82,17 +82,26 @@ constexpr int kRouteMaxExperts = 4096;
 // matrix-core kernel, 2, 4 or 8 for the decode kernel's tile form.
 int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs, int tile);
 int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs, int tile);
+// With the matrix-core tiles, a workspace of at least route_workspace_bytes
+// + route_x16_bytes also holds an fp16 copy of X (after the routing table),
+// which lets the two-group kernel run; results are the same bits.
+int64_t route_x16_bytes(int64_t n_tokens, int64_t x_slots, int64_t k);
 hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k,
                                     int64_t nb1, int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids,
-                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace, int tile,
-                                    hipStream_t stream);
+                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                                    int64_t workspace_bytes, int tile, hipStream_t stream);
 hipError_t launch_gemv_id_tiles(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k, int64_t nb1,
                                 int64_t nb2, const float *X, int64_t x_slots, int64_t n_ids, int64_t n_tokens,
                                 const int32_t *list, const int32_t *tiles, int64_t max_tiles, int nt, float *Y,
                                 hipStream_t stream);
+// The routed matrix-core product; with Xh (an fp16 copy of X) and enough
+// tile pairs to fill the GPU (routed_two_group) it runs two tiles per
+// workgroup on the two-group kernel, else the one-group kernel on fp32 X.
+bool routed_two_group(int qtype, int64_t k, int64_t n_rows, int64_t max_tiles, int64_t cus);
 hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
-                              const float *X, int64_t x_slots, int64_t n_ids, const int32_t *list,
-                              const int32_t *tiles, int64_t max_tiles, float *Y, hipStream_t stream);
+                              const float *X, const _Float16 *Xh, int64_t x_slots, int64_t n_ids,
+                              const int32_t *list, const int32_t *tiles, int64_t max_tiles, float *Y,
+                              hipStream_t stream);
 
 // Matrix-core kernel, any n_tokens >= 1.
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,

@@ -284,6 +284,17 @@ int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t 
   return qmm::route_workspace_bytes(n_experts, n_ids * n_tokens, plan.tile);
 }
 
+int64_t qmm_matmul_id_workspace_bytes_x16(int64_t n_experts, int64_t n_ids, int64_t n_tokens, int64_t k,
+                                          int64_t x_slots) {
+  const int64_t base = qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens);
+  if (base < 0) return base;
+  if (k <= 0 || k > kMaxDim || (x_slots != 1 && x_slots != n_ids)) return QMM_ERR_SHAPE;
+  const IdPlan plan = id_plan(n_experts, n_ids, n_tokens);
+  if (plan.route != IdPlan::kGemm) return base;
+  if (n_tokens > kMaxDim / (x_slots * k)) return QMM_ERR_SHAPE;
+  return base + qmm::route_x16_bytes(n_tokens, x_slots, k);
+}
+
 // Checks of a MUL_MAT_ID call, all on the host, except those of the
 // workspace; fills in the route and the workspace the sizes call for.
 static int check_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
@@ -316,7 +327,7 @@ static int check_matmul_id(const void *W, int ggml_type, int64_t n_experts, int6
 static int run_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
                          int64_t row_stride_bytes, int64_t expert_stride_bytes, const float *X, int64_t x_slots,
                          const int32_t *ids, int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
-                         const IdPlan &plan, hipStream_t s) {
+                         int64_t workspace_bytes, const IdPlan &plan, hipStream_t s) {
   const bool grouped = plan.route != IdPlan::kPerPair;
   const bool streaming = !grouped && qmm::id_streamable(W, n_rows, k, row_stride_bytes, expert_stride_bytes);
   if (trace_on())
@@ -328,7 +339,7 @@ static int run_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_
   if (grouped)
     return status_of(qmm::launch_matmul_id_grouped(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
                                                    expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y,
-                                                   workspace, plan.tile, s));
+                                                   workspace, workspace_bytes, plan.tile, s));
   if (streaming)
     return status_of(qmm::launch_gemv_id_stream(W, ggml_type, n_experts, n_rows, k, row_stride_bytes,
                                                 expert_stride_bytes, X, x_slots, ids, n_ids, n_tokens, Y, s));
@@ -351,7 +362,7 @@ int qmm_matmul_id(const void *W, int ggml_type, int64_t n_experts, int64_t n_row
     if (!aligned(workspace, 4)) return QMM_ERR_ALIGN;
   }
   return run_matmul_id(W, ggml_type, n_experts, n_rows, k, row_stride_bytes, expert_stride_bytes, X, x_slots, ids,
-                       n_ids, n_tokens, Y, workspace, plan, static_cast<hipStream_t>(stream));
+                       n_ids, n_tokens, Y, workspace, workspace_bytes, plan, static_cast<hipStream_t>(stream));
 }
 
 int qmm_matmul_id_noalloc(const void *W, int ggml_type, int64_t n_experts, int64_t n_rows, int64_t k,
@@ -370,7 +381,8 @@ int qmm_matmul_id_noalloc(const void *W, int ggml_type, int64_t n_experts, int64
     if (ws == nullptr) return QMM_ERR_HIP;
   }
   return run_matmul_id(W, ggml_type, n_experts, n_rows, k, row_stride_bytes, expert_stride_bytes, X, x_slots, ids,
-                       n_ids, n_tokens, Y, ws, plan, static_cast<hipStream_t>(stream));
+                       n_ids, n_tokens, Y, ws, ws ? QMM_NOALLOC_SCRATCH_BYTES : 0, plan,
+                       static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

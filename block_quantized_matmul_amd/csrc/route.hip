@@ -21,6 +21,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace qmm {
 
 namespace {
@@ -170,7 +172,22 @@ __global__ __launch_bounds__(64) void route_small_kernel(const int32_t *__restri
   }
 }
 
+// fp32 -> fp16 copy of the activations for the two-group routed kernel
+// (round to nearest even, the conversion the one-group kernel applies while
+// staging), four values per thread, grid-stride.
+__global__ __launch_bounds__(256) void x16_copy_kernel(const float *__restrict__ X, _Float16 *__restrict__ Xh,
+                                                       int64_t n4) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float4_t f = reinterpret_cast<const float4_a4 *>(X)[i];
+    const half2_t a = cvt_half2(f.x, f.y), b = cvt_half2(f.z, f.w);
+    reinterpret_cast<u32x2_a4 *>(Xh)[i] = u32x2_a4{as_u32(a), as_u32(b)};
+  }
+}
+
 }  // namespace
+
+int64_t route_x16_bytes(int64_t n_tokens, int64_t x_slots, int64_t k) { return n_tokens * x_slots * k * 2; }
 
 int64_t route_max_tiles(int64_t n_experts, int64_t n_pairs, int tile) {
   // sum over experts of ceil(count / tile) <= n_pairs / tile + (experts used)
@@ -183,8 +200,8 @@ int64_t route_workspace_bytes(int64_t n_experts, int64_t n_pairs, int tile) {
 
 hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts, int64_t n_rows, int64_t k,
                                     int64_t nb1, int64_t nb2, const float *X, int64_t x_slots, const int32_t *ids,
-                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace, int tile,
-                                    hipStream_t stream) {
+                                    int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
+                                    int64_t workspace_bytes, int tile, hipStream_t stream) {
   const int64_t n_pairs = n_tokens * n_ids;
   const int64_t max_tiles = route_max_tiles(n_experts, n_pairs, tile);
   int32_t *list = static_cast<int32_t *>(workspace);
@@ -197,8 +214,22 @@ hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts,
                                 static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
                                 static_cast<int>(n_rows));
   if (e != hipSuccess) return e;
-  if (tile == kTileTokens)
-    return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, x_slots, n_ids, list, tiles, max_tiles, Y, stream);
+  if (tile == kTileTokens) {
+    // the fp16 copy of X, after the routing table, when the workspace holds
+    // it and the two-group kernel will take the call
+    const int64_t route_bytes = route_workspace_bytes(n_experts, n_pairs, tile);
+    const int64_t x16 = route_x16_bytes(n_tokens, x_slots, k);
+    _Float16 *Xh = nullptr;
+    if (workspace_bytes >= route_bytes + x16 && routed_two_group(qtype, k, n_rows, max_tiles, device_cus())) {
+      Xh = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + route_bytes);
+      const int64_t n4 = n_tokens * x_slots * k / 4;
+      const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+      e = launch(x16_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Xh, n4);
+      if (e != hipSuccess) return e;
+    }
+    return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, Xh, x_slots, n_ids, list, tiles, max_tiles, Y,
+                              stream);
+  }
   return launch_gemv_id_tiles(W, qtype, n_experts, n_rows, k, nb1, nb2, X, x_slots, n_ids, n_tokens, list, tiles,
                               max_tiles, tile, Y, stream);
 }

@@ -308,6 +308,22 @@ int qmm_matmul_id_noalloc(const void *W, int ggml_type, int64_t n_experts, int64
 int64_t qmm_matmul_id_workspace_bytes(int64_t n_experts, int64_t n_ids, int64_t n_tokens);
 
 /*
+ * qmm_matmul_id_workspace_bytes_x16 - the workspace with which qmm_matmul_id
+ * takes its fastest route for these sizes: for the matrix-core route, the
+ * routing table plus an fp16 copy of X (n_tokens * x_slots * k * 2 bytes),
+ * from which a kernel that runs two tiles of 128 pairs per workgroup copies
+ * activations straight into LDS when the call has enough tiles to fill the
+ * GPU; otherwise the same as qmm_matmul_id_workspace_bytes. A call given at
+ * least qmm_matmul_id_workspace_bytes but fewer than these bytes takes the
+ * one-tile kernel, which reads X in fp32; both round X to fp16 the same way
+ * and add the same products in the same order, so the result is the same
+ * bits. QMM_ERR_SHAPE for negative or too large sizes, k <= 0, or x_slots
+ * other than 1 or n_ids.
+ */
+int64_t qmm_matmul_id_workspace_bytes_x16(int64_t n_experts, int64_t n_ids, int64_t n_tokens, int64_t k,
+                                          int64_t x_slots);
+
+/*
  * qmm_row_bytes - the dense row stride (k / 32) * block bytes, i.e. nb[1]
  * without padding ([Graph] ggml_tensor stride comment). Negative status code
  * for an unknown type or a k that is not a positive multiple of 32.

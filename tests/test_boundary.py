@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
                             "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc",
-                            "qmm_matmul_id_workspace_bytes", "qmm_row_bytes", "qmm_supports", "qmm_status_string"])
+                            "qmm_matmul_id_workspace_bytes", "qmm_matmul_id_workspace_bytes_x16", "qmm_row_bytes",
+                            "qmm_supports", "qmm_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -217,6 +218,22 @@ def test_matmul_id_workspace_sizes(L):
     assert W(2, 1, 9) == 48 + 16 * (1 + 2)
     assert W(-1, 2, 512) == qmm.QMM_ERR_SHAPE
     assert W(8, 1 << 16, 1 << 16) == qmm.QMM_ERR_SHAPE
+
+
+def test_matmul_id_workspace_sizes_x16(L):
+    W, X16 = L.qmm_matmul_id_workspace_bytes, L.qmm_matmul_id_workspace_bytes_x16
+    # the matrix-core route adds an fp16 copy of X: n_tokens * x_slots * k * 2 bytes
+    assert X16(8, 2, 512, 4096, 1) == W(8, 2, 512) + 512 * 4096 * 2
+    assert X16(8, 2, 512, 4096, 2) == W(8, 2, 512) + 512 * 2 * 4096 * 2
+    assert X16(8, 2, 16, 256, 2) == W(8, 2, 16) + 16 * 2 * 256 * 2
+    # other routes need no copy
+    for args in ((8, 2, 1), (8, 2, 8), (8, 2, 15), (5000, 2, 512), (8, 0, 512)):
+        assert X16(*args, 4096, 1) == W(*args), args
+    # bad sizes
+    assert X16(8, 2, 512, 0, 1) == qmm.QMM_ERR_SHAPE
+    assert X16(8, 2, 512, 4096, 3) == qmm.QMM_ERR_SHAPE
+    assert X16(-1, 2, 512, 4096, 1) == qmm.QMM_ERR_SHAPE
+    assert X16(8, 2, 1 << 20, 1 << 16, 2) == qmm.QMM_ERR_SHAPE
 
 
 def _mid_na(L, W=P, t=Q4, ne=8, rows=16, k=64, nb1=36, nb2=576, X=P2, xs=2, ids=ctypes.c_void_p(0x40000), n_ids=2,

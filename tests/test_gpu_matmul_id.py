@@ -207,6 +207,36 @@ def test_matmul_id_grouped_repeatable_and_agrees_with_decode(qtype):
         _check(Y1[t:t + 1], y_ref, s, "grouped route")
 
 
+@pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
+@pytest.mark.parametrize("layout", ["aligned", "padded"])
+@pytest.mark.parametrize("shared_x", [False, True])
+def test_matmul_id_two_group_tiles(qtype, layout, shared_x):
+    """Enough 128-row tiles x tile pairs to fill the 256 CUs (4096 rows, 512
+    tokens, 2 of 8 experts): the two-group routed kernel, two tiles of the
+    routing table per workgroup. Skewed routing gives experts of more than
+    one tile and an odd tile count (a workgroup with one empty group), one
+    id names no expert; every element against the oracle, NaN rows exact,
+    and bitwise repeatable."""
+    rng = np.random.Generator(np.random.PCG64([507, qtype, len(layout), int(shared_x)]))
+    n_experts, n_ids, rows, k, n_tokens = 8, 2, 4096, 256, 512
+    dense = synth.dense_row_bytes(qtype, k)
+    if layout == "aligned":
+        nb1, nb2, offset = dense, rows * dense, 0
+    else:  # 2-byte-aligned rows: the unaligned staging
+        nb1, nb2, offset = dense + 2, rows * (dense + 2) + 2, 2
+    W = _stack(qtype, n_experts, rows, k, nb1, nb2, rng)
+    slots = 1 if shared_x else n_ids
+    X = synth.make_activations(n_tokens * slots, k, rng, np.float32).reshape(n_tokens, slots, k)
+    ids = _skewed_ids(rng, n_tokens, n_ids, n_experts)
+    ids[3, 1] = n_experts
+    say(f"matmul_id two-group type={qtype} layout={layout} shared_x={shared_x}")
+    Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
+    y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
+    _check(Y, y_ref, s, "two-group routed")
+    Y2 = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32)), "not repeatable"
+
+
 @pytest.mark.parametrize("qtype", [Q4, Q8])
 def test_matmul_id_mixtral_prefill_sampled(qtype):
     """512 tokens through 8 experts of 14336 x 4096, 2 selected per token
