@@ -431,7 +431,8 @@ def time_matmul_id(torch, qmm, synth, with_oracle=False):
     2 selected per token (seeded random routing), activations shared by the
     slots. Decode (1 token, per-pair decode kernel), batched decode (8
     tokens, routing kernel + decode tiles of 2 pairs) and the probe's
-    512-token batch (routing kernel + matrix-core tiles), each as back-to-back
+    512-token batch (routing kernel, fp16 copy of the activations, two-group
+    matrix-core kernel on 160-pair tiles), each as back-to-back
     launches in a graph over >= 1.1 GiB of expert-stack copies, a different
     routing per launch, so the weights come from HBM."""
     import numpy as np
@@ -501,7 +502,7 @@ def time_matmul_id(torch, qmm, synth, with_oracle=False):
     tfl = flops / (us_p * 1e-6) / 1e12
     res["prefill"] = {"tokens": T, "us_per_launch": round(us_p, 3), "flops_per_launch": flops,
                       "TFLOP_per_s": round(tfl, 2), "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
-                      "kernel": "route_kernel + gemm_kernel (routed)", "bound": "mfma"}
+                      "kernel": "route_kernel + x16_copy_kernel + gemm_pp_routed_kernel", "bound": "mfma"}
     if with_oracle:
         # the oracle as it stands, once, on the host: the decode call
         import oracle.qmm_oracle as O

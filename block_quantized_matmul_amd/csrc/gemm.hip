@@ -876,22 +876,34 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
 
 // Expert-routed MUL_MAT_ID with many pairs, on the two-group structure: a
 // workgroup takes two tiles of the routing table (tiles 2 p and 2 p + 1, up
-// to 128 pairs of one expert each) for one 128-row tile, one tile per
-// group. Each group has its own weight and activation stages in LDS (its
-// expert's rows, its pairs' activation rows) and does all of its own
+// to kPPRTile pairs of one expert each) for one 128-row tile, one tile per
+// group. The tile is 160 pairs wide, not 128, because under random top-k
+// routing an expert's pair count scatters around its mean: at 512 tokens, 2
+// of 8 experts, the counts are about 128 +- 10, and 128-pair tiles would give
+// half the experts a second, nearly empty tile that costs a full weight
+// decode. Each group has its own weight stage and activation stages in LDS
+// (its expert's rows, its pairs' activation rows) and does all of its own
 // staging in its memory phase: one block of one row per thread, decoded
-// from registers loaded two stages ahead, and its 128 activation rows
+// from registers loaded three memory phases ahead, and its activation rows
 // copied two stages ahead from an fp16 copy of X (made by the caller's
 // conversion kernel, the same rounding the one-group kernel applies)
 // straight into LDS, gathered through the pair list. The phases alternate
 // as in the dense kernel, so one group's MFMAs run beside the other's
-// staging. Each output element gets the same MFMAs in the same k order as
-// in the one-group routed kernel, so the two agree bit for bit. A group
-// whose tile is empty (past the routing table's last tile) runs on its
-// tile's valid placeholder entries and stores nothing; a workgroup whose
-// two tiles are empty returns at once.
-constexpr int kPPRXOps = (kPPBN / 2) * kBK * 2 / (kGemmThreads * 16);  // copies per lane per stage (4)
-constexpr size_t kPPRoutedLds = (2 * 2 * kPPWHalves + 3 * 2 * (kPPBN / 2) * kBK) * sizeof(_Float16);  // 160 KiB
+// staging. A group's weight stage is single-buffered: group 0 (compute
+// first) stores stage s + 1 in the memory phase after computing stage s,
+// group 1 (memory first) stores stage s in the memory phase before
+// computing it; either way the phase barrier separates the store from the
+// group's own reads. Each output element gets the same MFMAs in the same k
+// order as in the one-group routed kernel, so the two agree bit for bit. A
+// group whose tile is empty (past the routing table's last tile) runs on its
+// tile's valid placeholder entries and stores nothing; a workgroup whose two
+// tiles are empty returns at once.
+constexpr int kPPRTile = kTileTokensTwoGroup;                     // pairs per tile (10 column blocks)
+constexpr int kPPRJ = kPPRTile / 32;                              // column blocks per wavefront (5)
+constexpr int kPPRXOps = kPPRTile * kBK * 2 / (kGemmThreads * 16);  // copies per lane per stage (5)
+constexpr size_t kPPRoutedLds = (2 * kPPWHalves + 3 * 2 * kPPRTile * kBK) * sizeof(_Float16);  // 152 KiB
+static_assert(kPPRTile % 32 == 0 && kPPRXOps * kGemmThreads * 16 == kPPRTile * kBK * 2, "whole copies");
+static_assert(kPPRoutedLds <= 160 * 1024, "one workgroup per CU");
 
 template <int QT, bool ALIGN4>
 __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uint8_t *__restrict__ W, int n_rows,
@@ -901,16 +913,16 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
                                                                        int row_tiles, GemmRoute route,
                                                                        int n_tiles_all) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
-  constexpr int kXH = (kPPBN / 2) * kBK;  // one group's activation stage
+  constexpr int kXH = kPPRTile * kBK;  // one group's activation stage
   const int g = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kGemmThreads);
   const int tid = static_cast<int>(threadIdx.x) - g * kGemmThreads;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  // LDS: [stage][group] weight tiles (2 stages), then [stage][group]
-  // activation tiles (3 stages)
-  auto wtile = [&](int buf) { return lds_dynamic + (2 * buf + g) * kPPWHalves; };
-  auto xtile = [&](int buf) { return lds_dynamic + 4 * kPPWHalves + (2 * buf + g) * kXH; };
+  // LDS: one weight tile per group, then [stage][group] activation tiles (3
+  // stages)
+  _Float16 *const wt = lds_dynamic + g * kPPWHalves;
+  auto xtile = [&](int buf) { return lds_dynamic + 2 * kPPWHalves + (2 * buf + g) * kXH; };
 
   // tile order: as the dense kernels, tile pairs in place of token tiles
   const int n_wg = static_cast<int>(gridDim.x);
@@ -940,10 +952,10 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
   // weights of this group's expert: row tid / 2, block tid % 2 of the pair
   const int srow = tid >> 1, sh = tid & 1;
   const uint8_t *rp = W + static_cast<int64_t>(e) * route.nb2 + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
-  // activations: copy i of wavefront w fills LDS rows 8 (4 w + i) .. + 7 of
-  // the group's tile (token slots); lane p writes position p % 8 of row p / 8,
-  // which holds chunk (p % 8) ^ (row % 8) (the lds_at permutation); slots
-  // past the tile's count repeat its last pair
+  // activations: copy i of wavefront w fills LDS rows 8 (kPPRXOps w + i) ..
+  // + 7 of the group's tile (token slots); lane p writes position p % 8 of
+  // row p / 8, which holds chunk (p % 8) ^ (row % 8) (the lds_at
+  // permutation); slots past the tile's count repeat its last pair
   const _Float16 *xsrc[kPPRXOps];
 #pragma unroll
   for (int i = 0; i < kPPRXOps; ++i) {
@@ -954,13 +966,13 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
     const int64_t xr = static_cast<int64_t>(t) * route.x_slots + (route.x_slots > 1 ? p - t * route.n_ids : 0);
     xsrc[i] = Xh + xr * k + 8 * c;
   }
-  const uint32_t xdst0 = lds_byte_addr(lds_dynamic + 4 * kPPWHalves + g * kXH) + 8 * kPPRXOps * wave * (kBK * 2);
+  const uint32_t xdst0 = lds_byte_addr(xtile(0)) + 8 * kPPRXOps * wave * (kBK * 2);
 
-  float4_t acc[4][4];
+  float4_t acc[4][kPPRJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kPPRJ; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   const int n_st = nblk / 2;
   const int last = n_st - 1;
@@ -970,78 +982,94 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
     else
       r = load_half_u16<QT>(rp, 2 * st + sh, nblk);
   };
-  auto store_w = [&](int buf, const HalfRaw<QT> &r) {
-    store_half<QT>(wtile(buf), srow, 4 * sh, r, ALIGN4 && sh == 0);
-  };
+  auto store_w = [&](const HalfRaw<QT> &r) { store_half<QT>(wt, srow, 4 * sh, r, ALIGN4 && sh == 0); };
   // the copy of stage st into activation buffer b % 3
   auto copy_x = [&](int st, int b) {
     const uint32_t dst = xdst0 + static_cast<uint32_t>((b % 3) * 2 * kXH * 2);
 #pragma unroll
     for (int i = 0; i < kPPRXOps; ++i) dma16(xsrc[i] + kBK * st, dst + i * 1024);
   };
+  // wavefront (wm, wn): rows 64 wm .. + 63 of the tile, token column blocks
+  // wn, wn + 2, .., so a partly filled tile splits its columns evenly
   int aofs[2], bofs[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     aofs[h] = lds_at(64 * wm + (lane & 15), (lane >> 4) + 4 * h);
-    bofs[h] = lds_at(64 * wn + (lane & 15), (lane >> 4) + 4 * h);
+    bofs[h] = lds_at(16 * wn + (lane & 15), (lane >> 4) + 4 * h);
   }
+  // Column blocks of this wavefront that hold pairs (wave-uniform): the
+  // MFMAs of the last two run only when their block is in use, so a tile
+  // of 128 pairs costs what it did on 128-pair tiles. Skipped blocks hold
+  // no pair, and nothing of theirs is stored.
+  const int nj = min(kPPRJ, max(0, (cnt - 16 * wn + 31) / 32));
+  static_assert(kPPRJ == 5, "three unconditional column blocks, two conditional");
   auto compute = [&](int s) {
-    const _Float16 *ws = wtile(s & 1), *xs = xtile(s % 3);
-    half8_t a[2][4], b[2][4];
+    const _Float16 *xs = xtile(s % 3);
+    half8_t a[2][4], b[2][kPPRJ];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
+      for (int i = 0; i < 4; ++i) a[h][i] = *reinterpret_cast<const half8_t *>(wt + aofs[h] + 16 * i * kBK);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
+      for (int j = 0; j < kPPRJ; ++j) b[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 32 * j * kBK);
     }
+    auto block = [&](int j) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+    };
+    block(0);
+    block(1);
+    block(2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 8 + 2 * kPPRJ; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
 #pragma unroll
-    for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
-#pragma unroll
-    for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+    for (int i = 0; i < 24; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+    if (nj > 3) block(3);
+    if (nj > 4) block(4);
   };
   auto phase_end = [] {
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // memory(s): the weights of stage s + 1 into buffer (s + 1) % 2 from
-  // registers loaded three memory phases earlier (three register sets: the
-  // weights come from HBM, each expert's rows being read by one or two
-  // workgroups), the copy of stage s + 2, then a wait that leaves only that
-  // copy and the weight loads issued after stage s + 1's copy in flight (so
-  // stage s + 1's copy, issued one memory phase earlier, has landed before
-  // the barrier; the weight loads are counted as two operations, at most
-  // their number, so the wait is at worst stricter), then the weight loads
-  // of stage s + 4. Past the last stage copies and loads re-read it into the
-  // free buffer and the registers, whose stores go to the idle buffer; none
-  // of it is read.
+  // memory(s, r): the weights in r into the group's weight tile (stage s + 1
+  // for group 0, stage s for group 1), the copy of stage s + 2, then a wait
+  // that leaves only that copy and the weight loads issued after stage
+  // s + 1's copy in flight (so stage s + 1's copy, issued one memory phase
+  // earlier, has landed before the barrier; the weight loads are counted as
+  // two operations, at most their number, so the wait is at worst stricter),
+  // then the weight loads of the stage stored three memory phases later
+  // (s + 4 for group 0, s + 3 for group 1). The weights come from HBM, each
+  // expert's rows being read by one or two workgroups, hence three register
+  // sets. Past the last stage copies and loads re-read it into the free
+  // buffer and the registers; nothing reads them.
+  const int ahead = g == 0 ? 4 : 3;
   HalfRaw<QT> r0, r1, r2;
   auto memory = [&](int s, HalfRaw<QT> &r) {
-    store_w((s + 1) & 1, r);
+    store_w(r);
     copy_x(min(s + 2, last), s + 2);
     wait_vmcnt<kPPRXOps + 2>();
-    load_w(r, min(s + 4, last));
+    load_w(r, min(s + ahead, last));
   };
 
-  // prologue: copies of stages 0 and 1, weights of stages 0 to 3, stage 0
-  // stored (the wait for its weight registers covers its copy, issued before
-  // them)
+  // prologue: copies of stages 0 and 1, weights of stages 0 to 2; group 0
+  // stores stage 0 (the wait for its weight registers covers its copy,
+  // issued before them), waits for stage 0's copy and loads stage 3 into the
+  // freed registers
   copy_x(0, 0);
   load_w(r0, 0);
   copy_x(min(1, last), 1);
   load_w(r1, min(1, last));
   load_w(r2, min(2, last));
-  store_w(0, r0);
-  wait_vmcnt<kPPRXOps + 4>();  // stage 0's copy has landed (stage 1's copy and two weight sets may not)
-  load_w(r0, min(3, last));
-  phase_end();  // stage 0 is in LDS
+  if (g == 0) {
+    store_w(r0);
+    wait_vmcnt<kPPRXOps + 4>();  // stage 0's copy has landed (stage 1's copy and two weight sets may not)
+    load_w(r0, min(3, last));
+  }
+  phase_end();  // group 0's stage 0 is in LDS
   // Whole triples of stages (straight-line bodies, so the wait for one
   // register set leaves the others' loads in flight), then up to two.
   int s = 0;
@@ -1074,27 +1102,27 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
     }
   } else {
     for (; s + 2 < n_st; s += 3) {
-      memory(s, r1);
+      memory(s, r0);
       phase_end();
       compute(s);
       phase_end();
-      memory(s + 1, r2);
+      memory(s + 1, r1);
       phase_end();
       compute(s + 1);
       phase_end();
-      memory(s + 2, r0);
+      memory(s + 2, r2);
       phase_end();
       compute(s + 2);
       phase_end();
     }
     if (s < n_st) {
-      memory(s, r1);
+      memory(s, r0);
       phase_end();
       compute(s);
       phase_end();
     }
     if (s + 1 < n_st) {
-      memory(s + 1, r2);
+      memory(s + 1, r1);
       phase_end();
       compute(s + 1);
       phase_end();
@@ -1103,10 +1131,10 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
   wait_vmcnt<0>();  // no copy outlives the workgroup
 
   // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
-  // token slot 64 wn + 16 j + l % 16 of this group's tile
+  // token slot 16 (2 j + wn) + l % 16 of this group's tile
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int slot = 64 * wn + 16 * j + (lane & 15);
+  for (int j = 0; j < kPPRJ; ++j) {
+    const int slot = 16 * (2 * j + wn) + (lane & 15);
     if (slot >= cnt) continue;
     float *yrow = Y + static_cast<int64_t>(route.list[first + slot]) * n_rows;
 #pragma unroll
@@ -1155,12 +1183,10 @@ hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t 
   const GemmRoute route{list, tiles, nb2, static_cast<int>(n_ids), static_cast<int>(x_slots)};
   const int rt = static_cast<int>(row_tiles), nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows),
             kk = static_cast<int>(k);
-  // With the fp16 copy of X (Xh), two tiles per workgroup on the two-group
-  // kernel when the tile pairs give at least one workgroup per CU and the
-  // block count is whole stages.
+  // With the fp16 copy of X (Xh), the caller has routed into the two-group
+  // kernel's tiles (routed_two_group held): two tiles per workgroup.
   const int64_t pairs_of_tiles = (max_tiles + 1) / 2;
-  const int64_t cus = device_cus();
-  if (Xh != nullptr && routed_two_group(qtype, k, n_rows, max_tiles, cus)) {
+  if (Xh != nullptr) {
     const dim3 pgrid(static_cast<unsigned>(row_tiles * pairs_of_tiles));
     const int nt_all = static_cast<int>(max_tiles);
     return by_qtype(qtype, [&](auto qt) {

@@ -94,9 +94,12 @@ hipError_t launch_gemv_id_tiles(const void *W, int qtype, int64_t n_experts, int
                                 int64_t nb2, const float *X, int64_t x_slots, int64_t n_ids, int64_t n_tokens,
                                 const int32_t *list, const int32_t *tiles, int64_t max_tiles, int nt, float *Y,
                                 hipStream_t stream);
-// The routed matrix-core product; with Xh (an fp16 copy of X) and enough
-// tile pairs to fill the GPU (routed_two_group) it runs two tiles per
-// workgroup on the two-group kernel, else the one-group kernel on fp32 X.
+// The routed matrix-core product. Without Xh, the one-group kernel on fp32 X
+// over tiles of at most kTileTokens pairs. With Xh (an fp16 copy of X), the
+// two-group kernel, two tiles per workgroup, over tiles of at most
+// kTileTokensTwoGroup pairs; the caller routes with that tile size when
+// routed_two_group (given the larger tile's max_tiles) holds.
+constexpr int kTileTokensTwoGroup = 160;
 bool routed_two_group(int qtype, int64_t k, int64_t n_rows, int64_t max_tiles, int64_t cus);
 hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, int64_t nb2,
                               const float *X, const _Float16 *Xh, int64_t x_slots, int64_t n_ids,

@@ -203,6 +203,20 @@ hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts,
                                     int64_t n_ids, int64_t n_tokens, float *Y, void *workspace,
                                     int64_t workspace_bytes, int tile, hipStream_t stream) {
   const int64_t n_pairs = n_tokens * n_ids;
+  // The matrix-core route runs the two-group kernel, on wider tiles, when
+  // the workspace also holds the fp16 copy of X (after the routing table,
+  // whose size for kTileTokens bounds the wider tiles' table too) and the
+  // tile pairs fill the GPU.
+  _Float16 *Xh = nullptr;
+  if (tile == kTileTokens) {
+    const int64_t route_bytes = route_workspace_bytes(n_experts, n_pairs, tile);
+    const int64_t x16 = route_x16_bytes(n_tokens, x_slots, k);
+    if (workspace_bytes >= route_bytes + x16 &&
+        routed_two_group(qtype, k, n_rows, route_max_tiles(n_experts, n_pairs, kTileTokensTwoGroup), device_cus())) {
+      Xh = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + route_bytes);
+      tile = kTileTokensTwoGroup;
+    }
+  }
   const int64_t max_tiles = route_max_tiles(n_experts, n_pairs, tile);
   int32_t *list = static_cast<int32_t *>(workspace);
   int32_t *tiles = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + (n_pairs * 4 + 15) / 16 * 16);
@@ -214,22 +228,15 @@ hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts,
                                 static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
                                 static_cast<int>(n_rows));
   if (e != hipSuccess) return e;
-  if (tile == kTileTokens) {
-    // the fp16 copy of X, after the routing table, when the workspace holds
-    // it and the two-group kernel will take the call
-    const int64_t route_bytes = route_workspace_bytes(n_experts, n_pairs, tile);
-    const int64_t x16 = route_x16_bytes(n_tokens, x_slots, k);
-    _Float16 *Xh = nullptr;
-    if (workspace_bytes >= route_bytes + x16 && routed_two_group(qtype, k, n_rows, max_tiles, device_cus())) {
-      Xh = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + route_bytes);
-      const int64_t n4 = n_tokens * x_slots * k / 4;
-      const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
-      e = launch(x16_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Xh, n4);
-      if (e != hipSuccess) return e;
-    }
+  if (Xh != nullptr) {
+    const int64_t n4 = n_tokens * x_slots * k / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+    e = launch(x16_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Xh, n4);
+    if (e != hipSuccess) return e;
+  }
+  if (tile == kTileTokens || tile == kTileTokensTwoGroup)
     return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, Xh, x_slots, n_ids, list, tiles, max_tiles, Y,
                               stream);
-  }
   return launch_gemv_id_tiles(W, qtype, n_experts, n_rows, k, nb1, nb2, X, x_slots, n_ids, n_tokens, list, tiles,
                               max_tiles, tile, Y, stream);
 }

@@ -212,11 +212,10 @@ def test_matmul_id_grouped_repeatable_and_agrees_with_decode(qtype):
 @pytest.mark.parametrize("shared_x", [False, True])
 def test_matmul_id_two_group_tiles(qtype, layout, shared_x):
     """Enough 128-row tiles x tile pairs to fill the 256 CUs (4096 rows, 512
-    tokens, 2 of 8 experts): the two-group routed kernel, two tiles of the
-    routing table per workgroup. Skewed routing gives experts of more than
-    one tile and an odd tile count (a workgroup with one empty group), one
-    id names no expert; every element against the oracle, NaN rows exact,
-    and bitwise repeatable."""
+    tokens, 2 of 8 experts): the two-group routed kernel, two 160-pair tiles
+    of the routing table per workgroup. Skewed routing gives an expert of
+    several tiles, the last one partial, one id names no expert; every
+    element against the oracle, NaN rows exact, and bitwise repeatable."""
     rng = np.random.Generator(np.random.PCG64([507, qtype, len(layout), int(shared_x)]))
     n_experts, n_ids, rows, k, n_tokens = 8, 2, 4096, 256, 512
     dense = synth.dense_row_bytes(qtype, k)
@@ -235,6 +234,42 @@ def test_matmul_id_two_group_tiles(qtype, layout, shared_x):
     _check(Y, y_ref, s, "two-group routed")
     Y2 = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
     assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32)), "not repeatable"
+
+
+@pytest.mark.parametrize("qtype,layout", [(Q4, "aligned"), (Q4, "padded"), (Q51, "aligned"), (Q8, "aligned")])
+def test_matmul_id_two_group_tile_edges(qtype, layout):
+    """Pair counts at the two-group kernel's tile edges (160 pairs per tile):
+    161 (a full tile and a one-pair tile), 160, 129, 1, 300 (160 + 140), 150,
+    123 and 0 pairs for experts 0..7, 9 tiles in all, so one workgroup's
+    second group is empty. Every element against the oracle, and the same
+    bits as the one-group kernel (128-pair tiles, chosen by a workspace
+    without room for the fp16 activations)."""
+    import torch
+    import block_quantized_matmul_amd as qmm
+    from gpu_util import place_weights
+    rng = np.random.Generator(np.random.PCG64([512, qtype, len(layout)]))
+    n_experts, n_ids, rows, k, n_tokens = 8, 2, 4096, 256, 512
+    counts = [161, 160, 129, 1, 300, 150, 123, 0]
+    assert sum(counts) == n_tokens * n_ids
+    ids = rng.permutation(np.repeat(np.arange(n_experts, dtype=np.int32), counts)).reshape(n_tokens, n_ids)
+    dense = synth.dense_row_bytes(qtype, k)
+    if layout == "aligned":
+        nb1, nb2, offset = dense, rows * dense, 0
+    else:
+        nb1, nb2, offset = dense + 2, rows * (dense + 2) + 2, 2
+    W = _stack(qtype, n_experts, rows, k, nb1, nb2, rng)
+    X = synth.make_activations(n_tokens, k, rng, np.float32).reshape(n_tokens, 1, k)
+    say(f"matmul_id two-group tile edges type={qtype} layout={layout}")
+    Y = _run(W, qtype, n_experts, rows, k, nb1, nb2, X, ids, offset)
+    y_ref, s = O.matmul_id(W, qtype, n_experts, rows, k, nb1, nb2, X, ids)
+    _check(Y, y_ref, s, "two-group tile edges")
+    _keep, Wd = place_weights(W, offset)
+    ws = torch.empty(qmm.qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens), dtype=torch.uint8,
+                     device="cuda")
+    Y1 = qmm.qmm_matmul_id(Wd, qtype, k, dev(X), dev(ids), n_experts=n_experts, n_rows=rows, row_stride_bytes=nb1,
+                           expert_stride_bytes=nb2, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint32), Y1.cpu().numpy().view(np.uint32)), "two-group != one-group kernel"
 
 
 @pytest.mark.parametrize("qtype", [Q4, Q8])
