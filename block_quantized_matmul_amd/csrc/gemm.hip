@@ -895,9 +895,8 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
 // computing it; either way the phase barrier separates the store from the
 // group's own reads. Each output element gets the same MFMAs in the same k
 // order as in the one-group routed kernel, so the two agree bit for bit. A
-// group whose tile is empty (past the routing table's last tile) runs on its
-// tile's valid placeholder entries and stores nothing; a workgroup whose two
-// tiles are empty returns at once.
+// group whose tile is empty (the second of an odd tile count) runs on
+// placeholder entries and stores nothing.
 constexpr int kPPRTile = kTileTokensTwoGroup;                     // pairs per tile (10 column blocks)
 constexpr int kPPRJ = kPPRTile / 32;                              // column blocks per wavefront (5)
 constexpr int kPPRXOps = kPPRTile * kBK * 2 / (kGemmThreads * 16);  // copies per lane per stage (5)
@@ -924,29 +923,36 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
   _Float16 *const wt = lds_dynamic + g * kPPWHalves;
   auto xtile = [&](int buf) { return lds_dynamic + 2 * kPPWHalves + (2 * buf + g) * kXH; };
 
-  // tile order: as the dense kernels, tile pairs in place of token tiles
+  // Work items are (128-row tile, tile pair) over the tiles the routing
+  // kernel made (their number is in every table entry), so no workgroup
+  // waits for a dispatch slot only to find its tiles empty. The grid is at
+  // most one workgroup per CU; workgroup w takes items v = w, w + grid, ..,
+  // in the dense kernels' order (XCD-contiguous runs of v, then groups of
+  // kGroupRows row tiles with all tile pairs).
   const int n_wg = static_cast<int>(gridDim.x);
   const int bid = static_cast<int>(blockIdx.x);
   const int per_xcd = n_wg / kXcds;
-  const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
-  const int pair_tiles = n_wg / row_tiles;
+  const int lin0 = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
+  const int n_tiles = min(n_tiles_all, __builtin_amdgcn_readfirstlane(route.tiles[3]));
+  const int pair_tiles = (n_tiles + 1) / 2;
+  const int n_items = row_tiles * pair_tiles;
   const int in_group = kGroupRows * pair_tiles;
+  for (int lin = lin0; lin < n_items; lin += n_wg) {
   const int first_row = (lin / in_group) * kGroupRows;
   const int group_rows = min(row_tiles - first_row, kGroupRows);
   const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
   const int tp = (lin % in_group) / group_rows;
 
-  // the two tiles; entries past the table read as empty
+  // the two tiles; the second of an odd count reads as empty
   int e2[2], f2[2], c2[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = 2 * tp + h;
-    const bool in = t < n_tiles_all;
+    const bool in = t < n_tiles;
     e2[h] = in ? __builtin_amdgcn_readfirstlane(route.tiles[4 * t]) : 0;
     f2[h] = in ? __builtin_amdgcn_readfirstlane(route.tiles[4 * t + 1]) : 0;
     c2[h] = in ? __builtin_amdgcn_readfirstlane(route.tiles[4 * t + 2]) : 0;
   }
-  if (c2[0] == 0 && c2[1] == 0) return;  // whole workgroup: no pairs
   const int e = g ? e2[1] : e2[0], first = g ? f2[1] : f2[0], cnt = g ? c2[1] : c2[0];
 
   // weights of this group's expert: row tid / 2, block tid % 2 of the pair
@@ -1149,6 +1155,7 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_routed_kernel(const uin
       }
     }
   }
+  }  // work items (the last phase barrier has ordered every LDS read before the next item's stores)
 }
 
 template <int QT, bool XF16, int BM, int KS = 1>
@@ -1187,7 +1194,9 @@ hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t 
   // kernel's tiles (routed_two_group held): two tiles per workgroup.
   const int64_t pairs_of_tiles = (max_tiles + 1) / 2;
   if (Xh != nullptr) {
-    const dim3 pgrid(static_cast<unsigned>(row_tiles * pairs_of_tiles));
+    const int64_t cus = device_cus();
+    const int64_t items = row_tiles * pairs_of_tiles;  // the host's bound; the kernel reads the actual count
+    const dim3 pgrid(static_cast<unsigned>(cus > 0 && cus < items ? cus : items));
     const int nt_all = static_cast<int>(max_tiles);
     return by_qtype(qtype, [&](auto qt) {
       constexpr int QT = decltype(qt)::value;

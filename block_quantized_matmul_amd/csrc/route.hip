@@ -12,8 +12,9 @@
 // Routing (one 1024-thread workgroup, or one wavefront for up to 64 experts
 // and 512 pairs; ids are device data): count the pairs
 // per expert in LDS, scan the counts into list offsets and token-tile
-// offsets, write the tile table (expert, first list entry, count <= tile) padded
-// with empty tiles up to the host's bound, then place every pair in its
+// offsets, write the tile table (expert, first list entry, count <= tile,
+// number of tiles in the table) padded with empty tiles up to the host's
+// bound, then place every pair in its
 // expert's bucket. Pairs whose id names no expert go after the valid ones
 // and get rows of NaN. Within a bucket the order depends on LDS atomics; a
 // pair's result does not, because every output element is the same
@@ -80,13 +81,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
       t[0] = e;
       t[1] = off + j * tile;
       t[2] = min(tile, c - j * tile);
-      t[3] = 0;
+      t[3] = n_tiles;
     }
     off += c;
   }
   for (int i = n_tiles + tid; i < max_tiles; i += kRouteThreads) {
     int32_t *t = tiles + 4 * static_cast<int64_t>(i);
-    t[0] = 0, t[1] = 0, t[2] = 0, t[3] = 0;  // empty: its workgroups exit at once
+    t[0] = 0, t[1] = 0, t[2] = 0, t[3] = n_tiles;  // empty: its workgroups exit at once
   }
   if (tid == 0) bad_cur = n_valid;
   __syncthreads();
@@ -148,11 +149,11 @@ __global__ __launch_bounds__(64) void route_small_kernel(const int32_t *__restri
     q[0] = lane;
     q[1] = off + j * tile;
     q[2] = min(tile, c - j * tile);
-    q[3] = 0;
+    q[3] = n_tiles;
   }
   for (int i = n_tiles + lane; i < max_tiles; i += 64) {
     int32_t *q = tiles + 4 * static_cast<int64_t>(i);
-    q[0] = 0, q[1] = 0, q[2] = 0, q[3] = 0;  // empty: its workgroups exit at once
+    q[0] = 0, q[1] = 0, q[2] = 0, q[3] = n_tiles;  // empty: its workgroups exit at once
   }
   if (lane == 0) bad_cur = n_valid;
   __syncthreads();
