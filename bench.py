@@ -502,7 +502,7 @@ def time_matmul_id(torch, qmm, synth, with_oracle=False):
     tfl = flops / (us_p * 1e-6) / 1e12
     res["prefill"] = {"tokens": T, "us_per_launch": round(us_p, 3), "flops_per_launch": flops,
                       "TFLOP_per_s": round(tfl, 2), "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
-                      "kernel": "route_kernel + x16_copy_kernel + gemm_pp_routed_kernel", "bound": "mfma"}
+                      "kernel": "route_small_kernel (+ fp16 copy of X) + gemm_pp_routed_kernel", "bound": "mfma"}
     if with_oracle:
         # the oracle as it stands, once, on the host: the decode call
         import oracle.qmm_oracle as O

@@ -10,7 +10,7 @@
 // [n_ids, 512]); the 512-token batch is what makes grouping pay.
 //
 // Routing (one 1024-thread workgroup, or one wavefront for up to 64 experts
-// and 512 pairs; ids are device data): count the pairs
+// and 1024 pairs; ids are device data): count the pairs
 // per expert in LDS, scan the counts into list offsets and token-tile
 // offsets, write the tile table (expert, first list entry, count <= tile,
 // number of tiles in the table) padded with empty tiles up to the host's
@@ -28,6 +28,19 @@ namespace qmm {
 
 namespace {
 
+// fp32 -> fp16 copy of the activations for the two-group routed kernel
+// (round to nearest even, the conversion the one-group kernel applies while
+// staging), four values per step, by the routing launch's workgroups after
+// the first, grid-stride over them: the copy runs beside the routing.
+__device__ __forceinline__ void x16_convert(const float *__restrict__ X, _Float16 *__restrict__ Xh, int64_t n4) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x - 1) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4_t f = reinterpret_cast<const float4_a4 *>(X)[i];
+    const half2_t a = cvt_half2(f.x, f.y), b = cvt_half2(f.z, f.w);
+    reinterpret_cast<u32x2_a4 *>(Xh)[i] = u32x2_a4{as_u32(a), as_u32(b)};
+  }
+}
+
 constexpr int kRouteThreads = 1024;
 constexpr int kPerThread = kRouteMaxExperts / kRouteThreads;
 static_assert(kRouteMaxExperts % kRouteThreads == 0, "experts split evenly over the threads");
@@ -35,7 +48,12 @@ static_assert(kRouteMaxExperts % kRouteThreads == 0, "experts split evenly over 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__restrict__ ids, int n_pairs,
                                                               int n_experts, int max_tiles, int tile,
                                                               int32_t *__restrict__ list, int32_t *__restrict__ tiles,
-                                                              float *__restrict__ Y, int n_rows) {
+                                                              float *__restrict__ Y, int n_rows, const float *X,
+                                                              _Float16 *Xh, int64_t n4) {
+  if (blockIdx.x > 0) {  // the activation copy's workgroups
+    x16_convert(X, Xh, n4);
+    return;
+  }
   __shared__ int cnt[kRouteMaxExperts];
   __shared__ int cur[kRouteMaxExperts];
   __shared__ int scan_c[2][kRouteThreads];
@@ -109,13 +127,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
 // with cross-lane shuffles, so the kernel runs no workgroup-wide scans and
 // only three barriers. Expert e is lane e's.
 constexpr int kSmallExperts = 64;
-constexpr int kSmallPairsPerLane = 8;
+constexpr int kSmallPairsPerLane = 16;
 constexpr int kSmallPairs = 64 * kSmallPairsPerLane;
 
 __global__ __launch_bounds__(64) void route_small_kernel(const int32_t *__restrict__ ids, int n_pairs, int n_experts,
                                                          int max_tiles, int tile, int32_t *__restrict__ list,
                                                          int32_t *__restrict__ tiles, float *__restrict__ Y,
-                                                         int n_rows) {
+                                                         int n_rows, const float *X, _Float16 *Xh, int64_t n4) {
+  if (blockIdx.x > 0) {  // the activation copy's workgroups
+    x16_convert(X, Xh, n4);
+    return;
+  }
   __shared__ int cnt[kSmallExperts];
   __shared__ int cur[kSmallExperts];
   __shared__ int bad_cur;
@@ -173,19 +195,6 @@ __global__ __launch_bounds__(64) void route_small_kernel(const int32_t *__restri
   }
 }
 
-// fp32 -> fp16 copy of the activations for the two-group routed kernel
-// (round to nearest even, the conversion the one-group kernel applies while
-// staging), four values per thread, grid-stride.
-__global__ __launch_bounds__(256) void x16_copy_kernel(const float *__restrict__ X, _Float16 *__restrict__ Xh,
-                                                       int64_t n4) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    const float4_t f = reinterpret_cast<const float4_a4 *>(X)[i];
-    const half2_t a = cvt_half2(f.x, f.y), b = cvt_half2(f.z, f.w);
-    reinterpret_cast<u32x2_a4 *>(Xh)[i] = u32x2_a4{as_u32(a), as_u32(b)};
-  }
-}
-
 }  // namespace
 
 int64_t route_x16_bytes(int64_t n_tokens, int64_t x_slots, int64_t k) { return n_tokens * x_slots * k * 2; }
@@ -222,19 +231,19 @@ hipError_t launch_matmul_id_grouped(const void *W, int qtype, int64_t n_experts,
   int32_t *list = static_cast<int32_t *>(workspace);
   int32_t *tiles = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + (n_pairs * 4 + 15) / 16 * 16);
   const bool small = n_experts <= kSmallExperts && n_pairs <= kSmallPairs;
-  hipError_t e = small ? launch(route_small_kernel, dim3(1), dim3(64), 0, stream, ids, static_cast<int>(n_pairs),
+  // workgroup 0 routes; with Xh, workgroups 1.. make the fp16 copy of X,
+  // about four float4 per thread
+  const int block = small ? 64 : kRouteThreads;
+  const int64_t n4 = Xh != nullptr ? n_tokens * x_slots * k / 4 : 0;
+  const int64_t conv = std::min<int64_t>((n4 + 4 * block - 1) / (4 * block), 4096);
+  const dim3 grid(static_cast<unsigned>(1 + conv));
+  hipError_t e = small ? launch(route_small_kernel, grid, dim3(64), 0, stream, ids, static_cast<int>(n_pairs),
                                 static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
-                                static_cast<int>(n_rows))
-                       : launch(route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, ids, static_cast<int>(n_pairs),
+                                static_cast<int>(n_rows), X, Xh, n4)
+                       : launch(route_kernel, grid, dim3(kRouteThreads), 0, stream, ids, static_cast<int>(n_pairs),
                                 static_cast<int>(n_experts), static_cast<int>(max_tiles), tile, list, tiles, Y,
-                                static_cast<int>(n_rows));
+                                static_cast<int>(n_rows), X, Xh, n4);
   if (e != hipSuccess) return e;
-  if (Xh != nullptr) {
-    const int64_t n4 = n_tokens * x_slots * k / 4;
-    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
-    e = launch(x16_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, X, Xh, n4);
-    if (e != hipSuccess) return e;
-  }
   if (tile == kTileTokens || tile == kTileTokensTwoGroup)
     return launch_gemm_routed(W, qtype, n_rows, k, nb1, nb2, X, Xh, x_slots, n_ids, list, tiles, max_tiles, Y,
                               stream);

@@ -329,13 +329,13 @@ def test_matmul_id_mixtral_batched_decode_sampled(qtype):
             assert ok.all(), f"token {t} expert {e}: {int((~ok).sum())} sampled rows outside tolerance"
 
 
-@pytest.mark.parametrize("n_experts,n_tokens", [(64, 256), (64, 257), (65, 256), (64, 100), (65, 100)])
+@pytest.mark.parametrize("n_experts,n_tokens", [(64, 256), (64, 512), (64, 513), (65, 256), (64, 100), (65, 100)])
 def test_matmul_id_routing_kernel_sizes(n_experts, n_tokens):
-    """Both routing kernels: up to 64 experts and 512 pairs take the
+    """Both routing kernels: up to 64 experts and 1024 pairs take the
     one-wavefront kernel, more of either the workgroup kernel; the grouped
-    GEMM (256 / 257 tokens: 4 pairs per expert) and decode tiles (100 tokens:
-    about 3) on each side of the boundary, with ids that name no expert,
-    against the oracle."""
+    GEMM (256 to 513 tokens: 8 to 16 pairs per expert) and decode tiles (100
+    tokens: about 3) on each side of the boundary, with ids that name no
+    expert, against the oracle."""
     import block_quantized_matmul_amd as qmm
     rng = np.random.Generator(np.random.PCG64([511, n_experts, n_tokens]))
     qtype, n_ids, rows, k = Q4, 2, 40, 256
