@@ -459,11 +459,24 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT, G
   // whole wavefront's share of k in one round for the common shapes), then
   // the stages are consumed in order. Other wavefronts on the CU overlap
   // their computation with this one's loads.
+  // With 8 token slots (the heaviest stages), a wavefront raises its
+  // priority while it issues a round's loads, so loads of wavefronts that
+  // reach their issue point go out ahead of other wavefronts' arithmetic
+  // (32000 x 4096 at 8 tokens: 26.4 -> 23.9 us; no change at 1 to 4 tokens).
+  constexpr bool kIssuePrio = NT >= 8;
   RRegs<QT, NT, XF16, G> st[D];
   for (int q = q_lo; q < q_hi; q += D) {
+    if constexpr (kIssuePrio) {
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < D; ++i)
       if (q + i < q_hi) issue(st[i], q + i);
+    if constexpr (kIssuePrio) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int i = 0; i < D; ++i)
       if (q + i < q_hi) r_consume<QT, NT, XF16, G>(st[i], L, wl, xs, lane, acc);
