@@ -67,10 +67,11 @@ KERNELS = {
     "gemv_stream_kernel": ("gemv_stream.hip", "gemv_common.h", "common.h", "launch.h"),
     "gemm_kernel": ("gemm.hip", "common.h", "launch.h"),
     "gemm_pp_kernel": ("gemm.hip", "common.h", "launch.h"),
+    "gemm_pp_routed_kernel": ("gemm.hip", "common.h", "launch.h"),
 }
 # Template arguments of the plain (MUL_MAT) instantiations; the expert-routed
 # (MUL_MAT_ID) ones carry one more, which the demangled name shows.
-KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3, "gemm_pp_kernel": 2}
+KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3, "gemm_pp_kernel": 2, "gemm_pp_routed_kernel": 2}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -106,7 +107,8 @@ def parse():
                     help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run one plain {COPY_CAL_BYTES >> 20} MiB device copy (for counter calibration)")
-    ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill", "output_projection", "prefill_512"),
+    ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill", "output_projection", "prefill_512",
+                                       "matmul_id"),
                     help="run just this pass (eagerly once, then --steps graph replays) and print no JSON; "
                          "for hardware-counter runs, whose per-dispatch averages must cover one pass only")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -484,7 +486,7 @@ def time_matmul_id(torch, qmm, synth, with_oracle=False):
     res["batched_decode"] = {"tokens": Tb, "mean_distinct_experts": distinct, "us_per_launch": round(us_b, 3),
                              "algorithmic_bytes_per_launch": byts_b, "GB_per_s": round(gbs_b, 2),
                              "frac_of_hbm_peak": round(gbs_b / HBM_PEAK_GBS, 4),
-                             "kernel": "route_kernel + gemv_stream_kernel (tiles)", "bound": "hbm"}
+                             "kernel": "route_small_kernel + gemv_stream_kernel (tiles)", "bound": "hbm"}
     # prefill-sized batch
     T = MOE_PREFILL_TOKENS
     reps_p = copies
@@ -626,7 +628,7 @@ def main():
     layers = args.layers
     cpu_layers = 0 if args.no_cpu_baseline else max(1, min(args.cpu_layers, layers))
 
-    if args.only in ("output_projection", "prefill_512"):
+    if args.only in ("output_projection", "prefill_512", "matmul_id"):
         # one of the single-matrix workloads alone (for counter runs): its
         # timed graphs, after a plain copy of known size when calibrating
         if args.copy_calibration:
@@ -634,7 +636,8 @@ def main():
             torch.empty_like(a).copy_(a)
             torch.cuda.synchronize()
             del a
-        res = (time_output_projection if args.only == "output_projection" else time_prefill_512)(torch, qmm, synth)
+        res = {"output_projection": time_output_projection, "prefill_512": time_prefill_512,
+               "matmul_id": time_matmul_id}[args.only](torch, qmm, synth)
         log(json.dumps(res))
         return
 
