@@ -753,21 +753,25 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // memory(s), group 0: the weights of stage s + 1 into buffer (s + 1) % 2
-  // from registers loaded two stages earlier, the loads of stage s + 3 into
-  // those registers (past the last stage they re-read it; what they bring
-  // is stored into the idle buffer and never read), and the activation
-  // operands of stage s + 1. Group 1: the copy of stage s + 3's activations
-  // and a wait that leaves the copies of stages s + 2 and s + 3 in flight, so
-  // stage s + 1's (issued two memory phases earlier) has landed before the
-  // barrier; then the operands of stage s.
+  // memory(s), group 0: the activation operands of stage s + 1 (complete
+  // since the previous barrier; read first, so their latency passes under
+  // the decode rather than at this phase's barrier), the weights of stage
+  // s + 1 into buffer (s + 1) % 2 from registers loaded two stages earlier,
+  // and the loads of stage s + 3 into those registers (past the last stage
+  // they re-read it; what they bring is stored into the idle buffer and never
+  // read). Group 1: the operands of stage s (complete since the previous
+  // barrier), the copy of stage s + 3's activations and a wait that leaves the
+  // copies of stages s + 2 and s + 3 in flight, so stage s + 1's (issued two
+  // memory phases earlier) has landed before the barrier.
   HalfRaw<QT> r0, r1;
   auto memory = [&](int s, HalfRaw<QT> &r, int buf) {
     if (g == 0) {
+      if (s < last) read_b(s + 1);
       store_w(buf, r);
       load_w(r, min(s + 3, last));
-      if (s < last) read_b(s + 1);
     } else {
+      read_a(s);
+      read_b(s);
       if (s + 3 <= last) {
         copy_x(s + 3);
         wait_vmcnt<2 * kPPXOps>();
@@ -776,8 +780,6 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
       } else {
         wait_vmcnt<0>();
       }
-      read_a(s);
-      read_b(s);
     }
   };
   auto compute = [&](int s) {
