@@ -33,6 +33,13 @@ static __device__ __align__(256) uint8_t scratch[QMM_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+// Bounds that keep every byte or element count the library computes on the
+// host inside int64: a matrix or expert stack spans fewer than 2^62 bytes,
+// an activation or output array holds fewer than 2^60 elements.
+constexpr int64_t kMaxBytes = int64_t{1} << 62;
+constexpr int64_t kMaxElems = int64_t{1} << 60;
+// a * b <= limit, for a, b >= 0, without forming the product
+bool product_within(int64_t a, int64_t b, int64_t limit) { return b == 0 || a <= limit / b; }
 
 // Bytes and weights of one block of the type (0 for an unknown type). The
 // 32-weight types follow [Bind] section 2.3 and the library's readings; Q4_K
@@ -72,6 +79,7 @@ int check_weights(const void *W, int type, int64_t n_rows, int64_t k, int64_t nb
   if (k <= 0 || k % bw != 0 || k > kMaxDim || n_rows < 0 || n_rows > kMaxDim) return QMM_ERR_SHAPE;
   if (nb1 % 2 != 0 || nb1 < (k / bw) * bb) return QMM_ERR_STRIDE;
   if (type == QMM_TYPE_Q4_K && nb1 % 16 != 0) return QMM_ERR_STRIDE;
+  if (!product_within(n_rows, nb1, kMaxBytes)) return QMM_ERR_SHAPE;
   // the decode kernel addresses a Q4_K matrix with 32-bit offsets
   if (type == QMM_TYPE_Q4_K && (n_rows * nb1 >= (int64_t{1} << 32) || nb1 >= (int64_t{1} << 24))) return QMM_ERR_SHAPE;
   if (!aligned(W, type == QMM_TYPE_Q4_K ? 16 : 2)) return QMM_ERR_ALIGN;
@@ -156,6 +164,7 @@ static int check_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k,
   if (st != QMM_OK) return st;
   if (x_type != QMM_X_F32 && x_type != QMM_X_F16) return QMM_ERR_TYPE;
   if (n_tokens < 0 || n_tokens > kMaxDim) return QMM_ERR_SHAPE;
+  if (!product_within(n_tokens, k, kMaxElems) || !product_within(n_tokens, n_rows, kMaxElems)) return QMM_ERR_SHAPE;
   if (path != QMM_PATH_AUTO && path != QMM_PATH_GEMV && path != QMM_PATH_GEMM) return QMM_ERR_PATH;
   if (path == QMM_PATH_GEMV && n_tokens > QMM_GEMV_MAX_TOKENS) return QMM_ERR_PATH;
   if (!aligned(X, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
@@ -227,6 +236,7 @@ int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
   if (out == nullptr) return QMM_ERR_NULL;
   int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
   if (st != QMM_OK) return st;
+  if (!product_within(n_rows, k, kMaxElems)) return QMM_ERR_SHAPE;
   if (!aligned(out, 4)) return QMM_ERR_ALIGN;
   if (n_rows == 0) return QMM_OK;
   if (trace_on())
@@ -240,7 +250,7 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
   if (ids == nullptr || out == nullptr) return QMM_ERR_NULL;
   int st = check_weights(W, ggml_type, n_rows, k, row_stride_bytes);
   if (st != QMM_OK) return st;
-  if (n_ids < 0 || n_ids > kMaxDim) return QMM_ERR_SHAPE;
+  if (n_ids < 0 || n_ids > kMaxDim || !product_within(n_ids, k, kMaxElems)) return QMM_ERR_SHAPE;
   if (!aligned(ids, 4) || !aligned(out, 4)) return QMM_ERR_ALIGN;
   if (n_ids == 0) return QMM_OK;
   if (trace_on())
@@ -308,6 +318,9 @@ static int check_matmul_id(const void *W, int ggml_type, int64_t n_experts, int6
   if (*need < 0) return static_cast<int>(*need);
   if (x_slots != 1 && x_slots != n_ids) return QMM_ERR_SHAPE;
   if (expert_stride_bytes % 2 != 0 || expert_stride_bytes < n_rows * row_stride_bytes) return QMM_ERR_STRIDE;
+  if (!product_within(n_experts, expert_stride_bytes, kMaxBytes) ||
+      !product_within(n_tokens * x_slots, k, kMaxElems) || !product_within(n_tokens * n_ids, n_rows, kMaxElems))
+    return QMM_ERR_SHAPE;
   if (ggml_type == QMM_TYPE_Q4_K && expert_stride_bytes % 16 != 0) return QMM_ERR_STRIDE;
   if (!aligned(X, 4) || !aligned(ids, 4) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
   *plan = id_plan(n_experts, n_ids, n_tokens);

@@ -151,7 +151,9 @@ extern "C" {
  *   Y                device pointer, fp32 [n_tokens][n_rows], 4-byte aligned
  *   stream           hipStream_t or NULL
  * n_rows == 0 or n_tokens == 0 returns QMM_OK and launches nothing. Sizes must
- * satisfy n_rows, n_tokens, k < 2^31. Returns QMM_OK or a negative code.
+ * satisfy n_rows, n_tokens, k < 2^31, n_rows * row_stride_bytes <= 2^62 and
+ * n_tokens * k, n_tokens * n_rows <= 2^60 (QMM_ERR_SHAPE otherwise, so every
+ * byte count stays inside int64). Returns QMM_OK or a negative code.
  */
 int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                const float *X, int64_t n_tokens, float *Y, void *stream);
@@ -209,6 +211,7 @@ int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream);
  * [Arch] reconstruction equation): out[r][i] = fp32(d) * fp32(q - z) for
  * element i of row r. out is fp32 [n_rows][k], 4-byte aligned, caller-owned.
  * The result is bit-exact (NaN scales give NaN). n_rows == 0 is a no-op.
+ * Sizes as in qmm_matmul, with n_rows * k <= 2^60.
  */
 int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                    float *out, void *stream);
@@ -220,7 +223,7 @@ int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
  * vector, [Load] section 第六步).
  *   W, ggml_type, n_rows, k, row_stride_bytes  as in qmm_matmul
  *   ids      device pointer, int32 [n_ids], 4-byte aligned, caller-owned
- *   n_ids    number of rows to gather (>= 0; 0 is a no-op)
+ *   n_ids    number of rows to gather (>= 0, n_ids * k <= 2^60; 0 is a no-op)
  *   out      device pointer, fp32 [n_ids][k], 4-byte aligned, caller-owned
  *   stream   hipStream_t or NULL
  * An index outside [0, n_rows) cannot be checked on the host (ids are device
@@ -249,6 +252,9 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
  *   x_slots              1 or n_ids
  *   ids                  device pointer, int32 [n_tokens][n_ids], 4-byte aligned
  *   n_ids, n_tokens      >= 0, n_ids * n_tokens < 2^31; 0 is a no-op
+ *                        (also n_experts * expert_stride_bytes <= 2^62 and
+ *                        n_tokens * x_slots * k, n_tokens * n_ids * n_rows
+ *                        <= 2^60, else QMM_ERR_SHAPE)
  *   Y                    device pointer, fp32 [n_tokens][n_ids][n_rows], 4-byte aligned
  *   workspace            device scratch of at least
  *                        qmm_matmul_id_workspace_bytes(n_experts, n_ids, n_tokens)
@@ -260,8 +266,10 @@ int qmm_get_rows(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_
  * grouped ones, which first bucket the pairs by expert in the workspace):
  * one token, or about one pair per selected expert: every pair is a
  * single-token product on the decode kernels; more than QMM_GEMV_MAX_TOKENS
- * tokens and at least 4 pairs per expert on average: the matrix-core kernel
- * runs tiles of 128 pairs of one expert; otherwise the streaming decode
+ * tokens and at least 4 pairs per expert on average: a matrix-core kernel
+ * runs tiles of pairs of one expert (128 per tile, or 160 on the two-group
+ * kernel when the workspace also holds the fp16 copy of X, see
+ * qmm_matmul_id_workspace_bytes_x16); otherwise the streaming decode
  * kernel runs tiles of 2, 4 or 8 pairs of one expert (the per-pair route
  * when the weights do not have the streaming layout: 16-byte aligned W,
  * row and expert strides, k a multiple of 256). Results do not depend on the route's tile order. An id outside
