@@ -70,7 +70,8 @@ KERNELS = {
     "gemm_pp_routed_kernel": ("gemm.hip", "common.h", "launch.h"),
 }
 # Template arguments of the plain (MUL_MAT) instantiations; the expert-routed
-# (MUL_MAT_ID) ones carry one more, which the demangled name shows.
+# (MUL_MAT_ID) ones carry one more, which the demangled name shows (for
+# gemm_pp_kernel that flag marks the k-split form, kept apart the same way).
 KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3, "gemm_pp_kernel": 2, "gemm_pp_routed_kernel": 2}
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -380,11 +381,13 @@ def time_prefill_512(torch, qmm, synth):
     """The 512-token prefill workload: Q4_0 4096x4096 and 11008x4096 with
     fp16 activations of 512 tokens (the batch of the capability probe), on
     the matrix-core kernel; back-to-back launches in a graph over >= 1.1 GiB
-    of weight copies. Flops: 2 * rows * k * tokens."""
+    of weight copies. Flops: 2 * rows * k * tokens. Beside them, the
+    4096x11008 down projection at the same batch through qmm_matmul_ws (the
+    k split), with the unsplit launch's time."""
     import numpy as np
     qt, k, T = synth.TYPE_Q4_0, synth.N_EMBD, 512
     rng = np.random.Generator(np.random.PCG64(4500))
-    out = {"workload": f"Q4_0 4096x4096 and 11008x4096, {T} fp16 tokens"}
+    out = {"workload": f"Q4_0 4096x4096 and 11008x4096 (and the 4096x11008 down projection), {T} fp16 tokens"}
     for rows in (synth.N_EMBD, synth.N_FF):
         W0 = torch.from_numpy(synth.make_weights(qt, rows, k, None, rng)).cuda()
         copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
@@ -398,6 +401,26 @@ def time_prefill_512(torch, qmm, synth):
                               "TFLOP_per_s": round(tfl, 2), "kernel": "gemm_kernel",
                               "roofline": _roof(tfl, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma")}
         del Ws, W0
+    # the stack's down projection at the same batch: 64 tiles over k = 11008,
+    # the shape qmm_matmul_ws splits in k (four parts per tile), against the
+    # unsplit launch
+    rows, k = synth.N_EMBD, synth.N_FF
+    W0 = torch.from_numpy(synth.make_weights(qt, rows, k, None, rng)).cuda()
+    copies = int(np.ceil(1.1 * 2**30 / W0.numel()))
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    X = torch.from_numpy(synth.make_activations(T, k, rng, np.float16)).cuda()
+    Y = torch.empty((T, rows), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(qmm.qmm_matmul_workspace_bytes(qt, rows, k, T, qmm.QMM_X_F16), dtype=torch.uint8, device="cuda")
+    us = _graph_time(torch, lambda: [qmm.qmm_matmul_ws(Ws[i % copies], qt, k, X, ws, Y=Y) for i in range(copies)],
+                     copies)
+    us0 = _graph_time(torch, lambda: [qmm.qmm_matmul_x16(Ws[i % copies], qt, k, X, Y=Y) for i in range(copies)],
+                      copies)
+    tfl = 2 * rows * k * T / (us * 1e-6) / 1e12
+    out[f"{rows}x{k}"] = {"tokens": T, "us_per_launch": round(us, 3), "flops_per_launch": 2 * rows * k * T,
+                          "TFLOP_per_s": round(tfl, 2), "kernel": "gemm_pp_kernel (k split, qmm_matmul_ws)",
+                          "workspace_bytes": ws.numel(), "unsplit_us_per_launch": round(us0, 3),
+                          "roofline": _roof(tfl, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma")}
+    del Ws, W0
     return out
 
 

@@ -75,8 +75,11 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_id_workspace_bytes.restype = i64
         L.qmm_matmul_id_workspace_bytes_x16.argtypes = [i64, i64, i64, i64, i64]
         L.qmm_matmul_id_workspace_bytes_x16.restype = i64
-        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_dequantize", "qmm_matmul_batch",
-                  "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc"):
+        L.qmm_matmul_ws.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, vp, i64, vp]
+        L.qmm_matmul_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+        L.qmm_matmul_workspace_bytes.restype = i64
+        for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_ws", "qmm_dequantize",
+                  "qmm_matmul_batch", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc"):
             getattr(L, f).restype = i32
         L.qmm_row_bytes.argtypes = [i32, i64]
         L.qmm_row_bytes.restype = i64
@@ -149,10 +152,8 @@ def _weights_geometry(W, n_rows, row_stride_bytes):
     return int(n_rows), int(row_stride_bytes)
 
 
-def qmm_matmul_path(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_tokens=None, Y=None,
-                    path=QMM_PATH_AUTO, stream=None):
-    """Y[n_tokens][n_rows] = MUL_MAT(W, X) with the kernel chosen by `path`.
-    X is a GPU fp32 or fp16 tensor [n_tokens][k]; Y is allocated if None."""
+def _matmul_args(W, ggml_type, k, X, n_rows, row_stride_bytes, n_tokens, Y):
+    """Geometry, activation type and checked buffers of a MUL_MAT call."""
     import torch
     n_rows, nb1 = _weights_geometry(W, n_rows, row_stride_bytes)
     if X.dtype == torch.float32:
@@ -170,6 +171,14 @@ def qmm_matmul_path(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_to
     _check_span(W, torch.uint8, _weights_span(ggml_type, k, n_rows, nb1), "W")
     _check_span(X, X.dtype, int(n_tokens) * int(k), "X")
     _check_span(Y, torch.float32, int(n_tokens) * n_rows, "Y")
+    return n_rows, nb1, x_type, int(n_tokens), Y
+
+
+def qmm_matmul_path(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_tokens=None, Y=None,
+                    path=QMM_PATH_AUTO, stream=None):
+    """Y[n_tokens][n_rows] = MUL_MAT(W, X) with the kernel chosen by `path`.
+    X is a GPU fp32 or fp16 tensor [n_tokens][k]; Y is allocated if None."""
+    n_rows, nb1, x_type, n_tokens, Y = _matmul_args(W, ggml_type, k, X, n_rows, row_stride_bytes, n_tokens, Y)
     st = lib().qmm_matmul_path(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(X, "X"), x_type,
                                int(n_tokens), _gpu_ptr(Y, "Y"), int(path), _stream(stream))
     if st != QMM_OK:
@@ -191,6 +200,29 @@ def qmm_matmul_x16(W, ggml_type, k, X, n_rows=None, row_stride_bytes=None, n_tok
     if X.dtype != torch.float16:
         raise TypeError("qmm_matmul_x16 takes float16 activations")
     return qmm_matmul_path(W, ggml_type, k, X, n_rows, row_stride_bytes, n_tokens, Y, QMM_PATH_AUTO, stream)
+
+
+def qmm_matmul_workspace_bytes(ggml_type: int, n_rows: int, k: int, n_tokens: int, x_type: int = QMM_X_F16) -> int:
+    return int(lib().qmm_matmul_workspace_bytes(int(ggml_type), int(n_rows), int(k), int(n_tokens), int(x_type)))
+
+
+def qmm_matmul_ws(W, ggml_type, k, X, workspace, n_rows=None, row_stride_bytes=None, n_tokens=None, Y=None,
+                  stream=None):
+    """MUL_MAT with a caller workspace that lets the matrix-core kernel split
+    k across workgroups (C: qmm_matmul_ws). `workspace` is a GPU uint8 tensor
+    of at least qmm_matmul_workspace_bytes bytes that held zeros when first
+    used (torch.zeros), or None when that size is 0."""
+    import torch
+    n_rows, nb1, x_type, n_tokens, Y = _matmul_args(W, ggml_type, k, X, n_rows, row_stride_bytes, n_tokens, Y)
+    if workspace is not None:
+        _check_span(workspace, torch.uint8, 0, "workspace")
+    ws = _gpu_ptr(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = lib().qmm_matmul_ws(_gpu_ptr(W, "W"), int(ggml_type), n_rows, int(k), nb1, _gpu_ptr(X, "X"), x_type,
+                             n_tokens, _gpu_ptr(Y, "Y"), ws, ws_bytes, _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_matmul_ws")
+    return Y
 
 
 def qmm_dequantize(W, ggml_type, k, n_rows=None, row_stride_bytes=None, out=None, stream=None):

@@ -32,6 +32,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace qmm {
 
 constexpr int kBM = 128;  // weight rows per tile
@@ -646,11 +648,31 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int QT, bool ALIGN4>
+// The k split of the workspace form, for launches of few tiles with long k:
+// each of the t_sk tiles is computed by `parts` workgroups, part p (workgroup
+// parts * tile + p) summing stages [n_st p / parts, n_st (p + 1) / parts).
+// Each stores its partial sum into the workspace slot of (tile, p) and then
+// counts it on the tile's counter with an agent-scope acquire-release add,
+// which makes the stores visible to the workgroup that reads the count after
+// it. The workgroup whose add completes the count adds the parts in k order,
+// ((P0 + P1) + P2) + ..., and stores Y (with two parts, its own from
+// registers: a sum of two terms is the same either way round), then sets the
+// counter back to zero for the next call. No workgroup waits for another,
+// and the order of the additions depends only on the shape and the CU
+// count, so results repeat bit for bit.
+struct PPSplit {
+  int t_sk;        // tiles
+  int g_sk;        // workgroups (t_sk * parts)
+  int parts;       // parts per tile
+  int *cnt;        // t_sk counters, zero between calls
+  float4_t *part;  // t_sk * parts partial tiles, kPPThreads * 16 float4 each
+};
+
+template <int QT, bool ALIGN4, bool SK>
 __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
                                                                 int64_t nb1, const _Float16 *__restrict__ X,
                                                                 int n_tokens, int k, float *__restrict__ Y,
-                                                                bool y_vec4, int row_tiles) {
+                                                                bool y_vec4, int row_tiles, PPSplit sk) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
   _Float16 *const Wbuf = lds_dynamic;                   // 2 weight stages
   _Float16 *const Xbuf = lds_dynamic + 2 * kPPWHalves;  // kPPXBufs activation stages
@@ -659,220 +681,277 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
+  const int n_st = nblk / 2;
 
   // tile order: as gemm_kernel (XCD-contiguous ranges, groups of row tiles)
-  const int n_tiles = static_cast<int>(gridDim.x);
-  const int bid = static_cast<int>(blockIdx.x);
-  const int per_xcd = n_tiles / kXcds;
-  const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
+  // over the tile's index: the workgroup's, or in the split form the tile's
+  const int n_tiles = SK ? sk.t_sk : static_cast<int>(gridDim.x);
   const int tok_tiles = n_tiles / row_tiles;
-  const int in_group = kGroupRows * tok_tiles;
-  const int first_row = (lin / in_group) * kGroupRows;
-  const int group_rows = min(row_tiles - first_row, kGroupRows);
-  const int row0 = (first_row + (lin % in_group) % group_rows) * kBM;
-  const int tok0 = ((lin % in_group) / group_rows) * kPPBN;
+  auto coords = [&](int bid, int &row0, int &tok0) {
+    const int per_xcd = n_tiles / kXcds;
+    const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
+    const int in_group = kGroupRows * tok_tiles;
+    const int first_row = (lin / in_group) * kGroupRows;
+    const int group_rows = min(row_tiles - first_row, kGroupRows);
+    row0 = (first_row + (lin % in_group) % group_rows) * kBM;
+    tok0 = ((lin % in_group) / group_rows) * kPPBN;
+  };
 
   // group 0: row tid / 2, block tid % 2 of the stage's pair
   const int srow = tid >> 1, sh = tid & 1;
-  const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1;
-  // group 1: copy i of wavefront w fills LDS rows 8 (8 w + i) .. + 7 of the
-  // activation tile; lane p writes position p % 8 of row p / 8, which holds
-  // chunk (p % 8) ^ (row % 8) (the lds_at permutation). Token rows past the
-  // end re-read the last token.
-  uint32_t xoff[kPPXOps];
-#pragma unroll
-  for (int i = 0; i < kPPXOps; ++i) {
-    const int row = 8 * (kPPXOps * wave + i) + (lane >> 3);
-    const int c = (lane & 7) ^ (row & 7);
-    const int tok = min(tok0 + row, n_tokens - 1);
-    xoff[i] = static_cast<uint32_t>((tok * k + 8 * c) * 2);
-  }
   const uint32_t xlds0 = lds_byte_addr(Xbuf) + 8 * kPPXOps * wave * (kBK * 2);
-
-  float4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int n_st = nblk / 2;
-  const int last = n_st - 1;
-  auto load_w = [&](HalfRaw<QT> &r, int st) {
-    if constexpr (ALIGN4)
-      r = load_half_pair<QT>(rp, st, sh);
-    else
-      r = load_half_u16<QT>(rp, 2 * st + sh, nblk);
-  };
-  auto store_w = [&](int buf, const HalfRaw<QT> &r) {
-    store_half<QT>(Wbuf + buf * kPPWHalves, srow, 4 * sh, r, ALIGN4 && sh == 0);
-  };
-  auto copy_x = [&](int st) {
-    const _Float16 *base = X + static_cast<int64_t>(kBK) * st;
-    const uint32_t lds = xlds0 + static_cast<uint32_t>((st % kPPXBufs) * kPPXHalves * 2);
-#pragma unroll
-    for (int i = 0; i < kPPXOps; ++i) dma16(xoff[i], base, lds + i * 1024);
-  };
   int aofs[2], bofs[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     aofs[h] = lds_at(64 * wm + (lane & 15), (lane >> 4) + 4 * h);
     bofs[h] = lds_at((kPPBN / 2) * g + 64 * wn + (lane & 15), (lane >> 4) + 4 * h);
   }
-  // Operands of a stage in registers. A stage's activations are complete in
-  // LDS one phase before its weights, and both are complete for group 1 one
-  // phase before it computes the stage, so the reads are issued ahead:
-  // group 1 reads all operands of stage s during its memory phase, group 0
-  // the activations of stage s + 1 during its memory phase and the weights
-  // at the start of its compute phase. The MFMAs then wait on LDS latency
-  // once per stage at most.
-  half8_t pa[2][4], pb[2][4];
-  auto read_a = [&](int st) {
-    const _Float16 *ws = Wbuf + (st & 1) * kPPWHalves;
+  float4_t acc[4][4];
+
+  // Stages [sb, sb + ns) of the tile at (row0, tok0) into acc.
+  auto run = [&](int row0, int tok0, int sb, int ns) {
+    const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1 +
+                        static_cast<int64_t>(sb) * (2 * Block<QT>::bytes);
+    const int nb = nblk - 2 * sb;  // blocks from rp on
+    const _Float16 *xs0 = X + static_cast<int64_t>(kBK) * sb;
+    // group 1: copy i of wavefront w fills LDS rows 8 (8 w + i) .. + 7 of the
+    // activation tile; lane p writes position p % 8 of row p / 8, which holds
+    // chunk (p % 8) ^ (row % 8) (the lds_at permutation). Token rows past the
+    // end re-read the last token.
+    uint32_t xoff[kPPXOps];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < kPPXOps; ++i) {
+      const int row = 8 * (kPPXOps * wave + i) + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);
+      const int tok = min(tok0 + row, n_tokens - 1);
+      xoff[i] = static_cast<uint32_t>((tok * k + 8 * c) * 2);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pa[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
-  };
-  auto read_b = [&](int st) {
-    const _Float16 *xs = Xbuf + (st % kPPXBufs) * kPPXHalves;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int last = ns - 1;
+    auto load_w = [&](HalfRaw<QT> &r, int st) {
+      if constexpr (ALIGN4)
+        r = load_half_pair<QT>(rp, st, sh);
+      else
+        r = load_half_u16<QT>(rp, 2 * st + sh, nb);
+    };
+    auto store_w = [&](int buf, const HalfRaw<QT> &r) {
+      store_half<QT>(Wbuf + buf * kPPWHalves, srow, 4 * sh, r, ALIGN4 && sh == 0);
+    };
+    auto copy_x = [&](int st) {
+      const _Float16 *base = xs0 + static_cast<int64_t>(kBK) * st;
+      const uint32_t lds = xlds0 + static_cast<uint32_t>((st % kPPXBufs) * kPPXHalves * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pb[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
-  };
-  auto mfmas = [&] {
+      for (int i = 0; i < kPPXOps; ++i) dma16(xoff[i], base, lds + i * 1024);
+    };
+    // Operands of a stage in registers. A stage's activations are complete in
+    // LDS one phase before its weights, and both are complete for group 1 one
+    // phase before it computes the stage, so the reads are issued ahead:
+    // group 1 reads all operands of stage s during its memory phase, group 0
+    // the activations of stage s + 1 during its memory phase and the weights
+    // at the start of its compute phase. The MFMAs then wait on LDS latency
+    // once per stage at most.
+    half8_t pa[2][4], pb[2][4];
+    auto read_a = [&](int st) {
+      const _Float16 *ws = Wbuf + (st & 1) * kPPWHalves;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) pa[h][i] = *reinterpret_cast<const half8_t *>(ws + aofs[h] + 16 * i * kBK);
+    };
+    auto read_b = [&](int st) {
+      const _Float16 *xs = Xbuf + (st % kPPXBufs) * kPPXHalves;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[h][i], pb[h][j], acc[i][j], 0, 0, 0);
-  };
-  auto phase_end = [] {
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // memory(s), group 0: the activation operands of stage s + 1 (complete
-  // since the previous barrier; read first, so their latency passes under
-  // the decode rather than at this phase's barrier), the weights of stage
-  // s + 1 into buffer (s + 1) % 2 from registers loaded two stages earlier,
-  // and the loads of stage s + 3 into those registers (past the last stage
-  // they re-read it; what they bring is stored into the idle buffer and never
-  // read). Group 1: the operands of stage s (complete since the previous
-  // barrier), the copy of stage s + 3's activations and a wait that leaves the
-  // copies of stages s + 2 and s + 3 in flight, so stage s + 1's (issued two
-  // memory phases earlier) has landed before the barrier.
-  HalfRaw<QT> r0, r1;
-  auto memory = [&](int s, HalfRaw<QT> &r, int buf) {
-    if (g == 0) {
-      if (s < last) read_b(s + 1);
-      store_w(buf, r);
-      load_w(r, min(s + 3, last));
-    } else {
-      read_a(s);
-      read_b(s);
-      if (s + 3 <= last) {
-        copy_x(s + 3);
-        wait_vmcnt<2 * kPPXOps>();
-      } else if (s + 2 <= last) {
-        wait_vmcnt<kPPXOps>();
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pb[h][j] = *reinterpret_cast<const half8_t *>(xs + bofs[h] + 16 * j * kBK);
+    };
+    auto mfmas = [&] {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[h][i], pb[h][j], acc[i][j], 0, 0, 0);
+    };
+    auto phase_end = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // memory(s), group 0: the activation operands of stage s + 1 (complete
+    // since the previous barrier; read first, so their latency passes under
+    // the decode rather than at this phase's barrier), the weights of stage
+    // s + 1 into buffer (s + 1) % 2 from registers loaded two stages earlier,
+    // and the loads of stage s + 3 into those registers (past the last stage
+    // they re-read it; what they bring is stored into the idle buffer and
+    // never read). Group 1: the operands of stage s (complete since the
+    // previous barrier), the copy of stage s + 3's activations and a wait that
+    // leaves the copies of stages s + 2 and s + 3 in flight, so stage s + 1's
+    // (issued two memory phases earlier) has landed before the barrier.
+    HalfRaw<QT> r0, r1;
+    auto memory = [&](int s, HalfRaw<QT> &r, int buf) {
+      if (g == 0) {
+        if (s < last) read_b(s + 1);
+        store_w(buf, r);
+        load_w(r, min(s + 3, last));
       } else {
+        read_a(s);
+        read_b(s);
+        if (s + 3 <= last) {
+          copy_x(s + 3);
+          wait_vmcnt<2 * kPPXOps>();
+        } else if (s + 2 <= last) {
+          wait_vmcnt<kPPXOps>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      }
+    };
+    auto compute = [&](int s) {
+      if (g == 0) {
+        read_a(s);
+        mfmas();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
+#pragma unroll
+        for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
+      } else {
+        mfmas();
+      }
+    };
+
+    if (g == 0) {
+      load_w(r0, 0);
+      load_w(r1, min(1, last));
+      store_w(0, r0);
+      load_w(r0, min(2, last));
+    } else {
+      copy_x(0);
+      if (last >= 1) copy_x(1);
+      if (last >= 2) copy_x(2);
+      if (last >= 2)
+        wait_vmcnt<2 * kPPXOps>();
+      else
         wait_vmcnt<0>();
+    }
+    phase_end();  // stage 0 is in LDS
+    if (g == 0) read_b(0);
+    // Group 0 runs compute(s), memory(s); group 1 memory(s), compute(s): both
+    // pass the same barriers, and each phase pairs one group's MFMAs with the
+    // other's staging.
+    // The loops run whole pairs of stages (straight-line bodies, so the wait
+    // for a register set's loads leaves the other set's loads in flight), then
+    // an odd last stage. The last barrier orders every LDS access of the
+    // range before whatever the workgroup stores into LDS next.
+    int s = 0;
+    if (g == 0) {
+      for (; s + 1 < ns; s += 2) {
+        compute(s);
+        phase_end();
+        memory(s, r1, 1);
+        phase_end();
+        compute(s + 1);
+        phase_end();
+        memory(s + 1, r0, 0);
+        phase_end();
+      }
+      if (s < ns) {
+        compute(s);
+        phase_end();
+        memory(s, r1, 1);
+        phase_end();
+      }
+    } else {
+      for (; s + 1 < ns; s += 2) {
+        memory(s, r1, 1);
+        phase_end();
+        compute(s);
+        phase_end();
+        memory(s + 1, r0, 0);
+        phase_end();
+        compute(s + 1);
+        phase_end();
+      }
+      if (s < ns) {
+        memory(s, r1, 1);
+        phase_end();
+        compute(s);
+        phase_end();
       }
     }
+    wait_vmcnt<0>();  // no load outlives the range
   };
-  auto compute = [&](int s) {
-    if (g == 0) {
-      read_a(s);
-      mfmas();
-#pragma unroll
-      for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the reads first
-#pragma unroll
-      for (int i = 0; i < 32; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then the MFMAs
-    } else {
-      mfmas();
-    }
-  };
-
-  if (g == 0) {
-    load_w(r0, 0);
-    load_w(r1, min(1, last));
-    store_w(0, r0);
-    load_w(r0, min(2, last));
-  } else {
-    copy_x(0);
-    if (last >= 1) copy_x(1);
-    if (last >= 2) copy_x(2);
-    if (last >= 2)
-      wait_vmcnt<2 * kPPXOps>();
-    else
-      wait_vmcnt<0>();
-  }
-  phase_end();  // stage 0 is in LDS
-  if (g == 0) read_b(0);
-  // Group 0 runs compute(s), memory(s); group 1 memory(s), compute(s): both
-  // pass the same barriers, and each phase pairs one group's MFMAs with the
-  // other's staging.
-  // The loops run whole pairs of stages (straight-line bodies, so the wait
-  // for a register set's loads leaves the other set's loads in flight), then
-  // an odd last stage.
-  int s = 0;
-  if (g == 0) {
-    for (; s + 1 < n_st; s += 2) {
-      compute(s);
-      phase_end();
-      memory(s, r1, 1);
-      phase_end();
-      compute(s + 1);
-      phase_end();
-      memory(s + 1, r0, 0);
-      phase_end();
-    }
-    if (s < n_st) {
-      compute(s);
-      phase_end();
-      memory(s, r1, 1);
-      phase_end();
-    }
-  } else {
-    for (; s + 1 < n_st; s += 2) {
-      memory(s, r1, 1);
-      phase_end();
-      compute(s);
-      phase_end();
-      memory(s + 1, r0, 0);
-      phase_end();
-      compute(s + 1);
-      phase_end();
-    }
-    if (s < n_st) {
-      memory(s, r1, 1);
-      phase_end();
-      compute(s);
-      phase_end();
-    }
-  }
-  wait_vmcnt<0>();  // no load outlives the workgroup
 
   // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
   // token 128 g + 64 wn + 16 j + l % 16.
+  auto store_y = [&](int row0, int tok0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tok = tok0 + (kPPBN / 2) * g + 64 * wn + 16 * j + (lane & 15);
-    if (tok >= n_tokens) continue;
-    float *yrow = Y + static_cast<int64_t>(tok) * n_rows;
+    for (int j = 0; j < 4; ++j) {
+      const int tok = tok0 + (kPPBN / 2) * g + 64 * wn + 16 * j + (lane & 15);
+      if (tok >= n_tokens) continue;
+      float *yrow = Y + static_cast<int64_t>(tok) * n_rows;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + 64 * wm + 16 * i + 4 * (lane >> 4);
-      if (y_vec4 && r + 3 < n_rows) {
-        *reinterpret_cast<float4_t *>(yrow + r) = acc[i][j];
-      } else {
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + 64 * wm + 16 * i + 4 * (lane >> 4);
+        if (y_vec4 && r + 3 < n_rows) {
+          *reinterpret_cast<float4_t *>(yrow + r) = acc[i][j];
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (r + e < n_rows) yrow[r + e] = acc[i][j][e];
+          for (int e = 0; e < 4; ++e)
+            if (r + e < n_rows) yrow[r + e] = acc[i][j][e];
+        }
       }
     }
+  };
+
+  if constexpr (!SK) {
+    int row0, tok0;
+    coords(static_cast<int>(blockIdx.x), row0, tok0);
+    run(row0, tok0, 0, n_st);
+    store_y(row0, tok0);
+  } else {
+    const int t = static_cast<int>(blockIdx.x) / sk.parts, me = static_cast<int>(blockIdx.x) % sk.parts;
+    const int sb = n_st * me / sk.parts, se = n_st * (me + 1) / sk.parts;
+    int row0, tok0;
+    coords(t, row0, tok0);
+    run(row0, tok0, sb, se - sb);
+    // store the part, count it, and if it completes the count, add the parts
+    // (with more than two, its own read back too, so the sum needs no second
+    // register tile)
+    const float4_t *slots = sk.part + static_cast<int64_t>(t) * sk.parts * (kPPThreads * 16) + threadIdx.x;
+    float4_t *mine = sk.part + (static_cast<int64_t>(t) * sk.parts + me) * (kPPThreads * 16) + threadIdx.x;
+#pragma unroll
+    for (int f = 0; f < 16; ++f) mine[f * kPPThreads] = acc[f / 4][f % 4];
+    int *flag = reinterpret_cast<int *>(lds_dynamic);
+    __syncthreads();  // every part store is ordered before the count
+    if (threadIdx.x == 0) *flag = __hip_atomic_fetch_add(sk.cnt + t, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*flag != sk.parts - 1) return;
+    float4_t v[16];
+    if (sk.parts == 2) {
+      const float4_t *other = slots + static_cast<int64_t>(1 - me) * (kPPThreads * 16);
+#pragma unroll
+      for (int f = 0; f < 16; ++f) v[f] = other[f * kPPThreads];
+#pragma unroll
+      for (int f = 0; f < 16; ++f) acc[f / 4][f % 4] += v[f];
+    } else {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) acc[f / 4][f % 4] = slots[f * kPPThreads];
+      for (int c = 1; c < sk.parts; ++c) {
+        const float4_t *part = slots + static_cast<int64_t>(c) * (kPPThreads * 16);
+#pragma unroll
+        for (int f = 0; f < 16; ++f) v[f] = part[f * kPPThreads];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) acc[f / 4][f % 4] += v[f];
+      }
+    }
+    store_y(row0, tok0);
+    if (threadIdx.x == 0) __hip_atomic_store(sk.cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1253,12 +1332,13 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
     const dim3 ppgrid(static_cast<unsigned>(pp_tiles));
     const int prt = static_cast<int>((n_rows + kBM - 1) / kBM);
     const _Float16 *xh = static_cast<const _Float16 *>(X);
-    return by_qtype_k(qtype, [&](auto qt) {
+    return by_qtype(qtype, [&](auto qt) {
       constexpr int QT = decltype(qt)::value;
       auto go = [&](auto kern) {
-        return launch(kern, ppgrid, dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, xh, nt, kk, Y, y_vec4, prt);
+        return launch(kern, ppgrid, dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, xh, nt, kk, Y, y_vec4, prt,
+                      PPSplit{});
       };
-      return align4 ? go(gemm_pp_kernel<QT, true>) : go(gemm_pp_kernel<QT, false>);
+      return align4 ? go(gemm_pp_kernel<QT, true, false>) : go(gemm_pp_kernel<QT, false, false>);
     });
   }
   return by_qtype_k(qtype, [&](auto qt) {
@@ -1274,6 +1354,68 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
     }
     if (x_f16) return gemm_dispatch<QT, true, kBM>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
     return gemm_dispatch<QT, false, kBM>(align4, grid, stream, w, nr, nblk, nb1, X, nt, kk, Y, y_vec4, rt);
+  });
+}
+
+// The split form of the two-group kernel (PPSplit): fp16 activations, a
+// 32-weight block type, whole stages, and at most half as many 128 x 256
+// tiles as CUs. Each tile is split into P = min(4, CUs / tiles) parts of
+// equal stage ranges (one workgroup each, P * tiles workgroups), each at
+// least kPPMinUnits stages. Measured on the MI355X, a part costs its 128 KiB
+// partial tile twice (stored, then read by the workgroup that adds), and
+// with every CU storing at once that traffic takes several microseconds:
+// more tiles or shorter k (4096 x 4096 or 11008 x 4096 at 512 tokens, the
+// 11008-row launches at 2048 tokens) ran slower split than whole, few tiles
+// with long k (4096 x 14336 at 512 tokens, 4096 x 4096 at 1024) faster.
+constexpr int kPPMinUnits = 32;
+constexpr int kPPMaxParts = 4;
+constexpr int64_t kPPPartBytes = int64_t{kPPThreads} * 16 * sizeof(float4_t);  // one partial tile (128 KiB)
+
+struct PPPlan {
+  PPSplit sk{};
+  int64_t bytes = 0;  // workspace: t_sk counters (256-byte padded), then the partial tiles; 0: no split
+};
+
+static PPPlan pp_split_plan(int qtype, int64_t n_rows, int64_t k, int64_t n_tokens, bool x_f16) {
+  PPPlan p;
+  const int64_t cus = device_cus();
+  const int64_t nblk = k / 32;
+  if (!x_f16 || qtype == QMM_TYPE_Q4_K || cus <= 0 || n_rows <= 0 || nblk % 2 != 0 || n_tokens < kPPBN ||
+      n_tokens * k * 2 >= (int64_t{1} << 32))
+    return p;
+  const int64_t T = ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
+  const int64_t parts = std::min<int64_t>(kPPMaxParts, cus / T), n_st = nblk / 2;
+  if (parts < 2 || n_st < parts * kPPMinUnits || (T * n_st + 1) * T * parts > 0x7FFFFFFF) return p;
+  p.sk = PPSplit{static_cast<int>(T), static_cast<int>(T * parts), static_cast<int>(parts), nullptr, nullptr};
+  p.bytes = (T * 4 + 255) / 256 * 256 + T * parts * kPPPartBytes;
+  return p;
+}
+
+int64_t gemm_split_bytes(int qtype, int64_t n_rows, int64_t k, int64_t n_tokens, bool x_f16) {
+  return pp_split_plan(qtype, n_rows, k, n_tokens, x_f16).bytes;
+}
+
+hipError_t launch_gemm_split(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const _Float16 *X,
+                             int64_t n_tokens, float *Y, void *workspace, int64_t workspace_bytes,
+                             hipStream_t stream) {
+  PPPlan p = pp_split_plan(qtype, n_rows, k, n_tokens, true);
+  if (p.bytes == 0 || workspace == nullptr || workspace_bytes < p.bytes) return hipErrorInvalidValue;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  p.sk.cnt = reinterpret_cast<int *>(ws);
+  p.sk.part = reinterpret_cast<float4_t *>(ws + (static_cast<int64_t>(p.sk.t_sk) * 4 + 255) / 256 * 256);
+  const uint8_t *w = static_cast<const uint8_t *>(W);
+  const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0);
+  const bool y_vec4 = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && (n_rows % 4 == 0);
+  const int prt = static_cast<int>((n_rows + kBM - 1) / kBM);
+  const int nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows), nt = static_cast<int>(n_tokens),
+            kk = static_cast<int>(k);
+  return by_qtype(qtype, [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    auto go = [&](auto kern) {
+      return launch(kern, dim3(static_cast<unsigned>(p.sk.g_sk)), dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, X,
+                    nt, kk, Y, y_vec4, prt, p.sk);
+    };
+    return align4 ? go(gemm_pp_kernel<QT, true, true>) : go(gemm_pp_kernel<QT, false, true>);
   });
 }
 

@@ -109,5 +109,13 @@ hipError_t launch_gemm_routed(const void *W, int qtype, int64_t n_rows, int64_t 
 // Matrix-core kernel, any n_tokens >= 1.
 hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const void *X, bool x_f16,
                        int64_t n_tokens, float *Y, hipStream_t stream);
+// The two-group kernel with k split across workgroups, for launches of few
+// tiles with long k: gemm_split_bytes is the workspace it needs (per-tile
+// counters, zero between calls, then partial tiles), 0 for shapes it does
+// not take (then launch_gemm's choice holds).
+int64_t gemm_split_bytes(int qtype, int64_t n_rows, int64_t k, int64_t n_tokens, bool x_f16);
+hipError_t launch_gemm_split(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const _Float16 *X,
+                             int64_t n_tokens, float *Y, void *workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
 
 }  // namespace qmm

@@ -149,7 +149,7 @@ const char *qmm_status_string(int status) {
     case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: W needs 2-byte (Q4_K: 16-byte), X, Y and out 4-byte alignment";
     case QMM_ERR_HIP: return "QMM_ERR_HIP: the HIP runtime rejected the kernel launch";
     case QMM_ERR_PATH: return "QMM_ERR_PATH: unknown path, or GEMV forced with more than 8 tokens";
-    case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or smaller than qmm_matmul_id_workspace_bytes";
+    case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or smaller than the call's *_workspace_bytes";
     case QMM_ERR_SCRATCH:
       return "QMM_ERR_SCRATCH: the call needs more than the QMM_NOALLOC_SCRATCH_BYTES of scratch the no-allocation "
              "entry point holds";
@@ -199,6 +199,33 @@ int qmm_matmul(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t 
 int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                    const uint16_t *X, int64_t n_tokens, float *Y, void *stream) {
   return qmm_matmul_path(W, ggml_type, n_rows, k, row_stride_bytes, X, QMM_X_F16, n_tokens, Y, QMM_PATH_AUTO, stream);
+}
+
+int64_t qmm_matmul_workspace_bytes(int ggml_type, int64_t n_rows, int64_t k, int64_t n_tokens, int x_type) {
+  const int bb = block_bytes(ggml_type), bw = block_weights(ggml_type);
+  if (bb == 0 || (x_type != QMM_X_F32 && x_type != QMM_X_F16)) return QMM_ERR_TYPE;
+  if (k <= 0 || k % bw != 0 || k > kMaxDim || n_rows < 0 || n_rows > kMaxDim || n_tokens < 0 || n_tokens > kMaxDim)
+    return QMM_ERR_SHAPE;
+  if (!product_within(n_tokens, k, kMaxElems) || !product_within(n_tokens, n_rows, kMaxElems)) return QMM_ERR_SHAPE;
+  if (n_rows == 0 || n_tokens <= QMM_GEMV_MAX_TOKENS) return 0;
+  return qmm::gemm_split_bytes(ggml_type, n_rows, k, n_tokens, x_type == QMM_X_F16);
+}
+
+int qmm_matmul_ws(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, const void *X,
+                  int x_type, int64_t n_tokens, float *Y, void *workspace, int64_t workspace_bytes, void *stream) {
+  const int st = check_matmul(W, ggml_type, n_rows, k, row_stride_bytes, X, x_type, n_tokens, Y, QMM_PATH_AUTO);
+  if (st != QMM_OK) return st;
+  const int64_t need = qmm_matmul_workspace_bytes(ggml_type, n_rows, k, n_tokens, x_type);
+  if (need < 0) return static_cast<int>(need);
+  if (need == 0) return qmm_matmul_path(W, ggml_type, n_rows, k, row_stride_bytes, X, x_type, n_tokens, Y,
+                                        QMM_PATH_AUTO, stream);
+  if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+  if (trace_on())
+    fprintf(stderr, "qmm: gemm split %s rows=%lld k=%lld nb1=%lld tokens=%lld workspace=%lld\n", type_name(ggml_type),
+            (long long)n_rows, (long long)k, (long long)row_stride_bytes, (long long)n_tokens, (long long)need);
+  return status_of(qmm::launch_gemm_split(W, ggml_type, n_rows, k, row_stride_bytes, static_cast<const _Float16 *>(X),
+                                          n_tokens, Y, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream) {

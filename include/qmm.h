@@ -174,6 +174,47 @@ int qmm_matmul_x16(const void *W, int ggml_type, int64_t n_rows, int64_t k, int6
 int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
                     const void *X, int x_type, int64_t n_tokens, float *Y, int path, void *stream);
 
+/*
+ * qmm_matmul_workspace_bytes - device workspace qmm_matmul_ws needs for this
+ * shape on the current device: 0 when the call runs as qmm_matmul_path with
+ * QMM_PATH_AUTO, otherwise the bytes of its k split (counters and one
+ * 128 KiB partial tile per part). The split is taken by fp16 activations of
+ * at least 256 tokens, a 32-weight block type and an even block count, when
+ * the 128-row x 256-token tiles number at most half the compute units and k
+ * is long enough for 2 to 4 parts per tile of at least 32 stages of 64
+ * (k >= 4096 for 2 parts); every other shape returns 0. Negative status for
+ * invalid sizes or types.
+ */
+int64_t qmm_matmul_workspace_bytes(int ggml_type, int64_t n_rows, int64_t k, int64_t n_tokens, int x_type);
+
+/*
+ * qmm_matmul_ws - the MUL_MAT of qmm_matmul_path (QMM_PATH_AUTO; the same
+ * computation, [Bind] section 2.3) with a caller workspace that lets the
+ * matrix-core kernel split k across workgroups where its tiles would leave
+ * most compute units idle: few output tiles with a long k (e.g. a 4096-row
+ * projection over k = 14336 at the 512-token batch of [Load] section
+ * 第六步). Each tile is summed as 2 to 4 partial sums over equal k ranges,
+ * added in k order by the workgroup that finishes last; no workgroup waits
+ * for another.
+ *   W ... stream   as in qmm_matmul_path (x_type QMM_X_F32 or QMM_X_F16)
+ *   workspace      device pointer, 16-byte aligned, at least
+ *                  qmm_matmul_workspace_bytes(...) bytes, caller-owned; may
+ *                  be NULL when that is 0. It must hold zeros when first
+ *                  used (e.g. filled by hipMemset once); every call leaves
+ *                  its counters at zero again, so one workspace serves any
+ *                  later call enqueued after it. Calls that may run at the
+ *                  same time need workspaces of their own.
+ *   workspace_bytes its size
+ * Returns QMM_ERR_WORKSPACE if the workspace is NULL or too small where one
+ * is needed, QMM_ERR_ALIGN if it is misaligned, else as qmm_matmul_path.
+ * Results are reproducible bit for bit for a given shape on a given device
+ * (the split depends on the shape and the compute unit count) and may differ
+ * in their last bits from qmm_matmul_x16's, within the same error bound.
+ */
+int qmm_matmul_ws(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes,
+                  const void *X, int x_type, int64_t n_tokens, float *Y, void *workspace, int64_t workspace_bytes,
+                  void *stream);
+
 /* One MUL_MAT of a qmm_matmul_batch call; fields as in qmm_matmul_path. */
 typedef struct qmm_matmul_desc {
   const void *W;

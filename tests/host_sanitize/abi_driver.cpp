@@ -95,6 +95,26 @@ int main() {
   EXPECT(qmm_matmul_x16(W, QMM_TYPE_Q8_0, 5, 64, 68, (const uint16_t *)X, 0, Y, NULL), QMM_OK);
   EXPECT(qmm_dequantize(W, QMM_TYPE_Q4_0, 0, 64, 36, Y, NULL), QMM_OK);
   EXPECT(qmm_dequantize(W, QMM_TYPE_Q4_0, INT64_MAX, 64, 36, Y, NULL), QMM_ERR_SHAPE);
+  // MUL_MAT with a workspace: the same checks, then the workspace's; the
+  // size query agrees (no device here: no compute units, no split)
+  EXPECT(qmm_matmul_ws(NULL, QMM_TYPE_Q4_0, 16, 64, 36, X, QMM_X_F16, 600, Y, NULL, 0, NULL), QMM_ERR_NULL);
+  EXPECT(qmm_matmul_ws(W, 1, 16, 64, 36, X, QMM_X_F16, 600, Y, NULL, 0, NULL), QMM_ERR_TYPE);
+  EXPECT(qmm_matmul_ws(W, QMM_TYPE_Q4_0, 16, 64, 36, X, 7, 600, Y, NULL, 0, NULL), QMM_ERR_TYPE);
+  EXPECT(qmm_matmul_ws(W, QMM_TYPE_Q4_0, 16, 64, 36, X, QMM_X_F16, INT64_MAX, Y, NULL, 0, NULL), QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_ws(W, QMM_TYPE_Q4_0, (int64_t)1 << 30, 64, (int64_t)1 << 40, X, QMM_X_F16, 600, Y, NULL, 0,
+                       NULL), QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_ws(W, QMM_TYPE_Q4_0, 16, 64, 36, X, QMM_X_F16, 0, Y, (void *)0x50001, -7, NULL), QMM_OK);
+  EXPECT(qmm_matmul_ws(W, QMM_TYPE_Q4_0, 0, 64, 36, X, QMM_X_F16, 600, Y, NULL, 0, NULL), QMM_OK);
+  EXPECT(qmm_matmul_workspace_bytes(1, 16, 64, 600, QMM_X_F16), QMM_ERR_TYPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, 16, 64, 600, -1), QMM_ERR_TYPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, 16, 40, 600, QMM_X_F16), QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, INT64_MIN, 64, 600, QMM_X_F16), QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, 16, INT64_MAX, 600, QMM_X_F16), QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, 16, 64, INT64_MAX, QMM_X_F16), QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, ((int64_t)1 << 31) - 1, kbig, (int64_t)1 << 30, QMM_X_F16),
+         QMM_ERR_SHAPE);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_0, ((int64_t)1 << 31) - 1, kbig, 1 << 28, QMM_X_F16), 0);
+  EXPECT(qmm_matmul_workspace_bytes(QMM_TYPE_Q4_K, 4096, 4096, 600, QMM_X_F16), 0);
   EXPECT(qmm_get_rows(W, QMM_TYPE_Q4_0, 16, 64, 36, IDS, 0, Y, NULL), QMM_OK);
   EXPECT(qmm_get_rows(W, QMM_TYPE_Q4_0, 16, 64, 36, NULL, 4, Y, NULL), QMM_ERR_NULL);
   EXPECT(qmm_get_rows(W, QMM_TYPE_Q4_0, 16, 64, 36, IDS, -1, Y, NULL), QMM_ERR_SHAPE);

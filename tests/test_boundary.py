@@ -36,6 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
+                            "qmm_matmul_ws", "qmm_matmul_workspace_bytes",
                             "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc",
                             "qmm_matmul_id_workspace_bytes", "qmm_matmul_id_workspace_bytes_x16", "qmm_row_bytes",
                             "qmm_supports", "qmm_status_string"])
@@ -127,6 +128,41 @@ def test_validation_codes(L):
     assert _mm(L, Y=ctypes.c_void_p(0x30002)) == E.QMM_ERR_ALIGN
     assert _mm(L, path=3) == E.QMM_ERR_PATH
     assert _mm(L, path=qmm.QMM_PATH_GEMV, n=9) == E.QMM_ERR_PATH
+
+
+def _ws(L, W=P, t=Q4, rows=16, k=64, nb1=36, X=P2, xt=qmm.QMM_X_F16, n=1, Y=P3, ws=NULL, ws_bytes=0):
+    return L.qmm_matmul_ws(W, t, rows, k, nb1, X, xt, n, Y, ws, ws_bytes, NULL)
+
+
+def test_matmul_ws_validation(L):
+    """qmm_matmul_ws runs qmm_matmul_path's checks first, then the
+    workspace's; the size query rejects what the call rejects. (Without a
+    GPU the size query sees no compute units and asks for no workspace.)"""
+    E = qmm
+    assert _ws(L, W=NULL) == E.QMM_ERR_NULL
+    assert _ws(L, X=NULL) == E.QMM_ERR_NULL
+    assert _ws(L, Y=NULL) == E.QMM_ERR_NULL
+    assert _ws(L, t=1) == E.QMM_ERR_TYPE
+    assert _ws(L, xt=2) == E.QMM_ERR_TYPE
+    assert _ws(L, k=40) == E.QMM_ERR_SHAPE
+    assert _ws(L, n=-1) == E.QMM_ERR_SHAPE
+    assert _ws(L, rows=1 << 31) == E.QMM_ERR_SHAPE
+    assert _ws(L, nb1=35) == E.QMM_ERR_STRIDE
+    assert _ws(L, X=ctypes.c_void_p(0x20002)) == E.QMM_ERR_ALIGN
+    assert _ws(L, n=0) == E.QMM_OK and _ws(L, rows=0, n=600) == E.QMM_OK   # empty: no launch
+    assert _ws(L, n=0, ws=ctypes.c_void_p(0x50001), ws_bytes=-5) == E.QMM_OK  # unused workspace not checked
+    wb = L.qmm_matmul_workspace_bytes
+    assert wb(1, 16, 64, 600, qmm.QMM_X_F16) == E.QMM_ERR_TYPE
+    assert wb(Q4, 16, 64, 600, 2) == E.QMM_ERR_TYPE
+    assert wb(Q4, 16, 40, 600, qmm.QMM_X_F16) == E.QMM_ERR_SHAPE
+    assert wb(Q4, -1, 64, 600, qmm.QMM_X_F16) == E.QMM_ERR_SHAPE
+    assert wb(Q4, 16, 64, -1, qmm.QMM_X_F16) == E.QMM_ERR_SHAPE
+    assert wb(Q4, 16, 64, 1 << 31, qmm.QMM_X_F16) == E.QMM_ERR_SHAPE
+    assert wb(Q4, (1 << 31) - 1, (1 << 31) - 32, 1 << 30, qmm.QMM_X_F16) == E.QMM_ERR_SHAPE  # n * k > 2^60
+    for n in (0, 1, 8):
+        assert wb(Q4, 4096, 4096, n, qmm.QMM_X_F16) == 0   # decode sizes never split
+    assert wb(Q4, 0, 4096, 600, qmm.QMM_X_F16) == 0
+    assert wb(Q4, 4096, 4096, 512, qmm.QMM_X_F32) == 0     # fp32 activations never split
 
 
 def test_zero_sized_calls_launch_nothing(L):
