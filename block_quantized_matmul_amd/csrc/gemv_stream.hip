@@ -168,34 +168,60 @@ template <int QT, int NT, int G = 1> struct RLane {
   }
 };
 
+// A stage's weight chunks into the wavefront's LDS area (wl), rows
+// row_stride bytes apart.
+template <int QT, int NT, int G>
+__device__ __forceinline__ void r_copy_w(const u32x4_t (&w)[RCfg<QT, NT, G>::w_loads], const RLane<QT, NT, G> &L,
+                                         unsigned char *wl) {
+  using C = RCfg<QT, NT, G>;
+#pragma unroll
+  for (int j = 0; j < C::w_loads; ++j)
+    if (L.woff[j] >= 0) {
+      if constexpr (C::row_stride % 16 == 0) {
+        *reinterpret_cast<u32x4_t *>(wl + L.woff[j]) = w[j];
+      } else {
+        *reinterpret_cast<u32x2_t *>(wl + L.woff[j]) = u32x2_t{w[j].x, w[j].y};
+        *reinterpret_cast<u32x2_t *>(wl + L.woff[j] + 8) = u32x2_t{w[j].z, w[j].w};
+      }
+    }
+}
+
+// Four activations (elements 4 l .. 4 l + 3 of a quad, l the lane's piece)
+// of one token slot, as fp16 in MFMA operand order, into the staged set xs
+// at byte xw + 16 t.
+template <bool XF16>
+__device__ __forceinline__ void r_stage_x(const typename std::conditional<XF16, half4_t, float4_t>::type &x,
+                                          half8_t *xs, int xw, int t) {
+  half4_t h;
+  if constexpr (XF16) {
+    h = x;
+  } else {
+    const half2_t a = cvt_half2(x.x, x.y), b = cvt_half2(x.z, x.w);
+    h = half4_t{a.x, a.y, b.x, b.y};
+  }
+  *reinterpret_cast<half4_t *>(reinterpret_cast<unsigned char *>(xs) + xw + 16 * t) = h;
+}
+
+template <int QT, int NT, int G>
+__device__ __forceinline__ void r_mfma(const unsigned char *wl, const half8_t *xs, int lane, float (&acc)[G][4]);
+
 // Consume one stage: copy the weights into the wavefront's LDS area (wl) and
 // the activations, as fp16 in MFMA operand order, into xs; then run the 8
 // blocks (4 pairs) through the matrix cores into acc.
 template <int QT, int NT, bool XF16, int G>
 __device__ __forceinline__ void r_consume(const RRegs<QT, NT, XF16, G> &r, const RLane<QT, NT, G> &L, unsigned char *wl,
                                           half8_t *xs, int lane, float (&acc)[G][4]) {
+  r_copy_w<QT, NT, G>(r.w, L, wl);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) r_stage_x<XF16>(r.x[t], xs, L.xw, t);
+  r_mfma<QT, NT, G>(wl, xs, lane, acc);
+}
+
+// The stage's 8 blocks (4 pairs) through the matrix cores into acc: the
+// weights from the wavefront's LDS copy wl, the activations from xs.
+template <int QT, int NT, int G>
+__device__ __forceinline__ void r_mfma(const unsigned char *wl, const half8_t *xs, int lane, float (&acc)[G][4]) {
   using C = RCfg<QT, NT, G>;
-#pragma unroll
-  for (int j = 0; j < C::w_loads; ++j)
-    if (L.woff[j] >= 0) {
-      if constexpr (C::row_stride % 16 == 0) {
-        *reinterpret_cast<u32x4_t *>(wl + L.woff[j]) = r.w[j];
-      } else {
-        *reinterpret_cast<u32x2_t *>(wl + L.woff[j]) = u32x2_t{r.w[j].x, r.w[j].y};
-        *reinterpret_cast<u32x2_t *>(wl + L.woff[j] + 8) = u32x2_t{r.w[j].z, r.w[j].w};
-      }
-    }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    half4_t h;
-    if constexpr (XF16) {
-      h = r.x[t];
-    } else {
-      const half2_t a = cvt_half2(r.x[t].x, r.x[t].y), b = cvt_half2(r.x[t].z, r.x[t].w);
-      h = half4_t{a.x, a.y, b.x, b.y};
-    }
-    *reinterpret_cast<half4_t *>(reinterpret_cast<unsigned char *>(xs) + L.xw + 16 * t) = h;
-  }
   const int r16 = lane & 15, g = lane >> 4;
   const int slot = min(r16, NT - 1);
   if constexpr (QTraits<QT>::kquant) {
@@ -484,6 +510,130 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == kKSplitLarge ? RCfg<QT, NT, G
   r_reduce<NT, WAVES, G>(red, wave, lane, acc, Y, row0, n_rows, n_tokens, tok);
 }
 
+// Tall matrices with 3 to 8 tokens (the output projection of a small
+// decode batch). The k-split kernel above stages all n_tokens x k activations
+// once per 16 or 32 rows; at 8 tokens that is 1.7 activation bytes per
+// weight byte, read from L2 and converted by every workgroup. Here a
+// workgroup owns 128 rows, one 16-row group per wavefront, each wavefront
+// running the full k of its rows, and the workgroup stages each chunk of
+// activations (up to 64 KiB of fp16) in LDS once for all eight wavefronts:
+// a quarter of the activation traffic per weight byte, and no reduction
+// across wavefronts (each output is one wavefront's running sum over the
+// blocks in order). Weights stream as in the k-split kernel (the same
+// 16-row stages, the same LDS copy and MFMAs), kTallDepth stages ahead, and
+// the stream runs on across chunk boundaries.
+constexpr int kTallWaves = 8;
+constexpr int kTallRows = 16 * kTallWaves;
+constexpr int kTallXBytes = 64 * 1024;  // staged activations per chunk
+
+template <int QT, int NT> struct TallCfg {
+  using C = RCfg<QT, NT>;
+  // stages in flight per wavefront: 4 (2 for Q8_0, whose stage takes 20
+  // registers); a power of two, so it divides the chunk
+  static constexpr int depth = 4 * C::w_loads <= 16 ? 4 : 2;
+  // quads per activation chunk (128 / NT)
+  static constexpr int chunk_quads = kTallXBytes / C::x_lds;
+  static_assert(chunk_quads % depth == 0, "chunks are whole rounds of stages");
+  static constexpr size_t lds = static_cast<size_t>(kTallWaves) * C::w_lds + kTallXBytes;
+};
+
+template <int QT, int NT, bool XF16>
+__global__ __launch_bounds__(64 * kTallWaves, 4) void gemv_tall_kernel(const uint8_t *W, const void *X, float *Y0,
+                                                                        int64_t nb1, int n_rows, int nblk,
+                                                                        int n_tokens, int k) {
+  using C = RCfg<QT, NT>;
+  using T = TallCfg<QT, NT>;
+  constexpr int QC = C::quad_chunks;
+  constexpr int D = T::depth;
+  constexpr int CQ = T::chunk_quads;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned char *wl = smem + wave * C::w_lds;
+  half8_t *xs = reinterpret_cast<half8_t *>(smem + kTallWaves * C::w_lds);
+  __attribute__((address_space(1))) float *Y = (__attribute__((address_space(1))) float *)Y0;
+
+  const int row0 = static_cast<int>(blockIdx.x) * kTallRows + 16 * wave;
+  const RLane<QT, NT> L(lane, static_cast<uint32_t>(nb1));
+  // the wavefront's rows start the resource (rows past n_rows read as zero)
+  const int64_t left = static_cast<int64_t>(n_rows - row0) * nb1;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(W) + (row0 < n_rows ? static_cast<int64_t>(row0) * nb1 : 0), 0,
+      static_cast<int>(static_cast<uint32_t>(left > 0 ? left : 0)), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(X), 0, static_cast<int>(static_cast<uint32_t>(n_tokens * k * (XF16 ? 2 : 4))), kRsrcWord3);
+  const int qn = nblk >> 3;
+
+  u32x4_t st[D][C::w_loads];
+  auto issue = [&](u32x4_t (&w)[C::w_loads], int q) {
+    const int wq = q * (QC * 16);
+#pragma unroll
+    for (int j = 0; j < C::w_loads; ++j)
+      w[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wres, L.wv[j], wq, 0));
+  };
+  // Stage quads [q0, q0 + nq) of every token slot: piece i is slot i / (64 nq),
+  // quad i / 64 % nq, elements 4 l .. 4 l + 3 (l = i % 64) of that quad,
+  // placed as the k-split kernel places a lane's piece. Token slots past
+  // n_tokens repeat the last token (their outputs are not stored).
+  auto stage = [&](int q0, int nq) {
+    const int pieces = NT * nq * 64;
+    for (int i = threadIdx.x; i < pieces; i += 64 * kTallWaves) {
+      const int l = i & 63, qi = (i >> 6) % nq, t = (i >> 6) / nq;
+      const RLane<QT, NT> P(l, 0u);
+      const uint32_t off =
+          (static_cast<uint32_t>(min(t, n_tokens - 1)) * k + (q0 + qi) * 256 + 4 * l) * (XF16 ? 2 : 4);
+      if constexpr (XF16) {
+        const half4_t h = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(xres, off, 0, 0));
+        r_stage_x<true>(h, xs + qi * (C::x_lds / 16), P.xw, t);
+      } else {
+        const float4_t f = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+        r_stage_x<false>(f, xs + qi * (C::x_lds / 16), P.xw, t);
+      }
+    }
+  };
+
+  float acc[1][4] = {{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (i < qn) issue(st[i], i);
+  for (int c0 = 0; c0 < qn; c0 += CQ) {
+    const int nq = min(CQ, qn - c0);
+    if (c0 > 0) {  // every wavefront is done with the previous chunk
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    stage(c0, nq);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's pieces are in LDS
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // quads q = c0 + j; stage register set (q % D) is fixed at compile time
+    // by stepping the chunk in whole rounds of D quads
+    for (int j = 0; j < nq; j += D) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const int q = c0 + j + i;
+        if (j + i < nq) {
+          // quads are issued in order, so set i holds quad q (chunks are a
+          // whole number of rounds: CQ % D == 0)
+          r_copy_w<QT, NT, 1>(st[i], L, wl);
+          if (q + D < qn) issue(st[i], q + D);
+          r_mfma<QT, NT, 1>(wl, xs + (j + i) * (C::x_lds / 16), lane, acc);
+        }
+      }
+    }
+  }
+  if (lane < (NT > 4 ? 32 : 16) && row0 + (lane & 15) < n_rows) {
+    const int row = row0 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * (lane >> 4) + e;
+      if (t < n_tokens) Y[static_cast<int64_t>(t) * n_rows + row] = acc[0][e];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 // Row groups per workgroup. A multi-token call reads its n_tokens x k
@@ -640,6 +790,31 @@ hipError_t launch_gemv_id_tiles(const void *W, int qtype, int64_t n_experts, int
   return hipSuccess;
 }
 
+// A single streamable MUL_MAT of 3 to 8 tokens whose 128-row tiles nearly
+// fill the GPU (at least 7/8 of a tile per compute unit) runs on the
+// row-split kernel.
+static bool tall_for(const MatmulDesc &d, int cus) {
+  return d.n_tokens >= 3 && d.n_tokens <= 8 && cus > 0 && (d.n_rows + kTallRows - 1) / kTallRows * 8 >= 7 * cus;
+}
+
+static hipError_t launch_gemv_tall(const MatmulDesc &d, hipStream_t stream) {
+  const int nt = nt_slots(d.n_tokens);
+  const int tiles = static_cast<int>((d.n_rows + kTallRows - 1) / kTallRows);
+  return by_qtype_k(d.qtype, [&](auto q) {
+    constexpr int QT = decltype(q)::value;
+    auto go = [&](auto ntc, auto xc) {
+      constexpr int NT = decltype(ntc)::value;
+      constexpr bool XF = decltype(xc)::value;
+      return launch(gemv_tall_kernel<QT, NT, XF>, dim3(tiles), dim3(64 * kTallWaves), TallCfg<QT, NT>::lds, stream,
+                    static_cast<const uint8_t *>(d.W), d.X, d.Y, d.nb1, static_cast<int>(d.n_rows),
+                    static_cast<int>(d.k / 32), static_cast<int>(d.n_tokens), static_cast<int>(d.k));
+    };
+    auto by_x = [&](auto ntc) { return d.x_f16 ? go(ntc, std::true_type{}) : go(ntc, std::false_type{}); };
+    if (nt <= 4) return by_x(std::integral_constant<int, 4>{});
+    return by_x(std::integral_constant<int, 8>{});
+  });
+}
+
 hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t stream) {
   // Consecutive streamable descriptors with the same (type, activation type,
   // token-slot count) share a launch of up to kRMaxMats matrices; the rest
@@ -673,12 +848,18 @@ hipError_t launch_gemv_batch(const MatmulDesc *d, int count_all, hipStream_t str
       total_rg += (d[j].n_rows + 15) / 16;
       ++j;
     }
-    const int waves = k_split_for(total_rg, device_cus());
-    const hipError_t e = by_qtype_k(qt, [&](auto q) {
-      constexpr int QT = decltype(q)::value;
-      return xf ? r_nt<QT, true>(nt, B, count, max_rg, waves, stream)
-                : r_nt<QT, false>(nt, B, count, max_rg, waves, stream);
-    });
+    const int cus = device_cus();
+    hipError_t e;
+    if (count == 1 && tall_for(d[i], cus)) {
+      e = launch_gemv_tall(d[i], stream);
+    } else {
+      const int waves = k_split_for(total_rg, cus);
+      e = by_qtype_k(qt, [&](auto q) {
+        constexpr int QT = decltype(q)::value;
+        return xf ? r_nt<QT, true>(nt, B, count, max_rg, waves, stream)
+                  : r_nt<QT, false>(nt, B, count, max_rg, waves, stream);
+      });
+    }
     if (e != hipSuccess) return e;
     i = j;
   }
