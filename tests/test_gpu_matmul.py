@@ -93,15 +93,16 @@ def test_gemm_full_size_tiles(qtype, xdt):
 
 @pytest.mark.parametrize("qtype", [Q4, Q41, Q50, Q51, Q8])
 @pytest.mark.parametrize("rows,k,n,extra,offset", [(2000, 320, 4000, 0, 0), (2048, 256, 4096, 0, 2),
-                                                   (3000, 384, 4000, 2, 0)])
+                                                   (3000, 384, 4000, 2, 0), (11003, 320, 505, 0, 0)])
 def test_gemm_two_group_tiles(qtype, rows, k, n, extra, offset):
-    """fp16 activations with at least one 128 x 256 tile per CU (256 and 384
-    tiles on the 256 CUs): the two-group kernel, with ragged rows and tokens,
+    """fp16 activations with 128 x 256 tiles for at least 2/3 of the CUs (172
+    tiles, one round; 256 and 384 tiles on the 256 CUs): the two-group
+    kernel, with ragged rows and tokens,
     an odd number of 64-wide stages (k = 320), 2-byte-aligned weights and
     padded rows (the unaligned staging), every element against the oracle,
     and bitwise the same as the fp32 copy of the activations (the one-group
     kernel, which adds the same products in the same order)."""
-    assert ((rows + 127) // 128) * ((n + 255) // 256) in (256, 384)
+    assert ((rows + 127) // 128) * ((n + 255) // 256) in (172, 256, 384)
     W, X = _inputs(qtype, rows, k, n, extra, xdt=np.float16)
     say(f"gemm two-group tiles type={qtype} rows={rows} k={k} n={n} nb1={W.shape[1]} offset={offset}")
     Y = run_matmul(W, qtype, k, X, GEMM, offset)
