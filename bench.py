@@ -65,6 +65,7 @@ CSRC = os.path.join(ROOT, "block_quantized_matmul_amd", "csrc")
 KERNELS = {
     # name fragment in the kernel symbol -> sources the kernel is built from
     "gemv_stream_kernel": ("gemv_stream.hip", "gemv_common.h", "common.h", "launch.h"),
+    "gemv_tall_kernel": ("gemv_stream.hip", "gemv_common.h", "common.h", "launch.h"),
     "gemm_kernel": ("gemm.hip", "common.h", "launch.h"),
     "gemm_pp_kernel": ("gemm.hip", "common.h", "launch.h"),
     "gemm_pp_routed_kernel": ("gemm.hip", "common.h", "launch.h"),
@@ -72,7 +73,8 @@ KERNELS = {
 # Template arguments of the plain (MUL_MAT) instantiations; the expert-routed
 # (MUL_MAT_ID) ones carry one more, which the demangled name shows (for
 # gemm_pp_kernel that flag marks the k-split form, kept apart the same way).
-KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemm_kernel": 3, "gemm_pp_kernel": 2, "gemm_pp_routed_kernel": 2}
+KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemv_tall_kernel": 3, "gemm_kernel": 3, "gemm_pp_kernel": 2,
+                "gemm_pp_routed_kernel": 2}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -231,17 +233,20 @@ def summarize_counters(dirs):
             print(f"TRAFFIC {kern} bytes_per_launch {total:.0f} source_sha256 {source_hash(kern)}")
 
 
-def traffic_from_profiles(kernel):
-    """HBM bytes per launch of `kernel` recorded under profiles/ (a line
-    'TRAFFIC <kernel> bytes_per_launch <B> source_sha256 <h>'), or None if
-    there is none for the current source."""
+def traffic_from_profiles(kernel, profile):
+    """HBM bytes per launch of `kernel` recorded in profiles/<profile> (a line
+    'TRAFFIC <kernel> bytes_per_launch <B> source_sha256 <h>', taken on the
+    workload that profile names), or None if it holds none for the current
+    source."""
     h = source_hash(kernel)
-    for f in sorted(glob.glob(os.path.join(PROFILES, "*.txt"))):
-        with open(f) as fh:
-            for line in fh:
-                m = re.match(r"TRAFFIC (\S+) bytes_per_launch (\d+) source_sha256 (\w+)", line)
-                if m and m.group(1) == kernel and m.group(3) == h:
-                    return int(m.group(2))
+    f = os.path.join(PROFILES, profile)
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        for line in fh:
+            m = re.match(r"TRAFFIC (\S+) bytes_per_launch (\d+) source_sha256 (\w+)", line)
+            if m and m.group(1) == kernel and m.group(3) == h:
+                return int(m.group(2))
     return None
 
 
@@ -354,7 +359,8 @@ def _roof(achieved, peak, unit, bound):
 def time_output_projection(torch, qmm, synth):
     """The output-projection workload: Q4_0 32000x4096 with rows padded to
     nb1 = 2560 (256 random padding bytes per row), fp32 activations of 1, 2,
-    4 and 8 tokens, on the decode kernel. Back-to-back launches in a graph
+    4 and 8 tokens, on the decode kernels (the k-split kernel at 1 and 2
+    tokens, the row-split one at 4 and 8). Back-to-back launches in a graph
     over >= 1.1 GiB of weight copies, so the weights come from HBM.
     Algorithmic bytes: the blocks (padding excluded), X and Y."""
     import numpy as np
@@ -371,8 +377,9 @@ def time_output_projection(torch, qmm, synth):
         us = _graph_time(torch, lambda: [qmm.qmm_matmul(Ws[i % copies], qt, k, X, Y=Y) for i in range(reps)], reps)
         byts = rows * synth.dense_row_bytes(qt, k) + 4 * n * k + 4 * n * rows
         gbs = byts / (us * 1e-6) / 1e9
+        # 3 to 8 tokens on this tall matrix: the row-split kernel
         out[f"n{n}"] = {"tokens": n, "us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": byts,
-                        "GB_per_s": round(gbs, 2), "kernel": "gemv_stream_kernel",
+                        "GB_per_s": round(gbs, 2), "kernel": "gemv_tall_kernel" if n >= 3 else "gemv_stream_kernel",
                         "roofline": _roof(gbs, HBM_PEAK_GBS, "GB/s", "hbm")}
     return out
 
@@ -397,8 +404,12 @@ def time_prefill_512(torch, qmm, synth):
         us = _graph_time(torch, lambda: [qmm.qmm_matmul_x16(Ws[i % copies], qt, k, X, Y=Y) for i in range(copies)],
                          copies)
         tfl = 2 * rows * k * T / (us * 1e-6) / 1e12
+        # the library's choice: the two-group kernel when its 128 x 256 tiles
+        # cover at least 2/3 of the CUs (11008 rows), else the one-group kernel
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        pp = 3 * ((rows + 127) // 128) * ((T + 255) // 256) >= 2 * cus
         out[f"{rows}x{k}"] = {"tokens": T, "us_per_launch": round(us, 3), "flops_per_launch": 2 * rows * k * T,
-                              "TFLOP_per_s": round(tfl, 2), "kernel": "gemm_kernel",
+                              "TFLOP_per_s": round(tfl, 2), "kernel": "gemm_pp_kernel" if pp else "gemm_kernel",
                               "roofline": _roof(tfl, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma")}
         del Ws, W0
     # the stack's down projection at the same batch: 64 tiles over k = 11008,
@@ -769,16 +780,18 @@ def main():
     tfl = pre_flops / (ms["prefill"] * 1e-3) / 1e12
     us_launch = {k: ms[k] * 1e3 / launches[k] for k in ms}
 
-    def roof(kernel, bound, per_launch, unit, peak, achieved):
-        t = traffic_from_profiles(kernel)
+    def roof(kernel, profile, bound, per_launch, unit, peak, achieved):
+        t = traffic_from_profiles(kernel, profile)
         return {"kernel": kernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": t,
                 "algorithmic_per_launch": per_launch, "avg_launch_us": None}
 
-    r_dec = roof("gemv_stream_kernel", "hbm", dec_bytes / launches["decode"], "GB/s", HBM_PEAK_GBS,
+    r_dec = roof("gemv_stream_kernel", "gemv_stream_kernel__llama7b_q4_0_stack_decode.txt", "hbm",
+                 dec_bytes / launches["decode"], "GB/s", HBM_PEAK_GBS,
                  (dec_bytes / launches["decode"]) / (us_launch["decode"] * 1e-6) / 1e9)
     r_dec["avg_launch_us"] = round(us_launch["decode"], 3)
-    r_pre = roof("gemm_pp_kernel", "mfma", pre_flops / launches["prefill"], "TFLOP/s", MFMA_F16_PEAK_TFLOPS,
+    r_pre = roof("gemm_pp_kernel", "gemm_pp_kernel__llama7b_q4_0_stack_prefill.txt", "mfma",
+                 pre_flops / launches["prefill"], "TFLOP/s", MFMA_F16_PEAK_TFLOPS,
                  (pre_flops / launches["prefill"]) / (us_launch["prefill"] * 1e-6) / 1e12)
     r_pre["avg_launch_us"] = round(us_launch["prefill"], 3)
 

@@ -43,8 +43,10 @@ def test_traffic_is_used_only_for_the_profiled_source(tmp_path, monkeypatch):
     (tmp_path / "a.txt").write_text(f"x\nTRAFFIC gemm_kernel bytes_per_launch 12345 source_sha256 {h}\n")
     (tmp_path / "b.txt").write_text("TRAFFIC gemv_stream_kernel bytes_per_launch 99 source_sha256 0000000000000000\n")
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    assert bench.traffic_from_profiles("gemm_kernel") == 12345
-    assert bench.traffic_from_profiles("gemv_stream_kernel") is None
+    assert bench.traffic_from_profiles("gemm_kernel", "a.txt") == 12345
+    assert bench.traffic_from_profiles("gemm_kernel", "b.txt") is None     # only the named profile is read
+    assert bench.traffic_from_profiles("gemv_stream_kernel", "b.txt") is None  # another source's figure
+    assert bench.traffic_from_profiles("gemm_kernel", "missing.txt") is None
 
 
 def test_more_than_one_gpu_is_refused():
