@@ -64,8 +64,10 @@ template <int QT, int NT, int G = 1> struct RCfg {
   // per SIMD: more workgroups per CU overlap one another's loads and
   // compute. Q5_1, whose decode needs more registers, takes 6 wavefronts per
   // SIMD (~85 VGPRs; 4.5 % faster than 4 on 11008 x 4096, and 8 spill).
+  // Q4_K fits too (62 VGPRs at one token): 11008 x 4096 10.0 -> 8.95 us,
+  // 32000 x 4096 22.4 -> 19.6 us against rounds of 4 stages at 4 per SIMD.
   static constexpr bool mid = QTraits<QT>::has_qh && QTraits<QT>::has_min && NT <= 2;
-  static constexpr bool lean = QTraits<QT>::nibbles && !QTraits<QT>::kquant && !mid && NT <= 2;
+  static constexpr bool lean = QTraits<QT>::nibbles && !mid && NT <= 2;
   static constexpr int depth_large = (lean || mid) ? 2 : depth;
   static constexpr int w_lds = 16 * G * row_stride;
   static constexpr int x_lds = 8 * 4 * NT * 16;                      // 8 blocks x 4 lane groups x NT slots x 8 halves
