@@ -1324,18 +1324,18 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
   // and activations whose byte offsets fit 32 bits: the ping-pong kernel.
   // (One round on 172 of 256 CUs still beats the one-group kernel on all of
   // them: 11008 x 4096 at 512 tokens 78.7 -> 65.0 us, 14336 x 4096 80.9 ->
-  // 64.5 us. Q4_K, whose fp32 decode is the longest, measured slower there:
-  // 98.5 against 91.8 us on 4096 x 4096 at 2048 tokens.)
+  // 64.5 us. Q4_K, whose fp32 decode is the longest, takes it too: 4096 x
+  // 4096 at 2048 tokens 105-115 -> 86 us, 11008 x 4096 306 -> 257 us.)
   const int64_t pp_tiles = ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
   const int64_t pp_rounds = cus > 0 ? (pp_tiles + cus - 1) / cus : 0;
-  const bool pp = x_f16 && qtype != QMM_TYPE_Q4_K && cus > 0 && 3 * pp_tiles >= 2 * cus &&
+  const bool pp = x_f16 && cus > 0 && 3 * pp_tiles >= 2 * cus &&
                   (pp_tiles < cus || 4 * pp_tiles >= 3 * pp_rounds * cus) && nblk % 2 == 0 &&
                   pp_tiles <= 0x7FFFFFFF && n_tokens * k * 2 < (int64_t{1} << 32);
   if (pp) {
     const dim3 ppgrid(static_cast<unsigned>(pp_tiles));
     const int prt = static_cast<int>((n_rows + kBM - 1) / kBM);
     const _Float16 *xh = static_cast<const _Float16 *>(X);
-    return by_qtype(qtype, [&](auto qt) {
+    return by_qtype_k(qtype, [&](auto qt) {
       constexpr int QT = decltype(qt)::value;
       auto go = [&](auto kern) {
         return launch(kern, ppgrid, dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, xh, nt, kk, Y, y_vec4, prt,

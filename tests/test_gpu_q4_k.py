@@ -75,6 +75,22 @@ def test_gemm_kernel(xdt, rows, k, n):
     assert_close_to_oracle(run_matmul(W, QK4, k, X, GEMM), W, QK4, k, X, "q4_k gemm")
 
 
+@pytest.mark.parametrize("rows,k,n,extra", [(2000, 512, 4000, 16), (11003, 256, 505, 0), (1500, 1024, 3900, 0)])
+def test_gemm_two_group_tiles(rows, k, n, extra):
+    """fp16 activations with 128 x 256 tiles for at least 2/3 of the CUs:
+    the two-group kernel decodes whole super-blocks per pair of 64-wide
+    stages; every element against the oracle, and bitwise the same as the
+    fp32 copy of the activations on the one-group kernel."""
+    assert ((rows + 127) // 128) * ((n + 255) // 256) in (172, 192, 256)
+    W, rng = _weights(rows, k, extra, seed=3)
+    X = synth.make_activations(n, k, rng, np.float16)
+    say(f"q4_k gemm two-group rows={rows} k={k} n={n} nb1={W.shape[1]}")
+    Y = run_matmul(W, QK4, k, X, GEMM)
+    assert_close_to_oracle(Y, W, QK4, k, X, "q4_k gemm two-group")
+    say("fp32 copy of the activations")
+    assert_bitwise(run_matmul(W, QK4, k, X.astype(np.float32), GEMM), Y, "q4_k one-group vs two-group")
+
+
 def test_zero_scales_and_mins_give_zero():
     rows, k = 64, 512
     W, rng = _weights(rows, k)
