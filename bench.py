@@ -10,12 +10,16 @@ One step = the whole hot path over one batch of synthetic input:
             of Q4_0 blocks are read once per pass, far more than the 256 MB
             Infinity Cache holds.
   prefill - the same 224 weights, each with a 2048-token fp16 ubatch, on the
-            matrix-core (GEMM) kernel, one launch per MUL_MAT.
+            matrix-core (GEMM) kernel, in the same groups through
+            qmm_matmul_batch_ws: the group's MUL_MATs share one two-group
+            launch (q|k|v: 768 tiles, three full rounds on 256 CUs; gate|up:
+            1376 tiles, whose last round of 96 is split in k over the
+            workspace) - 4 launches per layer.
 Each pass is captured once into a HIP graph (its launches are exactly the C
 entry points' launches) and replayed; HIP events on the launch stream time
 every pass. Inputs are resident in HBM before the timed region starts. With
---per-call, the decode pass with one launch per MUL_MAT (qmm_matmul) is timed
-after the steps as well.
+--per-call, the decode and prefill passes with one launch per MUL_MAT
+(qmm_matmul, qmm_matmul_x16) are timed after the steps as well.
 
 Prints ONE JSON line. `value` is the decode pass's achieved HBM bandwidth:
 algorithmic bytes (weight blocks + activations + outputs) per pass / pass
@@ -107,10 +111,11 @@ def parse():
     ap.add_argument("--no-other-types", action="store_true", help="skip the Q8_0 / Q4_1 / Q5_0 / Q5_1 / Q4_K lines")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the decode pass the oracle times")
     ap.add_argument("--per-call", action="store_true",
-                    help="also time the decode pass with one launch per MUL_MAT (qmm_matmul)")
+                    help="also time the decode and prefill passes with one launch per MUL_MAT")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run one plain {COPY_CAL_BYTES >> 20} MiB device copy (for counter calibration)")
-    ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill", "output_projection", "prefill_512",
+    ap.add_argument("--only", choices=("decode", "decode_per_call", "prefill", "prefill_per_call",
+                                       "output_projection", "prefill_512",
                                        "matmul_id"),
                     help="run just this pass (eagerly once, then --steps graph replays) and print no JSON; "
                          "for hardware-counter runs, whose per-dispatch averages must cover one pass only")
@@ -390,7 +395,8 @@ def time_prefill_512(torch, qmm, synth):
     the matrix-core kernel; back-to-back launches in a graph over >= 1.1 GiB
     of weight copies. Flops: 2 * rows * k * tokens. Beside them, the
     4096x11008 down projection at the same batch through qmm_matmul_ws (the
-    k split), with the unsplit launch's time."""
+    k split), with the unsplit launch's time, and a layer's three 4096x4096
+    q, k, v projections in one qmm_matmul_batch call."""
     import numpy as np
     qt, k, T = synth.TYPE_Q4_0, synth.N_EMBD, 512
     rng = np.random.Generator(np.random.PCG64(4500))
@@ -412,6 +418,22 @@ def time_prefill_512(torch, qmm, synth):
                               "TFLOP_per_s": round(tfl, 2), "kernel": "gemm_pp_kernel" if pp else "gemm_kernel",
                               "roofline": _roof(tfl, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma")}
         del Ws, W0
+    # attn_q, attn_k and attn_v of a layer at the same batch in one
+    # qmm_matmul_batch call: 3 x 64 tiles share one two-group launch
+    rows = synth.N_EMBD
+    W0 = torch.from_numpy(synth.make_weights(qt, rows, k, None, rng)).cuda()
+    groups = int(np.ceil(1.1 * 2**30 / (3 * W0.numel())))
+    Ws = [W0] + [W0.clone() for _ in range(3 * groups - 1)]
+    Xs = [torch.from_numpy(synth.make_activations(T, k, rng, np.float16)).cuda() for _ in range(3)]
+    Ys = [torch.empty((T, rows), dtype=torch.float32, device="cuda") for _ in range(3)]
+    items = [[(Ws[3 * g + j], qt, k, Xs[j], Ys[j]) for j in range(3)] for g in range(groups)]
+    us = _graph_time(torch, lambda: [qmm.qmm_matmul_batch(it) for it in items], groups)
+    tfl = 3 * 2 * rows * k * T / (us * 1e-6) / 1e12
+    out[f"3x{rows}x{k}_batched"] = {"tokens": T, "us_per_launch": round(us, 3),
+                                     "flops_per_launch": 3 * 2 * rows * k * T, "TFLOP_per_s": round(tfl, 2),
+                                     "kernel": "gemm_pp_kernel (q|k|v in one qmm_matmul_batch launch)",
+                                     "roofline": _roof(tfl, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma")}
+    del Ws, W0, items
     # the stack's down projection at the same batch: 64 tiles over k = 11008,
     # the shape qmm_matmul_ws splits in k (four parts per tile), against the
     # unsplit launch
@@ -701,15 +723,28 @@ def main():
             c = dec[i]
             qmm.qmm_matmul(W[i], c.qtype, c.k, X1[i], Y=Y1b[i % 7])
 
+    pgroups = [[(W[7 * li + j], pre[7 * li + j].qtype, pre[7 * li + j].k, X2[7 * li + j], Y2[j]) for j in grp]
+               for li in range(layers) for grp in LAYER_GROUPS]
+    ws_bytes = max(qmm.qmm_matmul_batch_workspace_bytes(items) for items in pgroups)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")   # zero before first use
+
     def prefill_pass():
+        for items in pgroups:
+            qmm.qmm_matmul_batch_ws(items, ws)
+
+    Y2b = [torch.empty_like(y) for y in Y2]
+
+    def prefill_per_call_pass():
         for i in range(n):
             c = pre[i]
-            qmm.qmm_matmul_x16(W[i], c.qtype, c.k, X2[i], Y=Y2[i % 7])
+            qmm.qmm_matmul_x16(W[i], c.qtype, c.k, X2[i], Y=Y2b[i % 7])
 
-    passes = {"decode": decode_pass, "decode_per_call": decode_per_call_pass, "prefill": prefill_pass}
-    if not args.per_call and args.only != "decode_per_call":
-        del passes["decode_per_call"]
-    launches = {"decode": len(groups), "decode_per_call": n, "prefill": n}
+    passes = {"decode": decode_pass, "decode_per_call": decode_per_call_pass, "prefill": prefill_pass,
+              "prefill_per_call": prefill_per_call_pass}
+    for extra in ("decode_per_call", "prefill_per_call"):
+        if not args.per_call and args.only != extra:
+            del passes[extra]
+    launches = {"decode": len(groups), "decode_per_call": n, "prefill": len(pgroups), "prefill_per_call": n}
     if args.only:
         f = passes[args.only]
         f()
@@ -725,14 +760,15 @@ def main():
     for f in passes.values():
         f()
     torch.cuda.synchronize()
-    outs = Y1 + (Y1b if "decode_per_call" in passes else []) + Y2
+    outs = Y1 + (Y1b if "decode_per_call" in passes else []) + Y2 + (Y2b if "prefill_per_call" in passes else [])
     refs = [y.clone() for y in outs]
-    if "decode_per_call" in passes:
-        # a batched launch may split k differently from a single call, so the
-        # two agree within rounding, not bitwise
-        for a, b in zip(Y1, Y1b):
-            if not torch.allclose(a, b, rtol=2e-3, atol=1e-4 * float(b.abs().max())):
-                raise RuntimeError("batched and per-call decode outputs differ beyond rounding")
+    # a batched launch may split k differently from a single call, so the
+    # two agree within rounding, not bitwise
+    for name, ya, yb in (("decode", Y1, Y1b), ("prefill", Y2, Y2b)):
+        if f"{name}_per_call" in passes:
+            for a, b in zip(ya, yb):
+                if not torch.allclose(a, b, rtol=2e-3, atol=1e-4 * float(b.abs().max())):
+                    raise RuntimeError(f"batched and per-call {name} outputs differ beyond rounding")
     graphs = {}
     for name, f in passes.items():
         graphs[name] = torch.cuda.CUDAGraph()
@@ -759,15 +795,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     span = {"decode": (0, 1), "prefill": (1, 2)}
-    if "decode_per_call" in graphs:
-        # timed after the steps, outside the step clock
-        for s in range(K):
-            ev[s][3].record()
-            graphs["decode_per_call"].replay()
-            ev[s][4].record()
-        torch.cuda.synchronize()
-        span["decode_per_call"] = (3, 4)
     ms = {name: sorted(ev[s][a].elapsed_time(ev[s][b]) for s in range(K))[K // 2] for name, (a, b) in span.items()}
+    for extra in ("decode_per_call", "prefill_per_call"):
+        if extra in graphs:
+            # timed after the steps, outside the step clock
+            for s in range(K):
+                ev[s][3].record()
+                graphs[extra].replay()
+                ev[s][4].record()
+            torch.cuda.synchronize()
+            ms[extra] = sorted(ev[s][3].elapsed_time(ev[s][4]) for s in range(K))[K // 2]
 
     for a, b in zip(outs, refs):
         if not torch.equal(a, b):
@@ -811,7 +848,8 @@ def main():
         "config": {
             "workload": f"{layers}-layer Llama-7B-shaped Q4_0 stack (per layer q,k,v,o 4096x4096; gate,up "
                         f"11008x4096; down 4096x11008): decode n_tokens=1 fp32 x (4 batched launches per layer) "
-                        f"+ prefill ubatch n_tokens=2048 fp16 x (one launch per MUL_MAT)",
+                        f"+ prefill ubatch n_tokens=2048 fp16 x (4 batched launches per layer, last round "
+                        f"of the gate|up launch split in k)",
             "layers": layers,
             "matmuls_per_pass": n,
             "weight_bytes": sum(c.w_bytes() for c in dec),
@@ -821,7 +859,8 @@ def main():
         "decode": {"ms_per_pass": round(ms["decode"], 4), "launches": launches["decode"],
                    "us_per_launch": round(us_launch["decode"], 3), "GB_per_s": round(gbs, 2),
                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_pass": dec_bytes},
-        "prefill": {"ms_per_pass": round(ms["prefill"], 4), "launches": n,
+        "prefill": {"ms_per_pass": round(ms["prefill"], 4), "launches": launches["prefill"],
+                    "workspace_bytes": ws_bytes,
                     "us_per_launch": round(us_launch["prefill"], 3), "TFLOP_per_s": round(tfl, 2),
                     "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4), "flops_per_pass": pre_flops},
         "roofline": r_dec,
@@ -832,6 +871,12 @@ def main():
         out["decode_per_call"] = {"ms_per_pass": round(ms["decode_per_call"], 4), "launches": n,
                                   "us_per_launch": round(us_launch["decode_per_call"], 3),
                                   "GB_per_s": round(gbs_pc, 2), "frac_of_hbm_peak": round(gbs_pc / HBM_PEAK_GBS, 4)}
+    if "prefill_per_call" in ms:
+        tfl_pc = pre_flops / (ms["prefill_per_call"] * 1e-3) / 1e12
+        out["prefill_per_call"] = {"ms_per_pass": round(ms["prefill_per_call"], 4), "launches": n,
+                                   "us_per_launch": round(us_launch["prefill_per_call"], 3),
+                                   "TFLOP_per_s": round(tfl_pc, 2),
+                                   "frac_of_mfma_f16_peak": round(tfl_pc / MFMA_F16_PEAK_TFLOPS, 4)}
     out["output_projection"] = time_output_projection(torch, qmm, synth)
     out["prefill_512"] = time_prefill_512(torch, qmm, synth)
     if not args.no_get_rows:

@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_path.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, vp]
         L.qmm_dequantize.argtypes = [vp, i32, i64, i64, i64, vp, vp]
         L.qmm_matmul_batch.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp]
+        L.qmm_matmul_batch_ws.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32, vp, i64, vp]
+        L.qmm_matmul_batch_workspace_bytes.argtypes = [ctypes.POINTER(qmm_matmul_desc), i32]
+        L.qmm_matmul_batch_workspace_bytes.restype = i64
         L.qmm_get_rows.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp]
         L.qmm_matmul_id.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp, i64, vp]
         L.qmm_matmul_id_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
@@ -79,7 +82,8 @@ def lib() -> ctypes.CDLL:
         L.qmm_matmul_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
         L.qmm_matmul_workspace_bytes.restype = i64
         for f in ("qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_ws", "qmm_dequantize",
-                  "qmm_matmul_batch", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc"):
+                  "qmm_matmul_batch", "qmm_matmul_batch_ws", "qmm_get_rows", "qmm_matmul_id",
+                  "qmm_matmul_id_noalloc"):
             getattr(L, f).restype = i32
         L.qmm_row_bytes.argtypes = [i32, i64]
         L.qmm_row_bytes.restype = i64
@@ -344,13 +348,7 @@ def qmm_matmul_id_noalloc(W, ggml_type, k, X, ids, n_experts=None, n_rows=None, 
     return Y
 
 
-def qmm_matmul_batch(items, stream=None):
-    """Independent MUL_MATs in one call (C: qmm_matmul_batch).
-
-    items: sequence of (W, ggml_type, k, X, Y) with W a contiguous uint8
-    [rows][nb1] GPU tensor, X a contiguous fp32/fp16 [n_tokens][k] GPU tensor
-    and Y a preallocated fp32 [n_tokens][rows] GPU tensor. Returns the Ys.
-    """
+def _batch_descs(items):
     import torch
     arr = (qmm_matmul_desc * max(1, len(items)))()
     for i, (W, t, k, X, Y) in enumerate(items):
@@ -362,7 +360,42 @@ def qmm_matmul_batch(items, stream=None):
         arr[i] = qmm_matmul_desc(_gpu_ptr(W, "W").value, int(t), rows, int(k), nb1, _gpu_ptr(X, "X").value,
                                  QMM_X_F16 if X.dtype == torch.float16 else QMM_X_F32, int(X.shape[0]),
                                  _gpu_ptr(Y, "Y").value)
-    st = lib().qmm_matmul_batch(arr, len(items), _stream(stream))
+    return arr
+
+
+def qmm_matmul_batch(items, stream=None):
+    """Independent MUL_MATs in one call (C: qmm_matmul_batch).
+
+    items: sequence of (W, ggml_type, k, X, Y) with W a contiguous uint8
+    [rows][nb1] GPU tensor, X a contiguous fp32/fp16 [n_tokens][k] GPU tensor
+    and Y a preallocated fp32 [n_tokens][rows] GPU tensor. Returns the Ys.
+    """
+    st = lib().qmm_matmul_batch(_batch_descs(items), len(items), _stream(stream))
     if st != QMM_OK:
         raise QmmError(st, "qmm_matmul_batch")
+    return [it[4] for it in items]
+
+
+def qmm_matmul_batch_workspace_bytes(items) -> int:
+    """Workspace qmm_matmul_batch_ws needs for these items (C:
+    qmm_matmul_batch_workspace_bytes); items as in qmm_matmul_batch."""
+    n = int(lib().qmm_matmul_batch_workspace_bytes(_batch_descs(items), len(items)))
+    if n < 0:
+        raise QmmError(n, "qmm_matmul_batch_workspace_bytes")
+    return n
+
+
+def qmm_matmul_batch_ws(items, workspace, stream=None):
+    """qmm_matmul_batch with a caller workspace that lets its matrix-core
+    launches split k (C: qmm_matmul_batch_ws). `workspace` is a GPU uint8
+    tensor of at least qmm_matmul_batch_workspace_bytes(items) bytes that held
+    zeros when first used, or None when that size is 0. Returns the Ys."""
+    import torch
+    if workspace is not None:
+        _check_span(workspace, torch.uint8, 0, "workspace")
+    ws = _gpu_ptr(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = lib().qmm_matmul_batch_ws(_batch_descs(items), len(items), ws, ws_bytes, _stream(stream))
+    if st != QMM_OK:
+        raise QmmError(st, "qmm_matmul_batch_ws")
     return [it[4] for it in items]

@@ -660,19 +660,37 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 // counter back to zero for the next call. No workgroup waits for another,
 // and the order of the additions depends only on the shape and the CU
 // count, so results repeat bit for bit.
+// A launch may also run whole tiles before the split ones (t_whole of them,
+// workgroups 0 .. t_whole - 1, the split tiles' workgroups after them): a
+// launch of a few rounds of tiles whose last round would leave at least half
+// of the CUs idle splits only that round's tiles in two, so it takes half a
+// round.
 struct PPSplit {
-  int t_sk;        // tiles
-  int g_sk;        // workgroups (t_sk * parts)
-  int parts;       // parts per tile
+  int t_sk;        // split tiles
+  int g_sk;        // workgroups (t_whole + t_sk * parts)
+  int parts;       // parts per split tile
   int *cnt;        // t_sk counters, zero between calls
   float4_t *part;  // t_sk * parts partial tiles, kPPThreads * 16 float4 each
+  int t_whole;     // tiles run whole, before the split ones
+};
+
+// The MUL_MATs of one launch: up to kPPMaxItems matrices of the same type and
+// shape (rows, k, row stride, tokens), each with its own weights, fp16
+// activations and output. Their row tiles follow one another in the tile
+// order, as the row tiles of one matrix do, so independent MUL_MATs of a
+// layer fill the rounds of a single launch together.
+constexpr int kPPMaxItems = kGemmMaxItems;
+struct PPItems {
+  const uint8_t *W[kPPMaxItems];
+  const _Float16 *X[kPPMaxItems];
+  float *Y[kPPMaxItems];
+  int n;
 };
 
 template <int QT, bool ALIGN4, bool SK>
-__global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *__restrict__ W, int n_rows, int nblk,
-                                                                int64_t nb1, const _Float16 *__restrict__ X,
-                                                                int n_tokens, int k, float *__restrict__ Y,
-                                                                bool y_vec4, int row_tiles, PPSplit sk) {
+__global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(PPItems items, int n_rows, int nblk, int64_t nb1,
+                                                                int n_tokens, int k, bool y_vec4, int row_tiles,
+                                                                PPSplit sk) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds_dynamic[];
   _Float16 *const Wbuf = lds_dynamic;                   // 2 weight stages
   _Float16 *const Xbuf = lds_dynamic + 2 * kPPWHalves;  // kPPXBufs activation stages
@@ -684,17 +702,34 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
   const int n_st = nblk / 2;
 
   // tile order: as gemm_kernel (XCD-contiguous ranges, groups of row tiles)
-  // over the tile's index: the workgroup's, or in the split form the tile's
-  const int n_tiles = SK ? sk.t_sk : static_cast<int>(gridDim.x);
-  const int tok_tiles = n_tiles / row_tiles;
-  auto coords = [&](int bid, int &row0, int &tok0) {
+  // over the tile's index: the workgroup's, or in the split form the tile's;
+  // the row tiles are the items' row tiles one after another
+  const int v_rows = items.n * row_tiles;
+  const int n_tiles = SK ? sk.t_whole + sk.t_sk : static_cast<int>(gridDim.x);
+  const int tok_tiles = n_tiles / v_rows;
+  auto coords = [&](int bid, int &item, int &row0, int &tok0) {
     const int per_xcd = n_tiles / kXcds;
     const int lin = bid < per_xcd * kXcds ? (bid % kXcds) * per_xcd + bid / kXcds : bid;
     const int in_group = kGroupRows * tok_tiles;
     const int first_row = (lin / in_group) * kGroupRows;
-    const int group_rows = min(row_tiles - first_row, kGroupRows);
-    row0 = (first_row + (lin % in_group) % group_rows) * kBM;
+    const int group_rows = min(v_rows - first_row, kGroupRows);
+    const int vr = first_row + (lin % in_group) % group_rows;
+    item = vr / row_tiles;
+    row0 = (vr - item * row_tiles) * kBM;
     tok0 = ((lin % in_group) / group_rows) * kPPBN;
+  };
+  // the item's pointers, selected without indexing the argument array
+  auto item_ptrs = [&](int item, const uint8_t *&w, const _Float16 *&x, float *&y) {
+    w = items.W[0];
+    x = items.X[0];
+    y = items.Y[0];
+#pragma unroll
+    for (int i = 1; i < kPPMaxItems; ++i)
+      if (item == i) {
+        w = items.W[i];
+        x = items.X[i];
+        y = items.Y[i];
+      }
   };
 
   // group 0: row tid / 2, block tid % 2 of the stage's pair
@@ -709,7 +744,7 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
   float4_t acc[4][4];
 
   // Stages [sb, sb + ns) of the tile at (row0, tok0) into acc.
-  auto run = [&](int row0, int tok0, int sb, int ns) {
+  auto run = [&](const uint8_t *W, const _Float16 *X, int row0, int tok0, int sb, int ns) {
     const uint8_t *rp = W + static_cast<int64_t>(min(row0 + srow, n_rows - 1)) * nb1 +
                         static_cast<int64_t>(sb) * (2 * Block<QT>::bytes);
     const int nb = nblk - 2 * sb;  // blocks from rp on
@@ -889,7 +924,7 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
 
   // D element e of lane l in tile (i, j): row 64 wm + 16 i + 4 (l / 16) + e,
   // token 128 g + 64 wn + 16 j + l % 16.
-  auto store_y = [&](int row0, int tok0) {
+  auto store_y = [&](float *Y, int row0, int tok0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tok = tok0 + (kPPBN / 2) * g + 64 * wn + 16 * j + (lane & 15);
@@ -909,17 +944,29 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
     }
   };
 
+  const uint8_t *w;
+  const _Float16 *x;
+  float *y;
   if constexpr (!SK) {
-    int row0, tok0;
-    coords(static_cast<int>(blockIdx.x), row0, tok0);
-    run(row0, tok0, 0, n_st);
-    store_y(row0, tok0);
+    int item, row0, tok0;
+    coords(static_cast<int>(blockIdx.x), item, row0, tok0);
+    item_ptrs(item, w, x, y);
+    run(w, x, row0, tok0, 0, n_st);
+    store_y(y, row0, tok0);
   } else {
-    const int t = static_cast<int>(blockIdx.x) / sk.parts, me = static_cast<int>(blockIdx.x) % sk.parts;
-    const int sb = n_st * me / sk.parts, se = n_st * (me + 1) / sk.parts;
-    int row0, tok0;
-    coords(t, row0, tok0);
-    run(row0, tok0, sb, se - sb);
+    // workgroups past the whole tiles take part `me` of split tile `t`
+    const int b = static_cast<int>(blockIdx.x);
+    const bool whole = b < sk.t_whole;
+    const int t = whole ? b : (b - sk.t_whole) / sk.parts, me = whole ? 0 : (b - sk.t_whole) % sk.parts;
+    const int sb = whole ? 0 : n_st * me / sk.parts, se = whole ? n_st : n_st * (me + 1) / sk.parts;
+    int item, row0, tok0;
+    coords(whole ? t : sk.t_whole + t, item, row0, tok0);
+    item_ptrs(item, w, x, y);
+    run(w, x, row0, tok0, sb, se - sb);
+    if (whole) {
+      store_y(y, row0, tok0);
+      return;
+    }
     // store the part, count it, and if it completes the count, add the parts
     // (with more than two, its own read back too, so the sum needs no second
     // register tile)
@@ -950,7 +997,7 @@ __global__ __launch_bounds__(kPPThreads, 2) void gemm_pp_kernel(const uint8_t *_
         for (int f = 0; f < 16; ++f) acc[f / 4][f % 4] += v[f];
       }
     }
-    store_y(row0, tok0);
+    store_y(y, row0, tok0);
     if (threadIdx.x == 0) __hip_atomic_store(sk.cnt + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1337,8 +1384,9 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
     const _Float16 *xh = static_cast<const _Float16 *>(X);
     return by_qtype_k(qtype, [&](auto qt) {
       constexpr int QT = decltype(qt)::value;
+      const PPItems one{{w}, {xh}, {Y}, 1};
       auto go = [&](auto kern) {
-        return launch(kern, ppgrid, dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, xh, nt, kk, Y, y_vec4, prt,
+        return launch(kern, ppgrid, dim3(kPPThreads), kPPLds, stream, one, nr, nblk, nb1, nt, kk, y_vec4, prt,
                       PPSplit{});
       };
       return align4 ? go(gemm_pp_kernel<QT, true, false>) : go(gemm_pp_kernel<QT, false, false>);
@@ -1361,15 +1409,22 @@ hipError_t launch_gemm(const void *W, int qtype, int64_t n_rows, int64_t k, int6
 }
 
 // The split form of the two-group kernel (PPSplit): fp16 activations, a
-// 32-weight block type, whole stages, and at most half as many 128 x 256
-// tiles as CUs. Each tile is split into P = min(4, CUs / tiles) parts of
-// equal stage ranges (one workgroup each, P * tiles workgroups), each at
-// least kPPMinUnits stages. Measured on the MI355X, a part costs its 128 KiB
-// partial tile twice (stored, then read by the workgroup that adds), and
-// with every CU storing at once that traffic takes several microseconds:
-// more tiles or shorter k (4096 x 4096 or 11008 x 4096 at 512 tokens, the
-// 11008-row launches at 2048 tokens) ran slower split than whole, few tiles
-// with long k (4096 x 14336 at 512 tokens, 4096 x 4096 at 1024) faster.
+// 32-weight block type, whole stages. Two plans:
+//  * few tiles with long k (at most half as many 128 x 256 tiles as CUs):
+//    each tile is split into P = min(4, CUs / tiles) parts of equal stage
+//    ranges (one workgroup each, P * tiles workgroups), each at least
+//    kPPMinUnits stages. Measured on the MI355X, a part costs its 128 KiB
+//    partial tile twice (stored, then read by the workgroup that adds), and
+//    with every CU storing at once that traffic takes several microseconds:
+//    more tiles or shorter k (4096 x 4096 or 11008 x 4096 at 512 tokens)
+//    ran slower split than whole, few tiles with long k (4096 x 14336 at 512
+//    tokens, 4096 x 4096 at 1024) faster.
+//  * more tiles than CUs whose last round would fill at most half of the
+//    CUs: the tiles of whole rounds run whole, the last round's tiles in two
+//    parts each (t_whole whole tiles, then 2 * tail workgroups), so the last
+//    round takes about half the time. A last round fuller than half gains
+//    nothing from two parts (they would need two rounds), and a stream-K
+//    remainder spread over all CUs measured slower (its ranges cross tiles).
 constexpr int kPPMinUnits = 32;
 constexpr int kPPMaxParts = 4;
 constexpr int64_t kPPPartBytes = int64_t{kPPThreads} * 16 * sizeof(float4_t);  // one partial tile (128 KiB)
@@ -1379,47 +1434,104 @@ struct PPPlan {
   int64_t bytes = 0;  // workspace: t_sk counters (256-byte padded), then the partial tiles; 0: no split
 };
 
-static PPPlan pp_split_plan(int qtype, int64_t n_rows, int64_t k, int64_t n_tokens, bool x_f16) {
+static PPPlan pp_split_plan(int qtype, int64_t n_items, int64_t n_rows, int64_t k, int64_t n_tokens, bool x_f16) {
   PPPlan p;
   const int64_t cus = device_cus();
   const int64_t nblk = k / 32;
-  if (!x_f16 || qtype == QMM_TYPE_Q4_K || cus <= 0 || n_rows <= 0 || nblk % 2 != 0 || n_tokens < kPPBN ||
-      n_tokens * k * 2 >= (int64_t{1} << 32))
+  if (!x_f16 || qtype == QMM_TYPE_Q4_K || cus <= 0 || n_rows <= 0 || n_items < 1 || n_items > kPPMaxItems ||
+      nblk % 2 != 0 || n_tokens < kPPBN || n_tokens * k * 2 >= (int64_t{1} << 32))
     return p;
-  const int64_t T = ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
-  const int64_t parts = std::min<int64_t>(kPPMaxParts, cus / T), n_st = nblk / 2;
-  if (parts < 2 || n_st < parts * kPPMinUnits || (T * n_st + 1) * T * parts > 0x7FFFFFFF) return p;
-  p.sk = PPSplit{static_cast<int>(T), static_cast<int>(T * parts), static_cast<int>(parts), nullptr, nullptr};
-  p.bytes = (T * 4 + 255) / 256 * 256 + T * parts * kPPPartBytes;
+  const int64_t T = n_items * ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
+  const int64_t n_st = nblk / 2;
+  int64_t t_whole = 0, t_sk = 0, parts = 0;
+  if (2 * T <= cus) {
+    t_sk = T;
+    parts = std::min<int64_t>(kPPMaxParts, cus / T);
+    if (n_st < parts * kPPMinUnits) return p;
+  } else {
+    const int64_t tail = T % cus, rounds = (T + cus - 1) / cus;
+    // the whole rounds must be ones the two-group kernel takes (launch_gemm's rule)
+    if (T <= cus || tail == 0 || 2 * tail > cus || n_st < 2 * kPPMinUnits || 4 * T < 3 * rounds * cus) return p;
+    t_whole = T - tail;
+    t_sk = tail;
+    parts = 2;
+  }
+  const int64_t groups = t_whole + t_sk * parts;
+  if (groups > 0x7FFFFFFF || (t_sk * n_st + 1) * t_sk * parts > 0x7FFFFFFF) return p;
+  p.sk = PPSplit{static_cast<int>(t_sk), static_cast<int>(groups), static_cast<int>(parts), nullptr, nullptr,
+                 static_cast<int>(t_whole)};
+  p.bytes = (t_sk * 4 + 255) / 256 * 256 + t_sk * parts * kPPPartBytes;
   return p;
 }
 
 int64_t gemm_split_bytes(int qtype, int64_t n_rows, int64_t k, int64_t n_tokens, bool x_f16) {
-  return pp_split_plan(qtype, n_rows, k, n_tokens, x_f16).bytes;
+  return pp_split_plan(qtype, 1, n_rows, k, n_tokens, x_f16).bytes;
+}
+
+int64_t gemm_items_split_bytes(int qtype, int n_items, int64_t n_rows, int64_t k, int64_t n_tokens) {
+  return pp_split_plan(qtype, n_items, n_rows, k, n_tokens, true).bytes;
+}
+
+bool gemm_items_merge(int qtype, int n_items, int64_t n_rows, int64_t k, int64_t n_tokens) {
+  if (n_items < 2 || n_items > kPPMaxItems || n_rows <= 0 || n_tokens <= 0) return false;
+  if (pp_split_plan(qtype, n_items, n_rows, k, n_tokens, true).bytes > 0) return true;
+  // whole tiles only: the two-group kernel's rule on the launch's tiles
+  const int64_t cus = device_cus(), nblk = k / 32;
+  const int64_t T = n_items * ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
+  const int64_t rounds = cus > 0 ? (T + cus - 1) / cus : 0;
+  return cus > 0 && 3 * T >= 2 * cus && (T < cus || 4 * T >= 3 * rounds * cus) && nblk % 2 == 0 &&
+         T <= 0x7FFFFFFF && n_tokens * k * 2 < (int64_t{1} << 32);
+}
+
+hipError_t launch_gemm_items(const void *const *W, int qtype, int n_items, int64_t n_rows, int64_t k, int64_t nb1,
+                             const _Float16 *const *X, int64_t n_tokens, float *const *Y, void *workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+  if (n_items < 1 || n_items > kPPMaxItems) return hipErrorInvalidValue;
+  PPPlan p = pp_split_plan(qtype, n_items, n_rows, k, n_tokens, true);
+  const bool split = p.bytes > 0 && workspace != nullptr && workspace_bytes >= p.bytes;
+  PPItems items{};
+  bool align4 = nb1 % 4 == 0, y_vec4 = n_rows % 4 == 0;
+  for (int i = 0; i < n_items; ++i) {
+    items.W[i] = static_cast<const uint8_t *>(W[i]);
+    items.X[i] = X[i];
+    items.Y[i] = Y[i];
+    align4 = align4 && reinterpret_cast<uintptr_t>(W[i]) % 4 == 0;
+    y_vec4 = y_vec4 && reinterpret_cast<uintptr_t>(Y[i]) % 16 == 0;
+  }
+  items.n = n_items;
+  const int64_t T = n_items * ((n_rows + kBM - 1) / kBM) * ((n_tokens + kPPBN - 1) / kPPBN);
+  if (T > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (split) {
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    p.sk.cnt = reinterpret_cast<int *>(ws);
+    p.sk.part = reinterpret_cast<float4_t *>(ws + (static_cast<int64_t>(p.sk.t_sk) * 4 + 255) / 256 * 256);
+  }
+  const int prt = static_cast<int>((n_rows + kBM - 1) / kBM);
+  const int nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows), nt = static_cast<int>(n_tokens),
+            kk = static_cast<int>(k);
+  const dim3 grid(static_cast<unsigned>(split ? p.sk.g_sk : T));
+  return by_qtype_k(qtype, [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    auto go = [&](auto kern, const PPSplit &sk) {
+      return launch(kern, grid, dim3(kPPThreads), kPPLds, stream, items, nr, nblk, nb1, nt, kk, y_vec4, prt, sk);
+    };
+    if constexpr (QT != QMM_TYPE_Q4_K) {
+      if (split)
+        return align4 ? go(gemm_pp_kernel<QT, true, true>, p.sk) : go(gemm_pp_kernel<QT, false, true>, p.sk);
+    }
+    return align4 ? go(gemm_pp_kernel<QT, true, false>, PPSplit{}) : go(gemm_pp_kernel<QT, false, false>, PPSplit{});
+  });
 }
 
 hipError_t launch_gemm_split(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const _Float16 *X,
                              int64_t n_tokens, float *Y, void *workspace, int64_t workspace_bytes,
                              hipStream_t stream) {
-  PPPlan p = pp_split_plan(qtype, n_rows, k, n_tokens, true);
+  const PPPlan p = pp_split_plan(qtype, 1, n_rows, k, n_tokens, true);
   if (p.bytes == 0 || workspace == nullptr || workspace_bytes < p.bytes) return hipErrorInvalidValue;
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  p.sk.cnt = reinterpret_cast<int *>(ws);
-  p.sk.part = reinterpret_cast<float4_t *>(ws + (static_cast<int64_t>(p.sk.t_sk) * 4 + 255) / 256 * 256);
-  const uint8_t *w = static_cast<const uint8_t *>(W);
-  const bool align4 = (reinterpret_cast<uintptr_t>(W) % 4 == 0) && (nb1 % 4 == 0);
-  const bool y_vec4 = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && (n_rows % 4 == 0);
-  const int prt = static_cast<int>((n_rows + kBM - 1) / kBM);
-  const int nblk = static_cast<int>(k / 32), nr = static_cast<int>(n_rows), nt = static_cast<int>(n_tokens),
-            kk = static_cast<int>(k);
-  return by_qtype(qtype, [&](auto qt) {
-    constexpr int QT = decltype(qt)::value;
-    auto go = [&](auto kern) {
-      return launch(kern, dim3(static_cast<unsigned>(p.sk.g_sk)), dim3(kPPThreads), kPPLds, stream, w, nr, nblk, nb1, X,
-                    nt, kk, Y, y_vec4, prt, p.sk);
-    };
-    return align4 ? go(gemm_pp_kernel<QT, true, true>) : go(gemm_pp_kernel<QT, false, true>);
-  });
+  const void *w[1] = {W};
+  const _Float16 *x[1] = {X};
+  float *y[1] = {Y};
+  return launch_gemm_items(w, qtype, 1, n_rows, k, nb1, x, n_tokens, y, workspace, workspace_bytes, stream);
 }
 
 }  // namespace qmm

@@ -117,5 +117,19 @@ int64_t gemm_split_bytes(int qtype, int64_t n_rows, int64_t k, int64_t n_tokens,
 hipError_t launch_gemm_split(const void *W, int qtype, int64_t n_rows, int64_t k, int64_t nb1, const _Float16 *X,
                              int64_t n_tokens, float *Y, void *workspace, int64_t workspace_bytes,
                              hipStream_t stream);
+// Up to kGemmMaxItems MUL_MATs of one type and shape (rows, k, row stride,
+// tokens; fp16 activations) in one two-group launch, their row tiles one
+// after another. gemm_items_merge: the launch is worth making (its tiles
+// suit the two-group kernel, or its last round splits).
+// gemm_items_split_bytes: the workspace that lets the launch split its last
+// round's tiles in k (0 if it does not). launch_gemm_items splits only with a
+// workspace of at least that size; whole tiles give the same bits as the
+// MUL_MATs launched one by one.
+constexpr int kGemmMaxItems = 4;
+bool gemm_items_merge(int qtype, int n_items, int64_t n_rows, int64_t k, int64_t n_tokens);
+int64_t gemm_items_split_bytes(int qtype, int n_items, int64_t n_rows, int64_t k, int64_t n_tokens);
+hipError_t launch_gemm_items(const void *const *W, int qtype, int n_items, int64_t n_rows, int64_t k, int64_t nb1,
+                             const _Float16 *const *X, int64_t n_tokens, float *const *Y, void *workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
 
 }  // namespace qmm

@@ -15,6 +15,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -228,34 +229,146 @@ int qmm_matmul_ws(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64
                                           n_tokens, Y, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
-int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream) {
+namespace {
+
+// The many-token MUL_MATs of a batch that can share one two-group launch:
+// fp16 activations, the same type, rows, k, row stride and tokens, at most
+// qmm::kGemmMaxItems of them, in the order of their first descriptor.
+struct GemmGroup {
+  std::vector<int> idx;
+};
+
+std::vector<GemmGroup> gemm_groups(const qmm_matmul_desc *descs, int count) {
+  std::vector<GemmGroup> groups;
+  for (int i = 0; i < count; ++i) {
+    const qmm_matmul_desc &d = descs[i];
+    if (d.n_rows == 0 || d.n_tokens <= QMM_GEMV_MAX_TOKENS) continue;
+    GemmGroup *to = nullptr;
+    if (d.x_type == QMM_X_F16)
+      for (GemmGroup &g : groups) {
+        const qmm_matmul_desc &f = descs[g.idx[0]];
+        if (f.x_type == QMM_X_F16 && f.ggml_type == d.ggml_type && f.n_rows == d.n_rows && f.k == d.k &&
+            f.row_stride_bytes == d.row_stride_bytes && f.n_tokens == d.n_tokens &&
+            static_cast<int>(g.idx.size()) < qmm::kGemmMaxItems) {
+          to = &g;
+          break;
+        }
+      }
+    if (to == nullptr) {
+      groups.emplace_back();
+      to = &groups.back();
+    }
+    to->idx.push_back(i);
+  }
+  return groups;
+}
+
+// Workspace of a group: its merged launch's split, or that of qmm_matmul_ws
+// for a lone fp16 MUL_MAT.
+int64_t group_bytes(const qmm_matmul_desc *descs, const GemmGroup &g) {
+  const qmm_matmul_desc &d = descs[g.idx[0]];
+  const int n = static_cast<int>(g.idx.size());
+  if (n > 1 && qmm::gemm_items_merge(d.ggml_type, n, d.n_rows, d.k, d.n_tokens))
+    return qmm::gemm_items_split_bytes(d.ggml_type, n, d.n_rows, d.k, d.n_tokens);
+  int64_t most = 0;
+  for (int i : g.idx) {
+    const qmm_matmul_desc &e = descs[i];
+    if (e.x_type == QMM_X_F16) most = std::max(most, qmm::gemm_split_bytes(e.ggml_type, e.n_rows, e.k, e.n_tokens, true));
+  }
+  return most;
+}
+
+int check_batch(const qmm_matmul_desc *descs, int count) {
   if (count < 0) return QMM_ERR_SHAPE;
-  if (count == 0) return QMM_OK;
-  if (descs == nullptr) return QMM_ERR_NULL;
+  if (count > 0 && descs == nullptr) return QMM_ERR_NULL;
   for (int i = 0; i < count; ++i) {
     const qmm_matmul_desc &d = descs[i];
     const int st = check_matmul(d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X, d.x_type, d.n_tokens, d.Y,
                                 QMM_PATH_AUTO);
     if (st != QMM_OK) return st;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return QMM_OK;
+}
+
+// The batch after validation; with a workspace (of at least the batch's
+// size), many-token launches split as qmm_matmul_ws does.
+int run_batch(const qmm_matmul_desc *descs, int count, void *workspace, int64_t workspace_bytes, hipStream_t s) {
   std::vector<qmm::MatmulDesc> gemv;
   gemv.reserve(count);
   for (int i = 0; i < count; ++i) {
     const qmm_matmul_desc &d = descs[i];
-    if (d.n_rows == 0 || d.n_tokens == 0) continue;
-    const bool x_f16 = d.x_type == QMM_X_F16;
-    if (d.n_tokens <= QMM_GEMV_MAX_TOKENS) {
-      gemv.push_back(qmm::MatmulDesc{d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X, x_f16, d.n_tokens, d.Y});
-    } else {
-      const hipError_t e =
-          qmm::launch_gemm(d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X, x_f16, d.n_tokens, d.Y, s);
-      if (e != hipSuccess) return QMM_ERR_HIP;
+    if (d.n_rows == 0 || d.n_tokens == 0 || d.n_tokens > QMM_GEMV_MAX_TOKENS) continue;
+    gemv.push_back(qmm::MatmulDesc{d.W, d.ggml_type, d.n_rows, d.k, d.row_stride_bytes, d.X,
+                                   d.x_type == QMM_X_F16, d.n_tokens, d.Y});
+  }
+  int merged = 0;
+  for (const GemmGroup &g : gemm_groups(descs, count)) {
+    const qmm_matmul_desc &d = descs[g.idx[0]];
+    const int n = static_cast<int>(g.idx.size());
+    if (n > 1 && qmm::gemm_items_merge(d.ggml_type, n, d.n_rows, d.k, d.n_tokens)) {
+      const void *w[qmm::kGemmMaxItems];
+      const _Float16 *x[qmm::kGemmMaxItems];
+      float *y[qmm::kGemmMaxItems];
+      for (int j = 0; j < n; ++j) {
+        w[j] = descs[g.idx[j]].W;
+        x[j] = static_cast<const _Float16 *>(descs[g.idx[j]].X);
+        y[j] = descs[g.idx[j]].Y;
+      }
+      if (trace_on())
+        fprintf(stderr, "qmm: gemm of %d %s rows=%lld k=%lld tokens=%lld in one launch%s\n", n, type_name(d.ggml_type),
+                (long long)d.n_rows, (long long)d.k, (long long)d.n_tokens,
+                workspace != nullptr && qmm::gemm_items_split_bytes(d.ggml_type, n, d.n_rows, d.k, d.n_tokens) > 0
+                    ? ", last round split"
+                    : "");
+      if (qmm::launch_gemm_items(w, d.ggml_type, n, d.n_rows, d.k, d.row_stride_bytes, x, d.n_tokens, y, workspace,
+                                 workspace_bytes, s) != hipSuccess)
+        return QMM_ERR_HIP;
+      ++merged;
+      continue;
+    }
+    for (int i : g.idx) {
+      const qmm_matmul_desc &e = descs[i];
+      const bool x_f16 = e.x_type == QMM_X_F16;
+      hipError_t err;
+      if (workspace != nullptr && x_f16 && qmm::gemm_split_bytes(e.ggml_type, e.n_rows, e.k, e.n_tokens, true) > 0)
+        err = qmm::launch_gemm_split(e.W, e.ggml_type, e.n_rows, e.k, e.row_stride_bytes,
+                                     static_cast<const _Float16 *>(e.X), e.n_tokens, e.Y, workspace, workspace_bytes, s);
+      else
+        err = qmm::launch_gemm(e.W, e.ggml_type, e.n_rows, e.k, e.row_stride_bytes, e.X, x_f16, e.n_tokens, e.Y, s);
+      if (err != hipSuccess) return QMM_ERR_HIP;
     }
   }
-  if (trace_on()) fprintf(stderr, "qmm: batch of %d (%zu decode-sized)\n", count, gemv.size());
+  if (trace_on()) fprintf(stderr, "qmm: batch of %d (%zu decode-sized, %d merged gemm launches)\n", count, gemv.size(), merged);
   if (gemv.empty()) return QMM_OK;
   return status_of(qmm::launch_gemv_batch(gemv.data(), static_cast<int>(gemv.size()), s));
+}
+
+}  // namespace
+
+int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream) {
+  const int st = check_batch(descs, count);
+  if (st != QMM_OK || count == 0) return st;
+  return run_batch(descs, count, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+int64_t qmm_matmul_batch_workspace_bytes(const qmm_matmul_desc *descs, int count) {
+  const int st = check_batch(descs, count);
+  if (st != QMM_OK) return st;
+  int64_t most = 0;
+  for (const GemmGroup &g : gemm_groups(descs, count)) most = std::max(most, group_bytes(descs, g));
+  return most;
+}
+
+int qmm_matmul_batch_ws(const qmm_matmul_desc *descs, int count, void *workspace, int64_t workspace_bytes,
+                        void *stream) {
+  const int64_t need = qmm_matmul_batch_workspace_bytes(descs, count);
+  if (need < 0) return static_cast<int>(need);
+  if (count == 0) return QMM_OK;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return QMM_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+  }
+  return run_batch(descs, count, need > 0 ? workspace : nullptr, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int qmm_dequantize(const void *W, int ggml_type, int64_t n_rows, int64_t k, int64_t row_stride_bytes, float *out,

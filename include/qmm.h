@@ -179,11 +179,13 @@ int qmm_matmul_path(const void *W, int ggml_type, int64_t n_rows, int64_t k, int
  * shape on the current device: 0 when the call runs as qmm_matmul_path with
  * QMM_PATH_AUTO, otherwise the bytes of its k split (counters and one
  * 128 KiB partial tile per part). The split is taken by fp16 activations of
- * at least 256 tokens, a 32-weight block type and an even block count, when
- * the 128-row x 256-token tiles number at most half the compute units and k
- * is long enough for 2 to 4 parts per tile of at least 32 stages of 64
- * (k >= 4096 for 2 parts); every other shape returns 0. Negative status for
- * invalid sizes or types.
+ * at least 256 tokens, a 32-weight block type and an even block count, in
+ * two cases: (1) the 128-row x 256-token tiles number at most half the
+ * compute units and k is long enough for 2 to 4 parts per tile of at least
+ * 32 stages of 64 (k >= 4096 for 2 parts); (2) the tiles number more than
+ * the compute units and the last of their rounds would occupy at most half
+ * of them (k >= 4096): that round's tiles run in 2 parts, the others whole.
+ * Every other shape returns 0. Negative status for invalid sizes or types.
  */
 int64_t qmm_matmul_workspace_bytes(int ggml_type, int64_t n_rows, int64_t k, int64_t n_tokens, int x_type);
 
@@ -193,9 +195,10 @@ int64_t qmm_matmul_workspace_bytes(int ggml_type, int64_t n_rows, int64_t k, int
  * matrix-core kernel split k across workgroups where its tiles would leave
  * most compute units idle: few output tiles with a long k (e.g. a 4096-row
  * projection over k = 14336 at the 512-token batch of [Load] section
- * 第六步). Each tile is summed as 2 to 4 partial sums over equal k ranges,
- * added in k order by the workgroup that finishes last; no workgroup waits
- * for another.
+ * 第六步), or a last round of tiles that would leave half of them idle. A
+ * split tile is summed as 2 to 4 partial sums over equal k ranges, added in
+ * k order by the workgroup that finishes last; no workgroup waits for
+ * another.
  *   W ... stream   as in qmm_matmul_path (x_type QMM_X_F32 or QMM_X_F16)
  *   workspace      device pointer, 16-byte aligned, at least
  *                  qmm_matmul_workspace_bytes(...) bytes, caller-owned; may
@@ -235,17 +238,56 @@ typedef struct qmm_matmul_desc {
  * ([Bind] section 3.2: a layer's attn_q/k/v, or ffn_gate and ffn_up); the
  * decode-sized ones (n_tokens <= QMM_GEMV_MAX_TOKENS) with 16-byte-aligned
  * layouts are grouped into shared launches, which removes the per-launch
- * fixed cost that dominates small decode matmuls. `descs` is a host array
+ * fixed cost that dominates small decode matmuls. Many-token ones with fp16
+ * activations and the same type, rows, k, row stride and token count (up to
+ * 4 together) share one matrix-core launch where its tiles suit the
+ * two-group kernel, so the MUL_MATs fill its rounds together. `descs` is a host array
  * read only during the call. Every descriptor is validated before anything is
  * launched; on failure the status of the first invalid descriptor is
  * returned and nothing is enqueued. Outputs must not overlap any input or
  * each other. Results are reproducible for a given batch; a MUL_MAT in a batch
  * may differ in its last bits from the same MUL_MAT called alone, because the
- * decode kernel splits k according to the size of its launch (both are within
- * the stated error bound). count == 0 is a no-op; count < 0 or descs == NULL with
- * count > 0 returns QMM_ERR_NULL / QMM_ERR_SHAPE.
+ * decode kernel splits k according to the size of its launch, and a shared
+ * matrix-core launch may take the two-group kernel where a lone call takes
+ * the one-group kernel with its k split inside the workgroup (both are
+ * within the stated error bound). count == 0 is a no-op; count < 0 or
+ * descs == NULL with count > 0 returns QMM_ERR_SHAPE / QMM_ERR_NULL.
  */
 int qmm_matmul_batch(const qmm_matmul_desc *descs, int count, void *stream);
+
+/*
+ * qmm_matmul_batch_workspace_bytes - device workspace qmm_matmul_batch_ws
+ * needs for these descriptors on the current device: the largest k split
+ * of its matrix-core launches (as qmm_matmul_workspace_bytes, over the
+ * tiles of a shared launch), 0 if none splits. Negative status for an
+ * invalid descriptor (as qmm_matmul_batch).
+ */
+int64_t qmm_matmul_batch_workspace_bytes(const qmm_matmul_desc *descs, int count);
+
+/*
+ * qmm_matmul_batch_ws - qmm_matmul_batch with a caller workspace that lets
+ * its matrix-core launches split k as qmm_matmul_ws does ([Bind] section
+ * 3.2 for the independent MUL_MATs of a layer; [Bind] section 2.3 for each
+ * one). For ffn_gate and ffn_up of 11008 x 4096 at 2048 tokens, the shared
+ * launch has 1376 tiles: five full rounds on 256 compute units and a sixth
+ * of 96 tiles, which run in two halves of k on 192 of them.
+ *   descs, count, stream  as in qmm_matmul_batch
+ *   workspace      device pointer, 16-byte aligned, at least
+ *                  qmm_matmul_batch_workspace_bytes(descs, count) bytes,
+ *                  caller-owned, zero when first used, left at zero by every
+ *                  call (as for qmm_matmul_ws); may be NULL when that is 0.
+ *                  The launches of one call run in order on the stream and
+ *                  share it. Calls that may run at the same time need
+ *                  workspaces of their own.
+ *   workspace_bytes its size
+ * Returns QMM_ERR_WORKSPACE if the workspace is NULL or too small where one
+ * is needed, QMM_ERR_ALIGN if it is misaligned, else as qmm_matmul_batch.
+ * Results repeat bit for bit for given descriptors on a given device; split
+ * tiles may differ in their last bits from qmm_matmul_batch's, within the
+ * same error bound.
+ */
+int qmm_matmul_batch_ws(const qmm_matmul_desc *descs, int count, void *workspace, int64_t workspace_bytes,
+                        void *stream);
 
 /*
  * qmm_dequantize - the block decoder alone ([Bind] section 2.3 layout,

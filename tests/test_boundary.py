@@ -36,6 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["qmm_matmul", "qmm_matmul_x16", "qmm_matmul_path", "qmm_matmul_batch",
+                            "qmm_matmul_batch_ws", "qmm_matmul_batch_workspace_bytes",
                             "qmm_matmul_ws", "qmm_matmul_workspace_bytes",
                             "qmm_dequantize", "qmm_get_rows", "qmm_matmul_id", "qmm_matmul_id_noalloc",
                             "qmm_matmul_id_workspace_bytes", "qmm_matmul_id_workspace_bytes_x16", "qmm_row_bytes",
@@ -324,3 +325,23 @@ def test_batch_validation(L):
     assert L.qmm_matmul_batch((D * 1)(bad_x), 1, NULL) == qmm.QMM_ERR_TYPE
     nullw = D(0, Q4, 16, 64, 36, 0x20000, qmm.QMM_X_F32, 1, 0x30000)
     assert L.qmm_matmul_batch((D * 2)(ok, nullw), 2, NULL) == qmm.QMM_ERR_NULL
+
+
+def test_batch_ws_validation(L):
+    """The workspace form validates as the plain batch does, sizes no
+    workspace for decode-sized, empty or fp32 descriptors, and checks the
+    workspace only where one is needed."""
+    D = qmm.qmm_matmul_desc
+    empty = D(0x10000, Q4, 16, 64, 36, 0x20000, qmm.QMM_X_F16, 0, 0x30000)
+    decode = D(0x10000, Q4, 4096, 4096, 2304, 0x20000, qmm.QMM_X_F32, 1, 0x30000)
+    f32 = D(0x10000, Q4, 4096, 4096, 2304, 0x20000, qmm.QMM_X_F32, 2048, 0x30000)
+    bad_stride = D(0x10000, Q4, 16, 64, 35, 0x20000, qmm.QMM_X_F16, 600, 0x30000)
+    wb, bw = L.qmm_matmul_batch_workspace_bytes, L.qmm_matmul_batch_ws
+    assert wb((D * 3)(empty, decode, f32), 3) == 0
+    assert wb(None, 0) == 0 and wb(None, 1) == qmm.QMM_ERR_NULL and wb((D * 1)(empty), -1) == qmm.QMM_ERR_SHAPE
+    assert wb((D * 2)(empty, bad_stride), 2) == qmm.QMM_ERR_STRIDE
+    assert bw((D * 2)(empty, bad_stride), 2, NULL, 0, NULL) == qmm.QMM_ERR_STRIDE
+    assert bw((D * 2)(empty, empty), 2, NULL, 0, NULL) == qmm.QMM_OK        # nothing to launch
+    assert bw((D * 1)(empty), 1, ctypes.c_void_p(0x50001), -5, NULL) == qmm.QMM_OK  # unused workspace not checked
+    assert bw(None, 0, NULL, 0, NULL) == qmm.QMM_OK
+    assert bw(None, 2, NULL, 0, NULL) == qmm.QMM_ERR_NULL

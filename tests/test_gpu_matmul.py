@@ -339,6 +339,42 @@ def test_config5_decode_batched_as_benchmarked():
                 assert O.within_tolerance(it[4].cpu().numpy()[0, rows], y_ref, s).all(), c.name
 
 
+def test_config5_prefill_batched_as_benchmarked():
+    """Layer 0 of the stack at 2048 fp16 tokens through qmm_matmul_batch_ws in
+    the benchmark's launch groups (q+k+v in one two-group launch, o, gate+up
+    in one launch whose last round is split in k, down), sampled outputs of
+    every tensor against the oracle, with one workspace for all groups."""
+    import torch
+    import bench
+    from gpu_util import dev
+    cases = {c.tensor: c for c in synth.stack_cases(2048, layers=1)}
+    groups = []
+    for grp in bench.LAYER_GROUPS:
+        items, host = [], []
+        for t in grp:
+            c = cases[t]
+            W, X = c.weights(), c.activations()
+            items.append((dev(W), c.qtype, c.k, dev(X),
+                          torch.full((c.n_tokens, c.rows), float("nan"), dtype=torch.float32, device="cuda")))
+            host.append((c, W, X))
+        groups.append((grp, items, host))
+    need = max(qmm.qmm_matmul_batch_workspace_bytes(items) for _, items, _ in groups)
+    assert need > 0, "the gate+up launch should split its last round"
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for grp, items, host in groups:
+        say(f"prefill batch layer 0 tensors {grp}")
+        qmm.qmm_matmul_batch_ws(items, ws)
+        torch.cuda.synchronize()
+        for (c, W, X), it in zip(host, items):
+            rng = np.random.default_rng(2000 + c.tensor)
+            rows = np.concatenate([[0, 127, 128, c.rows - 1], rng.integers(0, c.rows, 3000)])
+            toks = np.concatenate([[0, 255, 256, c.n_tokens - 1], rng.integers(0, c.n_tokens, 3000)])
+            y_ref, s = O.matmul_sampled(W, c.qtype, c.rows, c.k, c.nb1, X, toks, rows)
+            assert O.within_tolerance(it[4].cpu().numpy()[toks, rows], y_ref, s).all(), c.name
+    tail = 2 * 86 * 8 % torch.cuda.get_device_properties(0).multi_processor_count   # gate+up: 1376 tiles
+    assert torch.count_nonzero(ws[:4 * tail]).item() == 0, "split counters not back at zero"
+
+
 # ------------------------------------------------------------ batched calls and graph replay
 def _batch_specs():
     # (type, rows, k, n_tokens, x dtype): streaming-eligible, general-kernel and matrix-core entries,
