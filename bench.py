@@ -79,6 +79,10 @@ KERNELS = {
 # gemm_pp_kernel that flag marks the k-split form, kept apart the same way).
 KERNEL_TARGS = {"gemv_stream_kernel": 4, "gemv_tall_kernel": 3, "gemm_kernel": 3, "gemm_pp_kernel": 2,
                 "gemm_pp_routed_kernel": 2}
+# Kernels whose extra flag marks a k-split form of the same MUL_MAT rather
+# than MUL_MAT_ID: their traffic counts every form (the stack's prefill pass
+# launches both), and trace summaries list the forms apart and together.
+SPLIT_FORM = {"gemm_pp_kernel"}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -194,9 +198,15 @@ def summarize_trace(d):
             if m:
                 groups.setdefault((int(m.group(1)), _routed(k, kern)), []).extend(xs)
         for (qt, routed), v in sorted(groups.items()):
-            tag = " routed" if routed else ""
+            tag = (" split" if kern in SPLIT_FORM else " routed") if routed else ""
             print(f"ALL {kern} type {qt}{tag}: calls {len(v)} avg_us {statistics.mean(v):.3f} "
                   f"source_sha256 {source_hash(kern)}")
+        if kern in SPLIT_FORM:
+            for qt in sorted({q for q, _ in groups}):
+                if (qt, False) in groups and (qt, True) in groups:
+                    v = groups[(qt, False)] + groups[(qt, True)]
+                    print(f"ALL {kern} type {qt} every form: calls {len(v)} avg_us {statistics.mean(v):.3f} "
+                          f"source_sha256 {source_hash(kern)}")
 
 
 def summarize_counters(dirs):
@@ -227,7 +237,8 @@ def summarize_counters(dirs):
     for kern in KERNELS:
         total = 0.0
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-            v = [x for (k, c), xs in agg.items() if kern in k and not _routed(k, kern) and c == cn for x in xs]
+            v = [x for (k, c), xs in agg.items()
+                 if kern in k and (kern in SPLIT_FORM or not _routed(k, kern)) and c == cn for x in xs]
             if not v or cn not in factor:
                 total = None
                 break
@@ -345,7 +356,7 @@ def time_type(torch, qmm, synth, qt, with_oracle=False):
                       "kernel": "gemv_stream_kernel", "bound": "hbm"},
            "prefill": {"tokens": T, "us_per_launch": round(us2, 3), "TFLOP_per_s": round(tfl, 2),
                        "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
-                       "kernel": "gemm_kernel" if qt == synth.TYPE_Q4_K else "gemm_pp_kernel", "bound": "mfma"}}
+                       "kernel": "gemm_pp_kernel", "bound": "mfma"}}
     if with_oracle:
         import oracle.qmm_oracle as O
         t0 = time.perf_counter()
